@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of the fused in-place QK RMSNorm + RoPE (HIP, gfx950).
+
+A step is one launch of the op over one batch: every Q/K head vector of the
+workload normalised and rotated in place. Default workload: the DiT-shaped
+image+text sequence (T=4608 tokens, 24+24 heads, head_dim 128, interleaved
+pairing, bf16, int64 positions). The metric is achieved HBM bandwidth in
+algorithmic bytes (every Q/K element read and written once, one positions entry
+and one fp32 cos|sin row per token, both weight rows) per second.
+
+Inputs are resident in HBM before timing. The timed loop cycles through enough
+independent copies of the mutable buffers (>= 1 GiB in total) that the 256 MB
+Infinity Cache cannot serve a launch from the previous visit of its copy.
+
+Prints ONE JSON line. Extra per-configuration / sweep lines go to --extra-out.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+ROT_BYTES = 1 << 30    # rotate through >= 1 GiB of copies
+KERNEL_SRC = os.path.join(ROOT, "head_qk_rmsnorm_amd", "csrc", "qknr.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", default="dit", help="tiny | dit | gqa | partial | large")
+    ap.add_argument("--launch", default="", help="JSON launch configuration (qknr_launch_cfg fields)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle timing budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-yardstick", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="time a grid of launch configurations")
+    ap.add_argument("--all-configs", action="store_true", help="also time every workload")
+    ap.add_argument("--extra-out", default="", help="file for per-config / sweep JSON lines")
+    return ap.parse_args()
+
+
+class Rig:
+    """Device copies of one workload and prepared launches over them."""
+
+    def __init__(self, cfg, dev, launch=None, n_rot=None):
+        import numpy as np
+        import torch
+
+        from head_qk_rmsnorm_amd import binding as B
+        from head_qk_rmsnorm_amd import workloads as W
+
+        self.cfg = cfg
+        wl = W.make_workload(cfg)
+        tdt = torch.bfloat16 if cfg.dtype == W.BF16 else torch.float16
+
+        def d16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(tdt)
+
+        wq, wk = d16(wl.wq), d16(wl.wk)
+        cache = torch.from_numpy(wl.cache).to(dev)
+        pos0 = torch.from_numpy(wl.positions).to(dev)
+        D = cfg.head_dim
+        if cfg.layout == "qkv":
+            base = [d16(wl.qkv)]
+        else:
+            base = [d16(wl.q), d16(wl.k)]
+        footprint = sum(t.numel() * t.element_size() for t in base) + pos0.numel() * pos0.element_size()
+        self.n_rot = n_rot or max(2, math.ceil(ROT_BYTES / max(footprint, 1)))
+        self.footprint = footprint
+        self.calls = []
+        self.keep = [wq, wk, cache]
+        del wl
+        for r in range(self.n_rot):
+            bufs = [t.clone() for t in base]
+            pos = pos0.clone()
+            if cfg.layout == "qkv":
+                qkv = bufs[0]
+                q = torch.as_strided(qkv, (cfg.T, cfg.Hq, D), (qkv.stride(0), D, 1), 0)
+                k = torch.as_strided(qkv, (cfg.T, cfg.Hkv, D), (qkv.stride(0), D, 1), cfg.Hq * D)
+            else:
+                q, k = bufs
+            call = B.PreparedCall(q, k, wq, wk, cache, pos, is_neox=cfg.is_neox, eps=cfg.eps,
+                                  launch=launch)
+            self.calls.append(call)
+            self.keep += bufs + [pos]
+        self.calls[0]()
+        torch.cuda.synchronize(dev)
+        self.info = self.calls[0].info.as_dict()
+
+    def time(self, steps, warmup):
+        import torch
+
+        n = self.n_rot
+        for i in range(warmup):
+            self.calls[i % n]()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            self.calls[i % n]()
+        e1.record()
+        host_s = time.perf_counter() - h0
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - h0
+        ms = e0.elapsed_time(e1) / steps
+        return ms, host_s / steps * 1e3, wall_s
+
+
+def yardstick(nbytes, steps, warmup, dev):
+    """In-place read-xor(0)-write over the op's Q/K byte count, rotated copies."""
+    import torch
+
+    from head_qk_rmsnorm_amd import binding as B
+
+    nbytes = (nbytes + 15) // 16 * 16
+    n_rot = max(2, math.ceil(ROT_BYTES / nbytes))
+    bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(i) for i in range(n_rot)]
+    for i in range(warmup):
+        B.qknr_rmw(bufs[i % n_rot], nbytes, 0)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        B.qknr_rmw(bufs[i % n_rot], nbytes, 0)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del bufs
+    return ms, 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def calibration_copy(dev, nbytes=512 << 20, reps=3):
+    """A few plain copies of a known size: their FETCH_SIZE / WRITE_SIZE counters
+    calibrate counter runs of this same command."""
+    import torch
+
+    from head_qk_rmsnorm_amd import binding as B
+
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        B.qknr_copy(dst, src, nbytes)
+    torch.cuda.synchronize()
+    del src, dst
+    return {"bytes_per_copy": nbytes, "copies": reps}
+
+
+def cpu_baseline(cfg, seconds):
+    """The fp64 oracle as it stands, on the host, over whole tokens of the same
+    workload until the time budget is spent."""
+    import numpy as np
+
+    from head_qk_rmsnorm_amd import workloads as W
+    from oracle import qknr_oracle as O
+
+    wl = W.make_workload(cfg)
+    chunk = max(1, min(cfg.T, 65536 // max(cfg.heads, 1)))
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        sl = slice(done % cfg.T, min(done % cfg.T + chunk, cfg.T))
+        n = sl.stop - sl.start
+        O.qknorm_rope_io(wl.q[sl], wl.k[sl], wl.wq, wl.wk, wl.cache, wl.positions[sl],
+                         is_neox=cfg.is_neox, eps=cfg.eps, dtype=cfg.dtype, rope_dim=cfg.rope_dim)
+        done += n
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_tok = cfg.algorithmic_bytes() / cfg.T
+    return {
+        "value": round(done * per_tok / el / 1e9, 6), "unit": "GB/s", "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} tokens ({done * cfg.heads} head vectors) of the '{cfg.name}' workload "
+                  f"in chunks of {chunk} tokens, {el:.1f} s, single-threaded numpy fp64",
+        "host_cpu": platform.processor() or platform.machine(), "host_logical_cpus": os.cpu_count(),
+        "gheads_per_s": round(done * cfg.heads / el / 1e9, 9),
+    }
+
+
+def counters_for(cfg_name):
+    """Counter-based HBM traffic per launch, if it was measured on this kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None, "no counter file"
+    with open(COUNTERS) as f:
+        data = json.load(f)
+    ent = data.get(cfg_name)
+    if not ent:
+        return None, "workload not in counter file"
+    if ent.get("kernel_sha") != kernel_sha():
+        return None, "kernel changed since the counters were taken"
+    return ent, None
+
+
+def measure(cfg, dev, steps, warmup, launch, want_yard=True):
+    rig = Rig(cfg, dev, launch=launch)
+    ms, host_ms, wall = rig.time(steps, warmup)
+    B = cfg.algorithmic_bytes()
+    gbs = B / (ms * 1e-3) / 1e9
+    out = {
+        "workload": cfg.name, "ms_per_step": ms, "GB_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
+        "gheads_per_s": cfg.units / (ms * 1e-3) / 1e9, "host_ms_per_launch": host_ms,
+        "algorithmic_bytes": B, "n_rot": rig.n_rot, "footprint_bytes": rig.footprint,
+        "launch": rig.info,
+    }
+    del rig
+    if want_yard:
+        ymsn, ygbs = yardstick(cfg.units * cfg.head_dim * 2, steps, warmup // 4 + 1, dev)
+        out["yardstick_GB_s"] = ygbs
+        out["frac_of_yardstick"] = gbs / ygbs
+    return out
+
+
+SWEEP = [
+    dict(), dict(unroll=1), dict(unroll=4),
+    dict(groups_per_item=1), dict(groups_per_item=2), dict(groups_per_item=3), dict(groups_per_item=4),
+    dict(groups_per_item=6), dict(groups_per_item=2, unroll=1), dict(groups_per_item=4, unroll=4),
+    dict(block_waves=2), dict(block_waves=8), dict(max_blocks=-1), dict(max_blocks=-1, groups_per_item=2),
+    dict(max_blocks=-1, groups_per_item=4), dict(lanes_per_head=32),
+]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this op runs on one GPU; every (token, head) vector is "
+                          "independent, so N GPUs would each run the same kernel on their own "
+                          "shard (see DESIGN.md). Run with --gpus 1."}), flush=True)
+        sys.exit(2)
+    import torch
+
+    from head_qk_rmsnorm_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no HIP device"}), flush=True)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    launch = json.loads(args.launch) if args.launch else None
+    cfg = W.CONFIGS[args.config]
+    extra = open(args.extra_out, "a") if args.extra_out else None
+
+    calib = calibration_copy(dev)
+    print(f"[bench] calibration copies done: {calib}", file=sys.stderr, flush=True)
+
+    if args.sweep:
+        for lc in SWEEP:
+            try:
+                r = measure(cfg, dev, args.steps, args.warmup, lc, want_yard=False)
+            except RuntimeError as e:
+                r = {"workload": cfg.name, "error": str(e)}
+            r["sweep_launch"] = lc
+            print(f"[bench] sweep {lc}: {r.get('GB_s', 0):.1f} GB/s", file=sys.stderr, flush=True)
+            if extra:
+                extra.write(json.dumps(r) + "\n")
+                extra.flush()
+    if args.all_configs:
+        for name in W.CONFIG_ORDER:
+            r = measure(W.CONFIGS[name], dev, args.steps, args.warmup, launch)
+            print(f"[bench] {name}: {r['GB_s']:.1f} GB/s ({r['frac_of_peak'] * 100:.1f}% of peak), "
+                  f"{r['gheads_per_s']:.2f} Gheads/s, yardstick {r['yardstick_GB_s']:.1f} GB/s",
+                  file=sys.stderr, flush=True)
+            if extra:
+                extra.write(json.dumps(r) + "\n")
+                extra.flush()
+
+    r = measure(cfg, dev, args.steps, args.warmup, launch, want_yard=not args.no_yardstick)
+    print(f"[bench] {cfg.name}: {r['GB_s']:.1f} GB/s, {r['ms_per_step'] * 1e3:.2f} us/launch",
+          file=sys.stderr, flush=True)
+    ent, why = counters_for(cfg.name)
+    traffic = None
+    if ent:
+        traffic = ent["fetch_bytes_per_launch"] + ent["write_bytes_per_launch"]
+    roof = {"bound": "hbm", "achieved": round(r["GB_s"], 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(r["GB_s"] / HBM_PEAK_GBS, 5), "traffic": traffic}
+    line = {
+        "metric": "achieved HBM GB/s (and % of peak) + Gheads/s for fused QK RMSNorm+RoPE",
+        "value": round(r["GB_s"], 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
+                   "head_dim": cfg.head_dim, "rope_dim": cfg.rope_dim,
+                   "pairing": "neox" if cfg.is_neox else "interleaved", "io_dtype": cfg.dtype,
+                   "pos_dtype": cfg.pos_dtype, "layout": cfg.layout,
+                   "algorithmic_bytes_per_step": cfg.algorithmic_bytes(), "launch": r["launch"],
+                   "rotated_copies": r["n_rot"]},
+        "gheads_per_s": round(r["gheads_per_s"], 4),
+        "frac_of_hbm_peak": round(r["frac_of_peak"], 5),
+        "roofline": roof,
+    }
+    if ent is None:
+        line["roofline_traffic_note"] = why
+    else:
+        line["traffic_detail"] = ent
+    if "yardstick_GB_s" in r:
+        line["yardstick"] = {"kind": "in-place 16-byte read-xor-write over the same Q/K bytes",
+                             "GB_s": round(r["yardstick_GB_s"], 3),
+                             "frac_of_yardstick": round(r["frac_of_yardstick"], 5)}
+    line["host_ms_per_launch"] = round(r["host_ms_per_launch"], 5)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    if extra:
+        extra.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

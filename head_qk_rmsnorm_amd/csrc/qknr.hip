@@ -1,0 +1,643 @@
+// Fused in-place QK RMSNorm + rotary position embedding for MI355X (gfx950).
+//
+// The operation follows the page "SGLang Diffusion fused operator
+// fused_inplace_qknorm_rope: in-depth technical analysis" (m.lsln.cn/news/241376):
+// section 2.1 (per-head RMSNorm with a learned weight), section 2.2 (cos|sin
+// cache rows, interleaved and NeoX pairing, partial rotary), section 2.3 (the
+// fused per-head flow: load, widen to fp32, sum of squares, rsqrt, scale,
+// rotate, narrow, store in place) and section 3 (tensor contract). The C ABI is
+// declared in include/qknr.h.
+//
+// Design for the 64-lane CDNA4 wavefront (the page's kernel is a 32-lane
+// warp-per-head CUDA design; only its arithmetic is kept):
+//   * L = head_dim / E lanes share one head vector, each lane owning E
+//     contiguous elements. E = 8 gives 16-byte accesses per lane (L = 8, 16, 32
+//     for head_dim 64, 128, 256: 8, 4 or 2 heads per wave instruction); the
+//     half-wave mapping (L = 32, E = head_dim/32) covers the NeoX rotary widths
+//     whose rotary lanes would not be a power of two with E = 8.
+//   * A wave's work item is a run of head groups of ONE token, so the position
+//     and the cos|sin row are wave-uniform: the row is staged once per item in
+//     the wave's own LDS slice and each lane keeps its cos/sin values in
+//     registers for every head of the item.
+//   * The fp32 sum of squares is reduced over the L lanes of a head with DPP
+//     row operations (quad_perm, row_half_mirror, row_mirror) and, for L = 32,
+//     one ds_swizzle; every lane of a head ends with the bit-identical sum.
+//   * NeoX partners sit in lane (lane ^ m), m = (rope_dim/2)/E, within the same
+//     head; they are fetched with ds_bpermute.
+//   * Heads of one token that belong to Q and to K may share a wave
+//     instruction: each lane group selects its base pointer, strides and weight
+//     row. Only Q/K elements are loaded or stored.
+//   * Loads of `unroll` head groups are issued before the first is computed, to
+//     keep enough bytes in flight per wave; stores are 16-byte and in place.
+// Nothing here is a contraction, so there is no MFMA.
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "qknr.h"
+#include "qknr_bench.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kMaxBlockWaves = 8;
+
+// ----------------------------------------------------------------------------
+// I/O element formats: two 16-bit values per dword, lower address in the low
+// half. Widening is exact; narrowing rounds to nearest even (gfx950
+// v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
+// ----------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+struct Bf16 {
+  static __device__ __forceinline__ void unpack(uint32_t u, float& lo, float& hi) {
+    lo = __uint_as_float(u << 16);
+    hi = __uint_as_float(u & 0xffff0000u);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+struct Fp16 {
+  static __device__ __forceinline__ void unpack(uint32_t u, float& lo, float& hi) {
+    f16x2_t v = __builtin_bit_cast(f16x2_t, u);
+    lo = (float)v.x;
+    hi = (float)v.y;
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f16x2_t v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+// NV packed dwords (2*NV elements) owned by one lane.
+template <int NV>
+struct Raw {
+  uint32_t w[NV];
+};
+
+template <int NV>
+__device__ __forceinline__ Raw<NV> load_raw(const char* p) {
+  Raw<NV> r;
+  if constexpr (NV == 4) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  } else if constexpr (NV == 2) {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+    r.w[0] = v.x; r.w[1] = v.y;
+  } else {
+    static_assert(NV == 1, "1, 2 or 4 dwords per lane");
+    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+  return r;
+}
+
+template <int NV>
+__device__ __forceinline__ void store_raw(char* p, const Raw<NV>& r) {
+  if constexpr (NV == 4) {
+    *reinterpret_cast<u32x4_t*>(p) = u32x4_t{r.w[0], r.w[1], r.w[2], r.w[3]};
+  } else if constexpr (NV == 2) {
+    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{r.w[0], r.w[1]};
+  } else {
+    *reinterpret_cast<uint32_t*>(p) = r.w[0];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Cross-lane helpers
+// ----------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kSwizzleXor16 = 0x401F;  // ds_swizzle bit mode: and 0x1f, xor 0x10
+
+// Sum over aligned groups of L lanes; every lane of a group gets the same bits.
+// After the two quad steps a quad is uniform, so a mirror inside 8 (16) lanes
+// adds exactly the other quad (half row).
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(L == 8 || L == 16 || L == 32, "lanes per head");
+  v += dpp_mov<kDppQuadXor1>(v);
+  v += dpp_mov<kDppQuadXor2>(v);
+  v += dpp_mov<kDppRowHalfMirror>(v);
+  if constexpr (L >= 16) v += dpp_mov<kDppRowMirror>(v);
+  if constexpr (L >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16));
+  return v;
+}
+
+__device__ __forceinline__ float lane_fetch(int byte_addr, float v) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(byte_addr, __float_as_int(v)));
+}
+
+// ----------------------------------------------------------------------------
+// Kernel
+// ----------------------------------------------------------------------------
+struct Params {
+  char* q;
+  char* k;
+  const void* wq;
+  const void* wk;
+  const float* cache;
+  const void* pos;
+  int64_t q_tok, q_head, k_tok, k_head;  // byte strides
+  int32_t Hq, Hkv, R;
+  int32_t pos64;
+  float eps;
+  int32_t ng;       // head groups per token = ceil((Hq+Hkv) / heads_per_wave)
+  int32_t gpi;      // head groups per work item
+  int32_t nc;       // work items per token = ceil(ng / gpi)
+  int32_t n_items;  // T * nc
+};
+
+// IO: Bf16 | Fp16.  D: head_dim.  E: elements per lane.  NEOX: pairing.
+// FULL: rope_dim == head_dim (no pass-through dims).  U: head groups loaded ahead.
+template <class IO, int D, int E, bool NEOX, bool FULL, int U>
+__global__ void __launch_bounds__(kMaxBlockWaves * kWave) qknr_kernel(const Params p) {
+  constexpr int L = D / E;      // lanes per head
+  constexpr int G = kWave / L;  // heads per wave instruction
+  constexpr int NV = E / 2;     // packed dwords per lane
+  constexpr int NCS = NEOX ? E : E / 2;  // cos (and sin) values per lane
+  static_assert(D % E == 0 && E % 2 == 0 && G >= 2, "lane mapping");
+  extern __shared__ float lds_all[];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wpb = blockDim.x / kWave;
+  float* lds = lds_all + wib * D;  // cos at [0, D/2), sin at [D/2, D)
+  const int sub = lane / L;        // head slot of this lane in a wave instruction
+  const int li = lane % L;         // lane inside the head
+  const int d0 = li * E;           // first dim owned by this lane
+  const int H = p.Hq + p.Hkv;
+  const int R = FULL ? D : p.R;
+  const int half = R / 2;
+
+  // Weights of the dims this lane owns, for Q and for K (loop invariant).
+  float wq[E], wk[E];
+  {
+    const Raw<NV> a = load_raw<NV>(static_cast<const char*>(p.wq) + d0 * 2);
+    const Raw<NV> b = load_raw<NV>(static_cast<const char*>(p.wk) + d0 * 2);
+#pragma unroll
+    for (int w = 0; w < NV; ++w) {
+      IO::unpack(a.w[w], wq[2 * w], wq[2 * w + 1]);
+      IO::unpack(b.w[w], wk[2 * w], wk[2 * w + 1]);
+    }
+  }
+
+  // NeoX lane roles: this lane holds dims d0..d0+E-1; their partners d +- R/2
+  // sit at the same offsets in lane ^ m. Lanes of the lower half subtract.
+  int partner_addr = 0, j0 = 0;
+  bool lower = false, lane_rot = true;
+  if constexpr (NEOX) {
+    const int m = half / E;
+    partner_addr = (lane ^ m) << 2;
+    lower = (li & m) == 0;
+    j0 = d0 & (half - 1);  // half is a power of two for NeoX
+    lane_rot = FULL || d0 < R;
+  }
+
+  const int total_waves = gridDim.x * wpb;
+  for (int item = blockIdx.x * wpb + wib; item < p.n_items; item += total_waves) {
+    const int t = item / p.nc;
+    const int g_begin = (item - t * p.nc) * p.gpi;
+    const int g_end = min(g_begin + p.gpi, p.ng);
+
+    // Stage the token's cos|sin row in this wave's LDS slice.
+    const int64_t pos = p.pos64 ? static_cast<const int64_t*>(p.pos)[t]
+                                : static_cast<int64_t>(static_cast<const int32_t*>(p.pos)[t]);
+    const float* row = p.cache + pos * R;
+    for (int i = lane; i < R; i += kWave) {
+      const float v = row[i];
+      lds[i < half ? i : i - half + D / 2] = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    float cs[NCS], sn[NCS];
+    {
+      const int c0 = NEOX ? j0 : d0 / 2;
+#pragma unroll
+      for (int i = 0; i < NCS; ++i) {
+        cs[i] = lds[c0 + i];
+        sn[i] = lds[D / 2 + c0 + i];
+        if constexpr (NEOX) sn[i] = lower ? -sn[i] : sn[i];
+      }
+    }
+
+    for (int g = g_begin; g < g_end; g += U) {
+      Raw<NV> raw[U];
+      char* ptr[U];
+      bool ok[U], isk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int h = (g + u) * G + sub;
+        ok[u] = (g + u < g_end) && (h < H);
+        isk[u] = h >= p.Hq;
+        const int hh = isk[u] ? h - p.Hq : h;
+        char* base = isk[u] ? p.k + t * p.k_tok + static_cast<int64_t>(hh) * p.k_head
+                            : p.q + t * p.q_tok + static_cast<int64_t>(hh) * p.q_head;
+        ptr[u] = base + d0 * 2;
+        if (ok[u]) {
+          raw[u] = load_raw<NV>(ptr[u]);
+        } else {
+#pragma unroll
+          for (int w = 0; w < NV; ++w) raw[u].w[w] = 0u;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float x[E];
+        float ss = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NV; ++w) IO::unpack(raw[u].w[w], x[2 * w], x[2 * w + 1]);
+#pragma unroll
+        for (int i = 0; i < E; ++i) ss = fmaf(x[i], x[i], ss);
+        ss = group_sum<L>(ss);
+        const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / D, p.eps));
+
+        float n[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i) n[i] = x[i] * r * (isk[u] ? wk[i] : wq[i]);
+
+        float o[E];
+        if constexpr (NEOX) {
+#pragma unroll
+          for (int i = 0; i < E; ++i) {
+            const float pn = lane_fetch(partner_addr, n[i]);
+            const float v = fmaf(n[i], cs[i], pn * sn[i]);
+            o[i] = (FULL || lane_rot) ? v : n[i];
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < E / 2; ++kk) {
+            const float a = n[2 * kk], b = n[2 * kk + 1];
+            const float oa = fmaf(a, cs[kk], -(b * sn[kk]));
+            const float ob = fmaf(b, cs[kk], a * sn[kk]);
+            const bool rot = FULL || (d0 + 2 * kk < R);
+            o[2 * kk] = rot ? oa : a;
+            o[2 * kk + 1] = rot ? ob : b;
+          }
+        }
+
+        Raw<NV> out;
+#pragma unroll
+        for (int w = 0; w < NV; ++w) out.w[w] = IO::pack(o[2 * w], o[2 * w + 1]);
+        if (ok[u]) store_raw<NV>(ptr[u], out);
+      }
+    }
+    // The next item rewrites this wave's LDS slice only after these reads
+    // (LDS operations of one wave complete in order).
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Measurement aids (see qknr_bench.h).
+__global__ void __launch_bounds__(256) copy_kernel(u32x4_t* __restrict__ dst,
+                                                   const u32x4_t* __restrict__ src, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = src[i];
+}
+
+__global__ void __launch_bounds__(256) rmw_kernel(u32x4_t* buf, int64_t n, uint32_t key) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const u32x4_t v = buf[i];
+    buf[i] = v ^ key;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Kernel table
+// ----------------------------------------------------------------------------
+template <class IO, int D, int E, bool NEOX, bool FULL>
+const void* pick_unroll(int U) {
+  switch (U) {
+    case 1: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 1>);
+    case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2>);
+    case 4: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 4>);
+    default: return nullptr;
+  }
+}
+
+template <class IO, int D, int E>
+const void* pick_pairing(bool neox, bool full, int U) {
+  if (neox) return full ? pick_unroll<IO, D, E, true, true>(U) : pick_unroll<IO, D, E, true, false>(U);
+  return full ? pick_unroll<IO, D, E, false, true>(U) : pick_unroll<IO, D, E, false, false>(U);
+}
+
+template <class IO, int D>
+const void* pick_lanes(int E, bool neox, bool full, int U) {
+  if (E == 8) return pick_pairing<IO, D, 8>(neox, full, U);
+  if constexpr (D / 32 != 8) {
+    if (E == D / 32) return pick_pairing<IO, D, D / 32>(neox, full, U);
+  }
+  return nullptr;
+}
+
+template <class IO>
+const void* pick_dim(int D, int E, bool neox, bool full, int U) {
+  switch (D) {
+    case 64: return pick_lanes<IO, 64>(E, neox, full, U);
+    case 128: return pick_lanes<IO, 128>(E, neox, full, U);
+    case 256: return pick_lanes<IO, 256>(E, neox, full, U);
+    default: return nullptr;
+  }
+}
+
+const void* pick_kernel(int dtype, int D, int E, bool neox, bool full, int U) {
+  return dtype == QKNR_BF16 ? pick_dim<Bf16>(D, E, neox, full, U)
+                            : pick_dim<Fp16>(D, E, neox, full, U);
+}
+
+// ----------------------------------------------------------------------------
+// Host-side validation and planning (no HIP call before validation passes)
+// ----------------------------------------------------------------------------
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+bool shape_supported(int32_t D, int32_t R, int32_t neox) {
+  if (D != 64 && D != 128 && D != 256) return false;
+  if (R <= 0 || R > D) return false;
+  const int e = D / 32;
+  if (R % e != 0) return false;
+  if (neox) {
+    const int rotary_lanes = R / e;
+    if (rotary_lanes < 2 || !is_pow2(rotary_lanes)) return false;
+  }
+  return true;
+}
+
+// NeoX with E elements per lane needs rope_dim/E lanes, a power of two >= 2.
+bool lanes_fit(int32_t R, int32_t neox, int E) {
+  if (!neox) return true;
+  return R % E == 0 && R / E >= 2 && is_pow2(R / E);
+}
+
+// Head vectors of one tensor must not overlap: with the smaller of the two
+// strides inner, it must cover a vector and the outer one the inner extent.
+bool views_ok(int64_t T, int64_t H, int64_t tok, int64_t head, int64_t vec_bytes) {
+  if (tok < 0 || head < 0) return false;
+  const bool use_t = T > 1, use_h = H > 1;
+  if (!use_t && !use_h) return true;
+  if (use_t && !use_h) return tok >= vec_bytes;
+  if (!use_t && use_h) return head >= vec_bytes;
+  int64_t s_in = head, n_in = H, s_out = tok;
+  if (tok < head) { s_in = tok; n_in = T; s_out = head; }
+  if (s_in < vec_bytes) return false;
+  if (n_in > 0 && s_in > INT64_MAX / n_in) return false;
+  return s_out >= s_in * n_in;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Plan {
+  const void* fn = nullptr;
+  int E = 8, L = 8, G = 8, ng = 0, gpi = 0, nc = 0, U = 2, wpb = 4;
+  int64_t items = 0;
+  int max_blocks = 0;  // 0 auto, -1 uncapped, >0 explicit
+};
+
+int32_t make_plan(int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t R, int32_t neox,
+                  int32_t dtype, const qknr_launch_cfg* cfg, Plan* pl) {
+  qknr_launch_cfg c = cfg ? *cfg : qknr_launch_cfg{0, 0, 0, 0, 0};
+  int E;
+  if (c.lanes_per_head == 0) {
+    E = lanes_fit(R, neox, 8) ? 8 : D / 32;
+  } else {
+    if (c.lanes_per_head <= 0 || D % c.lanes_per_head != 0) return QKNR_E_ARG;
+    E = D / c.lanes_per_head;
+    if (E != 8 && E != D / 32) return QKNR_E_ARG;
+    if (!lanes_fit(R, neox, E)) return QKNR_E_ARG;
+  }
+  const int U = c.unroll == 0 ? 2 : c.unroll;
+  if (U != 1 && U != 2 && U != 4) return QKNR_E_ARG;
+  const int wpb = c.block_waves == 0 ? 4 : c.block_waves;
+  if (wpb < 1 || wpb > kMaxBlockWaves) return QKNR_E_ARG;
+  if (c.groups_per_item < 0 || c.max_blocks < -1) return QKNR_E_ARG;
+
+  pl->E = E;
+  pl->L = D / E;
+  pl->G = kWave / pl->L;
+  const int64_t H = static_cast<int64_t>(Hq) + Hkv;
+  pl->ng = static_cast<int>((H + pl->G - 1) / pl->G);
+  pl->gpi = std::max(1, c.groups_per_item == 0 ? pl->ng : std::min(c.groups_per_item, pl->ng));
+  pl->nc = (pl->ng + pl->gpi - 1) / pl->gpi;
+  pl->items = T * pl->nc;
+  if (pl->items > INT32_MAX) return QKNR_E_SHAPE;
+  pl->U = U;
+  pl->wpb = wpb;
+  pl->max_blocks = c.max_blocks;
+  pl->fn = pick_kernel(dtype, D, E, neox != 0, R == D, U);
+  return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
+}
+
+// Per-device CU count and per-kernel occupancy, computed once.
+std::mutex g_cache_mu;
+std::map<int, int> g_cus;
+std::map<std::pair<const void*, int>, int> g_occ;
+
+int32_t device_limits(const void* fn, int threads, size_t lds, int* cus, int* blocks_per_cu) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QKNR_E_DEVICE;
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  auto it = g_cus.find(dev);
+  if (it == g_cus.end()) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return QKNR_E_DEVICE;
+    it = g_cus.emplace(dev, n).first;
+  }
+  *cus = it->second;
+  auto key = std::make_pair(fn, threads);
+  auto jt = g_occ.find(key);
+  if (jt == g_occ.end()) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, lds) != hipSuccess || nb <= 0)
+      nb = 1;
+    jt = g_occ.emplace(key, nb).first;
+  }
+  *blocks_per_cu = jt->second;
+  return QKNR_OK;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// C ABI
+// ----------------------------------------------------------------------------
+extern "C" {
+
+QKNR_API int32_t qknr_can_use(int32_t head_dim, int32_t rope_dim, int32_t is_neox, int32_t dtype,
+                              int32_t pos_dtype) {
+  if (dtype != QKNR_BF16 && dtype != QKNR_FP16) return 0;
+  if (pos_dtype != QKNR_I32 && pos_dtype != QKNR_I64) return 0;
+  return shape_supported(head_dim, rope_dim, is_neox) ? 1 : 0;
+}
+
+QKNR_API const char* qknr_status_string(int32_t status) {
+  switch (status) {
+    case QKNR_OK: return "ok";
+    case QKNR_E_NULL: return "qknr: a required pointer is NULL";
+    case QKNR_E_SHAPE: return "qknr: bad shape or strides (negative, overlapping head vectors, or too large)";
+    case QKNR_E_UNSUPPORTED:
+      return "qknr: unsupported (head_dim, rope_dim, is_neox): need head_dim in {64,128,256}, "
+             "0 < rope_dim <= head_dim, rope_dim % (head_dim/32) == 0, and for NeoX "
+             "rope_dim/(head_dim/32) a power of two >= 2";
+    case QKNR_E_ALIGN:
+      return "qknr: misaligned: q, k, weights and q/k strides need 16-byte alignment, the cache 4 bytes, "
+             "positions their element size";
+    case QKNR_E_DTYPE: return "qknr: unknown dtype or pos_dtype code";
+    case QKNR_E_ARG: return "qknr: bad argument (eps must be finite and >= 0; launch configuration invalid)";
+    case QKNR_E_LAUNCH: return "qknr: the HIP runtime rejected the kernel launch";
+    case QKNR_E_DEVICE: return "qknr: could not query the current HIP device";
+    default: return "qknr: unknown status";
+  }
+}
+
+QKNR_API int32_t qknr_inplace_ex(void* q, void* k, const void* wq, const void* wk,
+                                 const float* cos_sin_cache, const void* positions, int64_t T,
+                                 int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t rope_dim,
+                                 int32_t is_neox, float eps, int64_t q_tok_stride_B,
+                                 int64_t q_head_stride_B, int64_t k_tok_stride_B,
+                                 int64_t k_head_stride_B, int32_t dtype, int32_t pos_dtype,
+                                 hipStream_t stream, const qknr_launch_cfg* cfg,
+                                 qknr_launch_info* info) {
+  if (T < 0 || Hq < 0 || Hkv < 0) return QKNR_E_SHAPE;
+  if (dtype != QKNR_BF16 && dtype != QKNR_FP16) return QKNR_E_DTYPE;
+  if (pos_dtype != QKNR_I32 && pos_dtype != QKNR_I64) return QKNR_E_DTYPE;
+  if (!shape_supported(head_dim, rope_dim, is_neox)) return QKNR_E_UNSUPPORTED;
+  if (!std::isfinite(eps) || eps < 0.0f) return QKNR_E_ARG;
+  if (T > INT32_MAX || T * (static_cast<int64_t>(Hq) + Hkv) > INT32_MAX) return QKNR_E_SHAPE;
+
+  Plan pl;
+  const int32_t prc = make_plan(T, Hq, Hkv, head_dim, rope_dim, is_neox, dtype, cfg, &pl);
+  if (prc != QKNR_OK) return prc;
+  if (info) {
+    info->lanes_per_head = pl.L;
+    info->elems_per_lane = pl.E;
+    info->heads_per_wave = pl.G;
+    info->groups_per_token = pl.ng;
+    info->groups_per_item = pl.gpi;
+    info->unroll = pl.U;
+    info->block_threads = pl.wpb * kWave;
+    info->grid_blocks = 0;
+    info->items = pl.items;
+  }
+  if (T == 0 || Hq + Hkv == 0) return QKNR_OK;
+
+  if ((Hq > 0 && (!q || !wq)) || (Hkv > 0 && (!k || !wk)) || !cos_sin_cache || !positions)
+    return QKNR_E_NULL;
+  const int64_t vec = 2 * static_cast<int64_t>(head_dim);
+  if (Hq > 0 && !views_ok(T, Hq, q_tok_stride_B, q_head_stride_B, vec)) return QKNR_E_SHAPE;
+  if (Hkv > 0 && !views_ok(T, Hkv, k_tok_stride_B, k_head_stride_B, vec)) return QKNR_E_SHAPE;
+  if (Hq > 0 && (!aligned(q, 16) || !aligned(wq, 16) || (T > 1 && q_tok_stride_B % 16) ||
+                 (Hq > 1 && q_head_stride_B % 16)))
+    return QKNR_E_ALIGN;
+  if (Hkv > 0 && (!aligned(k, 16) || !aligned(wk, 16) || (T > 1 && k_tok_stride_B % 16) ||
+                  (Hkv > 1 && k_head_stride_B % 16)))
+    return QKNR_E_ALIGN;
+  if (!aligned(cos_sin_cache, 4) || !aligned(positions, pos_dtype == QKNR_I64 ? 8 : 4))
+    return QKNR_E_ALIGN;
+
+  // ---- validation done; HIP calls from here on ----
+  const int threads = pl.wpb * kWave;
+  const size_t lds = static_cast<size_t>(pl.wpb) * head_dim * sizeof(float);
+  int cus = 0, per_cu = 0;
+  const int32_t drc = device_limits(pl.fn, threads, lds, &cus, &per_cu);
+  if (drc != QKNR_OK) return drc;
+  const int64_t needed = (pl.items + pl.wpb - 1) / pl.wpb;
+  int64_t cap = pl.max_blocks > 0 ? pl.max_blocks : static_cast<int64_t>(cus) * per_cu;
+  if (pl.max_blocks == -1) cap = needed;
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min(needed, cap)));
+  if (info) info->grid_blocks = grid;
+
+  Params prm;
+  prm.q = static_cast<char*>(q);
+  prm.k = static_cast<char*>(k);
+  prm.wq = wq ? wq : wk;  // the unused side (0 heads) still gets a readable row
+  prm.wk = wk ? wk : wq;
+  prm.cache = cos_sin_cache;
+  prm.pos = positions;
+  prm.q_tok = q_tok_stride_B;
+  prm.q_head = q_head_stride_B;
+  prm.k_tok = k_tok_stride_B;
+  prm.k_head = k_head_stride_B;
+  prm.Hq = Hq;
+  prm.Hkv = Hkv;
+  prm.R = rope_dim;
+  prm.pos64 = pos_dtype == QKNR_I64;
+  prm.eps = eps;
+  prm.ng = pl.ng;
+  prm.gpi = pl.gpi;
+  prm.nc = pl.nc;
+  prm.n_items = static_cast<int32_t>(pl.items);
+  void* args[] = {&prm};
+  if (hipLaunchKernel(pl.fn, dim3(grid), dim3(threads), args, lds, stream) != hipSuccess)
+    return QKNR_E_LAUNCH;
+  return QKNR_OK;
+}
+
+QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
+                              const float* cos_sin_cache, const void* positions, int64_t T,
+                              int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t rope_dim,
+                              int32_t is_neox, float eps, int64_t q_tok_stride_B,
+                              int64_t q_head_stride_B, int64_t k_tok_stride_B,
+                              int64_t k_head_stride_B, int32_t dtype, int32_t pos_dtype,
+                              hipStream_t stream) {
+  return qknr_inplace_ex(q, k, wq, wk, cos_sin_cache, positions, T, Hq, Hkv, head_dim, rope_dim,
+                         is_neox, eps, q_tok_stride_B, q_head_stride_B, k_tok_stride_B,
+                         k_head_stride_B, dtype, pos_dtype, stream, nullptr, nullptr);
+}
+
+static int32_t stream_launch(const void* fn, void** args, int64_t n16, hipStream_t stream) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QKNR_E_DEVICE;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return QKNR_E_DEVICE;
+  const int64_t needed = (n16 + 255) / 256;
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(needed, int64_t(cus) * 16)));
+  if (hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, stream) != hipSuccess) return QKNR_E_LAUNCH;
+  return QKNR_OK;
+}
+
+QKNR_API int32_t qknr_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+  if (bytes < 0) return QKNR_E_SHAPE;
+  if (bytes == 0) return QKNR_OK;
+  if (!dst || !src) return QKNR_E_NULL;
+  if (!aligned(dst, 16) || !aligned(src, 16) || bytes % 16) return QKNR_E_ALIGN;
+  u32x4_t* d = static_cast<u32x4_t*>(dst);
+  const u32x4_t* s = static_cast<const u32x4_t*>(src);
+  int64_t n = bytes / 16;
+  void* args[] = {&d, &s, &n};
+  return stream_launch(reinterpret_cast<const void*>(&copy_kernel), args, n, stream);
+}
+
+QKNR_API int32_t qknr_rmw(void* buf, int64_t bytes, uint32_t key, hipStream_t stream) {
+  if (bytes < 0) return QKNR_E_SHAPE;
+  if (bytes == 0) return QKNR_OK;
+  if (!buf) return QKNR_E_NULL;
+  if (!aligned(buf, 16) || bytes % 16) return QKNR_E_ALIGN;
+  u32x4_t* b = static_cast<u32x4_t*>(buf);
+  int64_t n = bytes / 16;
+  void* args[] = {&b, &n, &key};
+  return stream_launch(reinterpret_cast<const void*>(&rmw_kernel), args, n, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+/*
+ * qknr.h -- C ABI of the fused in-place QK RMSNorm + rotary position embedding
+ * for AMD MI355X (gfx950).
+ *
+ * The operation is the one described by the page "SGLang Diffusion fused
+ * operator fused_inplace_qknorm_rope: in-depth technical analysis"
+ * (m.lsln.cn/news/241376):
+ *   - section 2.1: per (token, head) vector x of length head_dim,
+ *       n_i = x_i * rsqrt(sum_j x_j^2 / head_dim + eps) * w_i
+ *     with w = q_weight for Q heads and k_weight for K heads;
+ *   - section 2.2: the first rope_dim dims of n are rotated pairwise by the
+ *     angles of cache row positions[token], laid out as
+ *       [cos_0 .. cos_{R/2-1} | sin_0 .. sin_{R/2-1}]  (fp32, R = rope_dim),
+ *     pairing (2j, 2j+1) when is_neox == 0 (interleaved, GPT-J) and
+ *     (j, j + R/2) when is_neox != 0 (NeoX); a pair (a, b) becomes
+ *     (a*cos_j - b*sin_j, b*cos_j + a*sin_j); dims >= rope_dim pass through;
+ *   - section 2.3: all of it in one pass, fp32 arithmetic in registers,
+ *     result rounded (to nearest even) to the I/O type and written in place;
+ *   - section 3 (I/O contract): q [T, Hq, D] and k [T, Hkv, D] fp16/bf16 with
+ *     innermost stride 1 (GQA: Hq != Hkv allowed), weights [D] of the same
+ *     dtype, the cos|sin cache [rows, R] fp32 row-contiguous, positions [T]
+ *     int32 or int64.
+ *
+ * Supported shapes (section 4.6 compile-time guards, section 5.2 predicate):
+ *   head_dim in {64, 128, 256}; 0 < rope_dim <= head_dim; rope_dim a multiple
+ *   of head_dim/32; for NeoX, rope_dim/(head_dim/32) a power of two >= 2.
+ *
+ * All entry points are thread-safe and keep no state besides small per-device
+ * caches of the CU count and kernel occupancy.
+ */
+#ifndef QKNR_H
+#define QKNR_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QKNR_API __attribute__((visibility("default")))
+
+/* Status codes. Every rejection happens before any HIP call or enqueue, so a
+ * rejected call leaves q and k untouched. */
+enum {
+  QKNR_OK = 0,
+  QKNR_E_NULL = -1,        /* a required pointer is NULL */
+  QKNR_E_SHAPE = -2,       /* negative size or stride, overlapping head views, size overflow */
+  QKNR_E_UNSUPPORTED = -3, /* (head_dim, rope_dim, is_neox) outside the supported set */
+  QKNR_E_ALIGN = -4,       /* q/k/weights or q/k strides not multiples of 16 bytes,
+                              cache not 4-byte aligned, positions not aligned to their type */
+  QKNR_E_DTYPE = -5,       /* unknown dtype or pos_dtype code */
+  QKNR_E_ARG = -6,         /* eps negative or not finite; bad launch configuration */
+  QKNR_E_LAUNCH = -7,      /* the HIP runtime refused the launch */
+  QKNR_E_DEVICE = -8       /* querying the current device failed */
+};
+
+/* I/O element types of q, k and the weights. */
+enum { QKNR_BF16 = 0, QKNR_FP16 = 1 };
+/* Element types of positions. */
+enum { QKNR_I32 = 0, QKNR_I64 = 1 };
+
+/*
+ * qknr_inplace -- apply the fused QK RMSNorm + RoPE to q and k in place.
+ *
+ *   q, k            device pointers to element [0,0,0] of q and k. Element
+ *                   (t, h, i) of q lives at  q + t*q_tok_stride_B
+ *                   + h*q_head_stride_B + 2*i  (bytes); likewise for k.
+ *                   Strides are in BYTES, must be >= 0, multiples of 16 and
+ *                   describe non-overlapping head vectors. Any layout works
+ *                   (contiguous [T,H,D], strided views into a fused qkv buffer,
+ *                   head-major); only the T*(Hq+Hkv)*head_dim Q/K elements are
+ *                   read and written, no other byte.
+ *   wq, wk          device pointers to the [head_dim] RMSNorm weights of Q and
+ *                   of K, in the I/O dtype, 16-byte aligned.
+ *   cos_sin_cache   device pointer to the fp32 table, row p at
+ *                   cos_sin_cache + p*rope_dim; it must hold every row that
+ *                   positions[] names (not checked: an out-of-range position
+ *                   is undefined behaviour, as in the source design).
+ *   positions       device pointer to T positions, int32 or int64 (pos_dtype).
+ *   T, Hq, Hkv      tokens, Q heads, K heads. T == 0 or Hq + Hkv == 0 is a
+ *                   no-op returning QKNR_OK (pointers are not inspected).
+ *   head_dim, rope_dim, is_neox   see "Supported shapes" above.
+ *   eps             added to the mean square; finite and >= 0 (passed as fp32).
+ *   dtype           QKNR_BF16 or QKNR_FP16 (q, k, wq, wk).
+ *   pos_dtype       QKNR_I32 or QKNR_I64.
+ *   stream          HIP stream of the current device; the work is enqueued
+ *                   there and the call returns without waiting.
+ *
+ * Ownership: all buffers belong to the caller; the library allocates, frees
+ * and retains nothing. q and k must not overlap each other (not checked).
+ * Returns QKNR_OK once enqueued, or a negative status (see above).
+ */
+QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
+                              const float* cos_sin_cache, const void* positions,
+                              int64_t T, int32_t Hq, int32_t Hkv,
+                              int32_t head_dim, int32_t rope_dim, int32_t is_neox,
+                              float eps,
+                              int64_t q_tok_stride_B, int64_t q_head_stride_B,
+                              int64_t k_tok_stride_B, int64_t k_head_stride_B,
+                              int32_t dtype, int32_t pos_dtype, hipStream_t stream);
+
+/*
+ * Launch configuration of qknr_inplace_ex. Zero in any field means "choose
+ * automatically" (what qknr_inplace does).
+ *   lanes_per_head   lanes of the 64-lane wavefront that share one head vector:
+ *                    head_dim/8 (16-byte accesses per lane) or 32 (half a wave).
+ *   groups_per_item  head groups (one per wave instruction: 64/lanes_per_head
+ *                    heads of one token) that a wave handles per work item;
+ *                    a work item never spans two tokens.
+ *   unroll           head groups loaded before the first is computed: 1, 2 or 4.
+ *   block_waves      wavefronts per workgroup: 1..8.
+ *   max_blocks       > 0 caps the grid (the kernel strides over the remaining
+ *                    items); -1 launches one workgroup per block_waves items.
+ */
+typedef struct qknr_launch_cfg {
+  int32_t lanes_per_head;
+  int32_t groups_per_item;
+  int32_t unroll;
+  int32_t block_waves;
+  int32_t max_blocks;
+} qknr_launch_cfg;
+
+/* What a call launches (filled by qknr_inplace_ex / qknr_plan). */
+typedef struct qknr_launch_info {
+  int32_t lanes_per_head;
+  int32_t elems_per_lane;
+  int32_t heads_per_wave;
+  int32_t groups_per_token;
+  int32_t groups_per_item;
+  int32_t unroll;
+  int32_t block_threads;
+  int32_t grid_blocks;
+  int64_t items;
+} qknr_launch_info;
+
+/* qknr_inplace with an explicit launch configuration (cfg may be NULL) and an
+ * optional report of what was launched (info may be NULL). Same contract and
+ * status codes as qknr_inplace; an invalid cfg field returns QKNR_E_ARG. */
+QKNR_API int32_t qknr_inplace_ex(void* q, void* k, const void* wq, const void* wk,
+                                 const float* cos_sin_cache, const void* positions,
+                                 int64_t T, int32_t Hq, int32_t Hkv,
+                                 int32_t head_dim, int32_t rope_dim, int32_t is_neox,
+                                 float eps,
+                                 int64_t q_tok_stride_B, int64_t q_head_stride_B,
+                                 int64_t k_tok_stride_B, int64_t k_head_stride_B,
+                                 int32_t dtype, int32_t pos_dtype, hipStream_t stream,
+                                 const qknr_launch_cfg* cfg, qknr_launch_info* info);
+
+/*
+ * qknr_can_use -- 1 if an instance exists for this combination, else 0.
+ * Mirrors the page's capability predicate (section 5.2): head_dim in
+ * {64,128,256}, 0 < rope_dim <= head_dim, rope_dim % (head_dim/32) == 0, and
+ * for NeoX rope_dim/(head_dim/32) a power of two >= 2; dtype and pos_dtype must
+ * be known codes. Pure host function, no HIP call.
+ */
+QKNR_API int32_t qknr_can_use(int32_t head_dim, int32_t rope_dim, int32_t is_neox,
+                              int32_t dtype, int32_t pos_dtype);
+
+/* Static, never-freed description of a status code ("unknown status" for
+ * codes not listed above). Pure host function. */
+QKNR_API const char* qknr_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKNR_H */

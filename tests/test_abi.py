@@ -1,0 +1,205 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, its
+capability predicate matches the page's rule, and every invalid argument is
+rejected with its documented status before any HIP call (no GPU needed: a call
+that reached the HIP runtime here would return QKNR_E_DEVICE instead)."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+from head_qk_rmsnorm_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        txt = open(h).read()
+        names += re.findall(r"QKNR_API\s+[\w\s\*]+?\b(qknr_\w+)\s*\(", txt)
+    return names
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    names = _declared()
+    assert {"qknr_inplace", "qknr_inplace_ex", "qknr_can_use", "qknr_status_string",
+            "qknr_copy", "qknr_rmw"} <= set(names)
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (qknr_\w+)", out))
+    assert set(names) == exported, (set(names) ^ exported)
+
+
+def _page_predicate(D, R, neox):
+    """The capability rule of section 5.2 of the page, restated."""
+    if D not in (64, 128, 256):
+        return False
+    if R <= 0 or R > D:
+        return False
+    e = D // 32
+    if R % e:
+        return False
+    if neox:
+        rl = R // e
+        if rl < 2 or (rl & (rl - 1)):
+            return False
+    return True
+
+
+def test_can_use_matches_page_predicate():
+    for D in (0, 32, 64, 96, 128, 192, 256, 512):
+        for R in range(-2, max(D, 8) + 3):
+            for neox in (0, 1):
+                assert B.qknr_can_use(D, R, neox) == _page_predicate(D, R, neox), (D, R, neox)
+    assert not B.lib().qknr_can_use(128, 128, 1, 2, 0)
+    assert not B.lib().qknr_can_use(128, 128, 1, 0, 2)
+    assert B.lib().qknr_can_use(128, 128, 1, 1, 1)
+
+
+def test_status_strings():
+    texts = {code: B.qknr_status_string(code) for code in range(-8, 1)}
+    assert len(set(texts.values())) == 9
+    assert "unknown status" not in " ".join(texts.values())
+    assert B.qknr_status_string(-99) == B.qknr_status_string(5) == "qknr: unknown status"
+
+
+P = ctypes.c_void_p
+A = 0x10000  # a 16-byte aligned fake address; never dereferenced
+
+
+def _call(**kw):
+    a = dict(q=P(A), k=P(A + 0x100000), wq=P(A), wk=P(A), cache=P(A), pos=P(A), T=5, Hq=4,
+             Hkv=4, D=128, R=128, neox=1, eps=1e-6, qt=4 * 256, qh=256, kt=4 * 256, kh=256,
+             dtype=0, pdt=0, stream=P(0), cfg=None)
+    a.update(kw)
+    cfg = a.pop("cfg")
+    info = B.LaunchInfo()
+    args = [a[n] for n in ("q", "k", "wq", "wk", "cache", "pos", "T", "Hq", "Hkv", "D", "R",
+                           "neox", "eps", "qt", "qh", "kt", "kh", "dtype", "pdt", "stream")]
+    return B.lib().qknr_inplace_ex(*args, ctypes.byref(cfg) if cfg else None, ctypes.byref(info))
+
+
+REJECT = [
+    (dict(T=-1), B.QKNR_E_SHAPE), (dict(Hq=-1), B.QKNR_E_SHAPE), (dict(Hkv=-3), B.QKNR_E_SHAPE),
+    (dict(T=1 << 31), B.QKNR_E_SHAPE), (dict(T=(1 << 28), Hq=8, Hkv=8), B.QKNR_E_SHAPE),
+    (dict(dtype=2), B.QKNR_E_DTYPE), (dict(dtype=-1), B.QKNR_E_DTYPE),
+    (dict(pdt=2), B.QKNR_E_DTYPE),
+    (dict(D=96, R=96), B.QKNR_E_UNSUPPORTED), (dict(R=0), B.QKNR_E_UNSUPPORTED),
+    (dict(R=130), B.QKNR_E_UNSUPPORTED), (dict(R=6), B.QKNR_E_UNSUPPORTED),
+    (dict(R=96, neox=1), B.QKNR_E_UNSUPPORTED), (dict(D=64, R=2, neox=1), B.QKNR_E_UNSUPPORTED),
+    (dict(eps=-1e-6), B.QKNR_E_ARG), (dict(eps=float("nan")), B.QKNR_E_ARG),
+    (dict(eps=float("inf")), B.QKNR_E_ARG),
+    (dict(q=P(0)), B.QKNR_E_NULL), (dict(k=P(0)), B.QKNR_E_NULL), (dict(wq=P(0)), B.QKNR_E_NULL),
+    (dict(wk=P(0)), B.QKNR_E_NULL), (dict(cache=P(0)), B.QKNR_E_NULL),
+    (dict(pos=P(0)), B.QKNR_E_NULL),
+    (dict(qh=128), B.QKNR_E_SHAPE),            # heads overlap (stride < 256 bytes)
+    (dict(qt=3 * 256), B.QKNR_E_SHAPE),        # token rows overlap
+    (dict(qh=-256), B.QKNR_E_SHAPE), (dict(kt=-1024), B.QKNR_E_SHAPE),
+    (dict(qt=256, qh=256), B.QKNR_E_SHAPE),    # equal strides overlap
+    (dict(q=P(A + 8)), B.QKNR_E_ALIGN), (dict(k=P(A + 2)), B.QKNR_E_ALIGN),
+    (dict(wq=P(A + 4)), B.QKNR_E_ALIGN), (dict(wk=P(A + 8)), B.QKNR_E_ALIGN),
+    (dict(qh=264, qt=4 * 264), B.QKNR_E_ALIGN), (dict(kt=4 * 256 + 8), B.QKNR_E_ALIGN),
+    (dict(cache=P(A + 2)), B.QKNR_E_ALIGN), (dict(pos=P(A + 2)), B.QKNR_E_ALIGN),
+    (dict(pos=P(A + 4), pdt=1), B.QKNR_E_ALIGN),
+    (dict(cfg=B.LaunchCfg(lanes_per_head=7)), B.QKNR_E_ARG),
+    (dict(cfg=B.LaunchCfg(lanes_per_head=64)), B.QKNR_E_ARG),
+    (dict(cfg=B.LaunchCfg(unroll=3)), B.QKNR_E_ARG),
+    (dict(cfg=B.LaunchCfg(block_waves=9)), B.QKNR_E_ARG),
+    (dict(cfg=B.LaunchCfg(block_waves=-1)), B.QKNR_E_ARG),
+    (dict(cfg=B.LaunchCfg(max_blocks=-2)), B.QKNR_E_ARG),
+    (dict(cfg=B.LaunchCfg(groups_per_item=-1)), B.QKNR_E_ARG),
+    # NeoX with 16-byte lanes needs rope_dim/8 rotary lanes, a power of two >= 2
+    (dict(D=128, R=8, cfg=B.LaunchCfg(lanes_per_head=16)), B.QKNR_E_ARG),
+]
+
+
+def _no_gpu():
+    try:
+        import torch
+
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: run on a host without a GPU")
+@pytest.mark.parametrize("kw,code", REJECT, ids=lambda v: str(v))
+def test_rejections(kw, code):
+    assert _call(**kw) == code
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: run on a host without a GPU")
+def test_empty_work_is_ok_without_pointers_or_device():
+    z = P(0)
+    assert _call(T=0, q=z, k=z, wq=z, wk=z, cache=z, pos=z) == B.QKNR_OK
+    assert _call(Hq=0, Hkv=0, q=z, k=z, wq=z, wk=z, cache=z, pos=z) == B.QKNR_OK
+    # with valid arguments the first HIP call is reached, which fails on a GPU-less host
+    assert _call() == B.QKNR_E_DEVICE
+
+
+def _plan(D, R, neox, Hq=24, Hkv=24, cfg=None):
+    info = B.LaunchInfo()
+    z = P(0)
+    args = [z, z, z, z, z, z, 0, Hq, Hkv, D, R, int(neox), 1e-6, 0, 0, 0, 0, 0, 0, z]
+    rc = B.lib().qknr_inplace_ex(*args, ctypes.byref(cfg) if cfg else None, ctypes.byref(info))
+    assert rc == 0
+    return info.as_dict()
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_plan_lane_mapping(D):
+    """16-byte lanes (head_dim/8 lanes per head) whenever the pairing allows it;
+    the half-wave mapping (32 lanes, head_dim/32 elements) otherwise."""
+    for neox in (0, 1):
+        for R in range(D // 32, D + 1, D // 32):
+            if not B.qknr_can_use(D, R, neox):
+                continue
+            info = _plan(D, R, neox)
+            fits16 = (not neox) or (R % 8 == 0 and R // 8 >= 2 and (R // 8) & (R // 8 - 1) == 0)
+            want_lanes = D // 8 if fits16 else 32
+            assert info["lanes_per_head"] == want_lanes, (D, R, neox, info)
+            assert info["elems_per_lane"] * info["lanes_per_head"] == D
+            assert info["heads_per_wave"] == 64 // info["lanes_per_head"]
+            assert info["groups_per_token"] == -(-48 // info["heads_per_wave"])
+
+
+def test_plan_explicit_cfg():
+    info = _plan(128, 128, 0, cfg=B.LaunchCfg(lanes_per_head=32, groups_per_item=5, unroll=4,
+                                              block_waves=8))
+    assert info == dict(lanes_per_head=32, elems_per_lane=4, heads_per_wave=2,
+                        groups_per_token=24, groups_per_item=5, unroll=4, block_threads=512,
+                        grid_blocks=0, items=0)
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(2, 2, 64, dtype=torch.bfloat16)
+    w = torch.ones(64, dtype=torch.bfloat16)
+    c = torch.zeros(4, 64)
+    p = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="HIP device"):
+        B.fused_inplace_qknorm_rope(q, q, w, w, c, p, is_neox=True)
+
+
+def test_harness_layouts_on_host():
+    """The test harness places q/k exactly where the views say (host check)."""
+    np = pytest.importorskip("numpy")
+    from head_qk_rmsnorm_amd import workloads as W
+    from tests import qknr_harness as Hn
+
+    for layout in ("contiguous", "padded", "head_major", "qkv"):
+        wl = W.make_workload(W.case(5, 3, 2, 64, 64, True, seed=1))
+        dc = Hn.DeviceCase(wl, layout=layout, device="cpu")
+        q, k = dc.outputs(dc.storages_host)
+        assert np.array_equal(q, wl.q) and np.array_equal(k, wl.k), layout
+        assert sum(int(m.sum()) for m in dc.masks) == wl.q.size + wl.k.size
+        import torch
+
+        assert torch.equal(dc.q.contiguous().view(torch.int16),
+                           torch.from_numpy(wl.q.view(np.int16))), layout

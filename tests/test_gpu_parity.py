@@ -1,0 +1,259 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, element
+by element, plus untouched bytes, determinism and error paths.
+
+Tolerance (every Q/K element): |gpu - ref| <= 2^-7 * (|ref| + 1), where ref is
+the oracle's fp64 result rounded once to the I/O type; no NaN. In addition at
+least 99% of elements must equal ref bit for bit: the kernel computes in fp32
+and rounds to nearest even, so it may differ from the correctly rounded value
+only where the fp64 result lies within the fp32 error of a rounding boundary.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from head_qk_rmsnorm_amd import workloads as W
+from tests import qknr_harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    from head_qk_rmsnorm_amd import binding as B
+
+    B.lib()  # fail loudly if the library is missing
+    yield
+
+
+# ---------------------------------------------------------------------------
+# The five workloads
+# ---------------------------------------------------------------------------
+
+def test_config_tiny_full():
+    wl = W.make_workload(W.CONFIGS["tiny"])
+    _say("case tiny")
+    cq, ck = Hn.run_and_check(wl)
+    _say("tiny", cq, ck)
+
+
+@pytest.mark.parametrize("name", ["dit", "gqa", "partial", "large"])
+def test_config_full_size_sampled(name):
+    """Full-size launch in the benchmark's (automatic) launch configuration;
+    all bytes outside Q/K checked; 512 sampled tokens checked against the oracle."""
+    cfg = W.CONFIGS[name]
+    _say(f"case {name}: T={cfg.T} Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.head_dim} R={cfg.rope_dim}")
+    wl = W.make_workload(cfg)
+    toks = W.sample_tokens(cfg.T, 512, seed=cfg.seed)
+    cq, ck = Hn.run_and_check(wl, tokens=toks)
+    _say(name, cq, ck)
+
+
+# ---------------------------------------------------------------------------
+# Grid: head_dim x rope_dim x pairing x dtype x positions x T, with GQA
+# ---------------------------------------------------------------------------
+
+GRID = [(D, R, neox, dt, pdt, T)
+        for D in (64, 128, 256)
+        for R in (D, D // 2)
+        for neox in (False, True)
+        for dt, pdt in ((W.BF16, W.I32), (W.FP16, W.I64), (W.BF16, W.I64), (W.FP16, W.I32))
+        for T in (1, 9, 129, 1000)]
+
+
+@pytest.mark.parametrize("D,R,neox,dt,pdt,T", GRID)
+def test_grid(D, R, neox, dt, pdt, T):
+    # Hq=5, Hkv=3: Q/K straddle inside a wave instruction for every lane mapping
+    cfg = W.case(T, 5, 3, D, R, neox, dtype=dt, pos_dtype=pdt, seed=T + D + R,
+                 positions="uniform")
+    _say("case", cfg.name)
+    Hn.run_and_check(W.make_workload(cfg))
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("neox", [False, True])
+def test_every_supported_rope_dim(D, neox):
+    """Every rope_dim the capability predicate accepts, including the NeoX
+    widths that need the half-wave lane mapping."""
+    from head_qk_rmsnorm_amd import binding as B
+
+    e = D // 32
+    Rs = [R for R in range(e, D + 1, e) if B.qknr_can_use(D, R, neox)]
+    assert Rs
+    for R in Rs:
+        cfg = W.case(7, 3, 2, D, R, neox, seed=R, positions="uniform")
+        _say("case", cfg.name)
+        Hn.run_and_check(W.make_workload(cfg))
+
+
+# ---------------------------------------------------------------------------
+# Launch configurations (all must give the same, correct result)
+# ---------------------------------------------------------------------------
+
+LAUNCHES = [
+    dict(),
+    dict(unroll=1), dict(unroll=4),
+    dict(groups_per_item=1), dict(groups_per_item=3, unroll=2),
+    dict(block_waves=1), dict(block_waves=8),
+    dict(max_blocks=1), dict(max_blocks=7, groups_per_item=2),
+    dict(max_blocks=-1, groups_per_item=1),
+    dict(lanes_per_head=32), dict(lanes_per_head=32, unroll=4, groups_per_item=5),
+]
+
+
+@pytest.mark.parametrize("launch", LAUNCHES, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()) or "auto")
+@pytest.mark.parametrize("D,R,neox", [(64, 64, True), (128, 128, False), (128, 64, True),
+                                      (256, 256, True), (256, 128, False)])
+def test_launch_variants(launch, D, R, neox):
+    # for head_dim 256, 32 lanes per head is the 16-byte mapping itself
+    cfg = W.case(33, 7, 3, D, R, neox, dtype=W.BF16, pos_dtype=W.I64, seed=D + R)
+    _say("case", cfg.name, launch)
+    Hn.run_and_check(W.make_workload(cfg), launch=launch)
+
+
+# ---------------------------------------------------------------------------
+# Layouts and degenerate shapes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layout", ["contiguous", "padded", "head_major", "qkv"])
+@pytest.mark.parametrize("D,R,neox", [(64, 32, True), (128, 128, True), (256, 256, False)])
+def test_layouts(layout, D, R, neox):
+    cfg = W.case(65, 6, 2, D, R, neox, dtype=W.FP16, seed=3)
+    _say("case", cfg.name, layout)
+    Hn.run_and_check(W.make_workload(cfg), layout=layout)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(0, 4), (4, 0), (1, 1), (1, 0), (31, 1), (3, 13)])
+def test_head_counts(Hq, Hkv):
+    cfg = W.case(17, Hq, Hkv, 128, 128, True, seed=Hq * 10 + Hkv)
+    _say("case", cfg.name)
+    Hn.run_and_check(W.make_workload(cfg))
+
+
+def test_zero_tokens_is_noop():
+    import torch
+
+    cfg = W.case(0, 4, 4, 128, 128, True)
+    wl = W.make_workload(cfg)
+    dc = Hn.DeviceCase(wl)
+    dc.run()
+    after = dc.fetch()
+    for b, a in zip(dc.storages_host, after):
+        assert np.array_equal(b, a)
+    torch.cuda.synchronize()
+
+
+def test_special_values():
+    """eps = 0; an all-zero head (eps > 0 gives exactly 0); heads scaled by 2^20
+    and 2^-20 (the norm removes the scale); position 0 (norm only)."""
+    import torch
+    from oracle import qknr_oracle as O
+
+    D = R = 128
+    T, Hq, Hkv = 4, 3, 1
+    g = np.random.default_rng(5)
+    x = g.standard_normal((T, Hq, D))
+    x[1, 0] = 0.0
+    x[2, 1] *= 2.0 ** 20
+    x[3, 2] *= 2.0 ** -20
+    for eps in (0.0, 1e-6):
+        if eps == 0.0:
+            x[1, 0] = 1.0  # 0/0 is NaN for eps = 0, as the formula says; keep it out
+        cfg = W.case(T, Hq, Hkv, D, R, True, eps=eps, seed=1)
+        wl = W.make_workload(cfg)
+        wl.q[...] = O.round_to_bf16_bits(x)
+        wl.positions[0] = 0
+        _say("case special eps", eps)
+        Hn.run_and_check(wl)
+    torch.cuda.synchronize()
+
+
+def test_outlier_magnitudes_fp16():
+    cfg = W.case(64, 4, 4, 256, 256, False, dtype=W.FP16, outlier_frac=0.05,
+                 outlier_scale=50.0, seed=8)
+    Hn.run_and_check(W.make_workload(cfg))
+
+
+def test_deterministic():
+    cfg = W.case(300, 8, 8, 128, 64, True, seed=2)
+    wl = W.make_workload(cfg)
+    outs = []
+    for _ in range(2):
+        dc = Hn.DeviceCase(wl)
+        dc.run()
+        outs.append(dc.fetch())
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+def test_side_stream():
+    import torch
+
+    cfg = W.case(129, 6, 2, 128, 128, False, seed=4)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Hn.run_and_check(W.make_workload(cfg), stream=s)
+
+
+# ---------------------------------------------------------------------------
+# Error paths: rejected before any launch, q and k untouched
+# ---------------------------------------------------------------------------
+
+def test_rejections_leave_buffers_untouched():
+    import torch
+    from head_qk_rmsnorm_amd import binding as B
+
+    cfg = W.case(9, 4, 4, 128, 128, True, seed=6)
+    wl = W.make_workload(cfg)
+    dc = Hn.DeviceCase(wl)
+    bad = [
+        dict(eps=-1.0),
+        dict(eps=float("nan")),
+        dict(rope_dim=96),  # NeoX: 96/4 = 24 rotary lanes, not a power of two
+    ]
+    for kw in bad:
+        args = dict(is_neox=True, eps=1e-6)
+        args.update(kw)
+        rope = args.pop("rope_dim", 0)
+        with pytest.raises((RuntimeError, ValueError)):
+            B.qknr_inplace(dc.q, dc.k, dc.wq, dc.wk,
+                           dc.cache if not rope else torch.zeros(4, rope, device=dc.device),
+                           dc.positions, rope_dim=rope, **args)
+    # misaligned q view (offset by one element)
+    q_mis = torch.as_strided(dc.storages_dev[0], dc.q.shape, dc.q.stride(),
+                             dc.q.storage_offset() + 1)
+    with pytest.raises(RuntimeError, match="misaligned"):
+        B.qknr_inplace(q_mis, dc.k, dc.wq, dc.wk, dc.cache, dc.positions, is_neox=True)
+    after = dc.fetch()
+    for b, a in zip(dc.storages_host, after):
+        assert np.array_equal(b, a)
+
+
+# ---------------------------------------------------------------------------
+# Measurement aids
+# ---------------------------------------------------------------------------
+
+def test_copy_and_rmw_kernels():
+    import torch
+    from head_qk_rmsnorm_amd import binding as B
+
+    n = (1 << 20) + 48
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    B.qknr_copy(dst, src, n)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    B.qknr_rmw(dst, n, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    B.qknr_rmw(dst, n, 0xFFFFFFFF)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, ~src)
