@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 ROT_BYTES = 1 << 30    # rotate through >= 1 GiB of copies
+MAX_ROT = 64           # (tiny workloads: at most 64 copies; they are latency-bound anyway)
 KERNEL_SRC = os.path.join(ROOT, "head_qk_rmsnorm_amd", "csrc", "qknr.hip")
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
@@ -50,7 +51,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-yardstick", action="store_true")
-    ap.add_argument("--sweep", action="store_true", help="time a grid of launch configurations")
+    ap.add_argument("--sweep", action="store_true", help="time a short list of launch configurations")
+    ap.add_argument("--sweep-grid", action="store_true",
+                    help="time every (grid kind, groups per item, unroll, block waves) combination")
     ap.add_argument("--all-configs", action="store_true", help="also time every workload")
     ap.add_argument("--extra-out", default="", help="file for per-config / sweep JSON lines")
     return ap.parse_args()
@@ -63,45 +66,54 @@ class Rig:
         import numpy as np
         import torch
 
-        from head_qk_rmsnorm_amd import binding as B
         from head_qk_rmsnorm_amd import workloads as W
 
         self.cfg = cfg
+        self.dev = dev
         wl = W.make_workload(cfg)
         tdt = torch.bfloat16 if cfg.dtype == W.BF16 else torch.float16
 
         def d16(a):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(tdt)
 
-        wq, wk = d16(wl.wq), d16(wl.wk)
-        cache = torch.from_numpy(wl.cache).to(dev)
+        self.wq, self.wk = d16(wl.wq), d16(wl.wk)
+        self.cache = torch.from_numpy(wl.cache).to(dev)
         pos0 = torch.from_numpy(wl.positions).to(dev)
-        D = cfg.head_dim
-        if cfg.layout == "qkv":
-            base = [d16(wl.qkv)]
-        else:
-            base = [d16(wl.q), d16(wl.k)]
-        footprint = sum(t.numel() * t.element_size() for t in base) + pos0.numel() * pos0.element_size()
-        self.n_rot = n_rot or max(2, math.ceil(ROT_BYTES / max(footprint, 1)))
-        self.footprint = footprint
-        self.calls = []
-        self.keep = [wq, wk, cache]
+        base = [d16(wl.qkv)] if cfg.layout == "qkv" else [d16(wl.q), d16(wl.k)]
         del wl
+        footprint = sum(t.numel() * t.element_size() for t in base) + pos0.numel() * pos0.element_size()
+        self.n_rot = n_rot or min(MAX_ROT, max(2, math.ceil(ROT_BYTES / max(footprint, 1))))
+        self.footprint = footprint
+        self.copies = []
         for r in range(self.n_rot):
-            bufs = [t.clone() for t in base]
-            pos = pos0.clone()
-            if cfg.layout == "qkv":
-                qkv = bufs[0]
-                q = torch.as_strided(qkv, (cfg.T, cfg.Hq, D), (qkv.stride(0), D, 1), 0)
-                k = torch.as_strided(qkv, (cfg.T, cfg.Hkv, D), (qkv.stride(0), D, 1), cfg.Hq * D)
-            else:
-                q, k = bufs
-            call = B.PreparedCall(q, k, wq, wk, cache, pos, is_neox=cfg.is_neox, eps=cfg.eps,
-                                  launch=launch)
-            self.calls.append(call)
-            self.keep += bufs + [pos]
+            bufs = [t.clone() for t in base] if r else base
+            self.copies.append((bufs, pos0.clone() if r else pos0))
+        self.prepare(launch)
+
+    def views(self, bufs):
+        import torch
+
+        c, D = self.cfg, self.cfg.head_dim
+        if c.layout == "qkv":
+            qkv = bufs[0]
+            q = torch.as_strided(qkv, (c.T, c.Hq, D), (qkv.stride(0), D, 1), 0)
+            k = torch.as_strided(qkv, (c.T, c.Hkv, D), (qkv.stride(0), D, 1), c.Hq * D)
+            return q, k
+        return bufs[0], bufs[1]
+
+    def prepare(self, launch=None):
+        import torch
+
+        from head_qk_rmsnorm_amd import binding as B
+
+        c = self.cfg
+        self.calls = []
+        for bufs, pos in self.copies:
+            q, k = self.views(bufs)
+            self.calls.append(B.PreparedCall(q, k, self.wq, self.wk, self.cache, pos,
+                                             is_neox=c.is_neox, eps=c.eps, launch=launch))
         self.calls[0]()
-        torch.cuda.synchronize(dev)
+        torch.cuda.synchronize(self.dev)
         self.info = self.calls[0].info.as_dict()
 
     def time(self, steps, warmup):
@@ -132,7 +144,7 @@ def yardstick(nbytes, steps, warmup, dev):
     from head_qk_rmsnorm_amd import binding as B
 
     nbytes = (nbytes + 15) // 16 * 16
-    n_rot = max(2, math.ceil(ROT_BYTES / nbytes))
+    n_rot = min(MAX_ROT, max(2, math.ceil(ROT_BYTES / nbytes)))
     bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(i) for i in range(n_rot)]
     for i in range(warmup):
         B.qknr_rmw(bufs[i % n_rot], nbytes, 0)
@@ -211,8 +223,12 @@ def counters_for(cfg_name):
     return ent, None
 
 
-def measure(cfg, dev, steps, warmup, launch, want_yard=True):
-    rig = Rig(cfg, dev, launch=launch)
+def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None):
+    own = rig is None
+    if own:
+        rig = Rig(cfg, dev, launch=launch)
+    else:
+        rig.prepare(launch)
     ms, host_ms, wall = rig.time(steps, warmup)
     B = cfg.algorithmic_bytes()
     gbs = B / (ms * 1e-3) / 1e9
@@ -222,7 +238,8 @@ def measure(cfg, dev, steps, warmup, launch, want_yard=True):
         "algorithmic_bytes": B, "n_rot": rig.n_rot, "footprint_bytes": rig.footprint,
         "launch": rig.info,
     }
-    del rig
+    if own:
+        del rig
     if want_yard:
         ymsn, ygbs = yardstick(cfg.units * cfg.head_dim * 2, steps, warmup // 4 + 1, dev)
         out["yardstick_GB_s"] = ygbs
@@ -235,8 +252,16 @@ SWEEP = [
     dict(groups_per_item=1), dict(groups_per_item=2), dict(groups_per_item=3), dict(groups_per_item=4),
     dict(groups_per_item=6), dict(groups_per_item=2, unroll=1), dict(groups_per_item=4, unroll=4),
     dict(block_waves=2), dict(block_waves=8), dict(max_blocks=-1), dict(max_blocks=-1, groups_per_item=2),
-    dict(max_blocks=-1, groups_per_item=4), dict(lanes_per_head=32),
+    dict(max_blocks=-1, groups_per_item=4), dict(lanes_per_head=32), dict(lanes_per_head=64),
 ]
+
+
+SWEEP_GRID = ([dict(max_blocks=mb, groups_per_item=g, unroll=u, block_waves=bw)
+               for mb in (0, -1) for g in (1, 2, 3, 4, 6, 8, 12) for u in (1, 2, 4)
+               for bw in (1, 2, 4, 8) if u <= max(g, 1) and not (g == 3 and u == 4)]
+              + [dict(lanes_per_head=lanes, groups_per_item=g, unroll=u, block_waves=bw)
+                 for lanes in (32, 64) for g, u in ((1, 1), (2, 2), (4, 2), (4, 4), (8, 4))
+                 for bw in (1, 2, 4)])
 
 
 def main():
@@ -262,10 +287,11 @@ def main():
     calib = calibration_copy(dev)
     print(f"[bench] calibration copies done: {calib}", file=sys.stderr, flush=True)
 
-    if args.sweep:
-        for lc in SWEEP:
+    if args.sweep or args.sweep_grid:
+        rig = Rig(cfg, dev)
+        for lc in (SWEEP_GRID if args.sweep_grid else SWEEP):
             try:
-                r = measure(cfg, dev, args.steps, args.warmup, lc, want_yard=False)
+                r = measure(cfg, dev, args.steps, args.warmup, lc, want_yard=False, rig=rig)
             except RuntimeError as e:
                 r = {"workload": cfg.name, "error": str(e)}
             r["sweep_launch"] = lc
@@ -273,6 +299,7 @@ def main():
             if extra:
                 extra.write(json.dumps(r) + "\n")
                 extra.flush()
+        del rig
     if args.all_configs:
         for name in W.CONFIG_ORDER:
             r = measure(W.CONFIGS[name], dev, args.steps, args.warmup, launch)

@@ -12,23 +12,29 @@
 // warp-per-head CUDA design; only its arithmetic is kept):
 //   * L = head_dim / E lanes share one head vector, each lane owning E
 //     contiguous elements. E = 8 gives 16-byte accesses per lane (L = 8, 16, 32
-//     for head_dim 64, 128, 256: 8, 4 or 2 heads per wave instruction); the
-//     half-wave mapping (L = 32, E = head_dim/32) covers the NeoX rotary widths
-//     whose rotary lanes would not be a power of two with E = 8.
+//     for head_dim 64, 128, 256: 8, 4 or 2 heads per wave instruction). Half a
+//     wave (L = 32) and a full wave (L = 64) per head are the other mappings;
+//     half a wave also covers the NeoX rotary widths whose rotary lanes would
+//     not be a power of two with E = 8.
 //   * A wave's work item is a run of head groups of ONE token, so the position
-//     and the cos|sin row are wave-uniform: the row is staged once per item in
-//     the wave's own LDS slice and each lane keeps its cos/sin values in
-//     registers for every head of the item.
+//     is wave-uniform and read with a scalar load (prefetched one item ahead);
+//     each lane loads the cos/sin values of its own dims once per item and keeps
+//     them in registers for every head of the item.
 //   * The fp32 sum of squares is reduced over the L lanes of a head with DPP
-//     row operations (quad_perm, row_half_mirror, row_mirror) and, for L = 32,
-//     one ds_swizzle; every lane of a head ends with the bit-identical sum.
+//     row operations (quad_perm, row_half_mirror, row_mirror), one ds_swizzle
+//     across 16-lane rows for L >= 32 and two readlanes across the wave halves
+//     for L = 64; every lane of a head ends with the bit-identical sum.
 //   * NeoX partners sit in lane (lane ^ m), m = (rope_dim/2)/E, within the same
 //     head; they are fetched with ds_bpermute.
 //   * Heads of one token that belong to Q and to K may share a wave
 //     instruction: each lane group selects its base pointer, strides and weight
 //     row. Only Q/K elements are loaded or stored.
-//   * Loads of `unroll` head groups are issued before the first is computed, to
-//     keep enough bytes in flight per wave; stores are 16-byte and in place.
+//   * The loads of `unroll` head groups are issued before the first is computed
+//     and before the position-dependent cos/sin fetch, so the data is in flight
+//     while the position -> cache-row chain resolves. Q/K traffic is streamed
+//     with nontemporal loads and stores (each byte is touched once).
+//   * By default every wave takes one work item and exits (no persistent grid):
+//     the dispatcher back-fills CUs as waves finish, which balances the tail.
 // Nothing here is a contraction, so there is no MFMA.
 
 #include <hip/hip_runtime.h>
@@ -133,12 +139,17 @@ constexpr int kSwizzleXor16 = 0x401F;  // ds_swizzle bit mode: and 0x1f, xor 0x1
 // adds exactly the other quad (half row).
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(L == 8 || L == 16 || L == 32, "lanes per head");
+  static_assert(L == 8 || L == 16 || L == 32 || L == 64, "lanes per head");
   v += dpp_mov<kDppQuadXor1>(v);
   v += dpp_mov<kDppQuadXor2>(v);
   v += dpp_mov<kDppRowHalfMirror>(v);
   if constexpr (L >= 16) v += dpp_mov<kDppRowMirror>(v);
   if constexpr (L >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16));
+  if constexpr (L == 64) {
+    // both halves are uniform now; add them in the same order on every lane
+    v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  }
   return v;
 }
 
@@ -149,118 +160,155 @@ __device__ __forceinline__ float lane_fetch(int byte_addr, float v) {
 // ----------------------------------------------------------------------------
 // Kernel
 // ----------------------------------------------------------------------------
+// Q/K are read and written exactly once: nontemporal accesses keep them from
+// displacing the reused weights, positions and cos|sin rows in L2.
+template <int NV>
+__device__ __forceinline__ Raw<NV> load_io(const char* p) {
+  Raw<NV> r;
+  if constexpr (NV == 4) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  } else if constexpr (NV == 2) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    r.w[0] = v.x; r.w[1] = v.y;
+  } else {
+    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  }
+  return r;
+}
+
+template <int NV>
+__device__ __forceinline__ void store_io(char* p, const Raw<NV>& r) {
+  if constexpr (NV == 4) {
+    __builtin_nontemporal_store(u32x4_t{r.w[0], r.w[1], r.w[2], r.w[3]}, reinterpret_cast<u32x4_t*>(p));
+  } else if constexpr (NV == 2) {
+    __builtin_nontemporal_store(u32x2_t{r.w[0], r.w[1]}, reinterpret_cast<u32x2_t*>(p));
+  } else {
+    __builtin_nontemporal_store(r.w[0], reinterpret_cast<uint32_t*>(p));
+  }
+}
+
+typedef __attribute__((address_space(4))) const int32_t* cpos32_t;
+typedef __attribute__((address_space(4))) const int64_t* cpos64_t;
+
+__device__ __forceinline__ int64_t token_position(const void* pos, int pos64, int t) {
+  return pos64 ? ((cpos64_t)pos)[t] : static_cast<int64_t>(((cpos32_t)pos)[t]);
+}
+
 struct Params {
-  char* q;
-  char* k;
-  const void* wq;
-  const void* wk;
-  const float* cache;
-  const void* pos;
   int64_t q_tok, q_head, k_tok, k_head;  // byte strides
   int32_t Hq, Hkv, R;
   int32_t pos64;
+  int32_t cs_vec;   // cache rows 16-byte aligned and R/2 % 4 == 0
   float eps;
-  int32_t ng;       // head groups per token = ceil((Hq+Hkv) / heads_per_wave)
-  int32_t gpi;      // head groups per work item
-  int32_t nc;       // work items per token = ceil(ng / gpi)
-  int32_t n_items;  // T * nc
+  int32_t ng, gpi, nc, n_items;
 };
 
-// IO: Bf16 | Fp16.  D: head_dim.  E: elements per lane.  NEOX: pairing.
-// FULL: rope_dim == head_dim (no pass-through dims).  U: head groups loaded ahead.
 template <class IO, int D, int E, bool NEOX, bool FULL, int U>
-__global__ void __launch_bounds__(kMaxBlockWaves * kWave) qknr_kernel(const Params p) {
-  constexpr int L = D / E;      // lanes per head
-  constexpr int G = kWave / L;  // heads per wave instruction
-  constexpr int NV = E / 2;     // packed dwords per lane
-  constexpr int NCS = NEOX ? E : E / 2;  // cos (and sin) values per lane
-  static_assert(D % E == 0 && E % 2 == 0 && G >= 2, "lane mapping");
-  extern __shared__ float lds_all[];
-
+__global__ void __launch_bounds__(kMaxBlockWaves * kWave)
+qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict__ wqp,
+            const void* __restrict__ wkp, const float* __restrict__ cache,
+            const void* __restrict__ posp, const Params p) {
+  constexpr int L = D / E;
+  constexpr int G = kWave / L;
+  constexpr int NV = E / 2;
+  constexpr int NCS = NEOX ? E : E / 2;
+  static_assert(D % E == 0 && E % 2 == 0 && G >= 1, "lane mapping");
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
-  float* lds = lds_all + wib * D;  // cos at [0, D/2), sin at [D/2, D)
-  const int sub = lane / L;        // head slot of this lane in a wave instruction
-  const int li = lane % L;         // lane inside the head
-  const int d0 = li * E;           // first dim owned by this lane
+  const int sub = lane / L;
+  const int li = lane % L;
+  const int d0 = li * E;
   const int H = p.Hq + p.Hkv;
   const int R = FULL ? D : p.R;
   const int half = R / 2;
 
-  // Weights of the dims this lane owns, for Q and for K (loop invariant).
   float wq[E], wk[E];
   {
-    const Raw<NV> a = load_raw<NV>(static_cast<const char*>(p.wq) + d0 * 2);
-    const Raw<NV> b = load_raw<NV>(static_cast<const char*>(p.wk) + d0 * 2);
+    const Raw<NV> a = load_raw<NV>(static_cast<const char*>(wqp) + d0 * 2);
+    const Raw<NV> b = load_raw<NV>(static_cast<const char*>(wkp) + d0 * 2);
 #pragma unroll
     for (int w = 0; w < NV; ++w) {
       IO::unpack(a.w[w], wq[2 * w], wq[2 * w + 1]);
       IO::unpack(b.w[w], wk[2 * w], wk[2 * w + 1]);
     }
   }
-
-  // NeoX lane roles: this lane holds dims d0..d0+E-1; their partners d +- R/2
-  // sit at the same offsets in lane ^ m. Lanes of the lower half subtract.
   int partner_addr = 0, j0 = 0;
   bool lower = false, lane_rot = true;
   if constexpr (NEOX) {
     const int m = half / E;
     partner_addr = (lane ^ m) << 2;
     lower = (li & m) == 0;
-    j0 = d0 & (half - 1);  // half is a power of two for NeoX
+    j0 = d0 & (half - 1);
     lane_rot = FULL || d0 < R;
+  } else {
+    j0 = d0 / 2;
   }
 
   const int total_waves = gridDim.x * wpb;
-  for (int item = blockIdx.x * wpb + wib; item < p.n_items; item += total_waves) {
+  int item = blockIdx.x * wpb + wib;
+  if (item >= p.n_items) return;
+  int64_t pos_next = token_position(posp, p.pos64, item / p.nc);
+
+  for (; item < p.n_items; item += total_waves) {
     const int t = item / p.nc;
     const int g_begin = (item - t * p.nc) * p.gpi;
     const int g_end = min(g_begin + p.gpi, p.ng);
+    const int64_t pos = pos_next;
+    if (item + total_waves < p.n_items)
+      pos_next = token_position(posp, p.pos64, (item + total_waves) / p.nc);
+    char* qrow = qb + t * p.q_tok;
+    char* krow = kb + t * p.k_tok;
 
-    // Stage the token's cos|sin row in this wave's LDS slice.
-    const int64_t pos = p.pos64 ? static_cast<const int64_t*>(p.pos)[t]
-                                : static_cast<int64_t>(static_cast<const int32_t*>(p.pos)[t]);
-    const float* row = p.cache + pos * R;
-    for (int i = lane; i < R; i += kWave) {
-      const float v = row[i];
-      lds[i < half ? i : i - half + D / 2] = v;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    float cs[NCS], sn[NCS];
-    {
-      const int c0 = NEOX ? j0 : d0 / 2;
-#pragma unroll
-      for (int i = 0; i < NCS; ++i) {
-        cs[i] = lds[c0 + i];
-        sn[i] = lds[D / 2 + c0 + i];
-        if constexpr (NEOX) sn[i] = lower ? -sn[i] : sn[i];
-      }
-    }
-
-    for (int g = g_begin; g < g_end; g += U) {
-      Raw<NV> raw[U];
-      char* ptr[U];
-      bool ok[U], isk[U];
+    Raw<NV> ra[U];
+    char* pa[U];
+    bool oka[U], ka[U];
+    auto issue = [&](Raw<NV>* raw, char** ptr, bool* ok, bool* isk, int g) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int h = (g + u) * G + sub;
         ok[u] = (g + u < g_end) && (h < H);
         isk[u] = h >= p.Hq;
         const int hh = isk[u] ? h - p.Hq : h;
-        char* base = isk[u] ? p.k + t * p.k_tok + static_cast<int64_t>(hh) * p.k_head
-                            : p.q + t * p.q_tok + static_cast<int64_t>(hh) * p.q_head;
+        char* base = isk[u] ? krow + static_cast<int64_t>(hh) * p.k_head
+                            : qrow + static_cast<int64_t>(hh) * p.q_head;
         ptr[u] = base + d0 * 2;
         if (ok[u]) {
-          raw[u] = load_raw<NV>(ptr[u]);
+          raw[u] = load_io<NV>(ptr[u]);
         } else {
 #pragma unroll
           for (int w = 0; w < NV; ++w) raw[u].w[w] = 0u;
         }
       }
+    };
+    issue(ra, pa, oka, ka, g_begin);
+
+    // cos / sin of this lane's dims at this token
+    float cs[NCS], sn[NCS];
+    const float* row = cache + pos * R;
+    if ((FULL || NEOX) && NCS % 4 == 0 && p.cs_vec) {
+#pragma unroll
+      for (int i = 0; i < NCS; i += 4) {
+        const float4 c4 = *reinterpret_cast<const float4*>(row + j0 + i);
+        const float4 s4 = *reinterpret_cast<const float4*>(row + half + j0 + i);
+        cs[i] = c4.x; cs[i + 1] = c4.y; cs[i + 2] = c4.z; cs[i + 3] = c4.w;
+        sn[i] = s4.x; sn[i + 1] = s4.y; sn[i + 2] = s4.z; sn[i + 3] = s4.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCS; ++i) {
+        const int j = (FULL || NEOX) ? j0 + i : min(j0 + i, half - 1);
+        cs[i] = row[j];
+        sn[i] = row[half + j];
+      }
+    }
+    if constexpr (NEOX) {
+#pragma unroll
+      for (int i = 0; i < NCS; ++i) sn[i] = lower ? -sn[i] : sn[i];
+    }
+
+    auto compute = [&](const Raw<NV>* raw, char* const* ptr, const bool* ok, const bool* isk) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float x[E];
@@ -271,11 +319,9 @@ __global__ void __launch_bounds__(kMaxBlockWaves * kWave) qknr_kernel(const Para
         for (int i = 0; i < E; ++i) ss = fmaf(x[i], x[i], ss);
         ss = group_sum<L>(ss);
         const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / D, p.eps));
-
         float n[E];
 #pragma unroll
         for (int i = 0; i < E; ++i) n[i] = x[i] * r * (isk[u] ? wk[i] : wq[i]);
-
         float o[E];
         if constexpr (NEOX) {
 #pragma unroll
@@ -295,32 +341,34 @@ __global__ void __launch_bounds__(kMaxBlockWaves * kWave) qknr_kernel(const Para
             o[2 * kk + 1] = rot ? ob : b;
           }
         }
-
         Raw<NV> out;
 #pragma unroll
         for (int w = 0; w < NV; ++w) out.w[w] = IO::pack(o[2 * w], o[2 * w + 1]);
-        if (ok[u]) store_raw<NV>(ptr[u], out);
+        if (ok[u]) store_io<NV>(ptr[u], out);
       }
+    };
+
+    for (int g = g_begin; g < g_end; g += U) {
+      if (g != g_begin) issue(ra, pa, oka, ka, g);
+      compute(ra, pa, oka, ka);
     }
-    // The next item rewrites this wave's LDS slice only after these reads
-    // (LDS operations of one wave complete in order).
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
-// Measurement aids (see qknr_bench.h).
+// Measurement aids (see qknr_bench.h): one 16-byte element per thread, one
+// pass over the grid, nontemporal like the op's Q/K traffic.
 __global__ void __launch_bounds__(256) copy_kernel(u32x4_t* __restrict__ dst,
                                                    const u32x4_t* __restrict__ src, int64_t n) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
-    dst[i] = src[i];
+    __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
 }
 
 __global__ void __launch_bounds__(256) rmw_kernel(u32x4_t* buf, int64_t n, uint32_t key) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
-    const u32x4_t v = buf[i];
-    buf[i] = v ^ key;
+    const u32x4_t v = __builtin_nontemporal_load(&buf[i]);
+    __builtin_nontemporal_store(v ^ key, &buf[i]);
   }
 }
 
@@ -343,11 +391,16 @@ const void* pick_pairing(bool neox, bool full, int U) {
   return full ? pick_unroll<IO, D, E, false, true>(U) : pick_unroll<IO, D, E, false, false>(U);
 }
 
+// Elements per lane: 8 (16-byte lanes), head_dim/32 (half a wave per head) and
+// head_dim/64 (a full wave per head; needs an even count, so not head_dim 64).
 template <class IO, int D>
 const void* pick_lanes(int E, bool neox, bool full, int U) {
   if (E == 8) return pick_pairing<IO, D, 8>(neox, full, U);
   if constexpr (D / 32 != 8) {
     if (E == D / 32) return pick_pairing<IO, D, D / 32>(neox, full, U);
+  }
+  if constexpr (D / 64 >= 2 && D / 64 != 8) {
+    if (E == D / 64) return pick_pairing<IO, D, D / 64>(neox, full, U);
   }
   return nullptr;
 }
@@ -407,11 +460,19 @@ bool views_ok(int64_t T, int64_t H, int64_t tok, int64_t head, int64_t vec_bytes
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Launch defaults, chosen by measurement on MI355X (launch-shape sweeps over
+// the five benchmark workloads): one work item per wave with no persistent
+// grid, 4 head groups per item, all 4 loaded before the first is computed,
+// 2 waves per workgroup.
+constexpr int kDefaultGroupsPerItem = 4;
+constexpr int kDefaultUnroll = 4;
+constexpr int kDefaultBlockWaves = 2;
+
 struct Plan {
   const void* fn = nullptr;
-  int E = 8, L = 8, G = 8, ng = 0, gpi = 0, nc = 0, U = 2, wpb = 4;
+  int E = 8, L = 8, G = 8, ng = 0, gpi = 0, nc = 0, U = kDefaultUnroll, wpb = kDefaultBlockWaves;
   int64_t items = 0;
-  int max_blocks = 0;  // 0 auto, -1 uncapped, >0 explicit
+  int max_blocks = 0;  // 0: one workgroup per wpb items; -1: occupancy x CUs; > 0: explicit cap
 };
 
 int32_t make_plan(int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t R, int32_t neox,
@@ -421,14 +482,15 @@ int32_t make_plan(int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t R, int3
   if (c.lanes_per_head == 0) {
     E = lanes_fit(R, neox, 8) ? 8 : D / 32;
   } else {
-    if (c.lanes_per_head <= 0 || D % c.lanes_per_head != 0) return QKNR_E_ARG;
+    if (c.lanes_per_head <= 0 || c.lanes_per_head > kWave || D % c.lanes_per_head != 0)
+      return QKNR_E_ARG;
     E = D / c.lanes_per_head;
-    if (E != 8 && E != D / 32) return QKNR_E_ARG;
+    if (E != 8 && E != D / 32 && !(E == D / 64 && E >= 2)) return QKNR_E_ARG;
     if (!lanes_fit(R, neox, E)) return QKNR_E_ARG;
   }
-  const int U = c.unroll == 0 ? 2 : c.unroll;
+  const int U = c.unroll == 0 ? kDefaultUnroll : c.unroll;
   if (U != 1 && U != 2 && U != 4) return QKNR_E_ARG;
-  const int wpb = c.block_waves == 0 ? 4 : c.block_waves;
+  const int wpb = c.block_waves == 0 ? kDefaultBlockWaves : c.block_waves;
   if (wpb < 1 || wpb > kMaxBlockWaves) return QKNR_E_ARG;
   if (c.groups_per_item < 0 || c.max_blocks < -1) return QKNR_E_ARG;
 
@@ -437,7 +499,8 @@ int32_t make_plan(int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t R, int3
   pl->G = kWave / pl->L;
   const int64_t H = static_cast<int64_t>(Hq) + Hkv;
   pl->ng = static_cast<int>((H + pl->G - 1) / pl->G);
-  pl->gpi = std::max(1, c.groups_per_item == 0 ? pl->ng : std::min(c.groups_per_item, pl->ng));
+  const int want_gpi = c.groups_per_item == 0 ? kDefaultGroupsPerItem : c.groups_per_item;
+  pl->gpi = std::max(1, std::min(want_gpi, pl->ng));
   pl->nc = (pl->ng + pl->gpi - 1) / pl->gpi;
   pl->items = T * pl->nc;
   if (pl->items > INT32_MAX) return QKNR_E_SHAPE;
@@ -558,23 +621,25 @@ QKNR_API int32_t qknr_inplace_ex(void* q, void* k, const void* wq, const void* w
 
   // ---- validation done; HIP calls from here on ----
   const int threads = pl.wpb * kWave;
-  const size_t lds = static_cast<size_t>(pl.wpb) * head_dim * sizeof(float);
+  const size_t lds = 0;
   int cus = 0, per_cu = 0;
   const int32_t drc = device_limits(pl.fn, threads, lds, &cus, &per_cu);
   if (drc != QKNR_OK) return drc;
   const int64_t needed = (pl.items + pl.wpb - 1) / pl.wpb;
-  int64_t cap = pl.max_blocks > 0 ? pl.max_blocks : static_cast<int64_t>(cus) * per_cu;
-  if (pl.max_blocks == -1) cap = needed;
+  int64_t cap = needed;
+  if (pl.max_blocks > 0) cap = pl.max_blocks;
+  if (pl.max_blocks == -1) cap = static_cast<int64_t>(cus) * per_cu;
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min(needed, cap)));
   if (info) info->grid_blocks = grid;
 
   Params prm;
-  prm.q = static_cast<char*>(q);
-  prm.k = static_cast<char*>(k);
-  prm.wq = wq ? wq : wk;  // the unused side (0 heads) still gets a readable row
-  prm.wk = wk ? wk : wq;
-  prm.cache = cos_sin_cache;
-  prm.pos = positions;
+  char* qarg = static_cast<char*>(q);
+  char* karg = static_cast<char*>(k);
+  const void* wqarg = wq ? wq : wk;  // the side with 0 heads still gets a readable row
+  const void* wkarg = wk ? wk : wq;
+  const float* carg = cos_sin_cache;
+  const void* parg = positions;
+  prm.cs_vec = (reinterpret_cast<uintptr_t>(cos_sin_cache) % 16 == 0) && ((rope_dim / 2) % 4 == 0);
   prm.q_tok = q_tok_stride_B;
   prm.q_head = q_head_stride_B;
   prm.k_tok = k_tok_stride_B;
@@ -588,7 +653,7 @@ QKNR_API int32_t qknr_inplace_ex(void* q, void* k, const void* wq, const void* w
   prm.gpi = pl.gpi;
   prm.nc = pl.nc;
   prm.n_items = static_cast<int32_t>(pl.items);
-  void* args[] = {&prm};
+  void* args[] = {&qarg, &karg, &wqarg, &wkarg, &carg, &parg, &prm};
   if (hipLaunchKernel(pl.fn, dim3(grid), dim3(threads), args, lds, stream) != hipSuccess)
     return QKNR_E_LAUNCH;
   return QKNR_OK;
@@ -607,12 +672,10 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
 }
 
 static int32_t stream_launch(const void* fn, void** args, int64_t n16, hipStream_t stream) {
-  int dev = 0, cus = 0;
+  int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return QKNR_E_DEVICE;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return QKNR_E_DEVICE;
   const int64_t needed = (n16 + 255) / 256;
-  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(needed, int64_t(cus) * 16)));
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(needed, INT32_MAX)));
   if (hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, stream) != hipSuccess) return QKNR_E_LAUNCH;
   return QKNR_OK;
 }

@@ -102,16 +102,22 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
 
 /*
  * Launch configuration of qknr_inplace_ex. Zero in any field means "choose
- * automatically" (what qknr_inplace does).
+ * automatically" (what qknr_inplace does; the automatic values are given in
+ * brackets).
  *   lanes_per_head   lanes of the 64-lane wavefront that share one head vector:
- *                    head_dim/8 (16-byte accesses per lane) or 32 (half a wave).
+ *                    head_dim/8 (16-byte accesses per lane), 32 (half a wave)
+ *                    or 64 (a full wave; head_dim 128 and 256 only). NeoX needs
+ *                    rope_dim/(head_dim/lanes_per_head) to be a power of two
+ *                    >= 2. [head_dim/8 when that holds, else 32]
  *   groups_per_item  head groups (one per wave instruction: 64/lanes_per_head
  *                    heads of one token) that a wave handles per work item;
- *                    a work item never spans two tokens.
- *   unroll           head groups loaded before the first is computed: 1, 2 or 4.
- *   block_waves      wavefronts per workgroup: 1..8.
- *   max_blocks       > 0 caps the grid (the kernel strides over the remaining
- *                    items); -1 launches one workgroup per block_waves items.
+ *                    a work item never spans two tokens. [4]
+ *   unroll           head groups loaded before the first is computed: 1, 2 or 4. [4]
+ *   block_waves      wavefronts per workgroup: 1..8. [2]
+ *   max_blocks       0: one workgroup per block_waves work items, each wave
+ *                    handles one item [default]; -1: a persistent grid of
+ *                    (occupancy x CUs) workgroups striding over the items;
+ *                    > 0: at most that many workgroups, striding.
  */
 typedef struct qknr_launch_cfg {
   int32_t lanes_per_head;

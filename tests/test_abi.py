@@ -108,7 +108,9 @@ REJECT = [
     (dict(cache=P(A + 2)), B.QKNR_E_ALIGN), (dict(pos=P(A + 2)), B.QKNR_E_ALIGN),
     (dict(pos=P(A + 4), pdt=1), B.QKNR_E_ALIGN),
     (dict(cfg=B.LaunchCfg(lanes_per_head=7)), B.QKNR_E_ARG),
-    (dict(cfg=B.LaunchCfg(lanes_per_head=64)), B.QKNR_E_ARG),
+    (dict(D=64, R=64, cfg=B.LaunchCfg(lanes_per_head=64)), B.QKNR_E_ARG),  # 1 element per lane
+    (dict(cfg=B.LaunchCfg(lanes_per_head=128)), B.QKNR_E_ARG),
+    (dict(cfg=B.LaunchCfg(lanes_per_head=4)), B.QKNR_E_ARG),
     (dict(cfg=B.LaunchCfg(unroll=3)), B.QKNR_E_ARG),
     (dict(cfg=B.LaunchCfg(block_waves=9)), B.QKNR_E_ARG),
     (dict(cfg=B.LaunchCfg(block_waves=-1)), B.QKNR_E_ARG),
@@ -167,6 +169,23 @@ def test_plan_lane_mapping(D):
             assert info["elems_per_lane"] * info["lanes_per_head"] == D
             assert info["heads_per_wave"] == 64 // info["lanes_per_head"]
             assert info["groups_per_token"] == -(-48 // info["heads_per_wave"])
+
+
+def test_plan_defaults():
+    """Automatic launch: 4 head groups per work item, all 4 loaded up front,
+    2 waves per workgroup."""
+    info = _plan(128, 128, 0)
+    assert info["groups_per_item"] == 4 and info["unroll"] == 4
+    assert info["block_threads"] == 128
+    assert _plan(64, 64, 1, Hq=4, Hkv=4)["groups_per_item"] == 1  # one group per token
+
+
+@pytest.mark.parametrize("D,lanes,E", [(128, 64, 2), (256, 64, 4), (128, 32, 4), (64, 32, 2),
+                                      (256, 32, 8)])
+def test_plan_wave_mappings(D, lanes, E):
+    info = _plan(D, D, 0, cfg=B.LaunchCfg(lanes_per_head=lanes))
+    assert (info["lanes_per_head"], info["elems_per_lane"]) == (lanes, E)
+    assert info["heads_per_wave"] == 64 // lanes
 
 
 def test_plan_explicit_cfg():
