@@ -162,29 +162,40 @@ __device__ __forceinline__ float lane_fetch(int byte_addr, float v) {
 // ----------------------------------------------------------------------------
 // Q/K are read and written exactly once: nontemporal accesses keep them from
 // displacing the reused weights, positions and cos|sin rows in L2.
+// Q/K accesses go through raw buffer instructions: a wave-uniform descriptor
+// (base address of the head group, in SGPRs) plus a 32-bit per-lane offset,
+// with the nontemporal cache policy. Offsets stay below 2^31 (checked on the
+// host), far inside the descriptor's range, so no access is out of range.
+constexpr int kBufferFlags = 0x00020000;  // gfx9 raw-buffer descriptor word 3
+constexpr int kCachePolicyNT = 2;          // nontemporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(char* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, kBufferFlags);
+}
+
 template <int NV>
-__device__ __forceinline__ Raw<NV> load_io(const char* p) {
+__device__ __forceinline__ Raw<NV> load_io(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   Raw<NV> r;
   if constexpr (NV == 4) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCachePolicyNT));
     r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
   } else if constexpr (NV == 2) {
-    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kCachePolicyNT));
     r.w[0] = v.x; r.w[1] = v.y;
   } else {
-    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kCachePolicyNT);
   }
   return r;
 }
 
 template <int NV>
-__device__ __forceinline__ void store_io(char* p, const Raw<NV>& r) {
+__device__ __forceinline__ void store_io(__amdgpu_buffer_rsrc_t rs, uint32_t off, const Raw<NV>& r) {
   if constexpr (NV == 4) {
-    __builtin_nontemporal_store(u32x4_t{r.w[0], r.w[1], r.w[2], r.w[3]}, reinterpret_cast<u32x4_t*>(p));
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{r.w[0], r.w[1], r.w[2], r.w[3]}, rs, off, 0, kCachePolicyNT);
   } else if constexpr (NV == 2) {
-    __builtin_nontemporal_store(u32x2_t{r.w[0], r.w[1]}, reinterpret_cast<u32x2_t*>(p));
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{r.w[0], r.w[1]}, rs, off, 0, kCachePolicyNT);
   } else {
-    __builtin_nontemporal_store(r.w[0], reinterpret_cast<uint32_t*>(p));
+    __builtin_amdgcn_raw_buffer_store_b32(r.w[0], rs, off, 0, kCachePolicyNT);
   }
 }
 
@@ -196,51 +207,54 @@ __device__ __forceinline__ int64_t token_position(const void* pos, int pos64, in
 }
 
 struct Params {
-  int64_t q_tok, q_head, k_tok, k_head;  // byte strides
+  int64_t q_tok, k_tok;          // token strides (bytes)
+  int64_t q_grp, k_grp;          // bytes between consecutive head groups (G head strides)
+  uint32_t q_head, k_head;       // head strides (bytes); (G-1)*stride + 2*D fits 32 bits
   int32_t Hq, Hkv, R;
+  int32_t ngq;                   // Q head groups per token; K groups follow them
   int32_t pos64;
-  int32_t cs_vec;   // cache rows 16-byte aligned and R/2 % 4 == 0
+  int32_t cs_vec;                // cache rows 16-byte aligned and R/2 % 4 == 0
   float eps;
-  int32_t ng, gpi, nc, n_items;
+  int32_t ng, gpi, nc, n_items;  // groups per token, groups per item, items per token, items
 };
 
+// One wave instruction covers one head group: G consecutive heads of Q, or of
+// K, of one token (groups never mix Q and K), so the group's base address is
+// wave-uniform and each lane adds a fixed 32-bit offset.
 template <class IO, int D, int E, bool NEOX, bool FULL, int U>
 __global__ void __launch_bounds__(kMaxBlockWaves * kWave)
 qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict__ wqp,
             const void* __restrict__ wkp, const float* __restrict__ cache,
             const void* __restrict__ posp, const Params p) {
-  constexpr int L = D / E;
-  constexpr int G = kWave / L;
-  constexpr int NV = E / 2;
-  constexpr int NCS = NEOX ? E : E / 2;
+  constexpr int L = D / E;      // lanes per head
+  constexpr int G = kWave / L;  // heads per wave instruction
+  constexpr int NV = E / 2;     // packed dwords per lane
+  constexpr int NCS = NEOX ? E : E / 2;  // cos (and sin) values per lane
   static_assert(D % E == 0 && E % 2 == 0 && G >= 1, "lane mapping");
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
-  const int sub = lane / L;
-  const int li = lane % L;
-  const int d0 = li * E;
-  const int H = p.Hq + p.Hkv;
+  const int sub = lane / L;  // head slot in the group
+  const int li = lane % L;   // lane inside the head
+  const int d0 = li * E;     // first dim owned by this lane
   const int R = FULL ? D : p.R;
   const int half = R / 2;
+  const uint32_t q_off = static_cast<uint32_t>(sub) * p.q_head + d0 * 2;
+  const uint32_t k_off = static_cast<uint32_t>(sub) * p.k_head + d0 * 2;
 
-  float wq[E], wk[E];
-  {
-    const Raw<NV> a = load_raw<NV>(static_cast<const char*>(wqp) + d0 * 2);
-    const Raw<NV> b = load_raw<NV>(static_cast<const char*>(wkp) + d0 * 2);
-#pragma unroll
-    for (int w = 0; w < NV; ++w) {
-      IO::unpack(a.w[w], wq[2 * w], wq[2 * w + 1]);
-      IO::unpack(b.w[w], wk[2 * w], wk[2 * w + 1]);
-    }
-  }
+  // Weights of this lane's dims, kept packed (widened per use).
+  const Raw<NV> wq_p = load_raw<NV>(static_cast<const char*>(wqp) + d0 * 2);
+  const Raw<NV> wk_p = load_raw<NV>(static_cast<const char*>(wkp) + d0 * 2);
+
+  // NeoX: this lane holds dims d0..d0+E-1; their partners d +- R/2 sit at the
+  // same offsets in lane ^ m. Lanes of the lower half subtract.
   int partner_addr = 0, j0 = 0;
   bool lower = false, lane_rot = true;
   if constexpr (NEOX) {
     const int m = half / E;
     partner_addr = (lane ^ m) << 2;
     lower = (li & m) == 0;
-    j0 = d0 & (half - 1);
+    j0 = d0 & (half - 1);  // half is a power of two for NeoX
     lane_rot = FULL || d0 < R;
   } else {
     j0 = d0 / 2;
@@ -258,33 +272,34 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
     const int64_t pos = pos_next;
     if (item + total_waves < p.n_items)
       pos_next = token_position(posp, p.pos64, (item + total_waves) / p.nc);
-    char* qrow = qb + t * p.q_tok;
-    char* krow = kb + t * p.k_tok;
+    char* const qrow = qb + t * p.q_tok;
+    char* const krow = kb + t * p.k_tok;
 
-    Raw<NV> ra[U];
-    char* pa[U];
-    bool oka[U], ka[U];
-    auto issue = [&](Raw<NV>* raw, char** ptr, bool* ok, bool* isk, int g) {
+    Raw<NV> raw[U];
+    __amdgpu_buffer_rsrc_t rs[U];
+    uint32_t off[U];
+    bool ok[U], isk[U];
+    auto issue = [&](int g) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int h = (g + u) * G + sub;
-        ok[u] = (g + u < g_end) && (h < H);
-        isk[u] = h >= p.Hq;
-        const int hh = isk[u] ? h - p.Hq : h;
-        char* base = isk[u] ? krow + static_cast<int64_t>(hh) * p.k_head
-                            : qrow + static_cast<int64_t>(hh) * p.q_head;
-        ptr[u] = base + d0 * 2;
+        const int gu = g + u;
+        isk[u] = gu >= p.ngq;  // wave-uniform
+        const int gg = isk[u] ? gu - p.ngq : gu;
+        rs[u] = head_rsrc(isk[u] ? krow + gg * p.k_grp : qrow + gg * p.q_grp);
+        off[u] = isk[u] ? k_off : q_off;
+        ok[u] = gu < g_end && gg * G + sub < (isk[u] ? p.Hkv : p.Hq);
         if (ok[u]) {
-          raw[u] = load_io<NV>(ptr[u]);
+          raw[u] = load_io<NV>(rs[u], off[u]);
         } else {
 #pragma unroll
           for (int w = 0; w < NV; ++w) raw[u].w[w] = 0u;
         }
       }
     };
-    issue(ra, pa, oka, ka, g_begin);
+    issue(g_begin);
 
-    // cos / sin of this lane's dims at this token
+    // cos / sin of this lane's dims at this token (loaded after the head data
+    // is in flight; kept in registers for every group of the item)
     float cs[NCS], sn[NCS];
     const float* row = cache + pos * R;
     if ((FULL || NEOX) && NCS % 4 == 0 && p.cs_vec) {
@@ -308,7 +323,8 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
       for (int i = 0; i < NCS; ++i) sn[i] = lower ? -sn[i] : sn[i];
     }
 
-    auto compute = [&](const Raw<NV>* raw, char* const* ptr, const bool* ok, const bool* isk) {
+    for (int g = g_begin; g < g_end; g += U) {
+      if (g != g_begin) issue(g);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float x[E];
@@ -321,7 +337,12 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
         const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / D, p.eps));
         float n[E];
 #pragma unroll
-        for (int i = 0; i < E; ++i) n[i] = x[i] * r * (isk[u] ? wk[i] : wq[i]);
+        for (int w = 0; w < NV; ++w) {
+          float w0, w1;
+          IO::unpack(isk[u] ? wk_p.w[w] : wq_p.w[w], w0, w1);
+          n[2 * w] = x[2 * w] * r * w0;
+          n[2 * w + 1] = x[2 * w + 1] * r * w1;
+        }
         float o[E];
         if constexpr (NEOX) {
 #pragma unroll
@@ -344,13 +365,8 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
         Raw<NV> out;
 #pragma unroll
         for (int w = 0; w < NV; ++w) out.w[w] = IO::pack(o[2 * w], o[2 * w + 1]);
-        if (ok[u]) store_io<NV>(ptr[u], out);
+        if (ok[u]) store_io<NV>(rs[u], off[u], out);
       }
-    };
-
-    for (int g = g_begin; g < g_end; g += U) {
-      if (g != g_begin) issue(ra, pa, oka, ka, g);
-      compute(ra, pa, oka, ka);
     }
   }
 }
@@ -461,32 +477,55 @@ bool views_ok(int64_t T, int64_t H, int64_t tok, int64_t head, int64_t vec_bytes
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Launch defaults, chosen by measurement on MI355X (launch-shape sweeps over
-// the five benchmark workloads): one work item per wave with no persistent
-// grid, 4 head groups per item, all 4 loaded before the first is computed,
-// 2 waves per workgroup.
-constexpr int kDefaultGroupsPerItem = 4;
-constexpr int kDefaultUnroll = 4;
-constexpr int kDefaultBlockWaves = 2;
+// the benchmark workloads): one work item per wave with no persistent grid,
+// 2 head groups per item, both loaded before the first is computed, 4 waves
+// per workgroup.
+constexpr int kDefaultGroupsPerItem = 2;
+constexpr int kDefaultUnroll = 2;
+constexpr int kDefaultBlockWaves = 4;
 
 struct Plan {
   const void* fn = nullptr;
-  int E = 8, L = 8, G = 8, ng = 0, gpi = 0, nc = 0, U = kDefaultUnroll, wpb = kDefaultBlockWaves;
+  int E = 8, L = 8, G = 8, ngq = 0, ng = 0, gpi = 0, nc = 0, U = kDefaultUnroll,
+      wpb = kDefaultBlockWaves;
   int64_t items = 0;
   int max_blocks = 0;  // 0: one workgroup per wpb items; -1: occupancy x CUs; > 0: explicit cap
 };
 
+// A lane's byte offset inside its head group, (heads-1)*head_stride + 2*D at
+// most, must stay below 2^31 (head-major layouts with a huge T can exceed it
+// for groups of several heads; a mapping with fewer heads per group is used).
+constexpr int64_t kMaxLaneOffset = (int64_t{1} << 31) - 1;
+
+bool lane_offsets_fit(int G, int32_t H, int64_t head_stride, int32_t D) {
+  const int64_t heads = std::min<int64_t>(G, H);
+  if (heads <= 1) return true;
+  if (head_stride < 0 || head_stride > (kMaxLaneOffset - 2 * D) / (heads - 1)) return false;
+  return true;
+}
+
 int32_t make_plan(int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t R, int32_t neox,
-                  int32_t dtype, const qknr_launch_cfg* cfg, Plan* pl) {
+                  int32_t dtype, int64_t q_head, int64_t k_head, const qknr_launch_cfg* cfg,
+                  Plan* pl) {
   qknr_launch_cfg c = cfg ? *cfg : qknr_launch_cfg{0, 0, 0, 0, 0};
-  int E;
+  auto fits = [&](int E) {
+    const int G = kWave / (D / E);
+    return lane_offsets_fit(G, Hq, q_head, D) && lane_offsets_fit(G, Hkv, k_head, D);
+  };
+  int E = 0;
   if (c.lanes_per_head == 0) {
-    E = lanes_fit(R, neox, 8) ? 8 : D / 32;
+    // 16-byte lanes first; then half a wave and a full wave per head
+    const int cand[3] = {8, D / 32, D / 64};
+    for (int e : cand) {
+      if (e >= 2 && lanes_fit(R, neox, e) && fits(e)) { E = e; break; }
+    }
+    if (E == 0) return QKNR_E_SHAPE;
   } else {
     if (c.lanes_per_head <= 0 || c.lanes_per_head > kWave || D % c.lanes_per_head != 0)
       return QKNR_E_ARG;
     E = D / c.lanes_per_head;
     if (E != 8 && E != D / 32 && !(E == D / 64 && E >= 2)) return QKNR_E_ARG;
-    if (!lanes_fit(R, neox, E)) return QKNR_E_ARG;
+    if (!lanes_fit(R, neox, E) || !fits(E)) return QKNR_E_ARG;
   }
   const int U = c.unroll == 0 ? kDefaultUnroll : c.unroll;
   if (U != 1 && U != 2 && U != 4) return QKNR_E_ARG;
@@ -497,8 +536,8 @@ int32_t make_plan(int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t R, int3
   pl->E = E;
   pl->L = D / E;
   pl->G = kWave / pl->L;
-  const int64_t H = static_cast<int64_t>(Hq) + Hkv;
-  pl->ng = static_cast<int>((H + pl->G - 1) / pl->G);
+  pl->ngq = (Hq + pl->G - 1) / pl->G;
+  pl->ng = pl->ngq + (Hkv + pl->G - 1) / pl->G;
   const int want_gpi = c.groups_per_item == 0 ? kDefaultGroupsPerItem : c.groups_per_item;
   pl->gpi = std::max(1, std::min(want_gpi, pl->ng));
   pl->nc = (pl->ng + pl->gpi - 1) / pl->gpi;
@@ -590,7 +629,8 @@ QKNR_API int32_t qknr_inplace_ex(void* q, void* k, const void* wq, const void* w
   if (T > INT32_MAX || T * (static_cast<int64_t>(Hq) + Hkv) > INT32_MAX) return QKNR_E_SHAPE;
 
   Plan pl;
-  const int32_t prc = make_plan(T, Hq, Hkv, head_dim, rope_dim, is_neox, dtype, cfg, &pl);
+  const int32_t prc = make_plan(T, Hq, Hkv, head_dim, rope_dim, is_neox, dtype, q_head_stride_B,
+                                k_head_stride_B, cfg, &pl);
   if (prc != QKNR_OK) return prc;
   if (info) {
     info->lanes_per_head = pl.L;
@@ -640,10 +680,15 @@ QKNR_API int32_t qknr_inplace_ex(void* q, void* k, const void* wq, const void* w
   const float* carg = cos_sin_cache;
   const void* parg = positions;
   prm.cs_vec = (reinterpret_cast<uintptr_t>(cos_sin_cache) % 16 == 0) && ((rope_dim / 2) % 4 == 0);
+  // head strides only matter for views with more than one head
+  const int64_t qh = Hq > 1 ? q_head_stride_B : 0, kh = Hkv > 1 ? k_head_stride_B : 0;
   prm.q_tok = q_tok_stride_B;
-  prm.q_head = q_head_stride_B;
   prm.k_tok = k_tok_stride_B;
-  prm.k_head = k_head_stride_B;
+  prm.q_grp = qh * pl.G;
+  prm.k_grp = kh * pl.G;
+  prm.q_head = static_cast<uint32_t>(qh);
+  prm.k_head = static_cast<uint32_t>(kh);
+  prm.ngq = pl.ngq;
   prm.Hq = Hq;
   prm.Hkv = Hkv;
   prm.R = rope_dim;

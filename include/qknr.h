@@ -111,9 +111,9 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
  *                    >= 2. [head_dim/8 when that holds, else 32]
  *   groups_per_item  head groups (one per wave instruction: 64/lanes_per_head
  *                    heads of one token) that a wave handles per work item;
- *                    a work item never spans two tokens. [4]
- *   unroll           head groups loaded before the first is computed: 1, 2 or 4. [4]
- *   block_waves      wavefronts per workgroup: 1..8. [2]
+ *                    a work item never spans two tokens. [2]
+ *   unroll           head groups loaded before the first is computed: 1, 2 or 4. [2]
+ *   block_waves      wavefronts per workgroup: 1..8. [4]
  *   max_blocks       0: one workgroup per block_waves work items, each wave
  *                    handles one item [default]; -1: a persistent grid of
  *                    (occupancy x CUs) workgroups striding over the items;

@@ -168,16 +168,22 @@ def test_plan_lane_mapping(D):
             assert info["lanes_per_head"] == want_lanes, (D, R, neox, info)
             assert info["elems_per_lane"] * info["lanes_per_head"] == D
             assert info["heads_per_wave"] == 64 // info["lanes_per_head"]
-            assert info["groups_per_token"] == -(-48 // info["heads_per_wave"])
+            G = info["heads_per_wave"]
+            assert info["groups_per_token"] == -(-24 // G) + -(-24 // G)
+            gqa = _plan(D, R, neox, Hq=7, Hkv=3)
+            assert gqa["groups_per_token"] == -(-7 // gqa["heads_per_wave"]) + -(-3 // gqa["heads_per_wave"])
 
 
 def test_plan_defaults():
-    """Automatic launch: 4 head groups per work item, all 4 loaded up front,
-    2 waves per workgroup."""
+    """Automatic launch: 2 head groups per work item, both loaded up front,
+    4 waves per workgroup."""
     info = _plan(128, 128, 0)
-    assert info["groups_per_item"] == 4 and info["unroll"] == 4
-    assert info["block_threads"] == 128
-    assert _plan(64, 64, 1, Hq=4, Hkv=4)["groups_per_item"] == 1  # one group per token
+    assert info["groups_per_item"] == 2 and info["unroll"] == 2
+    assert info["block_threads"] == 256
+    # head groups never mix Q and K heads: 4 Q + 4 K heads of head_dim 64 (8 per
+    # wave instruction) are two half-filled groups, one work item
+    tiny = _plan(64, 64, 1, Hq=4, Hkv=4)
+    assert tiny["groups_per_token"] == 2 and tiny["groups_per_item"] == 2
 
 
 @pytest.mark.parametrize("D,lanes,E", [(128, 64, 2), (256, 64, 4), (128, 32, 4), (64, 32, 2),
@@ -222,3 +228,27 @@ def test_harness_layouts_on_host():
 
         assert torch.equal(dc.q.contiguous().view(torch.int16),
                            torch.from_numpy(wl.q.view(np.int16))), layout
+
+
+def test_plan_falls_back_to_fewer_heads_per_group_for_huge_head_strides():
+    """Lane offsets inside a head group must stay below 2^31: with head-major
+    views whose head stride is ~1 GiB (or ~3 GiB) the planner takes a mapping
+    with fewer heads per wave instruction, and rejects what none can address."""
+    def plan(D, head_stride, Hq=8):
+        info = B.LaunchInfo()
+        z = P(0)
+        rc = B.lib().qknr_inplace_ex(z, z, z, z, z, z, 0, Hq, 0, D, D, 0, 1e-6, 2 * D,
+                                     head_stride, 2 * D, 2 * D, 0, 0, z, None,
+                                     ctypes.byref(info))
+        return rc, info.as_dict()
+
+    rc, info = plan(128, 2 * 128)
+    assert rc == 0 and info["lanes_per_head"] == 16
+    rc, info = plan(128, 1 << 30)
+    assert rc == 0 and info["lanes_per_head"] == 32
+    rc, info = plan(128, 3 << 30)
+    assert rc == 0 and info["lanes_per_head"] == 64
+    rc, _ = plan(64, 3 << 30)
+    assert rc == B.QKNR_E_SHAPE
+    rc, info = plan(64, 3 << 30, Hq=1)  # one head: its stride is never used
+    assert rc == 0 and info["lanes_per_head"] == 8
