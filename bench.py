@@ -51,6 +51,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-yardstick", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true", help="skip timing the two-launch baseline")
     ap.add_argument("--sweep", action="store_true", help="time a short list of launch configurations")
     ap.add_argument("--sweep-grid", action="store_true",
                     help="time every (grid kind, groups per item, unroll, block waves) combination")
@@ -101,7 +102,7 @@ class Rig:
             return q, k
         return bufs[0], bufs[1]
 
-    def prepare(self, launch=None):
+    def prepare(self, launch=None, unfused=False):
         import torch
 
         from head_qk_rmsnorm_amd import binding as B
@@ -111,7 +112,8 @@ class Rig:
         for bufs, pos in self.copies:
             q, k = self.views(bufs)
             self.calls.append(B.PreparedCall(q, k, self.wq, self.wk, self.cache, pos,
-                                             is_neox=c.is_neox, eps=c.eps, launch=launch))
+                                             is_neox=c.is_neox, eps=c.eps, launch=launch,
+                                             unfused=unfused))
         self.calls[0]()
         torch.cuda.synchronize(self.dev)
         self.info = self.calls[0].info.as_dict()
@@ -223,7 +225,15 @@ def counters_for(cfg_name):
     return ent, None
 
 
-def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None):
+def unfused_bytes(cfg):
+    """Bytes the two-launch chain must move: Q/K read and written by each step,
+    the weights by the norm step, positions and cos|sin rows by the rope step."""
+    D, R = cfg.head_dim, cfg.rope_dim
+    qk = 2 * cfg.units * D * cfg.io_bytes
+    return 2 * qk + 2 * D * cfg.io_bytes + cfg.T * cfg.pos_bytes + cfg.T * R * 4
+
+
+def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None, want_unfused=True):
     own = rig is None
     if own:
         rig = Rig(cfg, dev, launch=launch)
@@ -238,6 +248,16 @@ def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None):
         "algorithmic_bytes": B, "n_rot": rig.n_rot, "footprint_bytes": rig.footprint,
         "launch": rig.info,
     }
+    if want_unfused:
+        rig.prepare(unfused=True)
+        ums, _, _ = rig.time(steps, warmup)
+        ub = unfused_bytes(cfg)
+        out["unfused"] = {
+            "ms_per_step": ums, "launches_per_step": 2, "bytes_per_step": ub,
+            "GB_s": ub / (ums * 1e-3) / 1e9, "speedup_fused_over_unfused": ums / ms,
+            "bytes_ratio_unfused_over_fused": ub / B,
+        }
+        rig.prepare(launch)
     if own:
         del rig
     if want_yard:
@@ -291,7 +311,8 @@ def main():
         rig = Rig(cfg, dev)
         for lc in (SWEEP_GRID if args.sweep_grid else SWEEP):
             try:
-                r = measure(cfg, dev, args.steps, args.warmup, lc, want_yard=False, rig=rig)
+                r = measure(cfg, dev, args.steps, args.warmup, lc, want_yard=False, rig=rig,
+                            want_unfused=False)
             except RuntimeError as e:
                 r = {"workload": cfg.name, "error": str(e)}
             r["sweep_launch"] = lc
@@ -302,15 +323,22 @@ def main():
         del rig
     if args.all_configs:
         for name in W.CONFIG_ORDER:
-            r = measure(W.CONFIGS[name], dev, args.steps, args.warmup, launch)
-            print(f"[bench] {name}: {r['GB_s']:.1f} GB/s ({r['frac_of_peak'] * 100:.1f}% of peak), "
-                  f"{r['gheads_per_s']:.2f} Gheads/s, yardstick {r['yardstick_GB_s']:.1f} GB/s",
-                  file=sys.stderr, flush=True)
+            r = measure(W.CONFIGS[name], dev, args.steps, args.warmup, launch,
+                        want_yard=not args.no_yardstick, want_unfused=not args.no_unfused)
+            msg = (f"[bench] {name}: {r['GB_s']:.1f} GB/s ({r['frac_of_peak'] * 100:.1f}% of peak), "
+                   f"{r['gheads_per_s']:.2f} Gheads/s")
+            if "yardstick_GB_s" in r:
+                msg += f", yardstick {r['yardstick_GB_s']:.1f} GB/s"
+            if "unfused" in r:
+                msg += (f", unfused pair {r['unfused']['ms_per_step'] * 1e3:.2f} us "
+                        f"(fused {r['unfused']['speedup_fused_over_unfused']:.2f}x faster)")
+            print(msg, file=sys.stderr, flush=True)
             if extra:
                 extra.write(json.dumps(r) + "\n")
                 extra.flush()
 
-    r = measure(cfg, dev, args.steps, args.warmup, launch, want_yard=not args.no_yardstick)
+    r = measure(cfg, dev, args.steps, args.warmup, launch, want_yard=not args.no_yardstick,
+                want_unfused=not args.no_unfused)
     print(f"[bench] {cfg.name}: {r['GB_s']:.1f} GB/s, {r['ms_per_step'] * 1e3:.2f} us/launch",
           file=sys.stderr, flush=True)
     ent, why = counters_for(cfg.name)
@@ -343,6 +371,18 @@ def main():
         line["yardstick"] = {"kind": "in-place 16-byte read-xor-write over the same Q/K bytes",
                              "GB_s": round(r["yardstick_GB_s"], 3),
                              "frac_of_yardstick": round(r["frac_of_yardstick"], 5)}
+    if "unfused" in r:
+        u = r["unfused"]
+        line["fusion"] = {
+            "unfused_ms_per_step": round(u["ms_per_step"], 6),
+            "unfused_launches_per_step": 2,
+            "unfused_bytes_per_step": u["bytes_per_step"],
+            "speedup_fused_over_unfused": round(u["speedup_fused_over_unfused"], 4),
+            "bytes_ratio_unfused_over_fused": round(u["bytes_ratio_unfused_over_fused"], 4),
+            "page_claim": "separate norm + RoPE kernels: 2 launches, Q/K read and written twice; "
+                          "fused: about half the memory traffic and close to 2x faster (no "
+                          "hardware or measured figure given)",
+        }
     line["host_ms_per_launch"] = round(r["host_ms_per_launch"], 5)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)

@@ -7,7 +7,9 @@ status. torch provides device memory and streams, nothing else. There is no
 fallback: if the library is missing or rejects the call, an exception is raised.
 
 Names mirror the C entry points (``qknr_inplace``, ``qknr_inplace_ex``,
-``qknr_can_use``, ``qknr_status_string``), plus ``fused_inplace_qknorm_rope``
+``qknr_can_use``, ``qknr_status_string``, the unfused baseline
+``qknr_rmsnorm_inplace`` / ``qknr_rope_inplace`` / ``qknr_unfused_inplace``,
+and the measurement aids ``qknr_copy`` / ``qknr_rmw``), plus ``fused_inplace_qknorm_rope``
 with the signature of the op on the page "SGLang Diffusion fused operator
 fused_inplace_qknorm_rope: in-depth technical analysis" (m.lsln.cn/news/241376),
 section 5.3: q and k are modified in place and nothing is returned.
@@ -83,6 +85,14 @@ def lib() -> ctypes.CDLL:
             L.qknr_can_use.restype = _I32
             L.qknr_status_string.argtypes = [_I32]
             L.qknr_status_string.restype = ctypes.c_char_p
+            L.qknr_unfused_inplace.argtypes = INPLACE_ARGTYPES
+            L.qknr_unfused_inplace.restype = _I32
+            L.qknr_rmsnorm_inplace.argtypes = [_P, _P, _P, _P, _I64, _I32, _I32, _I32,
+                                               ctypes.c_float, _I64, _I64, _I64, _I64, _I32, _P]
+            L.qknr_rmsnorm_inplace.restype = _I32
+            L.qknr_rope_inplace.argtypes = [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32,
+                                            _I64, _I64, _I64, _I64, _I32, _I32, _P]
+            L.qknr_rope_inplace.restype = _I32
             L.qknr_copy.argtypes = [_P, _P, _I64, _P]
             L.qknr_copy.restype = _I32
             L.qknr_rmw.argtypes = [_P, _I64, ctypes.c_uint32, _P]
@@ -132,44 +142,71 @@ def _check(rc: int) -> None:
         raise RuntimeError(qknr_status_string(rc))
 
 
-def _marshal(q, k, q_weight, k_weight, cos_sin_cache, positions, is_neox, eps, head_dim,
-             rope_dim):
+def _on_device(ref, **named):
+    """Every named tensor is a torch tensor on ref's HIP device."""
     import torch
 
-    for name, t in (("q", q), ("k", k), ("q_weight", q_weight), ("k_weight", k_weight),
-                    ("cos_sin_cache", cos_sin_cache), ("positions", positions)):
+    for name, t in named.items():
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
         if t.device.type != "cuda":
             raise ValueError(f"{name} must be on a HIP device, got {t.device}")
-        if t.device != q.device:
-            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, q on {ref.device}")
+
+
+def _qk(q, k, head_dim):
+    """q [T,Hq,D], k [T,Hkv,D] -> pointers, sizes, byte strides, dtype code."""
+    _on_device(q, q=q, k=k)
     if q.dim() != 3 or k.dim() != 3:
         raise ValueError("q must be [T, Hq, D] and k [T, Hkv, D]")
     D = int(head_dim) or int(q.size(-1))
-    R = int(rope_dim) or int(cos_sin_cache.size(-1))
     T = int(q.size(0))
     if q.size(-1) != D or k.size(-1) != D or k.size(0) != T:
         raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} disagree with head_dim={D}")
     if (q.numel() and q.stride(2) != 1) or (k.numel() and k.stride(2) != 1):
         raise ValueError("the innermost (head_dim) stride of q and k must be 1")
-    if k.dtype != q.dtype or q_weight.dtype != q.dtype or k_weight.dtype != q.dtype:
-        raise TypeError("q, k, q_weight and k_weight must share one dtype")
+    if k.dtype != q.dtype:
+        raise TypeError("q and k must share one dtype")
+    es = q.element_size()
+    return dict(q=ctypes.c_void_p(q.data_ptr()), k=ctypes.c_void_p(k.data_ptr()), T=T,
+                Hq=int(q.size(1)), Hkv=int(k.size(1)), D=D, qt=int(q.stride(0)) * es,
+                qh=int(q.stride(1)) * es, kt=int(k.stride(0)) * es, kh=int(k.stride(1)) * es,
+                dtype=_dtype_code(q.dtype))
+
+
+def _weights(q, q_weight, k_weight, D):
+    _on_device(q, q_weight=q_weight, k_weight=k_weight)
+    if q_weight.dtype != q.dtype or k_weight.dtype != q.dtype:
+        raise TypeError("q_weight and k_weight must have the dtype of q and k")
     if tuple(q_weight.shape) != (D,) or tuple(k_weight.shape) != (D,) \
             or not q_weight.is_contiguous() or not k_weight.is_contiguous():
         raise ValueError(f"weights must be contiguous [{D}]")
+    return ctypes.c_void_p(q_weight.data_ptr()), ctypes.c_void_p(k_weight.data_ptr())
+
+
+def _rotation(q, cos_sin_cache, positions, T, rope_dim):
+    import torch
+
+    _on_device(q, cos_sin_cache=cos_sin_cache, positions=positions)
+    R = int(rope_dim) or int(cos_sin_cache.size(-1))
     if cos_sin_cache.dtype != torch.float32 or cos_sin_cache.dim() != 2 \
             or cos_sin_cache.size(1) != R or not cos_sin_cache.is_contiguous():
         raise ValueError(f"cos_sin_cache must be a contiguous float32 [rows, {R}] table")
     if positions.dim() != 1 or positions.size(0) != T or not positions.is_contiguous():
         raise ValueError(f"positions must be a contiguous [{T}] vector")
-    es = q.element_size()
-    return (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
-            ctypes.c_void_p(q_weight.data_ptr()), ctypes.c_void_p(k_weight.data_ptr()),
-            ctypes.c_void_p(cos_sin_cache.data_ptr()), ctypes.c_void_p(positions.data_ptr()),
-            T, int(q.size(1)), int(k.size(1)), D, R, int(bool(is_neox)), float(eps),
-            int(q.stride(0)) * es, int(q.stride(1)) * es, int(k.stride(0)) * es,
-            int(k.stride(1)) * es, _dtype_code(q.dtype), _pos_code(positions.dtype))
+    return (ctypes.c_void_p(cos_sin_cache.data_ptr()), ctypes.c_void_p(positions.data_ptr()), R,
+            _pos_code(positions.dtype))
+
+
+def _marshal(q, k, q_weight, k_weight, cos_sin_cache, positions, is_neox, eps, head_dim,
+             rope_dim):
+    """All arguments of qknr_inplace except the stream, in ABI order."""
+    v = _qk(q, k, head_dim)
+    wq, wk = _weights(q, q_weight, k_weight, v["D"])
+    cache, pos, R, pcode = _rotation(q, cos_sin_cache, positions, v["T"], rope_dim)
+    return (v["q"], v["k"], wq, wk, cache, pos, v["T"], v["Hq"], v["Hkv"], v["D"], R,
+            int(bool(is_neox)), float(eps), v["qt"], v["qh"], v["kt"], v["kh"], v["dtype"], pcode)
 
 
 def _stream_of(q, stream):
@@ -210,6 +247,44 @@ def qknr_inplace_ex(q, k, q_weight, k_weight, cos_sin_cache, positions, *, is_ne
     return info.as_dict()
 
 
+def qknr_unfused_inplace(q, k, q_weight, k_weight, cos_sin_cache, positions, *,
+                         is_neox: bool, eps: float = 1e-6, head_dim: int = 0, rope_dim: int = 0,
+                         stream=None) -> None:
+    """The two-launch baseline (RMSNorm step, intermediate rounded to the I/O
+    type, then RoPE step); same arguments and result layout as qknr_inplace."""
+    import torch
+
+    args = _marshal(q, k, q_weight, k_weight, cos_sin_cache, positions, is_neox, eps,
+                    head_dim, rope_dim)
+    with torch.cuda.device(q.device):
+        _check(lib().qknr_unfused_inplace(*args, _stream_of(q, stream)))
+
+
+def qknr_rmsnorm_inplace(q, k, q_weight, k_weight, *, eps: float = 1e-6, stream=None) -> None:
+    """The norm step alone, in place on q [T,Hq,D] and k [T,Hkv,D]."""
+    import torch
+
+    v = _qk(q, k, 0)
+    wq, wk = _weights(q, q_weight, k_weight, v["D"])
+    with torch.cuda.device(q.device):
+        _check(lib().qknr_rmsnorm_inplace(v["q"], v["k"], wq, wk, v["T"], v["Hq"], v["Hkv"], v["D"],
+                                          float(eps), v["qt"], v["qh"], v["kt"], v["kh"],
+                                          v["dtype"], _stream_of(q, stream)))
+
+
+def qknr_rope_inplace(q, k, cos_sin_cache, positions, *, is_neox: bool, rope_dim: int = 0,
+                      stream=None) -> None:
+    """The rotation step alone (no norm), in place on q and k."""
+    import torch
+
+    v = _qk(q, k, 0)
+    cache, pos, R, pcode = _rotation(q, cos_sin_cache, positions, v["T"], rope_dim)
+    with torch.cuda.device(q.device):
+        _check(lib().qknr_rope_inplace(v["q"], v["k"], cache, pos, v["T"], v["Hq"], v["Hkv"], v["D"],
+                                       R, int(bool(is_neox)), v["qt"], v["qh"], v["kt"], v["kh"],
+                                       v["dtype"], pcode, _stream_of(q, stream)))
+
+
 def fused_inplace_qknorm_rope(q, k, q_weight, k_weight, cos_sin_cache, positions, *,
                               is_neox: bool, eps: float = 1e-6, head_dim: int = 0,
                               rope_dim: int = 0) -> None:
@@ -246,16 +321,22 @@ class PreparedCall:
 
     def __init__(self, q, k, q_weight, k_weight, cos_sin_cache, positions, *, is_neox: bool,
                  eps: float = 1e-6, head_dim: int = 0, rope_dim: int = 0, stream=None,
-                 launch: Optional[dict] = None):
+                 launch: Optional[dict] = None, unfused: bool = False):
         self._keep = (q, k, q_weight, k_weight, cos_sin_cache, positions)
         self._device = q.device
         args = _marshal(q, k, q_weight, k_weight, cos_sin_cache, positions, is_neox, eps,
                         head_dim, rope_dim)
         self._cfg = LaunchCfg(**(launch or {}))
         self.info = LaunchInfo()
-        self._args = args + (_stream_of(q, stream), ctypes.byref(self._cfg),
-                             ctypes.byref(self.info))
-        self._fn = lib().qknr_inplace_ex
+        if unfused:
+            if launch:
+                raise ValueError("the unfused baseline takes no launch configuration")
+            self._args = args + (_stream_of(q, stream),)
+            self._fn = lib().qknr_unfused_inplace
+        else:
+            self._args = args + (_stream_of(q, stream), ctypes.byref(self._cfg),
+                                 ctypes.byref(self.info))
+            self._fn = lib().qknr_inplace_ex
 
     def __call__(self) -> None:
         rc = self._fn(*self._args)

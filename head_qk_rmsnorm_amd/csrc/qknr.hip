@@ -218,10 +218,15 @@ struct Params {
   int32_t ng, gpi, nc, n_items;  // groups per token, groups per item, items per token, items
 };
 
+// What a launch computes: the fused op, or one of the two steps of the
+// unfused chain it replaces (norm only: rotation skipped; rope only: the
+// stored values are rotated as they are, no norm).
+enum : int { kFused = 0, kNormOnly = 1, kRopeOnly = 2 };
+
 // One wave instruction covers one head group: G consecutive heads of Q, or of
 // K, of one token (groups never mix Q and K), so the group's base address is
 // wave-uniform and each lane adds a fixed 32-bit offset.
-template <class IO, int D, int E, bool NEOX, bool FULL, int U>
+template <class IO, int D, int E, bool NEOX, bool FULL, int U, int MODE>
 __global__ void __launch_bounds__(kMaxBlockWaves * kWave)
 qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict__ wqp,
             const void* __restrict__ wkp, const float* __restrict__ cache,
@@ -243,8 +248,11 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   const uint32_t k_off = static_cast<uint32_t>(sub) * p.k_head + d0 * 2;
 
   // Weights of this lane's dims, kept packed (widened per use).
-  const Raw<NV> wq_p = load_raw<NV>(static_cast<const char*>(wqp) + d0 * 2);
-  const Raw<NV> wk_p = load_raw<NV>(static_cast<const char*>(wkp) + d0 * 2);
+  Raw<NV> wq_p{}, wk_p{};
+  if constexpr (MODE != kRopeOnly) {
+    wq_p = load_raw<NV>(static_cast<const char*>(wqp) + d0 * 2);
+    wk_p = load_raw<NV>(static_cast<const char*>(wkp) + d0 * 2);
+  }
 
   // NeoX: this lane holds dims d0..d0+E-1; their partners d +- R/2 sit at the
   // same offsets in lane ^ m. Lanes of the lower half subtract.
@@ -263,14 +271,16 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   const int total_waves = gridDim.x * wpb;
   int item = blockIdx.x * wpb + wib;
   if (item >= p.n_items) return;
-  int64_t pos_next = token_position(posp, p.pos64, item / p.nc);
+  constexpr bool kRotate = MODE != kNormOnly;
+  constexpr bool kNorm = MODE != kRopeOnly;
+  int64_t pos_next = kRotate ? token_position(posp, p.pos64, item / p.nc) : 0;
 
   for (; item < p.n_items; item += total_waves) {
     const int t = item / p.nc;
     const int g_begin = (item - t * p.nc) * p.gpi;
     const int g_end = min(g_begin + p.gpi, p.ng);
     const int64_t pos = pos_next;
-    if (item + total_waves < p.n_items)
+    if (kRotate && item + total_waves < p.n_items)
       pos_next = token_position(posp, p.pos64, (item + total_waves) / p.nc);
     char* const qrow = qb + t * p.q_tok;
     char* const krow = kb + t * p.k_tok;
@@ -301,26 +311,28 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
     // cos / sin of this lane's dims at this token (loaded after the head data
     // is in flight; kept in registers for every group of the item)
     float cs[NCS], sn[NCS];
-    const float* row = cache + pos * R;
-    if ((FULL || NEOX) && NCS % 4 == 0 && p.cs_vec) {
+    if constexpr (kRotate) {
+      const float* row = cache + pos * R;
+      if ((FULL || NEOX) && NCS % 4 == 0 && p.cs_vec) {
 #pragma unroll
-      for (int i = 0; i < NCS; i += 4) {
-        const float4 c4 = *reinterpret_cast<const float4*>(row + j0 + i);
-        const float4 s4 = *reinterpret_cast<const float4*>(row + half + j0 + i);
-        cs[i] = c4.x; cs[i + 1] = c4.y; cs[i + 2] = c4.z; cs[i + 3] = c4.w;
-        sn[i] = s4.x; sn[i + 1] = s4.y; sn[i + 2] = s4.z; sn[i + 3] = s4.w;
+        for (int i = 0; i < NCS; i += 4) {
+          const float4 c4 = *reinterpret_cast<const float4*>(row + j0 + i);
+          const float4 s4 = *reinterpret_cast<const float4*>(row + half + j0 + i);
+          cs[i] = c4.x; cs[i + 1] = c4.y; cs[i + 2] = c4.z; cs[i + 3] = c4.w;
+          sn[i] = s4.x; sn[i + 1] = s4.y; sn[i + 2] = s4.z; sn[i + 3] = s4.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NCS; ++i) {
+          const int j = (FULL || NEOX) ? j0 + i : min(j0 + i, half - 1);
+          cs[i] = row[j];
+          sn[i] = row[half + j];
+        }
       }
-    } else {
+      if constexpr (NEOX) {
 #pragma unroll
-      for (int i = 0; i < NCS; ++i) {
-        const int j = (FULL || NEOX) ? j0 + i : min(j0 + i, half - 1);
-        cs[i] = row[j];
-        sn[i] = row[half + j];
+        for (int i = 0; i < NCS; ++i) sn[i] = lower ? -sn[i] : sn[i];
       }
-    }
-    if constexpr (NEOX) {
-#pragma unroll
-      for (int i = 0; i < NCS; ++i) sn[i] = lower ? -sn[i] : sn[i];
     }
 
     for (int g = g_begin; g < g_end; g += U) {
@@ -328,23 +340,31 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float x[E];
-        float ss = 0.0f;
 #pragma unroll
         for (int w = 0; w < NV; ++w) IO::unpack(raw[u].w[w], x[2 * w], x[2 * w + 1]);
-#pragma unroll
-        for (int i = 0; i < E; ++i) ss = fmaf(x[i], x[i], ss);
-        ss = group_sum<L>(ss);
-        const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / D, p.eps));
         float n[E];
+        if constexpr (kNorm) {
+          float ss = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NV; ++w) {
-          float w0, w1;
-          IO::unpack(isk[u] ? wk_p.w[w] : wq_p.w[w], w0, w1);
-          n[2 * w] = x[2 * w] * r * w0;
-          n[2 * w + 1] = x[2 * w + 1] * r * w1;
+          for (int i = 0; i < E; ++i) ss = fmaf(x[i], x[i], ss);
+          ss = group_sum<L>(ss);
+          const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / D, p.eps));
+#pragma unroll
+          for (int w = 0; w < NV; ++w) {
+            float w0, w1;
+            IO::unpack(isk[u] ? wk_p.w[w] : wq_p.w[w], w0, w1);
+            n[2 * w] = x[2 * w] * r * w0;
+            n[2 * w + 1] = x[2 * w + 1] * r * w1;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < E; ++i) n[i] = x[i];
         }
         float o[E];
-        if constexpr (NEOX) {
+        if constexpr (!kRotate) {
+#pragma unroll
+          for (int i = 0; i < E; ++i) o[i] = n[i];
+        } else if constexpr (NEOX) {
 #pragma unroll
           for (int i = 0; i < E; ++i) {
             const float pn = lane_fetch(partner_addr, n[i]);
@@ -392,48 +412,57 @@ __global__ void __launch_bounds__(256) rmw_kernel(u32x4_t* buf, int64_t n, uint3
 // Kernel table
 // ----------------------------------------------------------------------------
 template <class IO, int D, int E, bool NEOX, bool FULL>
-const void* pick_unroll(int U) {
-  switch (U) {
-    case 1: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 1>);
-    case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2>);
-    case 4: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 4>);
-    default: return nullptr;
+const void* pick_unroll(int U, int mode) {
+  if (mode == kFused) {
+    switch (U) {
+      case 1: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 1, kFused>);
+      case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kFused>);
+      case 4: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 4, kFused>);
+      default: return nullptr;
+    }
   }
+  // the unfused baseline steps exist at the default unroll only
+  if (U != 2) return nullptr;
+  if (mode == kRopeOnly)
+    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kRopeOnly>);
+  if (mode == kNormOnly && !NEOX && FULL)  // pairing and rope_dim play no part
+    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kNormOnly>);
+  return nullptr;
 }
 
 template <class IO, int D, int E>
-const void* pick_pairing(bool neox, bool full, int U) {
-  if (neox) return full ? pick_unroll<IO, D, E, true, true>(U) : pick_unroll<IO, D, E, true, false>(U);
-  return full ? pick_unroll<IO, D, E, false, true>(U) : pick_unroll<IO, D, E, false, false>(U);
+const void* pick_pairing(bool neox, bool full, int U, int mode) {
+  if (neox) return full ? pick_unroll<IO, D, E, true, true>(U, mode) : pick_unroll<IO, D, E, true, false>(U, mode);
+  return full ? pick_unroll<IO, D, E, false, true>(U, mode) : pick_unroll<IO, D, E, false, false>(U, mode);
 }
 
 // Elements per lane: 8 (16-byte lanes), head_dim/32 (half a wave per head) and
 // head_dim/64 (a full wave per head; needs an even count, so not head_dim 64).
 template <class IO, int D>
-const void* pick_lanes(int E, bool neox, bool full, int U) {
-  if (E == 8) return pick_pairing<IO, D, 8>(neox, full, U);
+const void* pick_lanes(int E, bool neox, bool full, int U, int mode) {
+  if (E == 8) return pick_pairing<IO, D, 8>(neox, full, U, mode);
   if constexpr (D / 32 != 8) {
-    if (E == D / 32) return pick_pairing<IO, D, D / 32>(neox, full, U);
+    if (E == D / 32) return pick_pairing<IO, D, D / 32>(neox, full, U, mode);
   }
   if constexpr (D / 64 >= 2 && D / 64 != 8) {
-    if (E == D / 64) return pick_pairing<IO, D, D / 64>(neox, full, U);
+    if (E == D / 64) return pick_pairing<IO, D, D / 64>(neox, full, U, mode);
   }
   return nullptr;
 }
 
 template <class IO>
-const void* pick_dim(int D, int E, bool neox, bool full, int U) {
+const void* pick_dim(int D, int E, bool neox, bool full, int U, int mode) {
   switch (D) {
-    case 64: return pick_lanes<IO, 64>(E, neox, full, U);
-    case 128: return pick_lanes<IO, 128>(E, neox, full, U);
-    case 256: return pick_lanes<IO, 256>(E, neox, full, U);
+    case 64: return pick_lanes<IO, 64>(E, neox, full, U, mode);
+    case 128: return pick_lanes<IO, 128>(E, neox, full, U, mode);
+    case 256: return pick_lanes<IO, 256>(E, neox, full, U, mode);
     default: return nullptr;
   }
 }
 
-const void* pick_kernel(int dtype, int D, int E, bool neox, bool full, int U) {
-  return dtype == QKNR_BF16 ? pick_dim<Bf16>(D, E, neox, full, U)
-                            : pick_dim<Fp16>(D, E, neox, full, U);
+const void* pick_kernel(int dtype, int D, int E, bool neox, bool full, int U, int mode) {
+  return dtype == QKNR_BF16 ? pick_dim<Bf16>(D, E, neox, full, U, mode)
+                            : pick_dim<Fp16>(D, E, neox, full, U, mode);
 }
 
 // ----------------------------------------------------------------------------
@@ -504,9 +533,9 @@ bool lane_offsets_fit(int G, int32_t H, int64_t head_stride, int32_t D) {
   return true;
 }
 
-int32_t make_plan(int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t R, int32_t neox,
-                  int32_t dtype, int64_t q_head, int64_t k_head, const qknr_launch_cfg* cfg,
-                  Plan* pl) {
+int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t R,
+                  int32_t neox, int32_t dtype, int64_t q_head, int64_t k_head,
+                  const qknr_launch_cfg* cfg, Plan* pl) {
   qknr_launch_cfg c = cfg ? *cfg : qknr_launch_cfg{0, 0, 0, 0, 0};
   auto fits = [&](int E) {
     const int G = kWave / (D / E);
@@ -527,7 +556,8 @@ int32_t make_plan(int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t R, int3
     if (E != 8 && E != D / 32 && !(E == D / 64 && E >= 2)) return QKNR_E_ARG;
     if (!lanes_fit(R, neox, E) || !fits(E)) return QKNR_E_ARG;
   }
-  const int U = c.unroll == 0 ? kDefaultUnroll : c.unroll;
+  // the unfused baseline steps exist at unroll 2 only
+  const int U = mode != kFused ? 2 : (c.unroll == 0 ? kDefaultUnroll : c.unroll);
   if (U != 1 && U != 2 && U != 4) return QKNR_E_ARG;
   const int wpb = c.block_waves == 0 ? kDefaultBlockWaves : c.block_waves;
   if (wpb < 1 || wpb > kMaxBlockWaves) return QKNR_E_ARG;
@@ -546,7 +576,7 @@ int32_t make_plan(int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t R, int3
   pl->U = U;
   pl->wpb = wpb;
   pl->max_blocks = c.max_blocks;
-  pl->fn = pick_kernel(dtype, D, E, neox != 0, R == D, U);
+  pl->fn = pick_kernel(dtype, D, E, neox != 0, R == D, U, mode);
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
 }
 
@@ -576,6 +606,112 @@ int32_t device_limits(const void* fn, int threads, size_t lds, int* cus, int* bl
     jt = g_occ.emplace(key, nb).first;
   }
   *blocks_per_cu = jt->second;
+  return QKNR_OK;
+}
+
+// One call of the op or of one unfused step, with every argument.
+struct Call {
+  void* q;
+  void* k;
+  const void* wq;
+  const void* wk;
+  const float* cache;
+  const void* pos;
+  int64_t T;
+  int32_t Hq, Hkv, D, R, neox;
+  float eps;
+  int64_t qt, qh, kt, kh;  // byte strides
+  int32_t dtype, pdt;
+  hipStream_t stream;
+};
+
+// Validation (no HIP call) and planning. For kNormOnly the rotation arguments
+// are ignored (pass rope_dim = head_dim); for kRopeOnly the weights and eps.
+int32_t prepare(int mode, const Call& c, const qknr_launch_cfg* cfg, Plan* pl,
+                qknr_launch_info* info) {
+  if (c.T < 0 || c.Hq < 0 || c.Hkv < 0) return QKNR_E_SHAPE;
+  if (c.dtype != QKNR_BF16 && c.dtype != QKNR_FP16) return QKNR_E_DTYPE;
+  if (c.pdt != QKNR_I32 && c.pdt != QKNR_I64) return QKNR_E_DTYPE;
+  if (!shape_supported(c.D, c.R, c.neox)) return QKNR_E_UNSUPPORTED;
+  if (!std::isfinite(c.eps) || c.eps < 0.0f) return QKNR_E_ARG;
+  if (c.T > INT32_MAX || c.T * (static_cast<int64_t>(c.Hq) + c.Hkv) > INT32_MAX) return QKNR_E_SHAPE;
+
+  const int32_t prc = make_plan(mode, c.T, c.Hq, c.Hkv, c.D, c.R, c.neox, c.dtype, c.qh, c.kh, cfg, pl);
+  if (prc != QKNR_OK) return prc;
+  if (info) {
+    info->lanes_per_head = pl->L;
+    info->elems_per_lane = pl->E;
+    info->heads_per_wave = pl->G;
+    info->groups_per_token = pl->ng;
+    info->groups_per_item = pl->gpi;
+    info->unroll = pl->U;
+    info->block_threads = pl->wpb * kWave;
+    info->grid_blocks = 0;
+    info->items = pl->items;
+  }
+  if (c.T == 0 || c.Hq + c.Hkv == 0) return QKNR_OK;
+
+  const bool need_w = mode != kRopeOnly, need_rot = mode != kNormOnly;
+  if ((c.Hq > 0 && (!c.q || (need_w && !c.wq))) || (c.Hkv > 0 && (!c.k || (need_w && !c.wk))) ||
+      (need_rot && (!c.cache || !c.pos)))
+    return QKNR_E_NULL;
+  const int64_t vec = 2 * static_cast<int64_t>(c.D);
+  if (c.Hq > 0 && !views_ok(c.T, c.Hq, c.qt, c.qh, vec)) return QKNR_E_SHAPE;
+  if (c.Hkv > 0 && !views_ok(c.T, c.Hkv, c.kt, c.kh, vec)) return QKNR_E_SHAPE;
+  if (c.Hq > 0 && (!aligned(c.q, 16) || (need_w && !aligned(c.wq, 16)) || (c.T > 1 && c.qt % 16) ||
+                   (c.Hq > 1 && c.qh % 16)))
+    return QKNR_E_ALIGN;
+  if (c.Hkv > 0 && (!aligned(c.k, 16) || (need_w && !aligned(c.wk, 16)) || (c.T > 1 && c.kt % 16) ||
+                    (c.Hkv > 1 && c.kh % 16)))
+    return QKNR_E_ALIGN;
+  if (need_rot && (!aligned(c.cache, 4) || !aligned(c.pos, c.pdt == QKNR_I64 ? 8 : 4)))
+    return QKNR_E_ALIGN;
+  return QKNR_OK;
+}
+
+// Enqueue a prepared call (HIP calls from here on).
+int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
+  if (c.T == 0 || c.Hq + c.Hkv == 0) return QKNR_OK;
+  const int threads = pl.wpb * kWave;
+  int cus = 0, per_cu = 0;
+  const int32_t drc = device_limits(pl.fn, threads, 0, &cus, &per_cu);
+  if (drc != QKNR_OK) return drc;
+  const int64_t needed = (pl.items + pl.wpb - 1) / pl.wpb;
+  int64_t cap = needed;
+  if (pl.max_blocks > 0) cap = pl.max_blocks;
+  if (pl.max_blocks == -1) cap = static_cast<int64_t>(cus) * per_cu;
+  const int grid = static_cast<int>(std::max<int64_t>(1, std::min(needed, cap)));
+  if (info) info->grid_blocks = grid;
+
+  Params prm;
+  char* qarg = static_cast<char*>(c.q);
+  char* karg = static_cast<char*>(c.k);
+  const void* wqarg = c.wq ? c.wq : c.wk;  // the side with 0 heads still gets a readable row
+  const void* wkarg = c.wk ? c.wk : c.wq;
+  const float* carg = c.cache;
+  const void* parg = c.pos;
+  prm.cs_vec = (reinterpret_cast<uintptr_t>(c.cache) % 16 == 0) && ((c.R / 2) % 4 == 0);
+  // head strides only matter for views with more than one head
+  const int64_t qh = c.Hq > 1 ? c.qh : 0, kh = c.Hkv > 1 ? c.kh : 0;
+  prm.q_tok = c.qt;
+  prm.k_tok = c.kt;
+  prm.q_grp = qh * pl.G;
+  prm.k_grp = kh * pl.G;
+  prm.q_head = static_cast<uint32_t>(qh);
+  prm.k_head = static_cast<uint32_t>(kh);
+  prm.ngq = pl.ngq;
+  prm.Hq = c.Hq;
+  prm.Hkv = c.Hkv;
+  prm.R = c.R;
+  prm.pos64 = c.pdt == QKNR_I64;
+  prm.eps = c.eps;
+  prm.ng = pl.ng;
+  prm.gpi = pl.gpi;
+  prm.nc = pl.nc;
+  prm.n_items = static_cast<int32_t>(pl.items);
+  void* args[] = {&qarg, &karg, &wqarg, &wkarg, &carg, &parg, &prm};
+  if (hipLaunchKernel(pl.fn, dim3(grid), dim3(threads), args, 0, c.stream) != hipSuccess)
+    return QKNR_E_LAUNCH;
   return QKNR_OK;
 }
 
@@ -621,87 +757,12 @@ QKNR_API int32_t qknr_inplace_ex(void* q, void* k, const void* wq, const void* w
                                  int64_t k_head_stride_B, int32_t dtype, int32_t pos_dtype,
                                  hipStream_t stream, const qknr_launch_cfg* cfg,
                                  qknr_launch_info* info) {
-  if (T < 0 || Hq < 0 || Hkv < 0) return QKNR_E_SHAPE;
-  if (dtype != QKNR_BF16 && dtype != QKNR_FP16) return QKNR_E_DTYPE;
-  if (pos_dtype != QKNR_I32 && pos_dtype != QKNR_I64) return QKNR_E_DTYPE;
-  if (!shape_supported(head_dim, rope_dim, is_neox)) return QKNR_E_UNSUPPORTED;
-  if (!std::isfinite(eps) || eps < 0.0f) return QKNR_E_ARG;
-  if (T > INT32_MAX || T * (static_cast<int64_t>(Hq) + Hkv) > INT32_MAX) return QKNR_E_SHAPE;
-
+  const Call c{q, k, wq, wk, cos_sin_cache, positions, T, Hq, Hkv, head_dim, rope_dim, is_neox,
+               eps, q_tok_stride_B, q_head_stride_B, k_tok_stride_B, k_head_stride_B, dtype,
+               pos_dtype, stream};
   Plan pl;
-  const int32_t prc = make_plan(T, Hq, Hkv, head_dim, rope_dim, is_neox, dtype, q_head_stride_B,
-                                k_head_stride_B, cfg, &pl);
-  if (prc != QKNR_OK) return prc;
-  if (info) {
-    info->lanes_per_head = pl.L;
-    info->elems_per_lane = pl.E;
-    info->heads_per_wave = pl.G;
-    info->groups_per_token = pl.ng;
-    info->groups_per_item = pl.gpi;
-    info->unroll = pl.U;
-    info->block_threads = pl.wpb * kWave;
-    info->grid_blocks = 0;
-    info->items = pl.items;
-  }
-  if (T == 0 || Hq + Hkv == 0) return QKNR_OK;
-
-  if ((Hq > 0 && (!q || !wq)) || (Hkv > 0 && (!k || !wk)) || !cos_sin_cache || !positions)
-    return QKNR_E_NULL;
-  const int64_t vec = 2 * static_cast<int64_t>(head_dim);
-  if (Hq > 0 && !views_ok(T, Hq, q_tok_stride_B, q_head_stride_B, vec)) return QKNR_E_SHAPE;
-  if (Hkv > 0 && !views_ok(T, Hkv, k_tok_stride_B, k_head_stride_B, vec)) return QKNR_E_SHAPE;
-  if (Hq > 0 && (!aligned(q, 16) || !aligned(wq, 16) || (T > 1 && q_tok_stride_B % 16) ||
-                 (Hq > 1 && q_head_stride_B % 16)))
-    return QKNR_E_ALIGN;
-  if (Hkv > 0 && (!aligned(k, 16) || !aligned(wk, 16) || (T > 1 && k_tok_stride_B % 16) ||
-                  (Hkv > 1 && k_head_stride_B % 16)))
-    return QKNR_E_ALIGN;
-  if (!aligned(cos_sin_cache, 4) || !aligned(positions, pos_dtype == QKNR_I64 ? 8 : 4))
-    return QKNR_E_ALIGN;
-
-  // ---- validation done; HIP calls from here on ----
-  const int threads = pl.wpb * kWave;
-  const size_t lds = 0;
-  int cus = 0, per_cu = 0;
-  const int32_t drc = device_limits(pl.fn, threads, lds, &cus, &per_cu);
-  if (drc != QKNR_OK) return drc;
-  const int64_t needed = (pl.items + pl.wpb - 1) / pl.wpb;
-  int64_t cap = needed;
-  if (pl.max_blocks > 0) cap = pl.max_blocks;
-  if (pl.max_blocks == -1) cap = static_cast<int64_t>(cus) * per_cu;
-  const int grid = static_cast<int>(std::max<int64_t>(1, std::min(needed, cap)));
-  if (info) info->grid_blocks = grid;
-
-  Params prm;
-  char* qarg = static_cast<char*>(q);
-  char* karg = static_cast<char*>(k);
-  const void* wqarg = wq ? wq : wk;  // the side with 0 heads still gets a readable row
-  const void* wkarg = wk ? wk : wq;
-  const float* carg = cos_sin_cache;
-  const void* parg = positions;
-  prm.cs_vec = (reinterpret_cast<uintptr_t>(cos_sin_cache) % 16 == 0) && ((rope_dim / 2) % 4 == 0);
-  // head strides only matter for views with more than one head
-  const int64_t qh = Hq > 1 ? q_head_stride_B : 0, kh = Hkv > 1 ? k_head_stride_B : 0;
-  prm.q_tok = q_tok_stride_B;
-  prm.k_tok = k_tok_stride_B;
-  prm.q_grp = qh * pl.G;
-  prm.k_grp = kh * pl.G;
-  prm.q_head = static_cast<uint32_t>(qh);
-  prm.k_head = static_cast<uint32_t>(kh);
-  prm.ngq = pl.ngq;
-  prm.Hq = Hq;
-  prm.Hkv = Hkv;
-  prm.R = rope_dim;
-  prm.pos64 = pos_dtype == QKNR_I64;
-  prm.eps = eps;
-  prm.ng = pl.ng;
-  prm.gpi = pl.gpi;
-  prm.nc = pl.nc;
-  prm.n_items = static_cast<int32_t>(pl.items);
-  void* args[] = {&qarg, &karg, &wqarg, &wkarg, &carg, &parg, &prm};
-  if (hipLaunchKernel(pl.fn, dim3(grid), dim3(threads), args, lds, stream) != hipSuccess)
-    return QKNR_E_LAUNCH;
-  return QKNR_OK;
+  const int32_t rc = prepare(kFused, c, cfg, &pl, info);
+  return rc != QKNR_OK ? rc : launch(c, pl, info);
 }
 
 QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
@@ -714,6 +775,58 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
   return qknr_inplace_ex(q, k, wq, wk, cos_sin_cache, positions, T, Hq, Hkv, head_dim, rope_dim,
                          is_neox, eps, q_tok_stride_B, q_head_stride_B, k_tok_stride_B,
                          k_head_stride_B, dtype, pos_dtype, stream, nullptr, nullptr);
+}
+
+QKNR_API int32_t qknr_rmsnorm_inplace(void* q, void* k, const void* wq, const void* wk, int64_t T,
+                                      int32_t Hq, int32_t Hkv, int32_t head_dim, float eps,
+                                      int64_t q_tok_stride_B, int64_t q_head_stride_B,
+                                      int64_t k_tok_stride_B, int64_t k_head_stride_B,
+                                      int32_t dtype, hipStream_t stream) {
+  const Call c{q, k, wq, wk, nullptr, nullptr, T, Hq, Hkv, head_dim, head_dim, 0, eps,
+               q_tok_stride_B, q_head_stride_B, k_tok_stride_B, k_head_stride_B, dtype, QKNR_I32,
+               stream};
+  Plan pl;
+  const int32_t rc = prepare(kNormOnly, c, nullptr, &pl, nullptr);
+  return rc != QKNR_OK ? rc : launch(c, pl, nullptr);
+}
+
+QKNR_API int32_t qknr_rope_inplace(void* q, void* k, const float* cos_sin_cache,
+                                   const void* positions, int64_t T, int32_t Hq, int32_t Hkv,
+                                   int32_t head_dim, int32_t rope_dim, int32_t is_neox,
+                                   int64_t q_tok_stride_B, int64_t q_head_stride_B,
+                                   int64_t k_tok_stride_B, int64_t k_head_stride_B, int32_t dtype,
+                                   int32_t pos_dtype, hipStream_t stream) {
+  const Call c{q, k, nullptr, nullptr, cos_sin_cache, positions, T, Hq, Hkv, head_dim, rope_dim,
+               is_neox, 0.0f, q_tok_stride_B, q_head_stride_B, k_tok_stride_B, k_head_stride_B,
+               dtype, pos_dtype, stream};
+  Plan pl;
+  const int32_t rc = prepare(kRopeOnly, c, nullptr, &pl, nullptr);
+  return rc != QKNR_OK ? rc : launch(c, pl, nullptr);
+}
+
+QKNR_API int32_t qknr_unfused_inplace(void* q, void* k, const void* wq, const void* wk,
+                                      const float* cos_sin_cache, const void* positions,
+                                      int64_t T, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                      int32_t rope_dim, int32_t is_neox, float eps,
+                                      int64_t q_tok_stride_B, int64_t q_head_stride_B,
+                                      int64_t k_tok_stride_B, int64_t k_head_stride_B,
+                                      int32_t dtype, int32_t pos_dtype, hipStream_t stream) {
+  // validate everything for both steps before enqueueing either
+  const Call c{q, k, wq, wk, cos_sin_cache, positions, T, Hq, Hkv, head_dim, rope_dim, is_neox,
+               eps, q_tok_stride_B, q_head_stride_B, k_tok_stride_B, k_head_stride_B, dtype,
+               pos_dtype, stream};
+  Plan fused, norm, rot;
+  int32_t rc = prepare(kFused, c, nullptr, &fused, nullptr);
+  if (rc != QKNR_OK) return rc;
+  Call cn = c;
+  cn.R = head_dim;
+  cn.neox = 0;
+  rc = prepare(kNormOnly, cn, nullptr, &norm, nullptr);
+  if (rc != QKNR_OK) return rc;
+  rc = prepare(kRopeOnly, c, nullptr, &rot, nullptr);
+  if (rc != QKNR_OK) return rc;
+  rc = launch(cn, norm, nullptr);
+  return rc != QKNR_OK ? rc : launch(c, rot, nullptr);
 }
 
 static int32_t stream_launch(const void* fn, void** args, int64_t n16, hipStream_t stream) {

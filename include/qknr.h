@@ -154,6 +154,46 @@ QKNR_API int32_t qknr_inplace_ex(void* q, void* k, const void* wq, const void* w
                                  const qknr_launch_cfg* cfg, qknr_launch_info* info);
 
 /*
+ * The unfused chain that the fused op replaces (section 2.4: two launches, the
+ * normalised values written to memory in the I/O type and read back; section 6:
+ * the fallback path runs a QK RMSNorm and then a RoPE in place). These exist as
+ * a measured baseline for the fused op; each step rounds its own output.
+ *
+ * qknr_rmsnorm_inplace -- section 2.1 only: q and k (same layout rules as
+ *   qknr_inplace) are replaced by x * rsqrt(mean(x^2) + eps) * w, rounded to the
+ *   I/O type. No cache, positions or rotation arguments.
+ * qknr_rope_inplace -- section 2.2 only: the first rope_dim dims of every head
+ *   of q and k are rotated by cache row positions[t] as stored (no norm); no
+ *   weights or eps.
+ * qknr_unfused_inplace -- same arguments and result contract as qknr_inplace,
+ *   computed as qknr_rmsnorm_inplace followed by qknr_rope_inplace on the same
+ *   stream (two launches, the intermediate rounded to the I/O type). Every
+ *   argument is validated before either launch; if the second launch is refused
+ *   (QKNR_E_LAUNCH), q and k hold the normalised, unrotated values.
+ * Status codes and ownership as for qknr_inplace.
+ */
+QKNR_API int32_t qknr_rmsnorm_inplace(void* q, void* k, const void* wq, const void* wk,
+                                      int64_t T, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                      float eps,
+                                      int64_t q_tok_stride_B, int64_t q_head_stride_B,
+                                      int64_t k_tok_stride_B, int64_t k_head_stride_B,
+                                      int32_t dtype, hipStream_t stream);
+QKNR_API int32_t qknr_rope_inplace(void* q, void* k, const float* cos_sin_cache,
+                                   const void* positions, int64_t T, int32_t Hq, int32_t Hkv,
+                                   int32_t head_dim, int32_t rope_dim, int32_t is_neox,
+                                   int64_t q_tok_stride_B, int64_t q_head_stride_B,
+                                   int64_t k_tok_stride_B, int64_t k_head_stride_B,
+                                   int32_t dtype, int32_t pos_dtype, hipStream_t stream);
+QKNR_API int32_t qknr_unfused_inplace(void* q, void* k, const void* wq, const void* wk,
+                                      const float* cos_sin_cache, const void* positions,
+                                      int64_t T, int32_t Hq, int32_t Hkv,
+                                      int32_t head_dim, int32_t rope_dim, int32_t is_neox,
+                                      float eps,
+                                      int64_t q_tok_stride_B, int64_t q_head_stride_B,
+                                      int64_t k_tok_stride_B, int64_t k_head_stride_B,
+                                      int32_t dtype, int32_t pos_dtype, hipStream_t stream);
+
+/*
  * qknr_can_use -- 1 if an instance exists for this combination, else 0.
  * Mirrors the page's capability predicate (section 5.2): head_dim in
  * {64,128,256}, 0 < rope_dim <= head_dim, rope_dim % (head_dim/32) == 0, and

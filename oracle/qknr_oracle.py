@@ -38,7 +38,8 @@ import numpy as np
 __all__ = [
     "decode_bf16", "decode_fp16", "decode_io", "round_to_bf16_bits", "round_to_fp16_bits",
     "round_to_io_bits", "rms_norm", "rope", "cache_cos_sin", "qknorm_rope",
-    "qknorm_rope_io", "within_tolerance", "tolerance",
+    "qknorm_rope_io", "rms_norm_io", "rope_io", "qknorm_rope_unfused_io",
+    "within_tolerance", "tolerance",
 ]
 
 
@@ -187,6 +188,39 @@ def qknorm_rope_io(q_bits, k_bits, wq_bits, wk_bits, cache, positions, *, is_neo
                          cache, positions, is_neox=is_neox, eps=eps, rope_dim=rope_dim)
     rq, rk = round_to_io_bits(oq, dtype), round_to_io_bits(ok, dtype)
     return rq, rk, decode_io(rq, dtype), decode_io(rk, dtype)
+
+
+# ----------------------------------------------------------------------------
+# The unfused chain the fused op replaces (section 2.4 table, section 6
+# fallback): an RMSNorm step that writes its result to memory in the I/O
+# type, then a RoPE step that reads it back, rotates and writes it again.
+# Each step rounds its own output once.
+# ----------------------------------------------------------------------------
+
+def rms_norm_io(x_bits, w_bits, *, eps, dtype):
+    """Section 2.1 alone on I/O bit patterns [..., D]: decode, fp64 norm with
+    eps as an fp32 value, one rounding to the I/O type."""
+    n = rms_norm(decode_io(x_bits, dtype), decode_io(w_bits, dtype), float(np.float32(eps)))
+    return round_to_io_bits(n, dtype)
+
+
+def rope_io(x_bits, cache, positions, *, is_neox, dtype, rope_dim=None):
+    """Section 2.2 alone on I/O bit patterns [T, H, D]: decode, rotate the first
+    rope_dim dims with row positions[t] of the cache, one rounding."""
+    R = int(cache.shape[-1] if rope_dim is None else rope_dim)
+    cos, sin = cache_cos_sin(cache, positions, R)
+    out = rope(decode_io(x_bits, dtype), cos[:, None, :], sin[:, None, :], R, is_neox)
+    return round_to_io_bits(out, dtype)
+
+
+def qknorm_rope_unfused_io(q_bits, k_bits, wq_bits, wk_bits, cache, positions, *, is_neox,
+                           eps, dtype, rope_dim=None):
+    """RMSNorm step then RoPE step, the intermediate rounded to the I/O type.
+    Returns (q_bits, k_bits)."""
+    nq = rms_norm_io(q_bits, wq_bits, eps=eps, dtype=dtype)
+    nk = rms_norm_io(k_bits, wk_bits, eps=eps, dtype=dtype)
+    return (rope_io(nq, cache, positions, is_neox=is_neox, dtype=dtype, rope_dim=rope_dim),
+            rope_io(nk, cache, positions, is_neox=is_neox, dtype=dtype, rope_dim=rope_dim))
 
 
 # ----------------------------------------------------------------------------

@@ -26,7 +26,8 @@ def _declared():
 def test_library_loads_and_exports_every_declared_symbol():
     names = _declared()
     assert {"qknr_inplace", "qknr_inplace_ex", "qknr_can_use", "qknr_status_string",
-            "qknr_copy", "qknr_rmw"} <= set(names)
+            "qknr_copy", "qknr_rmw", "qknr_unfused_inplace", "qknr_rmsnorm_inplace",
+            "qknr_rope_inplace"} <= set(names)
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -252,3 +253,39 @@ def test_plan_falls_back_to_fewer_heads_per_group_for_huge_head_strides():
     assert rc == B.QKNR_E_SHAPE
     rc, info = plan(64, 3 << 30, Hq=1)  # one head: its stride is never used
     assert rc == 0 and info["lanes_per_head"] == 8
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: run on a host without a GPU")
+def test_unfused_entry_points_validate_before_launching():
+    L = B.lib()
+    z = P(0)
+    a = P(A)
+    # the norm step needs no cache or positions; it does need the weights
+    assert L.qknr_rmsnorm_inplace(a, a, z, a, 5, 4, 4, 128, 1e-6, 1024, 256, 1024, 256, 0,
+                                  z) == B.QKNR_E_NULL
+    assert L.qknr_rmsnorm_inplace(a, a, a, a, 5, 4, 4, 96, 1e-6, 1024, 256, 1024, 256, 0,
+                                  z) == B.QKNR_E_UNSUPPORTED
+    assert L.qknr_rmsnorm_inplace(a, a, a, a, 5, 4, 4, 128, -1.0, 1024, 256, 1024, 256, 0,
+                                  z) == B.QKNR_E_ARG
+    assert L.qknr_rmsnorm_inplace(a, a, a, a, 5, 4, 4, 128, 1e-6, 1024, 256, 1024, 256, 0,
+                                  z) == B.QKNR_E_DEVICE  # valid: reaches the runtime
+    # the rope step needs cache and positions, no weights
+    assert L.qknr_rope_inplace(a, a, z, a, 5, 4, 4, 128, 128, 1, 1024, 256, 1024, 256, 0, 0,
+                               z) == B.QKNR_E_NULL
+    assert L.qknr_rope_inplace(a, a, a, a, 5, 4, 4, 128, 96, 1, 1024, 256, 1024, 256, 0, 0,
+                               z) == B.QKNR_E_UNSUPPORTED
+    assert L.qknr_rope_inplace(a, a, a, P(A + 4), 5, 4, 4, 128, 128, 1, 1024, 256, 1024, 256, 0,
+                               1, z) == B.QKNR_E_ALIGN
+    assert L.qknr_rope_inplace(a, a, a, a, 5, 4, 4, 128, 128, 1, 1024, 256, 1024, 256, 0, 0,
+                               z) == B.QKNR_E_DEVICE
+    # the unfused pair validates like the fused op, before either launch
+    args = [a, a, a, a, a, a, 5, 4, 4, 128, 128, 1, 1e-6, 1024, 256, 1024, 256, 0, 0, z]
+    assert L.qknr_unfused_inplace(*args) == B.QKNR_E_DEVICE
+    for i, bad, code in ((2, z, B.QKNR_E_NULL), (4, z, B.QKNR_E_NULL), (10, 96, B.QKNR_E_UNSUPPORTED),
+                         (12, float("nan"), B.QKNR_E_ARG), (14, 128, B.QKNR_E_SHAPE)):
+        bad_args = list(args)
+        bad_args[i] = bad
+        assert L.qknr_unfused_inplace(*bad_args) == code, i
+    zero = list(args)
+    zero[6] = 0
+    assert L.qknr_unfused_inplace(*zero) == B.QKNR_OK

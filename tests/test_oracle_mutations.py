@@ -40,6 +40,9 @@ MUTATIONS = {
                               "    if not is_neox:\n        a, b = n[..., :half]", True),
     "fp16_double_rounding": ("return x.astype(np.float16).view(np.uint16)",
                              "return x.astype(np.float32).astype(np.float16).view(np.uint16)", True),
+    "unfused_k_uses_q_weight": ("nk = rms_norm_io(k_bits, wk_bits", "nk = rms_norm_io(k_bits, wq_bits", True),
+    "rope_step_pairing_inverted": ("cos[:, None, :], sin[:, None, :], R, is_neox)\n    return round_to_io_bits(out, dtype)",
+                                   "cos[:, None, :], sin[:, None, :], R, not is_neox)\n    return round_to_io_bits(out, dtype)", True),
     "equivalent_rewrite": ("np.sum(x * x, axis=-1", "np.sum(np.abs(x) * np.abs(x), axis=-1", False),
 }
 

@@ -491,3 +491,95 @@ def test_brute_force_tiny(seed):
     bq, bk = _brute(q, k, wq, wk, cache, pos, neox, 1e-6, R)
     np.testing.assert_allclose(oq, bq, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(ok, bk, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# The unfused chain (norm step, intermediate rounded to the I/O type, rope step)
+# ---------------------------------------------------------------------------
+
+def test_rms_norm_io_matches_torch_bf16_rms_norm():
+    """Library routine: torch's CPU rms_norm on bf16 tensors computes in fp32 and
+    rounds once to bf16; it must agree with the oracle's correctly rounded norm
+    to within one bf16 ulp everywhere and bit for bit almost everywhere."""
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(41)
+    D = 128
+    x = O.round_to_bf16_bits(g.standard_normal((64, 6, D)) * 2.0)
+    w = O.round_to_bf16_bits(g.uniform(0.5, 1.5, D))
+    ours = O.rms_norm_io(x, w, eps=1e-6, dtype="bf16")
+    tx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    tw = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16)
+    theirs = torch.nn.functional.rms_norm(tx, (D,), tw, eps=1e-6).view(torch.int16).numpy().view(np.uint16)
+    ulps = np.abs(ours.astype(np.int64) - theirs.astype(np.int64))
+    assert ulps.max() <= 1
+    assert np.mean(ours == theirs) > 0.99
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_rms_norm_io_constant_vector_is_exact(dt):
+    """eps = 0, w = 1, x = c*1 gives exactly sign(c)."""
+    D = 64
+    for c in (-3.0, 0.25, 7.0):
+        x = O.round_to_io_bits(np.full((2, 1, D), c), dt)
+        w = O.round_to_io_bits(np.ones(D), dt)
+        n = O.decode_io(O.rms_norm_io(x, w, eps=0.0, dtype=dt), dt)
+        assert np.all(n == np.sign(c))
+
+
+@pytest.mark.parametrize("neox", [False, True])
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_rope_io_identity_and_quarter_turn_are_exact(neox, dt):
+    """With exact (cos, sin) the rotation of representable values is
+    representable: row (1, 0) returns the input bits, row (0, 1) swaps the pair
+    and negates the first member."""
+    D = R = 32
+    g = np.random.default_rng(5)
+    x = O.round_to_io_bits(g.standard_normal((3, 2, D)), dt)
+    cache = np.array([[1.0] * (R // 2) + [0.0] * (R // 2), [0.0] * (R // 2) + [1.0] * (R // 2)],
+                     np.float32)
+    same = O.rope_io(x, cache, np.zeros(3, np.int32), is_neox=neox, dtype=dt)
+    assert np.array_equal(same, x)
+    turned = O.decode_io(O.rope_io(x, cache, np.ones(3, np.int32), is_neox=neox, dtype=dt), dt)
+    xv = O.decode_io(x, dt)
+    a, b = (np.arange(R // 2), np.arange(R // 2) + R // 2) if neox else (np.arange(0, R, 2), np.arange(1, R, 2))
+    assert np.array_equal(turned[..., a], -xv[..., b])
+    assert np.array_equal(turned[..., b], xv[..., a])
+
+
+@pytest.mark.parametrize("neox", [False, True])
+def test_unfused_chain_agrees_with_fused_within_page_tolerance(neox):
+    """The page's unit test compares the fused op with the unfused chain at
+    bf16 atol 8e-2, rtol 1e-2 (Step 4 of its rewrite guide). The oracle's two
+    versions must satisfy that, differ somewhere (the intermediate rounding is
+    real), and differ by no more than the rounding analysis allows: rounding the
+    normalised pair (a, b) moves a rotated output by at most 2^-8 (|a| + |b|),
+    and each side's final rounding by at most 2^-8 of its own magnitude."""
+    g = np.random.default_rng(77)
+    D, R = 128, 64
+    q = O.round_to_bf16_bits(g.standard_normal((50, 4, D)))
+    k = O.round_to_bf16_bits(g.standard_normal((50, 2, D)))
+    wq = O.round_to_bf16_bits(g.uniform(0.5, 1.5, D))
+    wk = O.round_to_bf16_bits(g.uniform(0.5, 1.5, D))
+    cache = _cache_formula(100, R)
+    pos = g.integers(0, 100, 50)
+    fq, fk, fqv, fkv = O.qknorm_rope_io(q, k, wq, wk, cache, pos, is_neox=neox, eps=1e-6,
+                                        dtype="bf16", rope_dim=R)
+    uq, uk = O.qknorm_rope_unfused_io(q, k, wq, wk, cache, pos, is_neox=neox, eps=1e-6,
+                                      dtype="bf16", rope_dim=R)
+    e = float(np.float32(1e-6))
+    for x, w, f, u in ((q, wq, fqv, uq), (k, wk, fkv, uk)):
+        uv = O.decode_bf16(u)
+        assert np.all(np.abs(uv - f) <= 8e-2 + 1e-2 * np.abs(f))
+        assert np.any(uv != f)
+        n = np.abs(O.rms_norm(O.decode_bf16(x), O.decode_bf16(w), e))
+        pair = n.copy()
+        if neox:
+            pair[..., :R // 2] += n[..., R // 2:R]
+            pair[..., R // 2:R] += n[..., :R // 2]
+        else:
+            pair[..., 0:R:2] += n[..., 1:R:2]
+            pair[..., 1:R:2] += n[..., 0:R:2]
+        bound = 2.0 ** -8 * (pair + np.abs(uv) + np.abs(f)) * (1 + 1e-6)
+        assert np.all(np.abs(uv - f) <= bound)
+    # pass-through dims see only the norm step: there the two agree exactly
+    assert np.array_equal(uq[..., R:], fq[..., R:])
