@@ -37,8 +37,12 @@ COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
 def kernel_sha() -> str:
+    """Hash of the fused kernel's device code (between its begin/end markers)."""
     with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        src = f.read()
+    a = src.index(b"// ==== fused-kernel device code begin")
+    b = src.index(b"// ==== fused-kernel device code end")
+    return hashlib.sha256(src[a:b]).hexdigest()[:16]
 
 
 def parse():

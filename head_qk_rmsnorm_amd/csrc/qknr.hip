@@ -54,6 +54,8 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kMaxBlockWaves = 8;
 
+// ==== fused-kernel device code begin (the measured kernel; its hash keys the
+// ==== committed hardware-counter summaries)
 // ----------------------------------------------------------------------------
 // I/O element formats: two 16-bit values per dword, lower address in the low
 // half. Widening is exact; narrowing rounds to nearest even (gfx950
@@ -390,6 +392,8 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
     }
   }
 }
+
+// ==== fused-kernel device code end
 
 // Measurement aids (see qknr_bench.h): one 16-byte element per thread, one
 // pass over the grid, nontemporal like the op's Q/K traffic.
