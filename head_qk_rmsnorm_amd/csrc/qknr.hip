@@ -141,10 +141,10 @@ constexpr int kSwizzleXor16 = 0x401F;  // ds_swizzle bit mode: and 0x1f, xor 0x1
 // adds exactly the other quad (half row).
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(L == 8 || L == 16 || L == 32 || L == 64, "lanes per head");
+  static_assert(L == 2 || L == 4 || L == 8 || L == 16 || L == 32 || L == 64, "lanes per head");
   v += dpp_mov<kDppQuadXor1>(v);
-  v += dpp_mov<kDppQuadXor2>(v);
-  v += dpp_mov<kDppRowHalfMirror>(v);
+  if constexpr (L >= 4) v += dpp_mov<kDppQuadXor2>(v);
+  if constexpr (L >= 8) v += dpp_mov<kDppRowHalfMirror>(v);
   if constexpr (L >= 16) v += dpp_mov<kDppRowMirror>(v);
   if constexpr (L >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16));
   if constexpr (L == 64) {
@@ -213,6 +213,8 @@ struct Params {
   int64_t q_grp, k_grp;          // bytes between consecutive head groups (G head strides)
   uint32_t q_head, k_head;       // head strides (bytes); (G-1)*stride + 2*D fits 32 bits
   int32_t Hq, Hkv, R;
+  int32_t D;                     // head_dim (instances with a run-time head_dim)
+  float inv_d;                   // 1 / head_dim
   int32_t ngq;                   // Q head groups per token; K groups follow them
   int32_t pos64;
   int32_t cs_vec;                // cache rows 16-byte aligned and R/2 % 4 == 0
@@ -228,22 +230,28 @@ enum : int { kFused = 0, kNormOnly = 1, kRopeOnly = 2 };
 // One wave instruction covers one head group: G consecutive heads of Q, or of
 // K, of one token (groups never mix Q and K), so the group's base address is
 // wave-uniform and each lane adds a fixed 32-bit offset.
-template <class IO, int D, int E, bool NEOX, bool FULL, int U, int MODE>
+//
+// DMAX is the head_dim the instance is built for. EXACT instances have
+// head_dim == DMAX; the others take any multiple of E up to DMAX at run time
+// (each head keeps a lane group of DMAX/E lanes, the spare ones masked).
+template <class IO, int DMAX, int E, bool NEOX, bool FULL, int U, int MODE, bool EXACT>
 __global__ void __launch_bounds__(kMaxBlockWaves * kWave)
 qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict__ wqp,
             const void* __restrict__ wkp, const float* __restrict__ cache,
             const void* __restrict__ posp, const Params p) {
-  constexpr int L = D / E;      // lanes per head
+  constexpr int L = DMAX / E;   // lanes per head (lane group)
   constexpr int G = kWave / L;  // heads per wave instruction
   constexpr int NV = E / 2;     // packed dwords per lane
   constexpr int NCS = NEOX ? E : E / 2;  // cos (and sin) values per lane
-  static_assert(D % E == 0 && E % 2 == 0 && G >= 1, "lane mapping");
+  static_assert(DMAX % E == 0 && E % 2 == 0 && G >= 1, "lane mapping");
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
   const int sub = lane / L;  // head slot in the group
   const int li = lane % L;   // lane inside the head
   const int d0 = li * E;     // first dim owned by this lane
+  const int D = EXACT ? DMAX : p.D;
+  const bool in_head = EXACT || d0 < D;  // spare lanes of a run-time head_dim
   const int R = FULL ? D : p.R;
   const int half = R / 2;
   const uint32_t q_off = static_cast<uint32_t>(sub) * p.q_head + d0 * 2;
@@ -252,22 +260,28 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   // Weights of this lane's dims, kept packed (widened per use).
   Raw<NV> wq_p{}, wk_p{};
   if constexpr (MODE != kRopeOnly) {
-    wq_p = load_raw<NV>(static_cast<const char*>(wqp) + d0 * 2);
-    wk_p = load_raw<NV>(static_cast<const char*>(wkp) + d0 * 2);
+    if (in_head) {
+      wq_p = load_raw<NV>(static_cast<const char*>(wqp) + d0 * 2);
+      wk_p = load_raw<NV>(static_cast<const char*>(wkp) + d0 * 2);
+    }
   }
 
-  // NeoX: this lane holds dims d0..d0+E-1; their partners d +- R/2 sit at the
-  // same offsets in lane ^ m. Lanes of the lower half subtract.
-  int partner_addr = 0, j0 = 0;
+  // NeoX: this lane holds dims d0..d0+E-1. With m = (R/2)/E, lanes below m
+  // hold first-half dims and find their partners d + R/2 at the same offsets
+  // in lane + m; lanes m..2m-1 hold the second half and look m lanes down.
+  // Lanes from 2m on hold pass-through dims. Lower-half lanes subtract.
+  int partner_addr = lane << 2, j0 = 0;
   bool lower = false, lane_rot = true;
   if constexpr (NEOX) {
     const int m = half / E;
-    partner_addr = (lane ^ m) << 2;
-    lower = (li & m) == 0;
-    j0 = d0 & (half - 1);  // half is a power of two for NeoX
-    lane_rot = FULL || d0 < R;
+    lane_rot = (FULL && EXACT) || li < 2 * m;
+    lower = li < m;
+    if (lane_rot) {
+      partner_addr = (lower ? lane + m : lane - m) << 2;
+      j0 = lower ? d0 : d0 - half;
+    }
   } else {
-    j0 = d0 / 2;
+    j0 = in_head ? d0 / 2 : 0;
   }
 
   const int total_waves = gridDim.x * wpb;
@@ -299,7 +313,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
         const int gg = isk[u] ? gu - p.ngq : gu;
         rs[u] = head_rsrc(isk[u] ? krow + gg * p.k_grp : qrow + gg * p.q_grp);
         off[u] = isk[u] ? k_off : q_off;
-        ok[u] = gu < g_end && gg * G + sub < (isk[u] ? p.Hkv : p.Hq);
+        ok[u] = in_head && gu < g_end && gg * G + sub < (isk[u] ? p.Hkv : p.Hq);
         if (ok[u]) {
           raw[u] = load_io<NV>(rs[u], off[u]);
         } else {
@@ -350,7 +364,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 #pragma unroll
           for (int i = 0; i < E; ++i) ss = fmaf(x[i], x[i], ss);
           ss = group_sum<L>(ss);
-          const float r = __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / D, p.eps));
+          const float r = __builtin_amdgcn_rsqf(fmaf(ss, EXACT ? 1.0f / DMAX : p.inv_d, p.eps));
 #pragma unroll
           for (int w = 0; w < NV; ++w) {
             float w0, w1;
@@ -371,7 +385,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
           for (int i = 0; i < E; ++i) {
             const float pn = lane_fetch(partner_addr, n[i]);
             const float v = fmaf(n[i], cs[i], pn * sn[i]);
-            o[i] = (FULL || lane_rot) ? v : n[i];
+            o[i] = lane_rot ? v : n[i];
           }
         } else {
 #pragma unroll
@@ -379,7 +393,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
             const float a = n[2 * kk], b = n[2 * kk + 1];
             const float oa = fmaf(a, cs[kk], -(b * sn[kk]));
             const float ob = fmaf(b, cs[kk], a * sn[kk]);
-            const bool rot = FULL || (d0 + 2 * kk < R);
+            const bool rot = (FULL && EXACT) || (d0 + 2 * kk < R);
             o[2 * kk] = rot ? oa : a;
             o[2 * kk + 1] = rot ? ob : b;
           }
@@ -419,18 +433,18 @@ template <class IO, int D, int E, bool NEOX, bool FULL>
 const void* pick_unroll(int U, int mode) {
   if (mode == kFused) {
     switch (U) {
-      case 1: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 1, kFused>);
-      case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kFused>);
-      case 4: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 4, kFused>);
+      case 1: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 1, kFused, true>);
+      case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kFused, true>);
+      case 4: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 4, kFused, true>);
       default: return nullptr;
     }
   }
   // the unfused baseline steps exist at the default unroll only
   if (U != 2) return nullptr;
   if (mode == kRopeOnly)
-    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kRopeOnly>);
+    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kRopeOnly, true>);
   if (mode == kNormOnly && !NEOX && FULL)  // pairing and rope_dim play no part
-    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kNormOnly>);
+    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kNormOnly, true>);
   return nullptr;
 }
 
@@ -454,8 +468,32 @@ const void* pick_lanes(int E, bool neox, bool full, int U, int mode) {
   return nullptr;
 }
 
+// Run-time head_dim instances: 16-byte lanes, lane group of DMAX/8 lanes,
+// fused op at unroll 2.
+template <class IO, int DMAX>
+const void* pick_any_dim(bool neox, bool full) {
+  if (neox) {
+    return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, true, 2, kFused, false>)
+                : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, false, 2, kFused, false>);
+  }
+  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, kFused, false>)
+              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, false, 2, kFused, false>);
+}
+
 template <class IO>
-const void* pick_dim(int D, int E, bool neox, bool full, int U, int mode) {
+const void* pick_dim(int D, int E, bool neox, bool full, int U, int mode, bool exact) {
+  if (!exact) {
+    if (mode != kFused || U != 2 || E != 8) return nullptr;
+    switch (D) {  // D is the lane-group capacity DMAX here
+      case 16: return pick_any_dim<IO, 16>(neox, full);
+      case 32: return pick_any_dim<IO, 32>(neox, full);
+      case 64: return pick_any_dim<IO, 64>(neox, full);
+      case 128: return pick_any_dim<IO, 128>(neox, full);
+      case 256: return pick_any_dim<IO, 256>(neox, full);
+      case 512: return pick_any_dim<IO, 512>(neox, full);
+      default: return nullptr;
+    }
+  }
   switch (D) {
     case 64: return pick_lanes<IO, 64>(E, neox, full, U, mode);
     case 128: return pick_lanes<IO, 128>(E, neox, full, U, mode);
@@ -464,9 +502,9 @@ const void* pick_dim(int D, int E, bool neox, bool full, int U, int mode) {
   }
 }
 
-const void* pick_kernel(int dtype, int D, int E, bool neox, bool full, int U, int mode) {
-  return dtype == QKNR_BF16 ? pick_dim<Bf16>(D, E, neox, full, U, mode)
-                            : pick_dim<Fp16>(D, E, neox, full, U, mode);
+const void* pick_kernel(int dtype, int D, int E, bool neox, bool full, int U, int mode, bool exact) {
+  return dtype == QKNR_BF16 ? pick_dim<Bf16>(D, E, neox, full, U, mode, exact)
+                            : pick_dim<Fp16>(D, E, neox, full, U, mode, exact);
 }
 
 // ----------------------------------------------------------------------------
@@ -474,22 +512,39 @@ const void* pick_kernel(int dtype, int D, int E, bool neox, bool full, int U, in
 // ----------------------------------------------------------------------------
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
-bool shape_supported(int32_t D, int32_t R, int32_t neox) {
-  if (D != 64 && D != 128 && D != 256) return false;
-  if (R <= 0 || R > D) return false;
-  const int e = D / 32;
-  if (R % e != 0) return false;
-  if (neox) {
-    const int rotary_lanes = R / e;
-    if (rotary_lanes < 2 || !is_pow2(rotary_lanes)) return false;
-  }
-  return true;
+// head_dim with compile-time instances (every lane mapping)
+bool fast_head_dim(int32_t D) { return D == 64 || D == 128 || D == 256; }
+
+// other head_dims: multiples of 8 from 16 to 512, run-time instances
+bool any_head_dim(int32_t D) { return !fast_head_dim(D) && D % 8 == 0 && D >= 16 && D <= 512; }
+
+// lane-group capacity of a run-time head_dim: the next power of two, >= 16
+int any_dim_capacity(int32_t D) {
+  int c = 16;
+  while (c < D) c *= 2;
+  return c;
 }
 
-// NeoX with E elements per lane needs rope_dim/E lanes, a power of two >= 2.
+// NeoX pairs (d, d + R/2): with E elements per lane the partner sits a fixed
+// m = (R/2)/E lanes away when R/2 is a multiple of E.
 bool lanes_fit(int32_t R, int32_t neox, int E) {
   if (!neox) return true;
-  return R % E == 0 && R / E >= 2 && is_pow2(R / E);
+  return (R / 2) % E == 0 && R / 2 >= E;
+}
+
+// The supported set: the page's rule (head_dim 64/128/256, rope_dim a
+// multiple of head_dim/32, NeoX rotary lanes a power of two) widened to every
+// even rope_dim for interleaved pairing, every NeoX rope_dim whose half is a
+// multiple of some lane width, and other head_dims that are multiples of 8.
+bool shape_supported(int32_t D, int32_t R, int32_t neox) {
+  if (!fast_head_dim(D) && !any_head_dim(D)) return false;
+  if (R <= 0 || R > D || R % 2) return false;
+  if (!neox) return true;
+  if (fast_head_dim(D)) {
+    if (lanes_fit(R, neox, 8) || lanes_fit(R, neox, D / 32)) return true;
+    return D / 64 >= 2 && lanes_fit(R, neox, D / 64);
+  }
+  return lanes_fit(R, neox, 8);
 }
 
 // Head vectors of one tensor must not overlap: with the smaller of the two
@@ -523,6 +578,8 @@ struct Plan {
       wpb = kDefaultBlockWaves;
   int64_t items = 0;
   int max_blocks = 0;  // 0: one workgroup per wpb items; -1: occupancy x CUs; > 0: explicit cap
+  int dmax = 0;        // head_dim of the instance (lane-group capacity)
+  bool exact = true;   // head_dim == dmax
 };
 
 // A lane's byte offset inside its head group, (heads-1)*head_stride + 2*D at
@@ -546,7 +603,17 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
     return lane_offsets_fit(G, Hq, q_head, D) && lane_offsets_fit(G, Hkv, k_head, D);
   };
   int E = 0;
-  if (c.lanes_per_head == 0) {
+  const bool exact = fast_head_dim(D);
+  const int dmax = exact ? D : any_dim_capacity(D);
+  if (!exact) {
+    // run-time head_dim: 16-byte lanes in a lane group of dmax/8 lanes
+    E = 8;
+    const int G = kWave / (dmax / 8);
+    if (!lanes_fit(R, neox, 8)) return QKNR_E_UNSUPPORTED;
+    if (c.lanes_per_head != 0 && c.lanes_per_head != dmax / 8) return QKNR_E_ARG;
+    if (!lane_offsets_fit(G, Hq, q_head, D) || !lane_offsets_fit(G, Hkv, k_head, D))
+      return QKNR_E_SHAPE;
+  } else if (c.lanes_per_head == 0) {
     // 16-byte lanes first; then half a wave and a full wave per head
     const int cand[3] = {8, D / 32, D / 64};
     for (int e : cand) {
@@ -560,15 +627,17 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
     if (E != 8 && E != D / 32 && !(E == D / 64 && E >= 2)) return QKNR_E_ARG;
     if (!lanes_fit(R, neox, E) || !fits(E)) return QKNR_E_ARG;
   }
-  // the unfused baseline steps exist at unroll 2 only
-  const int U = mode != kFused ? 2 : (c.unroll == 0 ? kDefaultUnroll : c.unroll);
+  // the unfused baseline steps and the run-time head_dim instances exist at unroll 2 only
+  const int U = (mode != kFused || !exact) ? 2 : (c.unroll == 0 ? kDefaultUnroll : c.unroll);
   if (U != 1 && U != 2 && U != 4) return QKNR_E_ARG;
   const int wpb = c.block_waves == 0 ? kDefaultBlockWaves : c.block_waves;
   if (wpb < 1 || wpb > kMaxBlockWaves) return QKNR_E_ARG;
   if (c.groups_per_item < 0 || c.max_blocks < -1) return QKNR_E_ARG;
 
   pl->E = E;
-  pl->L = D / E;
+  pl->L = dmax / E;
+  pl->dmax = dmax;
+  pl->exact = exact;
   pl->G = kWave / pl->L;
   pl->ngq = (Hq + pl->G - 1) / pl->G;
   pl->ng = pl->ngq + (Hkv + pl->G - 1) / pl->G;
@@ -580,7 +649,7 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   pl->U = U;
   pl->wpb = wpb;
   pl->max_blocks = c.max_blocks;
-  pl->fn = pick_kernel(dtype, D, E, neox != 0, R == D, U, mode);
+  pl->fn = pick_kernel(dtype, dmax, E, neox != 0, R == D, U, mode, exact);
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
 }
 
@@ -707,6 +776,8 @@ int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
   prm.Hq = c.Hq;
   prm.Hkv = c.Hkv;
   prm.R = c.R;
+  prm.D = c.D;
+  prm.inv_d = static_cast<float>(1.0 / c.D);
   prm.pos64 = c.pdt == QKNR_I64;
   prm.eps = c.eps;
   prm.ng = pl.ng;
@@ -739,9 +810,10 @@ QKNR_API const char* qknr_status_string(int32_t status) {
     case QKNR_E_NULL: return "qknr: a required pointer is NULL";
     case QKNR_E_SHAPE: return "qknr: bad shape or strides (negative, overlapping head vectors, or too large)";
     case QKNR_E_UNSUPPORTED:
-      return "qknr: unsupported (head_dim, rope_dim, is_neox): need head_dim in {64,128,256}, "
-             "0 < rope_dim <= head_dim, rope_dim % (head_dim/32) == 0, and for NeoX "
-             "rope_dim/(head_dim/32) a power of two >= 2";
+      return "qknr: unsupported (head_dim, rope_dim, is_neox): need head_dim a multiple of 8 in "
+             "[16, 512], rope_dim even in (0, head_dim], and for NeoX rope_dim/2 a multiple of 8 "
+             "(for head_dim 64/128/256 a multiple of 2, 2 or 4); the unfused steps take head_dim "
+             "64/128/256 only";
     case QKNR_E_ALIGN:
       return "qknr: misaligned: q, k, weights and q/k strides need 16-byte alignment, the cache 4 bytes, "
              "positions their element size";

@@ -21,9 +21,17 @@
  *     dtype, the cos|sin cache [rows, R] fp32 row-contiguous, positions [T]
  *     int32 or int64.
  *
- * Supported shapes (section 4.6 compile-time guards, section 5.2 predicate):
- *   head_dim in {64, 128, 256}; 0 < rope_dim <= head_dim; rope_dim a multiple
- *   of head_dim/32; for NeoX, rope_dim/(head_dim/32) a power of two >= 2.
+ * Supported shapes. Every shape the page accepts (section 4.6 compile-time
+ * guards, section 5.2 predicate: head_dim in {64, 128, 256}, rope_dim a
+ * multiple of head_dim/32, for NeoX rope_dim/(head_dim/32) a power of two >= 2),
+ * widened to:
+ *   head_dim a multiple of 8 in [16, 512] (64, 128 and 256 have compile-time
+ *   instances with every lane mapping; the others run-time instances);
+ *   rope_dim even with 0 < rope_dim <= head_dim;
+ *   for NeoX, rope_dim/2 a multiple of a lane width E: 8 for any head_dim, or
+ *   also head_dim/32 and head_dim/64 (>= 2) for head_dim 64, 128, 256.
+ * qknr_can_use reports exactly this set. The unfused steps below exist for
+ * head_dim 64, 128 and 256.
  *
  * All entry points are thread-safe and keep no state besides small per-device
  * caches of the CU count and kernel occupancy.
@@ -194,11 +202,10 @@ QKNR_API int32_t qknr_unfused_inplace(void* q, void* k, const void* wq, const vo
                                       int32_t dtype, int32_t pos_dtype, hipStream_t stream);
 
 /*
- * qknr_can_use -- 1 if an instance exists for this combination, else 0.
- * Mirrors the page's capability predicate (section 5.2): head_dim in
- * {64,128,256}, 0 < rope_dim <= head_dim, rope_dim % (head_dim/32) == 0, and
- * for NeoX rope_dim/(head_dim/32) a power of two >= 2; dtype and pos_dtype must
- * be known codes. Pure host function, no HIP call.
+ * qknr_can_use -- 1 if qknr_inplace supports this combination, else 0: the
+ * "Supported shapes" set above (a superset of the page's capability predicate,
+ * section 5.2), with known dtype and pos_dtype codes. Pure host function, no
+ * HIP call.
  */
 QKNR_API int32_t qknr_can_use(int32_t head_dim, int32_t rope_dim, int32_t is_neox,
                               int32_t dtype, int32_t pos_dtype);

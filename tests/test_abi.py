@@ -53,11 +53,34 @@ def _page_predicate(D, R, neox):
     return True
 
 
-def test_can_use_matches_page_predicate():
-    for D in (0, 32, 64, 96, 128, 192, 256, 512):
+def _supported(D, R, neox):
+    """The library's documented set (include/qknr.h), restated: head_dim a
+    multiple of 8 in [16, 512]; rope_dim even in (0, head_dim]; NeoX needs
+    rope_dim/2 to be a multiple of a lane width E (8 for any head_dim; also
+    head_dim/32 and head_dim/64 >= 2 for head_dim 64, 128, 256)."""
+    if D % 8 or D < 16 or D > 512:
+        return False
+    if R <= 0 or R > D or R % 2:
+        return False
+    if not neox:
+        return True
+    widths = [8] + ([D // 32] + ([D // 64] if D // 64 >= 2 else []) if D in (64, 128, 256) else [])
+    return any((R // 2) % e == 0 and R // 2 >= e for e in widths)
+
+
+def test_can_use_covers_page_predicate_and_matches_documented_set():
+    n_page = n_more = 0
+    for D in (0, 8, 16, 24, 32, 40, 64, 80, 96, 100, 128, 192, 256, 320, 512, 520, 1024):
         for R in range(-2, max(D, 8) + 3):
             for neox in (0, 1):
-                assert B.qknr_can_use(D, R, neox) == _page_predicate(D, R, neox), (D, R, neox)
+                got = B.qknr_can_use(D, R, neox)
+                assert got == _supported(D, R, neox), (D, R, neox)
+                if _page_predicate(D, R, neox):
+                    assert got, (D, R, neox)
+                    n_page += 1
+                elif got:
+                    n_more += 1
+    assert n_page > 0 and n_more > n_page
     assert not B.lib().qknr_can_use(128, 128, 1, 2, 0)
     assert not B.lib().qknr_can_use(128, 128, 1, 0, 2)
     assert B.lib().qknr_can_use(128, 128, 1, 1, 1)
@@ -91,9 +114,12 @@ REJECT = [
     (dict(T=1 << 31), B.QKNR_E_SHAPE), (dict(T=(1 << 28), Hq=8, Hkv=8), B.QKNR_E_SHAPE),
     (dict(dtype=2), B.QKNR_E_DTYPE), (dict(dtype=-1), B.QKNR_E_DTYPE),
     (dict(pdt=2), B.QKNR_E_DTYPE),
-    (dict(D=96, R=96), B.QKNR_E_UNSUPPORTED), (dict(R=0), B.QKNR_E_UNSUPPORTED),
+    (dict(D=100, R=100), B.QKNR_E_UNSUPPORTED), (dict(D=1024, R=1024), B.QKNR_E_UNSUPPORTED),
+    (dict(D=8, R=8), B.QKNR_E_UNSUPPORTED), (dict(R=0), B.QKNR_E_UNSUPPORTED),
     (dict(R=130), B.QKNR_E_UNSUPPORTED), (dict(R=6), B.QKNR_E_UNSUPPORTED),
-    (dict(R=96, neox=1), B.QKNR_E_UNSUPPORTED), (dict(D=64, R=2, neox=1), B.QKNR_E_UNSUPPORTED),
+    (dict(R=7, neox=0), B.QKNR_E_UNSUPPORTED), (dict(R=98, neox=1), B.QKNR_E_UNSUPPORTED),
+    (dict(D=64, R=2, neox=1), B.QKNR_E_UNSUPPORTED),
+    (dict(D=96, R=40, neox=1, qt=4 * 192, qh=192, kt=4 * 192, kh=192), B.QKNR_E_UNSUPPORTED),
     (dict(eps=-1e-6), B.QKNR_E_ARG), (dict(eps=float("nan")), B.QKNR_E_ARG),
     (dict(eps=float("inf")), B.QKNR_E_ARG),
     (dict(q=P(0)), B.QKNR_E_NULL), (dict(k=P(0)), B.QKNR_E_NULL), (dict(wq=P(0)), B.QKNR_E_NULL),
@@ -158,14 +184,14 @@ def _plan(D, R, neox, Hq=24, Hkv=24, cfg=None):
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_plan_lane_mapping(D):
     """16-byte lanes (head_dim/8 lanes per head) whenever the pairing allows it;
-    the half-wave mapping (32 lanes, head_dim/32 elements) otherwise."""
+    then half a wave (32 lanes), then a full wave (64 lanes) per head."""
     for neox in (0, 1):
-        for R in range(D // 32, D + 1, D // 32):
+        for R in range(2, D + 1, 2):
             if not B.qknr_can_use(D, R, neox):
                 continue
             info = _plan(D, R, neox)
-            fits16 = (not neox) or (R % 8 == 0 and R // 8 >= 2 and (R // 8) & (R // 8 - 1) == 0)
-            want_lanes = D // 8 if fits16 else 32
+            fits = lambda e: (not neox) or ((R // 2) % e == 0 and R // 2 >= e)
+            want_lanes = D // 8 if fits(8) else (32 if fits(D // 32) else 64)
             assert info["lanes_per_head"] == want_lanes, (D, R, neox, info)
             assert info["elems_per_lane"] * info["lanes_per_head"] == D
             assert info["heads_per_wave"] == 64 // info["lanes_per_head"]
@@ -173,6 +199,16 @@ def test_plan_lane_mapping(D):
             assert info["groups_per_token"] == -(-24 // G) + -(-24 // G)
             gqa = _plan(D, R, neox, Hq=7, Hkv=3)
             assert gqa["groups_per_token"] == -(-7 // gqa["heads_per_wave"]) + -(-3 // gqa["heads_per_wave"])
+
+
+@pytest.mark.parametrize("D,lanes", [(16, 2), (24, 4), (40, 8), (80, 16), (96, 16), (112, 16),
+                                     (160, 32), (192, 32), (320, 64), (512, 64)])
+def test_plan_run_time_head_dims(D, lanes):
+    """Other head_dims use 16-byte lanes in a lane group padded to a power of two."""
+    info = _plan(D, D, 0)
+    assert (info["lanes_per_head"], info["elems_per_lane"]) == (lanes, 8)
+    assert info["heads_per_wave"] == 64 // lanes and info["unroll"] == 2
+    assert _plan(D, D - (D % 16), 1)["lanes_per_head"] == lanes
 
 
 def test_plan_defaults():
@@ -263,7 +299,10 @@ def test_unfused_entry_points_validate_before_launching():
     # the norm step needs no cache or positions; it does need the weights
     assert L.qknr_rmsnorm_inplace(a, a, z, a, 5, 4, 4, 128, 1e-6, 1024, 256, 1024, 256, 0,
                                   z) == B.QKNR_E_NULL
-    assert L.qknr_rmsnorm_inplace(a, a, a, a, 5, 4, 4, 96, 1e-6, 1024, 256, 1024, 256, 0,
+    # the unfused steps exist for head_dim 64/128/256 only
+    assert L.qknr_rmsnorm_inplace(a, a, a, a, 5, 4, 4, 96, 1e-6, 4 * 192, 192, 4 * 192, 192, 0,
+                                  z) == B.QKNR_E_UNSUPPORTED
+    assert L.qknr_rmsnorm_inplace(a, a, a, a, 5, 4, 4, 100, 1e-6, 4 * 208, 208, 4 * 208, 208, 0,
                                   z) == B.QKNR_E_UNSUPPORTED
     assert L.qknr_rmsnorm_inplace(a, a, a, a, 5, 4, 4, 128, -1.0, 1024, 256, 1024, 256, 0,
                                   z) == B.QKNR_E_ARG
@@ -272,7 +311,7 @@ def test_unfused_entry_points_validate_before_launching():
     # the rope step needs cache and positions, no weights
     assert L.qknr_rope_inplace(a, a, z, a, 5, 4, 4, 128, 128, 1, 1024, 256, 1024, 256, 0, 0,
                                z) == B.QKNR_E_NULL
-    assert L.qknr_rope_inplace(a, a, a, a, 5, 4, 4, 128, 96, 1, 1024, 256, 1024, 256, 0, 0,
+    assert L.qknr_rope_inplace(a, a, a, a, 5, 4, 4, 128, 98, 1, 1024, 256, 1024, 256, 0, 0,
                                z) == B.QKNR_E_UNSUPPORTED
     assert L.qknr_rope_inplace(a, a, a, P(A + 4), 5, 4, 4, 128, 128, 1, 1024, 256, 1024, 256, 0,
                                1, z) == B.QKNR_E_ALIGN
@@ -281,7 +320,7 @@ def test_unfused_entry_points_validate_before_launching():
     # the unfused pair validates like the fused op, before either launch
     args = [a, a, a, a, a, a, 5, 4, 4, 128, 128, 1, 1e-6, 1024, 256, 1024, 256, 0, 0, z]
     assert L.qknr_unfused_inplace(*args) == B.QKNR_E_DEVICE
-    for i, bad, code in ((2, z, B.QKNR_E_NULL), (4, z, B.QKNR_E_NULL), (10, 96, B.QKNR_E_UNSUPPORTED),
+    for i, bad, code in ((2, z, B.QKNR_E_NULL), (4, z, B.QKNR_E_NULL), (10, 98, B.QKNR_E_UNSUPPORTED),
                          (12, float("nan"), B.QKNR_E_ARG), (14, 128, B.QKNR_E_SHAPE)):
         bad_args = list(args)
         bad_args[i] = bad

@@ -81,17 +81,43 @@ def test_grid(D, R, neox, dt, pdt, T):
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("neox", [False, True])
 def test_every_supported_rope_dim(D, neox):
-    """Every rope_dim the capability predicate accepts, including the NeoX
-    widths that need the half-wave lane mapping."""
+    """Every rope_dim the capability predicate accepts for the compile-time
+    head_dims: all even widths (interleaved), every NeoX width whose half is a
+    multiple of a lane width (including rotary-lane counts that are not powers
+    of two and the widths that need half or full waves per head)."""
     from head_qk_rmsnorm_amd import binding as B
 
-    e = D // 32
-    Rs = [R for R in range(e, D + 1, e) if B.qknr_can_use(D, R, neox)]
+    Rs = [R for R in range(2, D + 1, 2) if B.qknr_can_use(D, R, neox)]
     assert Rs
     for R in Rs:
         cfg = W.case(7, 3, 2, D, R, neox, seed=R, positions="uniform")
         _say("case", cfg.name)
         Hn.run_and_check(W.make_workload(cfg))
+
+
+ANY_DIMS = [16, 24, 40, 48, 72, 80, 96, 112, 160, 192, 200, 320, 384, 504, 512]
+
+
+@pytest.mark.parametrize("D", ANY_DIMS)
+@pytest.mark.parametrize("neox", [False, True])
+@pytest.mark.parametrize("dt", [W.BF16, W.FP16])
+def test_run_time_head_dims(D, neox, dt):
+    """head_dims other than 64/128/256 (run-time instances, lane groups padded
+    to a power of two): full rotation and a partial one, Q/K straddling groups."""
+    from head_qk_rmsnorm_amd import binding as B
+
+    for R in (D - (D % 16) if neox else D, 16 if neox else 6):
+        assert B.qknr_can_use(D, R, neox), (D, R, neox)
+        cfg = W.case(33, 5, 3, D, R, neox, dtype=dt, pos_dtype=W.I64, seed=D + R)
+        _say("case", cfg.name)
+        Hn.run_and_check(W.make_workload(cfg))
+
+
+@pytest.mark.parametrize("layout", ["padded", "head_major", "qkv"])
+@pytest.mark.parametrize("D,R,neox", [(96, 96, True), (80, 64, False), (192, 128, True)])
+def test_run_time_head_dim_layouts(layout, D, R, neox):
+    cfg = W.case(40, 6, 2, D, R, neox, seed=7)
+    Hn.run_and_check(W.make_workload(cfg), layout=layout)
 
 
 # ---------------------------------------------------------------------------
@@ -217,10 +243,11 @@ def test_rejections_leave_buffers_untouched():
     cfg = W.case(9, 4, 4, 128, 128, True, seed=6)
     wl = W.make_workload(cfg)
     dc = Hn.DeviceCase(wl)
+    rows = int(wl.positions.max()) + 1  # any dummy table covers every position
     bad = [
         dict(eps=-1.0),
         dict(eps=float("nan")),
-        dict(rope_dim=96),  # NeoX: 96/4 = 24 rotary lanes, not a power of two
+        dict(rope_dim=98),  # NeoX: half of 98 is odd, no lane width divides it
     ]
     for kw in bad:
         args = dict(is_neox=True, eps=1e-6)
@@ -228,7 +255,7 @@ def test_rejections_leave_buffers_untouched():
         rope = args.pop("rope_dim", 0)
         with pytest.raises((RuntimeError, ValueError)):
             B.qknr_inplace(dc.q, dc.k, dc.wq, dc.wk,
-                           dc.cache if not rope else torch.zeros(4, rope, device=dc.device),
+                           dc.cache if not rope else torch.zeros(rows, rope, device=dc.device),
                            dc.positions, rope_dim=rope, **args)
     # misaligned q view (offset by one element)
     q_mis = torch.as_strided(dc.storages_dev[0], dc.q.shape, dc.q.stride(),
