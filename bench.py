@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-yardstick", action="store_true")
     ap.add_argument("--no-unfused", action="store_true", help="skip timing the two-launch baseline")
+    ap.add_argument("--op", default="fused", choices=["fused", "layernorm"],
+                    help="time the fused RMSNorm+RoPE op (default) or the per-head LayerNorm+RoPE sibling")
     ap.add_argument("--sweep", action="store_true", help="time a short list of launch configurations")
     ap.add_argument("--sweep-grid", action="store_true",
                     help="time every (grid kind, groups per item, unroll, block waves) combination")
@@ -106,18 +108,30 @@ class Rig:
             return q, k
         return bufs[0], bufs[1]
 
-    def prepare(self, launch=None, unfused=False):
+    def prepare(self, launch=None, unfused=False, layernorm=False):
         import torch
 
         from head_qk_rmsnorm_amd import binding as B
 
         c = self.cfg
+        bias = None
+        if layernorm:
+            # seeded bias rows for the LayerNorm sibling
+            import numpy as np
+
+            from head_qk_rmsnorm_amd import workloads as W
+
+            g = W.rng(c.seed, 77)
+            tdt = self.wq.dtype
+            bias = tuple(torch.from_numpy(W.to_io_bits(g.standard_normal(c.head_dim) * 0.5,
+                                                       c.dtype).view(np.int16)).to(self.dev).view(tdt)
+                         for _ in range(2))
         self.calls = []
         for bufs, pos in self.copies:
             q, k = self.views(bufs)
             self.calls.append(B.PreparedCall(q, k, self.wq, self.wk, self.cache, pos,
                                              is_neox=c.is_neox, eps=c.eps, launch=launch,
-                                             unfused=unfused))
+                                             unfused=unfused, layernorm_bias=bias))
         self.calls[0]()
         torch.cuda.synchronize(self.dev)
         self.info = self.calls[0].info.as_dict()
@@ -237,22 +251,27 @@ def unfused_bytes(cfg):
     return 2 * qk + 2 * D * cfg.io_bytes + cfg.T * cfg.pos_bytes + cfg.T * R * 4
 
 
-def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None, want_unfused=True):
+def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None, want_unfused=True,
+            op="fused"):
     own = rig is None
+    layernorm = op == "layernorm"
     if own:
         rig = Rig(cfg, dev, launch=launch)
-    else:
+    if layernorm:
+        rig.prepare(layernorm=True)
+    elif not own:
         rig.prepare(launch)
     ms, host_ms, wall = rig.time(steps, warmup)
-    B = cfg.algorithmic_bytes()
+    # the LayerNorm sibling also reads the two bias rows
+    B = cfg.algorithmic_bytes() + (2 * cfg.head_dim * cfg.io_bytes if layernorm else 0)
     gbs = B / (ms * 1e-3) / 1e9
     out = {
         "workload": cfg.name, "ms_per_step": ms, "GB_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
         "gheads_per_s": cfg.units / (ms * 1e-3) / 1e9, "host_ms_per_launch": host_ms,
         "algorithmic_bytes": B, "n_rot": rig.n_rot, "footprint_bytes": rig.footprint,
-        "launch": rig.info,
+        "launch": rig.info, "op": op,
     }
-    if want_unfused:
+    if want_unfused and not layernorm:
         rig.prepare(unfused=True)
         ums, _, _ = rig.time(steps, warmup)
         ub = unfused_bytes(cfg)
@@ -328,7 +347,8 @@ def main():
     if args.all_configs:
         for name in W.CONFIG_ORDER:
             r = measure(W.CONFIGS[name], dev, args.steps, args.warmup, launch,
-                        want_yard=not args.no_yardstick, want_unfused=not args.no_unfused)
+                        want_yard=not args.no_yardstick, want_unfused=not args.no_unfused,
+                        op=args.op)
             msg = (f"[bench] {name}: {r['GB_s']:.1f} GB/s ({r['frac_of_peak'] * 100:.1f}% of peak), "
                    f"{r['gheads_per_s']:.2f} Gheads/s")
             if "yardstick_GB_s" in r:
@@ -342,10 +362,10 @@ def main():
                 extra.flush()
 
     r = measure(cfg, dev, args.steps, args.warmup, launch, want_yard=not args.no_yardstick,
-                want_unfused=not args.no_unfused)
+                want_unfused=not args.no_unfused, op=args.op)
     print(f"[bench] {cfg.name}: {r['GB_s']:.1f} GB/s, {r['ms_per_step'] * 1e3:.2f} us/launch",
           file=sys.stderr, flush=True)
-    ent, why = counters_for(cfg.name)
+    ent, why = counters_for(cfg.name) if args.op == "fused" else (None, "counters cover the fused op")
     traffic = None
     if ent:
         traffic = ent["fetch_bytes_per_launch"] + ent["write_bytes_per_launch"]
@@ -353,6 +373,8 @@ def main():
             "frac": round(r["GB_s"] / HBM_PEAK_GBS, 5), "traffic": traffic}
     line = {
         "metric": "achieved HBM GB/s (and % of peak) + Gheads/s for fused QK RMSNorm+RoPE",
+        "op": "fused QK RMSNorm + RoPE" if args.op == "fused" else
+              "per-head QK LayerNorm (weight, bias) + RoPE (sibling op, not the headline metric)",
         "value": round(r["GB_s"], 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -361,7 +383,7 @@ def main():
                    "head_dim": cfg.head_dim, "rope_dim": cfg.rope_dim,
                    "pairing": "neox" if cfg.is_neox else "interleaved", "io_dtype": cfg.dtype,
                    "pos_dtype": cfg.pos_dtype, "layout": cfg.layout,
-                   "algorithmic_bytes_per_step": cfg.algorithmic_bytes(), "launch": r["launch"],
+                   "algorithmic_bytes_per_step": r["algorithmic_bytes"], "launch": r["launch"],
                    "rotated_copies": r["n_rot"]},
         "gheads_per_s": round(r["gheads_per_s"], 4),
         "frac_of_hbm_peak": round(r["frac_of_peak"], 5),

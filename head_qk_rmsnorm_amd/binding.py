@@ -93,6 +93,10 @@ def lib() -> ctypes.CDLL:
             L.qknr_rope_inplace.argtypes = [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32,
                                             _I64, _I64, _I64, _I64, _I32, _I32, _P]
             L.qknr_rope_inplace.restype = _I32
+            L.qknr_layernorm_rope_inplace.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32,
+                                                      _I32, _I32, _I32, _I32, ctypes.c_float,
+                                                      _I64, _I64, _I64, _I64, _I32, _I32, _P]
+            L.qknr_layernorm_rope_inplace.restype = _I32
             L.qknr_copy.argtypes = [_P, _P, _I64, _P]
             L.qknr_copy.restype = _I32
             L.qknr_rmw.argtypes = [_P, _I64, ctypes.c_uint32, _P]
@@ -285,6 +289,31 @@ def qknr_rope_inplace(q, k, cos_sin_cache, positions, *, is_neox: bool, rope_dim
                                        v["dtype"], pcode, _stream_of(q, stream)))
 
 
+def qknr_layernorm_rope_inplace(q, k, q_weight, k_weight, q_bias=None, k_bias=None,
+                                cos_sin_cache=None, positions=None, *, is_neox: bool = False,
+                                eps: float = 1e-6, rope_dim: int = 0, stream=None) -> None:
+    """Per-head QK LayerNorm (weight, optional bias) of q and k in place, then the
+    rotation of the first rope_dim dims when a cos|sin cache is given."""
+    import torch
+
+    v = _qk(q, k, 0)
+    wq, wk = _weights(q, q_weight, k_weight, v["D"])
+    bq = bk = ctypes.c_void_p(0)
+    if (q_bias is None) != (k_bias is None):
+        raise ValueError("give both biases or neither")
+    if q_bias is not None:
+        bq, bk = _weights(q, q_bias, k_bias, v["D"])
+    cache = pos = ctypes.c_void_p(0)
+    R, pcode = 0, QKNR_I32
+    if cos_sin_cache is not None:
+        cache, pos, R, pcode = _rotation(q, cos_sin_cache, positions, v["T"], rope_dim)
+    with torch.cuda.device(q.device):
+        _check(lib().qknr_layernorm_rope_inplace(
+            v["q"], v["k"], wq, wk, bq, bk, cache, pos, v["T"], v["Hq"], v["Hkv"], v["D"], R,
+            int(bool(is_neox)), float(eps), v["qt"], v["qh"], v["kt"], v["kh"], v["dtype"], pcode,
+            _stream_of(q, stream)))
+
+
 def fused_inplace_qknorm_rope(q, k, q_weight, k_weight, cos_sin_cache, positions, *,
                               is_neox: bool, eps: float = 1e-6, head_dim: int = 0,
                               rope_dim: int = 0) -> None:
@@ -321,18 +350,25 @@ class PreparedCall:
 
     def __init__(self, q, k, q_weight, k_weight, cos_sin_cache, positions, *, is_neox: bool,
                  eps: float = 1e-6, head_dim: int = 0, rope_dim: int = 0, stream=None,
-                 launch: Optional[dict] = None, unfused: bool = False):
-        self._keep = (q, k, q_weight, k_weight, cos_sin_cache, positions)
+                 launch: Optional[dict] = None, unfused: bool = False,
+                 layernorm_bias: Optional[tuple] = None):
+        """``unfused=True`` prepares the two-launch baseline; ``layernorm_bias=(bq, bk)``
+        prepares the LayerNorm sibling (with rotation) instead of the fused op."""
+        self._keep = (q, k, q_weight, k_weight, cos_sin_cache, positions, layernorm_bias)
         self._device = q.device
         args = _marshal(q, k, q_weight, k_weight, cos_sin_cache, positions, is_neox, eps,
                         head_dim, rope_dim)
         self._cfg = LaunchCfg(**(launch or {}))
         self.info = LaunchInfo()
+        if (unfused or layernorm_bias is not None) and launch:
+            raise ValueError("only the fused op takes a launch configuration")
         if unfused:
-            if launch:
-                raise ValueError("the unfused baseline takes no launch configuration")
             self._args = args + (_stream_of(q, stream),)
             self._fn = lib().qknr_unfused_inplace
+        elif layernorm_bias is not None:
+            bq, bk = _weights(q, layernorm_bias[0], layernorm_bias[1], int(args[9]))
+            self._args = args[:4] + (bq, bk) + args[4:] + (_stream_of(q, stream),)
+            self._fn = lib().qknr_layernorm_rope_inplace
         else:
             self._args = args + (_stream_of(q, stream), ctypes.byref(self._cfg),
                                  ctypes.byref(self.info))

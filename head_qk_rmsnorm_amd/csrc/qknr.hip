@@ -218,14 +218,16 @@ struct Params {
   int32_t ngq;                   // Q head groups per token; K groups follow them
   int32_t pos64;
   int32_t cs_vec;                // cache rows 16-byte aligned and R/2 % 4 == 0
+  int32_t has_bias;              // LayerNorm sibling: bias rows given
   float eps;
   int32_t ng, gpi, nc, n_items;  // groups per token, groups per item, items per token, items
 };
 
-// What a launch computes: the fused op, or one of the two steps of the
-// unfused chain it replaces (norm only: rotation skipped; rope only: the
-// stored values are rotated as they are, no norm).
-enum : int { kFused = 0, kNormOnly = 1, kRopeOnly = 2 };
+// What a launch computes: the fused op, one of the two steps of the unfused
+// chain it replaces (norm only: rotation skipped; rope only: the stored values
+// are rotated as they are, no norm), or the per-head LayerNorm sibling with or
+// without the rotation.
+enum : int { kFused = 0, kNormOnly = 1, kRopeOnly = 2, kLayerRope = 3, kLayerOnly = 4 };
 
 // One wave instruction covers one head group: G consecutive heads of Q, or of
 // K, of one token (groups never mix Q and K), so the group's base address is
@@ -238,7 +240,8 @@ template <class IO, int DMAX, int E, bool NEOX, bool FULL, int U, int MODE, bool
 __global__ void __launch_bounds__(kMaxBlockWaves * kWave)
 qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict__ wqp,
             const void* __restrict__ wkp, const float* __restrict__ cache,
-            const void* __restrict__ posp, const Params p) {
+            const void* __restrict__ posp, const void* __restrict__ bqp,
+            const void* __restrict__ bkp, const Params p) {
   constexpr int L = DMAX / E;   // lanes per head (lane group)
   constexpr int G = kWave / L;  // heads per wave instruction
   constexpr int NV = E / 2;     // packed dwords per lane
@@ -257,12 +260,22 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   const uint32_t q_off = static_cast<uint32_t>(sub) * p.q_head + d0 * 2;
   const uint32_t k_off = static_cast<uint32_t>(sub) * p.k_head + d0 * 2;
 
-  // Weights of this lane's dims, kept packed (widened per use).
-  Raw<NV> wq_p{}, wk_p{};
-  if constexpr (MODE != kRopeOnly) {
+  constexpr bool kRotate = MODE == kFused || MODE == kRopeOnly || MODE == kLayerRope;
+  constexpr bool kRms = MODE == kFused || MODE == kNormOnly;
+  constexpr bool kLayer = MODE == kLayerRope || MODE == kLayerOnly;
+
+  // Weights (and LayerNorm biases) of this lane's dims, kept packed.
+  Raw<NV> wq_p{}, wk_p{}, bq_p{}, bk_p{};
+  if constexpr (kRms || kLayer) {
     if (in_head) {
       wq_p = load_raw<NV>(static_cast<const char*>(wqp) + d0 * 2);
       wk_p = load_raw<NV>(static_cast<const char*>(wkp) + d0 * 2);
+    }
+  }
+  if constexpr (kLayer) {
+    if (in_head && p.has_bias) {
+      bq_p = load_raw<NV>(static_cast<const char*>(bqp) + d0 * 2);
+      bk_p = load_raw<NV>(static_cast<const char*>(bkp) + d0 * 2);
     }
   }
 
@@ -287,8 +300,6 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   const int total_waves = gridDim.x * wpb;
   int item = blockIdx.x * wpb + wib;
   if (item >= p.n_items) return;
-  constexpr bool kRotate = MODE != kNormOnly;
-  constexpr bool kNorm = MODE != kRopeOnly;
   int64_t pos_next = kRotate ? token_position(posp, p.pos64, item / p.nc) : 0;
 
   for (; item < p.n_items; item += total_waves) {
@@ -359,7 +370,29 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 #pragma unroll
         for (int w = 0; w < NV; ++w) IO::unpack(raw[u].w[w], x[2 * w], x[2 * w + 1]);
         float n[E];
-        if constexpr (kNorm) {
+        if constexpr (kLayer) {
+          // two passes in registers: mean, then the variance of the centred values
+          float sm = 0.0f;
+#pragma unroll
+          for (int i = 0; i < E; ++i) sm += x[i];
+          const float mean = group_sum<L>(sm) * (EXACT ? 1.0f / DMAX : p.inv_d);
+          float c[E], ss = 0.0f;
+#pragma unroll
+          for (int i = 0; i < E; ++i) {
+            c[i] = in_head ? x[i] - mean : 0.0f;
+            ss = fmaf(c[i], c[i], ss);
+          }
+          ss = group_sum<L>(ss);
+          const float r = __builtin_amdgcn_rsqf(fmaf(ss, EXACT ? 1.0f / DMAX : p.inv_d, p.eps));
+#pragma unroll
+          for (int w = 0; w < NV; ++w) {
+            float w0, w1, b0, b1;
+            IO::unpack(isk[u] ? wk_p.w[w] : wq_p.w[w], w0, w1);
+            IO::unpack(isk[u] ? bk_p.w[w] : bq_p.w[w], b0, b1);
+            n[2 * w] = fmaf(c[2 * w] * r, w0, b0);
+            n[2 * w + 1] = fmaf(c[2 * w + 1] * r, w1, b1);
+          }
+        } else if constexpr (kRms) {
           float ss = 0.0f;
 #pragma unroll
           for (int i = 0; i < E; ++i) ss = fmaf(x[i], x[i], ss);
@@ -439,12 +472,18 @@ const void* pick_unroll(int U, int mode) {
       default: return nullptr;
     }
   }
-  // the unfused baseline steps exist at the default unroll only
+  // the unfused baseline steps and the LayerNorm sibling exist at unroll 2 only
   if (U != 2) return nullptr;
   if (mode == kRopeOnly)
     return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kRopeOnly, true>);
-  if (mode == kNormOnly && !NEOX && FULL)  // pairing and rope_dim play no part
-    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kNormOnly, true>);
+  if (mode == kLayerRope)
+    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kLayerRope, true>);
+  if (!NEOX && FULL) {  // pairing and rope_dim play no part without a rotation
+    if (mode == kNormOnly)
+      return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kNormOnly, true>);
+    if (mode == kLayerOnly)
+      return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kLayerOnly, true>);
+  }
   return nullptr;
 }
 
@@ -468,29 +507,40 @@ const void* pick_lanes(int E, bool neox, bool full, int U, int mode) {
   return nullptr;
 }
 
-// Run-time head_dim instances: 16-byte lanes, lane group of DMAX/8 lanes,
-// fused op at unroll 2.
-template <class IO, int DMAX>
-const void* pick_any_dim(bool neox, bool full) {
+// Run-time head_dim instances: 16-byte lanes, lane group of DMAX/8 lanes, the
+// fused op and the LayerNorm sibling at unroll 2.
+template <class IO, int DMAX, int MODE>
+const void* pick_any_dim_mode(bool neox, bool full) {
   if (neox) {
-    return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, true, 2, kFused, false>)
-                : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, false, 2, kFused, false>);
+    return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, true, 2, MODE, false>)
+                : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, false, 2, MODE, false>);
   }
-  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, kFused, false>)
-              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, false, 2, kFused, false>);
+  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, MODE, false>)
+              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, false, 2, MODE, false>);
+}
+
+template <class IO, int DMAX>
+const void* pick_any_dim(bool neox, bool full, int mode) {
+  switch (mode) {
+    case kFused: return pick_any_dim_mode<IO, DMAX, kFused>(neox, full);
+    case kLayerRope: return pick_any_dim_mode<IO, DMAX, kLayerRope>(neox, full);
+    case kLayerOnly:
+      return reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, kLayerOnly, false>);
+    default: return nullptr;
+  }
 }
 
 template <class IO>
 const void* pick_dim(int D, int E, bool neox, bool full, int U, int mode, bool exact) {
   if (!exact) {
-    if (mode != kFused || U != 2 || E != 8) return nullptr;
+    if (U != 2 || E != 8) return nullptr;
     switch (D) {  // D is the lane-group capacity DMAX here
-      case 16: return pick_any_dim<IO, 16>(neox, full);
-      case 32: return pick_any_dim<IO, 32>(neox, full);
-      case 64: return pick_any_dim<IO, 64>(neox, full);
-      case 128: return pick_any_dim<IO, 128>(neox, full);
-      case 256: return pick_any_dim<IO, 256>(neox, full);
-      case 512: return pick_any_dim<IO, 512>(neox, full);
+      case 16: return pick_any_dim<IO, 16>(neox, full, mode);
+      case 32: return pick_any_dim<IO, 32>(neox, full, mode);
+      case 64: return pick_any_dim<IO, 64>(neox, full, mode);
+      case 128: return pick_any_dim<IO, 128>(neox, full, mode);
+      case 256: return pick_any_dim<IO, 256>(neox, full, mode);
+      case 512: return pick_any_dim<IO, 512>(neox, full, mode);
       default: return nullptr;
     }
   }
@@ -690,6 +740,8 @@ struct Call {
   const void* wk;
   const float* cache;
   const void* pos;
+  const void* bq;  // LayerNorm biases (NULL: none)
+  const void* bk;
   int64_t T;
   int32_t Hq, Hkv, D, R, neox;
   float eps;
@@ -724,10 +776,14 @@ int32_t prepare(int mode, const Call& c, const qknr_launch_cfg* cfg, Plan* pl,
   }
   if (c.T == 0 || c.Hq + c.Hkv == 0) return QKNR_OK;
 
-  const bool need_w = mode != kRopeOnly, need_rot = mode != kNormOnly;
-  if ((c.Hq > 0 && (!c.q || (need_w && !c.wq))) || (c.Hkv > 0 && (!c.k || (need_w && !c.wk))) ||
+  const bool need_w = mode != kRopeOnly;
+  const bool need_rot = mode == kFused || mode == kRopeOnly || mode == kLayerRope;
+  const bool bias = (mode == kLayerRope || mode == kLayerOnly) && (c.bq || c.bk);
+  if ((c.Hq > 0 && (!c.q || (need_w && !c.wq) || (bias && !c.bq))) ||
+      (c.Hkv > 0 && (!c.k || (need_w && !c.wk) || (bias && !c.bk))) ||
       (need_rot && (!c.cache || !c.pos)))
     return QKNR_E_NULL;
+  if (bias && ((c.bq && !aligned(c.bq, 16)) || (c.bk && !aligned(c.bk, 16)))) return QKNR_E_ALIGN;
   const int64_t vec = 2 * static_cast<int64_t>(c.D);
   if (c.Hq > 0 && !views_ok(c.T, c.Hq, c.qt, c.qh, vec)) return QKNR_E_SHAPE;
   if (c.Hkv > 0 && !views_ok(c.T, c.Hkv, c.kt, c.kh, vec)) return QKNR_E_SHAPE;
@@ -763,6 +819,9 @@ int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
   const void* wkarg = c.wk ? c.wk : c.wq;
   const float* carg = c.cache;
   const void* parg = c.pos;
+  const void* bqarg = c.bq ? c.bq : c.bk;  // the side with 0 heads still gets a readable row
+  const void* bkarg = c.bk ? c.bk : c.bq;
+  prm.has_bias = (c.bq || c.bk) ? 1 : 0;
   prm.cs_vec = (reinterpret_cast<uintptr_t>(c.cache) % 16 == 0) && ((c.R / 2) % 4 == 0);
   // head strides only matter for views with more than one head
   const int64_t qh = c.Hq > 1 ? c.qh : 0, kh = c.Hkv > 1 ? c.kh : 0;
@@ -784,7 +843,7 @@ int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
   prm.gpi = pl.gpi;
   prm.nc = pl.nc;
   prm.n_items = static_cast<int32_t>(pl.items);
-  void* args[] = {&qarg, &karg, &wqarg, &wkarg, &carg, &parg, &prm};
+  void* args[] = {&qarg, &karg, &wqarg, &wkarg, &carg, &parg, &bqarg, &bkarg, &prm};
   if (hipLaunchKernel(pl.fn, dim3(grid), dim3(threads), args, 0, c.stream) != hipSuccess)
     return QKNR_E_LAUNCH;
   return QKNR_OK;
@@ -833,9 +892,9 @@ QKNR_API int32_t qknr_inplace_ex(void* q, void* k, const void* wq, const void* w
                                  int64_t k_head_stride_B, int32_t dtype, int32_t pos_dtype,
                                  hipStream_t stream, const qknr_launch_cfg* cfg,
                                  qknr_launch_info* info) {
-  const Call c{q, k, wq, wk, cos_sin_cache, positions, T, Hq, Hkv, head_dim, rope_dim, is_neox,
-               eps, q_tok_stride_B, q_head_stride_B, k_tok_stride_B, k_head_stride_B, dtype,
-               pos_dtype, stream};
+  const Call c{q, k, wq, wk, cos_sin_cache, positions, nullptr, nullptr, T, Hq, Hkv, head_dim,
+               rope_dim, is_neox, eps, q_tok_stride_B, q_head_stride_B, k_tok_stride_B,
+               k_head_stride_B, dtype, pos_dtype, stream};
   Plan pl;
   const int32_t rc = prepare(kFused, c, cfg, &pl, info);
   return rc != QKNR_OK ? rc : launch(c, pl, info);
@@ -858,9 +917,9 @@ QKNR_API int32_t qknr_rmsnorm_inplace(void* q, void* k, const void* wq, const vo
                                       int64_t q_tok_stride_B, int64_t q_head_stride_B,
                                       int64_t k_tok_stride_B, int64_t k_head_stride_B,
                                       int32_t dtype, hipStream_t stream) {
-  const Call c{q, k, wq, wk, nullptr, nullptr, T, Hq, Hkv, head_dim, head_dim, 0, eps,
-               q_tok_stride_B, q_head_stride_B, k_tok_stride_B, k_head_stride_B, dtype, QKNR_I32,
-               stream};
+  const Call c{q, k, wq, wk, nullptr, nullptr, nullptr, nullptr, T, Hq, Hkv, head_dim, head_dim,
+               0, eps, q_tok_stride_B, q_head_stride_B, k_tok_stride_B, k_head_stride_B, dtype,
+               QKNR_I32, stream};
   Plan pl;
   const int32_t rc = prepare(kNormOnly, c, nullptr, &pl, nullptr);
   return rc != QKNR_OK ? rc : launch(c, pl, nullptr);
@@ -872,9 +931,9 @@ QKNR_API int32_t qknr_rope_inplace(void* q, void* k, const float* cos_sin_cache,
                                    int64_t q_tok_stride_B, int64_t q_head_stride_B,
                                    int64_t k_tok_stride_B, int64_t k_head_stride_B, int32_t dtype,
                                    int32_t pos_dtype, hipStream_t stream) {
-  const Call c{q, k, nullptr, nullptr, cos_sin_cache, positions, T, Hq, Hkv, head_dim, rope_dim,
-               is_neox, 0.0f, q_tok_stride_B, q_head_stride_B, k_tok_stride_B, k_head_stride_B,
-               dtype, pos_dtype, stream};
+  const Call c{q, k, nullptr, nullptr, cos_sin_cache, positions, nullptr, nullptr, T, Hq, Hkv,
+               head_dim, rope_dim, is_neox, 0.0f, q_tok_stride_B, q_head_stride_B, k_tok_stride_B,
+               k_head_stride_B, dtype, pos_dtype, stream};
   Plan pl;
   const int32_t rc = prepare(kRopeOnly, c, nullptr, &pl, nullptr);
   return rc != QKNR_OK ? rc : launch(c, pl, nullptr);
@@ -888,9 +947,9 @@ QKNR_API int32_t qknr_unfused_inplace(void* q, void* k, const void* wq, const vo
                                       int64_t k_tok_stride_B, int64_t k_head_stride_B,
                                       int32_t dtype, int32_t pos_dtype, hipStream_t stream) {
   // validate everything for both steps before enqueueing either
-  const Call c{q, k, wq, wk, cos_sin_cache, positions, T, Hq, Hkv, head_dim, rope_dim, is_neox,
-               eps, q_tok_stride_B, q_head_stride_B, k_tok_stride_B, k_head_stride_B, dtype,
-               pos_dtype, stream};
+  const Call c{q, k, wq, wk, cos_sin_cache, positions, nullptr, nullptr, T, Hq, Hkv, head_dim,
+               rope_dim, is_neox, eps, q_tok_stride_B, q_head_stride_B, k_tok_stride_B,
+               k_head_stride_B, dtype, pos_dtype, stream};
   Plan fused, norm, rot;
   int32_t rc = prepare(kFused, c, nullptr, &fused, nullptr);
   if (rc != QKNR_OK) return rc;
@@ -903,6 +962,24 @@ QKNR_API int32_t qknr_unfused_inplace(void* q, void* k, const void* wq, const vo
   if (rc != QKNR_OK) return rc;
   rc = launch(cn, norm, nullptr);
   return rc != QKNR_OK ? rc : launch(c, rot, nullptr);
+}
+
+QKNR_API int32_t qknr_layernorm_rope_inplace(void* q, void* k, const void* wq, const void* wk,
+                                             const void* bq, const void* bk,
+                                             const float* cos_sin_cache, const void* positions,
+                                             int64_t T, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                                             int32_t rope_dim, int32_t is_neox, float eps,
+                                             int64_t q_tok_stride_B, int64_t q_head_stride_B,
+                                             int64_t k_tok_stride_B, int64_t k_head_stride_B,
+                                             int32_t dtype, int32_t pos_dtype, hipStream_t stream) {
+  const bool rotate = rope_dim != 0;
+  const Call c{q, k, wq, wk, rotate ? cos_sin_cache : nullptr, rotate ? positions : nullptr, bq, bk,
+               T, Hq, Hkv, head_dim, rotate ? rope_dim : head_dim, rotate ? is_neox : 0, eps,
+               q_tok_stride_B, q_head_stride_B, k_tok_stride_B, k_head_stride_B, dtype,
+               rotate ? pos_dtype : QKNR_I32, stream};
+  Plan pl;
+  const int32_t rc = prepare(rotate ? kLayerRope : kLayerOnly, c, nullptr, &pl, nullptr);
+  return rc != QKNR_OK ? rc : launch(c, pl, nullptr);
 }
 
 static int32_t stream_launch(const void* fn, void** args, int64_t n16, hipStream_t stream) {

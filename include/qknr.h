@@ -202,6 +202,28 @@ QKNR_API int32_t qknr_unfused_inplace(void* q, void* k, const void* wq, const vo
                                       int32_t dtype, int32_t pos_dtype, hipStream_t stream);
 
 /*
+ * qknr_layernorm_rope_inplace -- the per-head QK LayerNorm sibling (the SGLang
+ * "Kernel Design Agent (KDA)" kernel-directory article, FLUX.2 fused producers:
+ * a per-head LayerNorm of Q and K): every head vector x of q and k becomes
+ *   (x - mean(x)) * rsqrt(mean((x - mean(x))^2) + eps) * w + b
+ * (biased variance, fp32 arithmetic, one rounding to the I/O type), followed,
+ * when rope_dim > 0, by the same rotation as qknr_inplace. rope_dim == 0 means
+ * the norm alone (cos_sin_cache, positions, is_neox and pos_dtype are then
+ * ignored and may be NULL/0). bq, bk: the [head_dim] bias rows of Q and K in
+ * the I/O dtype, 16-byte aligned, or both NULL for no bias. Same layout rules,
+ * supported shapes, status codes and ownership as qknr_inplace.
+ */
+QKNR_API int32_t qknr_layernorm_rope_inplace(void* q, void* k, const void* wq, const void* wk,
+                                             const void* bq, const void* bk,
+                                             const float* cos_sin_cache, const void* positions,
+                                             int64_t T, int32_t Hq, int32_t Hkv,
+                                             int32_t head_dim, int32_t rope_dim, int32_t is_neox,
+                                             float eps,
+                                             int64_t q_tok_stride_B, int64_t q_head_stride_B,
+                                             int64_t k_tok_stride_B, int64_t k_head_stride_B,
+                                             int32_t dtype, int32_t pos_dtype, hipStream_t stream);
+
+/*
  * qknr_can_use -- 1 if qknr_inplace supports this combination, else 0: the
  * "Supported shapes" set above (a superset of the page's capability predicate,
  * section 5.2), with known dtype and pos_dtype codes. Pure host function, no

@@ -39,6 +39,7 @@ __all__ = [
     "decode_bf16", "decode_fp16", "decode_io", "round_to_bf16_bits", "round_to_fp16_bits",
     "round_to_io_bits", "rms_norm", "rope", "cache_cos_sin", "qknorm_rope",
     "qknorm_rope_io", "rms_norm_io", "rope_io", "qknorm_rope_unfused_io",
+    "layer_norm", "qk_layernorm_rope", "qk_layernorm_rope_io",
     "within_tolerance", "tolerance",
 ]
 
@@ -221,6 +222,54 @@ def qknorm_rope_unfused_io(q_bits, k_bits, wq_bits, wk_bits, cache, positions, *
     nk = rms_norm_io(k_bits, wk_bits, eps=eps, dtype=dtype)
     return (rope_io(nq, cache, positions, is_neox=is_neox, dtype=dtype, rope_dim=rope_dim),
             rope_io(nk, cache, positions, is_neox=is_neox, dtype=dtype, rope_dim=rope_dim))
+
+
+# ----------------------------------------------------------------------------
+# Sibling: per-head QK LayerNorm (the SGLang "Kernel Design Agent (KDA)"
+# kernel-directory article, FLUX.2 fused producers: a per-head LayerNorm of Q
+# and K that reproduces torch's layer_norm). Read here as
+# (x - mean) / sqrt(var + eps) * w + b over head_dim, biased variance, bias
+# optional, optionally followed by the same rotation as the fused op.
+# ----------------------------------------------------------------------------
+
+def layer_norm(x: np.ndarray, w: np.ndarray, b, eps: float) -> np.ndarray:
+    """Per head vector (last axis): (x - mean) / sqrt(mean((x - mean)^2) + eps) * w + b."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    if eps < 0:
+        raise ValueError("eps must be >= 0")
+    head_dim = x.shape[-1]
+    mean = np.sum(x, axis=-1, keepdims=True) / head_dim
+    c = x - mean
+    var = np.sum(c * c, axis=-1, keepdims=True) / head_dim
+    out = c / np.sqrt(var + eps) * w
+    if b is not None:
+        out = out + np.asarray(b, dtype=np.float64)
+    return out
+
+
+def qk_layernorm_rope(q, k, wq, wk, bq, bk, cache, positions, *, is_neox, eps, rope_dim):
+    """Per-head LayerNorm of q [T,Hq,D] and k [T,Hkv,D], then (rope_dim > 0)
+    the rotation of the first rope_dim dims by row positions[t]."""
+    eps64 = float(np.float32(eps))
+    nq = layer_norm(q, wq, bq, eps64)
+    nk = layer_norm(k, wk, bk, eps64)
+    if not rope_dim:
+        return nq, nk
+    cos, sin = cache_cos_sin(cache, positions, rope_dim)
+    cos, sin = cos[:, None, :], sin[:, None, :]
+    return rope(nq, cos, sin, rope_dim, is_neox), rope(nk, cos, sin, rope_dim, is_neox)
+
+
+def qk_layernorm_rope_io(q_bits, k_bits, wq_bits, wk_bits, bq_bits, bk_bits, cache, positions,
+                         *, is_neox, eps, dtype, rope_dim):
+    """The LayerNorm sibling on I/O bit patterns (bias bits may be None): decode,
+    fp64, one rounding. Returns (q_bits, k_bits)."""
+    dec = lambda b: None if b is None else decode_io(b, dtype)
+    oq, ok = qk_layernorm_rope(decode_io(q_bits, dtype), decode_io(k_bits, dtype),
+                               dec(wq_bits), dec(wk_bits), dec(bq_bits), dec(bk_bits), cache,
+                               positions, is_neox=is_neox, eps=eps, rope_dim=rope_dim)
+    return round_to_io_bits(oq, dtype), round_to_io_bits(ok, dtype)
 
 
 # ----------------------------------------------------------------------------

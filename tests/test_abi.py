@@ -27,7 +27,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     names = _declared()
     assert {"qknr_inplace", "qknr_inplace_ex", "qknr_can_use", "qknr_status_string",
             "qknr_copy", "qknr_rmw", "qknr_unfused_inplace", "qknr_rmsnorm_inplace",
-            "qknr_rope_inplace"} <= set(names)
+            "qknr_rope_inplace", "qknr_layernorm_rope_inplace"} <= set(names)
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -328,3 +328,28 @@ def test_unfused_entry_points_validate_before_launching():
     zero = list(args)
     zero[6] = 0
     assert L.qknr_unfused_inplace(*zero) == B.QKNR_OK
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: run on a host without a GPU")
+def test_layernorm_entry_point_validates_before_launching():
+    L = B.lib()
+    z = P(0)
+    a = P(A)
+
+    def call(**kw):
+        d = dict(q=a, k=a, wq=a, wk=a, bq=a, bk=a, cache=a, pos=a, T=5, Hq=4, Hkv=4, D=128, R=64,
+                 neox=1, eps=1e-6, qt=1024, qh=256, kt=1024, kh=256, dtype=0, pdt=0)
+        d.update(kw)
+        return L.qknr_layernorm_rope_inplace(*[d[n] for n in ("q", "k", "wq", "wk", "bq", "bk", "cache", "pos", "T", "Hq", "Hkv", "D", "R", "neox", "eps", "qt", "qh", "kt", "kh", "dtype", "pdt")], z)
+
+    assert call() == B.QKNR_E_DEVICE                       # valid: reaches the runtime
+    assert call(bq=z, bk=z) == B.QKNR_E_DEVICE             # no bias is fine
+    assert call(bk=z) == B.QKNR_E_NULL                     # one bias without the other
+    assert call(bq=P(A + 8)) == B.QKNR_E_ALIGN
+    assert call(wq=z) == B.QKNR_E_NULL
+    assert call(cache=z) == B.QKNR_E_NULL                  # rotation asked, no table
+    assert call(R=0, cache=z, pos=z, neox=0) == B.QKNR_E_DEVICE  # norm alone needs no table
+    assert call(R=98) == B.QKNR_E_UNSUPPORTED
+    assert call(D=100, qt=800, qh=200, kt=800, kh=200, R=0) == B.QKNR_E_UNSUPPORTED
+    assert call(eps=-1.0) == B.QKNR_E_ARG
+    assert call(T=0, q=z, k=z, wq=z, wk=z, bq=z, bk=z, cache=z, pos=z) == B.QKNR_OK

@@ -374,3 +374,74 @@ def test_fused_and_unfused_agree_within_page_tolerance():
         xf, yf = x.float(), y.float()
         assert torch.all((xf - yf).abs() <= 8e-2 + 1e-2 * xf.abs())
         assert not torch.equal(xf, yf)
+
+
+# ---------------------------------------------------------------------------
+# Sibling: per-head QK LayerNorm (+ optional rotation)
+# ---------------------------------------------------------------------------
+
+def _layernorm_check(wl, rope_dim, bias, layout=None, bias_seed=0):
+    from head_qk_rmsnorm_amd import binding as B
+    from oracle import qknr_oracle as O
+
+    c = wl.cfg
+    dc = Hn.DeviceCase(wl, layout=layout)
+    bq_bits = bk_bits = None
+    bq = bk = None
+    if bias:
+        g = W.rng(c.seed + bias_seed, 77)
+        bq_bits = W.to_io_bits(g.standard_normal(c.head_dim) * 0.5, c.dtype)
+        bk_bits = W.to_io_bits(g.standard_normal(c.head_dim) * 0.5, c.dtype)
+        bq = torch_from_bits(bq_bits, dc)
+        bk = torch_from_bits(bk_bits, dc)
+    B.qknr_layernorm_rope_inplace(dc.q, dc.k, dc.wq, dc.wk, bq, bk,
+                                  dc.cache if rope_dim else None,
+                                  dc.positions if rope_dim else None,
+                                  is_neox=c.is_neox, eps=c.eps, rope_dim=rope_dim)
+    rq, rk = O.qk_layernorm_rope_io(wl.q, wl.k, wl.wq, wl.wk, bq_bits, bk_bits,
+                                    wl.cache[:, :rope_dim] if rope_dim else None, wl.positions,
+                                    is_neox=c.is_neox, eps=c.eps, dtype=c.dtype,
+                                    rope_dim=rope_dim)
+    after = dc.fetch()
+    dc.check_untouched(after)
+    dc.check_inputs_unchanged()
+    gq, gk = dc.outputs(after)
+    for name, g, r in (("q", gq, rq), ("k", gk, rk)):
+        cmp = Hn.compare_bits(g, r, c.dtype)
+        assert cmp.bad == 0, f"layernorm {c.name} {name}: {cmp}"
+        assert cmp.exact_frac >= 0.99, f"layernorm {c.name} {name}: {cmp}"
+
+
+def torch_from_bits(bits, dc):
+    import torch
+
+    return torch.from_numpy(bits.view(np.int16)).to(dc.device).view(dc.tdt)
+
+
+LN_GRID = [(D, R, neox, dt, bias)
+           for D in (64, 128, 256, 96, 192)
+           for R, neox in ((0, False), (D, False), (D, True), (D // 2, True), (D // 2, False))
+           for dt in (W.BF16, W.FP16) for bias in (False, True)]
+
+
+@pytest.mark.parametrize("D,R,neox,dt,bias", LN_GRID)
+def test_layernorm_sibling(D, R, neox, dt, bias):
+    cfg = W.case(65, 5, 3, D, D if R == 0 else R, neox, dtype=dt, pos_dtype=W.I64, seed=D + R,
+                 x_std=2.0)
+    wl = W.make_workload(cfg)
+    # a non-zero mean per head exercises the centring
+    from oracle import qknr_oracle as O
+    wl.q[...] = O.round_to_io_bits(O.decode_io(wl.q, dt) + 1.5, dt)
+    _say("case layernorm", cfg.name, R, bias)
+    _layernorm_check(wl, R, bias)
+
+
+@pytest.mark.parametrize("layout", ["padded", "qkv"])
+def test_layernorm_sibling_layouts(layout):
+    cfg = W.case(33, 6, 2, 128, 64, True, seed=5)
+    _layernorm_check(W.make_workload(cfg), 64, True, layout=layout)
+
+
+def test_layernorm_sibling_on_dit_workload():
+    """The DiT workload with LayerNorm instead of RMSNorm (all tokens)."""
+    _layernorm_check(W.make_workload(W.CONFIGS["dit"]), 128, True)

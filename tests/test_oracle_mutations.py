@@ -43,6 +43,10 @@ MUTATIONS = {
     "unfused_k_uses_q_weight": ("nk = rms_norm_io(k_bits, wk_bits", "nk = rms_norm_io(k_bits, wq_bits", True),
     "rope_step_pairing_inverted": ("cos[:, None, :], sin[:, None, :], R, is_neox)\n    return round_to_io_bits(out, dtype)",
                                    "cos[:, None, :], sin[:, None, :], R, not is_neox)\n    return round_to_io_bits(out, dtype)", True),
+    "layer_norm_unbiased_variance": ("var = np.sum(c * c, axis=-1, keepdims=True) / head_dim",
+                                     "var = np.sum(c * c, axis=-1, keepdims=True) / (head_dim - 1)", True),
+    "layer_norm_bias_dropped": ("        out = out + np.asarray(b, dtype=np.float64)", "        out = out", True),
+    "layer_norm_not_centered": ("    c = x - mean\n", "    c = x - 0 * mean\n", True),
     "equivalent_rewrite": ("np.sum(x * x, axis=-1", "np.sum(np.abs(x) * np.abs(x), axis=-1", False),
 }
 

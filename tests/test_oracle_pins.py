@@ -583,3 +583,70 @@ def test_unfused_chain_agrees_with_fused_within_page_tolerance(neox):
         assert np.all(np.abs(uv - f) <= bound)
     # pass-through dims see only the norm step: there the two agree exactly
     assert np.array_equal(uq[..., R:], fq[..., R:])
+
+
+# ---------------------------------------------------------------------------
+# Sibling: per-head QK LayerNorm (+ optional rotation)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 1e-2])
+@pytest.mark.parametrize("bias", [False, True])
+def test_layer_norm_matches_torch_layer_norm(eps, bias):
+    """Library routine: torch's layer_norm in float64 (biased variance, weight, bias)."""
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(13)
+    for D in (8, 64, 96, 128, 256):
+        x = g.standard_normal((5, 3, D)) * 3.0 + 1.5
+        w = g.uniform(0.5, 1.5, D)
+        b = g.standard_normal(D) if bias else None
+        want = torch.nn.functional.layer_norm(torch.from_numpy(x), (D,), torch.from_numpy(w),
+                                              None if b is None else torch.from_numpy(b),
+                                              eps=eps).numpy()
+        np.testing.assert_allclose(O.layer_norm(x, w, b, eps), want, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_norm_closed_forms():
+    """A constant head normalises to the bias; x = m + s*(+1,-1,...) normalises to
+    (+-1) * s/sqrt(s^2+eps) * w + b; a shift of x changes nothing."""
+    D = 16
+    w = np.linspace(0.5, 1.5, D)
+    b = np.linspace(-1.0, 1.0, D)
+    np.testing.assert_array_equal(O.layer_norm(np.full((1, D), 7.0), w, b, 1e-6)[0], b)
+    s, eps = 3.0, 0.5
+    sign = np.tile([1.0, -1.0], D // 2)
+    x = 10.0 + s * sign
+    np.testing.assert_allclose(O.layer_norm(x[None], w, b, eps)[0], sign * s / np.sqrt(s * s + eps) * w + b,
+                               rtol=1e-14)
+    g = np.random.default_rng(2)
+    y = g.standard_normal((4, D))
+    np.testing.assert_allclose(O.layer_norm(y + 123.0, w, None, 1e-6), O.layer_norm(y, w, None, 1e-6),
+                               rtol=1e-9, atol=1e-9)
+
+
+@pytest.mark.parametrize("neox", [False, True])
+def test_qk_layernorm_rope_composes_norm_and_rotation(neox):
+    """rope_dim 0 is the norm alone; position 0 of the formula cache is the
+    norm alone too; otherwise it is the rotation of the normalised heads
+    (numpy complex product with angles from the definition)."""
+    D, R = 64, 32
+    g = np.random.default_rng(9)
+    q, k = g.standard_normal((6, 3, D)), g.standard_normal((6, 2, D))
+    wq, wk = g.uniform(0.5, 1.5, D), g.uniform(0.5, 1.5, D)
+    bq, bk = g.standard_normal(D), None
+    cache = _cache_formula(50, R)
+    e = float(np.float32(1e-6))
+    nq, nk = O.qk_layernorm_rope(q, k, wq, wk, bq, bk, cache, np.zeros(6, np.int64), is_neox=neox,
+                                 eps=1e-6, rope_dim=0)
+    np.testing.assert_array_equal(nq, O.layer_norm(q, wq, bq, e))
+    np.testing.assert_array_equal(nk, O.layer_norm(k, wk, None, e))
+    z, _ = O.qk_layernorm_rope(q, k, wq, wk, bq, bk, cache, np.zeros(6, np.int64), is_neox=neox,
+                               eps=1e-6, rope_dim=R)
+    np.testing.assert_array_equal(z, nq)
+    pos = g.integers(0, 50, 6)
+    oq, _ = O.qk_layernorm_rope(q, k, wq, wk, bq, bk, cache, pos, is_neox=neox, eps=1e-6, rope_dim=R)
+    phi = pos[:, None, None] * 1e4 ** (-2.0 * np.arange(R // 2) / R)
+    ia, ib = (np.arange(R // 2), np.arange(R // 2) + R // 2) if neox else (np.arange(0, R, 2), np.arange(1, R, 2))
+    zc = (nq[..., ia] + 1j * nq[..., ib]) * np.exp(1j * phi)
+    np.testing.assert_allclose(oq[..., ia], zc.real, atol=2e-6 * np.abs(nq).max())
+    np.testing.assert_allclose(oq[..., ib], zc.imag, atol=2e-6 * np.abs(nq).max())
+    np.testing.assert_array_equal(oq[..., R:], nq[..., R:])
