@@ -1,0 +1,150 @@
+"""Integration of the C ABI beyond the Python binding: a plain C caller, HIP
+graph capture and concurrent callers from several host threads."""
+import os
+import subprocess
+import tempfile
+import threading
+
+import numpy as np
+import pytest
+
+from head_qk_rmsnorm_amd import workloads as W
+from tests import qknr_harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CAPI_BIN = os.path.join(HERE, "capi", "qknr_capi_run")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    from head_qk_rmsnorm_amd import binding as B
+
+    B.lib()
+    yield
+
+
+def _write_case(path, wl):
+    c = wl.cfg
+    hdr = np.array([c.T, c.Hq, c.Hkv, c.head_dim, c.rope_dim, int(c.is_neox),
+                    0 if c.dtype == W.BF16 else 1, 0 if c.pos_dtype == W.I32 else 1,
+                    c.cache_rows], dtype=np.int64)
+    with open(path, "wb") as f:
+        f.write(hdr.tobytes())
+        f.write(np.float32(c.eps).tobytes())
+        for a in (wl.q, wl.k, wl.wq, wl.wk, wl.cache, wl.positions):
+            f.write(np.ascontiguousarray(a).tobytes())
+
+
+@pytest.mark.parametrize("cfg", [
+    W.CONFIGS["tiny"],
+    W.case(37, 6, 2, 128, 128, False, dtype=W.FP16, pos_dtype=W.I64, seed=3),
+    W.case(19, 3, 5, 256, 128, True, seed=4),
+    W.case(23, 4, 4, 96, 96, True, seed=5),
+], ids=lambda c: c.name)
+def test_plain_c_caller(cfg):
+    """libqknr.so driven from C through include/qknr.h only; output checked
+    against the fp64 oracle."""
+    if not os.path.exists(CAPI_BIN):
+        pytest.fail(f"{CAPI_BIN} missing: run __graft_entry__.build()")
+    wl = W.make_workload(cfg)
+    with tempfile.TemporaryDirectory() as d:
+        case, out = os.path.join(d, "case.bin"), os.path.join(d, "out.bin")
+        _write_case(case, wl)
+        r = subprocess.run([CAPI_BIN, case, out], capture_output=True, text=True, timeout=120)
+        print(r.stdout, r.stderr, flush=True)
+        assert r.returncode == 0, r.stderr
+        got = np.fromfile(out, dtype=np.uint16)
+    nq = wl.q.size
+    gq = got[:nq].reshape(wl.q.shape)
+    gk = got[nq:].reshape(wl.k.shape)
+    rq, rk = Hn.oracle_ref(wl)
+    for g, ref in ((gq, rq), (gk, rk)):
+        cmp = Hn.compare_bits(g, ref, cfg.dtype)
+        assert cmp.bad == 0 and cmp.exact_frac >= 0.99, cmp
+
+
+def test_hip_graph_capture_and_replay():
+    """The op allocates nothing and never synchronises, so it can be captured
+    in a HIP graph. Each replay applies it again in place: after n replays
+    the tensors equal n eager applications, bit for bit, on every replay."""
+    import torch
+    from head_qk_rmsnorm_amd import binding as B
+
+    cfg = W.case(129, 8, 4, 128, 64, True, seed=12)
+    wl = W.make_workload(cfg)
+    g_case = Hn.DeviceCase(wl)
+    e_case = Hn.DeviceCase(wl)
+    kw = dict(is_neox=cfg.is_neox, eps=cfg.eps)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        # warm-up on the side stream: one application
+        B.qknr_inplace(g_case.q, g_case.k, g_case.wq, g_case.wk, g_case.cache, g_case.positions,
+                       stream=s, **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s):
+        B.qknr_inplace(g_case.q, g_case.k, g_case.wq, g_case.wk, g_case.cache, g_case.positions,
+                       stream=s, **kw)
+    B.qknr_inplace(e_case.q, e_case.k, e_case.wq, e_case.wk, e_case.cache, e_case.positions, **kw)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        B.qknr_inplace(e_case.q, e_case.k, e_case.wq, e_case.wk, e_case.cache, e_case.positions,
+                       **kw)
+        torch.cuda.synchronize()
+        for a, b in zip(g_case.fetch(), e_case.fetch()):
+            assert np.array_equal(a, b), f"replay {rep}"
+
+
+def test_concurrent_callers():
+    """Several host threads, each with its own stream and buffers, call the
+    library at once; every result matches three applications of the oracle."""
+    import torch
+    from head_qk_rmsnorm_amd import binding as B
+    from oracle import qknr_oracle as O
+
+    cases = [W.case(65, 4 + i, 2 + i % 3, (64, 128, 256, 96)[i % 4], (64, 128, 128, 96)[i % 4],
+                    bool(i % 2), seed=30 + i) for i in range(6)]
+    wls = [W.make_workload(c) for c in cases]
+    dcs = [Hn.DeviceCase(wl) for wl in wls]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            dc = dcs[i]
+            for _ in range(3):  # three applications in a row on this stream
+                B.qknr_inplace(dc.q, dc.k, dc.wq, dc.wk, dc.cache, dc.positions,
+                               is_neox=cases[i].is_neox, eps=cases[i].eps, stream=s)
+            s.synchronize()
+        except Exception as e:  # collected and reported below
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for wl, dc in zip(wls, dcs):
+        c = wl.cfg
+        q, k = wl.q, wl.k
+        for _ in range(3):
+            q, k, _, _ = O.qknorm_rope_io(q, k, wl.wq, wl.wk, wl.cache, wl.positions,
+                                          is_neox=c.is_neox, eps=c.eps, dtype=c.dtype,
+                                          rope_dim=c.rope_dim)
+        gq, gk = dc.outputs(dc.fetch())
+        for g, r in ((gq, q), (gk, k)):
+            # each application may land one ulp away from the correctly rounded
+            # value and the next one starts from there: check the tolerance only
+            cmp = Hn.compare_bits(g, r, c.dtype)
+            assert cmp.bad == 0, (c.name, cmp)
