@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 ROT_BYTES = 1 << 30    # rotate through >= 1 GiB of copies
 MAX_ROT = 64           # (tiny workloads: at most 64 copies; they are latency-bound anyway)
-KERNEL_SRC = os.path.join(ROOT, "head_qk_rmsnorm_amd", "csrc", "qknr.hip")
+KERNEL_SRC = os.path.join(ROOT, "head_qk_rmsnorm_amd", "csrc", "qknr_device.h")
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 

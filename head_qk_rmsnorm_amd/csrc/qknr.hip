@@ -1,44 +1,13 @@
-// Fused in-place QK RMSNorm + rotary position embedding for MI355X (gfx950).
-//
-// The operation follows the page "SGLang Diffusion fused operator
-// fused_inplace_qknorm_rope: in-depth technical analysis" (m.lsln.cn/news/241376):
-// section 2.1 (per-head RMSNorm with a learned weight), section 2.2 (cos|sin
-// cache rows, interleaved and NeoX pairing, partial rotary), section 2.3 (the
-// fused per-head flow: load, widen to fp32, sum of squares, rsqrt, scale,
-// rotate, narrow, store in place) and section 3 (tensor contract). The C ABI is
-// declared in include/qknr.h.
-//
-// Design for the 64-lane CDNA4 wavefront (the page's kernel is a 32-lane
-// warp-per-head CUDA design; only its arithmetic is kept):
-//   * L = head_dim / E lanes share one head vector, each lane owning E
-//     contiguous elements. E = 8 gives 16-byte accesses per lane (L = 8, 16, 32
-//     for head_dim 64, 128, 256: 8, 4 or 2 heads per wave instruction). Half a
-//     wave (L = 32) and a full wave (L = 64) per head are the other mappings;
-//     half a wave also covers the NeoX rotary widths whose rotary lanes would
-//     not be a power of two with E = 8.
-//   * A wave's work item is a run of head groups of ONE token, so the position
-//     is wave-uniform and read with a scalar load (prefetched one item ahead);
-//     each lane loads the cos/sin values of its own dims once per item and keeps
-//     them in registers for every head of the item.
-//   * The fp32 sum of squares is reduced over the L lanes of a head with DPP
-//     row operations (quad_perm, row_half_mirror, row_mirror), one ds_swizzle
-//     across 16-lane rows for L >= 32 and two readlanes across the wave halves
-//     for L = 64; every lane of a head ends with the bit-identical sum.
-//   * NeoX partners sit in lane (lane ^ m), m = (rope_dim/2)/E, within the same
-//     head; they are fetched with ds_bpermute.
-//   * Heads of one token that belong to Q and to K may share a wave
-//     instruction: each lane group selects its base pointer, strides and weight
-//     row. Only Q/K elements are loaded or stored.
-//   * The loads of `unroll` head groups are issued before the first is computed
-//     and before the position-dependent cos/sin fetch, so the data is in flight
-//     while the position -> cache-row chain resolves. Q/K traffic is streamed
-//     with nontemporal loads and stores (each byte is touched once).
-//   * By default every wave takes one work item and exits (no persistent grid):
-//     the dispatcher back-fills CUs as waves finish, which balances the tail.
-// Nothing here is a contraction, so there is no MFMA.
+// Host library of the fused in-place QK RMSNorm + rotary position embedding for
+// MI355X (gfx950): argument validation, launch planning, the C ABI declared in
+// include/qknr.h and include/qknr_bench.h, and the two measurement kernels.
+// The op's kernels live in qknr_device.h / qknr_inst.hip; the operation is the
+// one of the page "SGLang Diffusion fused operator fused_inplace_qknorm_rope:
+// in-depth technical analysis" (m.lsln.cn/news/241376), sections 2.1-2.3 and 3.
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -48,399 +17,11 @@
 
 #include "qknr.h"
 #include "qknr_bench.h"
+#include "qknr_device.h"
 
 namespace {
 
-constexpr int kWave = 64;
-constexpr int kMaxBlockWaves = 8;
-
-// ==== fused-kernel device code begin (the measured kernel; its hash keys the
-// ==== committed hardware-counter summaries)
-// ----------------------------------------------------------------------------
-// I/O element formats: two 16-bit values per dword, lower address in the low
-// half. Widening is exact; narrowing rounds to nearest even (gfx950
-// v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
-// ----------------------------------------------------------------------------
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-struct Bf16 {
-  static __device__ __forceinline__ void unpack(uint32_t u, float& lo, float& hi) {
-    lo = __uint_as_float(u << 16);
-    hi = __uint_as_float(u & 0xffff0000u);
-  }
-  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
-    return __builtin_bit_cast(uint32_t, v);
-  }
-};
-
-struct Fp16 {
-  static __device__ __forceinline__ void unpack(uint32_t u, float& lo, float& hi) {
-    f16x2_t v = __builtin_bit_cast(f16x2_t, u);
-    lo = (float)v.x;
-    hi = (float)v.y;
-  }
-  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    f16x2_t v = {(_Float16)lo, (_Float16)hi};
-    return __builtin_bit_cast(uint32_t, v);
-  }
-};
-
-// NV packed dwords (2*NV elements) owned by one lane.
-template <int NV>
-struct Raw {
-  uint32_t w[NV];
-};
-
-template <int NV>
-__device__ __forceinline__ Raw<NV> load_raw(const char* p) {
-  Raw<NV> r;
-  if constexpr (NV == 4) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
-    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
-  } else if constexpr (NV == 2) {
-    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
-    r.w[0] = v.x; r.w[1] = v.y;
-  } else {
-    static_assert(NV == 1, "1, 2 or 4 dwords per lane");
-    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
-  }
-  return r;
-}
-
-template <int NV>
-__device__ __forceinline__ void store_raw(char* p, const Raw<NV>& r) {
-  if constexpr (NV == 4) {
-    *reinterpret_cast<u32x4_t*>(p) = u32x4_t{r.w[0], r.w[1], r.w[2], r.w[3]};
-  } else if constexpr (NV == 2) {
-    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{r.w[0], r.w[1]};
-  } else {
-    *reinterpret_cast<uint32_t*>(p) = r.w[0];
-  }
-}
-
-// ----------------------------------------------------------------------------
-// Cross-lane helpers
-// ----------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
-constexpr int kDppRowHalfMirror = 0x141;
-constexpr int kDppRowMirror = 0x140;
-constexpr int kSwizzleXor16 = 0x401F;  // ds_swizzle bit mode: and 0x1f, xor 0x10
-
-// Sum over aligned groups of L lanes; every lane of a group gets the same bits.
-// After the two quad steps a quad is uniform, so a mirror inside 8 (16) lanes
-// adds exactly the other quad (half row).
-template <int L>
-__device__ __forceinline__ float group_sum(float v) {
-  static_assert(L == 2 || L == 4 || L == 8 || L == 16 || L == 32 || L == 64, "lanes per head");
-  v += dpp_mov<kDppQuadXor1>(v);
-  if constexpr (L >= 4) v += dpp_mov<kDppQuadXor2>(v);
-  if constexpr (L >= 8) v += dpp_mov<kDppRowHalfMirror>(v);
-  if constexpr (L >= 16) v += dpp_mov<kDppRowMirror>(v);
-  if constexpr (L >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16));
-  if constexpr (L == 64) {
-    // both halves are uniform now; add them in the same order on every lane
-    v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
-        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  }
-  return v;
-}
-
-__device__ __forceinline__ float lane_fetch(int byte_addr, float v) {
-  return __int_as_float(__builtin_amdgcn_ds_bpermute(byte_addr, __float_as_int(v)));
-}
-
-// ----------------------------------------------------------------------------
-// Kernel
-// ----------------------------------------------------------------------------
-// Q/K are read and written exactly once: nontemporal accesses keep them from
-// displacing the reused weights, positions and cos|sin rows in L2.
-// Q/K accesses go through raw buffer instructions: a wave-uniform descriptor
-// (base address of the head group, in SGPRs) plus a 32-bit per-lane offset,
-// with the nontemporal cache policy. Offsets stay below 2^31 (checked on the
-// host), far inside the descriptor's range, so no access is out of range.
-constexpr int kBufferFlags = 0x00020000;  // gfx9 raw-buffer descriptor word 3
-constexpr int kCachePolicyNT = 2;          // nontemporal
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(char* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, kBufferFlags);
-}
-
-template <int NV>
-__device__ __forceinline__ Raw<NV> load_io(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
-  Raw<NV> r;
-  if constexpr (NV == 4) {
-    const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCachePolicyNT));
-    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
-  } else if constexpr (NV == 2) {
-    const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kCachePolicyNT));
-    r.w[0] = v.x; r.w[1] = v.y;
-  } else {
-    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kCachePolicyNT);
-  }
-  return r;
-}
-
-template <int NV>
-__device__ __forceinline__ void store_io(__amdgpu_buffer_rsrc_t rs, uint32_t off, const Raw<NV>& r) {
-  if constexpr (NV == 4) {
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{r.w[0], r.w[1], r.w[2], r.w[3]}, rs, off, 0, kCachePolicyNT);
-  } else if constexpr (NV == 2) {
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{r.w[0], r.w[1]}, rs, off, 0, kCachePolicyNT);
-  } else {
-    __builtin_amdgcn_raw_buffer_store_b32(r.w[0], rs, off, 0, kCachePolicyNT);
-  }
-}
-
-typedef __attribute__((address_space(4))) const int32_t* cpos32_t;
-typedef __attribute__((address_space(4))) const int64_t* cpos64_t;
-
-__device__ __forceinline__ int64_t token_position(const void* pos, int pos64, int t) {
-  return pos64 ? ((cpos64_t)pos)[t] : static_cast<int64_t>(((cpos32_t)pos)[t]);
-}
-
-struct Params {
-  int64_t q_tok, k_tok;          // token strides (bytes)
-  int64_t q_grp, k_grp;          // bytes between consecutive head groups (G head strides)
-  uint32_t q_head, k_head;       // head strides (bytes); (G-1)*stride + 2*D fits 32 bits
-  int32_t Hq, Hkv, R;
-  int32_t D;                     // head_dim (instances with a run-time head_dim)
-  float inv_d;                   // 1 / head_dim
-  int32_t ngq;                   // Q head groups per token; K groups follow them
-  int32_t pos64;
-  int32_t cs_vec;                // cache rows 16-byte aligned and R/2 % 4 == 0
-  int32_t has_bias;              // LayerNorm sibling: bias rows given
-  float eps;
-  int32_t ng, gpi, nc, n_items;  // groups per token, groups per item, items per token, items
-};
-
-// What a launch computes: the fused op, one of the two steps of the unfused
-// chain it replaces (norm only: rotation skipped; rope only: the stored values
-// are rotated as they are, no norm), or the per-head LayerNorm sibling with or
-// without the rotation.
-enum : int { kFused = 0, kNormOnly = 1, kRopeOnly = 2, kLayerRope = 3, kLayerOnly = 4 };
-
-// One wave instruction covers one head group: G consecutive heads of Q, or of
-// K, of one token (groups never mix Q and K), so the group's base address is
-// wave-uniform and each lane adds a fixed 32-bit offset.
-//
-// DMAX is the head_dim the instance is built for. EXACT instances have
-// head_dim == DMAX; the others take any multiple of E up to DMAX at run time
-// (each head keeps a lane group of DMAX/E lanes, the spare ones masked).
-template <class IO, int DMAX, int E, bool NEOX, bool FULL, int U, int MODE, bool EXACT>
-__global__ void __launch_bounds__(kMaxBlockWaves * kWave)
-qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict__ wqp,
-            const void* __restrict__ wkp, const float* __restrict__ cache,
-            const void* __restrict__ posp, const void* __restrict__ bqp,
-            const void* __restrict__ bkp, const Params p) {
-  constexpr int L = DMAX / E;   // lanes per head (lane group)
-  constexpr int G = kWave / L;  // heads per wave instruction
-  constexpr int NV = E / 2;     // packed dwords per lane
-  constexpr int NCS = NEOX ? E : E / 2;  // cos (and sin) values per lane
-  static_assert(DMAX % E == 0 && E % 2 == 0 && G >= 1, "lane mapping");
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int wpb = blockDim.x / kWave;
-  const int sub = lane / L;  // head slot in the group
-  const int li = lane % L;   // lane inside the head
-  const int d0 = li * E;     // first dim owned by this lane
-  const int D = EXACT ? DMAX : p.D;
-  const bool in_head = EXACT || d0 < D;  // spare lanes of a run-time head_dim
-  const int R = FULL ? D : p.R;
-  const int half = R / 2;
-  const uint32_t q_off = static_cast<uint32_t>(sub) * p.q_head + d0 * 2;
-  const uint32_t k_off = static_cast<uint32_t>(sub) * p.k_head + d0 * 2;
-
-  constexpr bool kRotate = MODE == kFused || MODE == kRopeOnly || MODE == kLayerRope;
-  constexpr bool kRms = MODE == kFused || MODE == kNormOnly;
-  constexpr bool kLayer = MODE == kLayerRope || MODE == kLayerOnly;
-
-  // Weights (and LayerNorm biases) of this lane's dims, kept packed.
-  Raw<NV> wq_p{}, wk_p{}, bq_p{}, bk_p{};
-  if constexpr (kRms || kLayer) {
-    if (in_head) {
-      wq_p = load_raw<NV>(static_cast<const char*>(wqp) + d0 * 2);
-      wk_p = load_raw<NV>(static_cast<const char*>(wkp) + d0 * 2);
-    }
-  }
-  if constexpr (kLayer) {
-    if (in_head && p.has_bias) {
-      bq_p = load_raw<NV>(static_cast<const char*>(bqp) + d0 * 2);
-      bk_p = load_raw<NV>(static_cast<const char*>(bkp) + d0 * 2);
-    }
-  }
-
-  // NeoX: this lane holds dims d0..d0+E-1. With m = (R/2)/E, lanes below m
-  // hold first-half dims and find their partners d + R/2 at the same offsets
-  // in lane + m; lanes m..2m-1 hold the second half and look m lanes down.
-  // Lanes from 2m on hold pass-through dims. Lower-half lanes subtract.
-  int partner_addr = lane << 2, j0 = 0;
-  bool lower = false, lane_rot = true;
-  if constexpr (NEOX) {
-    const int m = half / E;
-    lane_rot = (FULL && EXACT) || li < 2 * m;
-    lower = li < m;
-    if (lane_rot) {
-      partner_addr = (lower ? lane + m : lane - m) << 2;
-      j0 = lower ? d0 : d0 - half;
-    }
-  } else {
-    j0 = in_head ? d0 / 2 : 0;
-  }
-
-  const int total_waves = gridDim.x * wpb;
-  int item = blockIdx.x * wpb + wib;
-  if (item >= p.n_items) return;
-  int64_t pos_next = kRotate ? token_position(posp, p.pos64, item / p.nc) : 0;
-
-  for (; item < p.n_items; item += total_waves) {
-    const int t = item / p.nc;
-    const int g_begin = (item - t * p.nc) * p.gpi;
-    const int g_end = min(g_begin + p.gpi, p.ng);
-    const int64_t pos = pos_next;
-    if (kRotate && item + total_waves < p.n_items)
-      pos_next = token_position(posp, p.pos64, (item + total_waves) / p.nc);
-    char* const qrow = qb + t * p.q_tok;
-    char* const krow = kb + t * p.k_tok;
-
-    Raw<NV> raw[U];
-    __amdgpu_buffer_rsrc_t rs[U];
-    uint32_t off[U];
-    bool ok[U], isk[U];
-    auto issue = [&](int g) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int gu = g + u;
-        isk[u] = gu >= p.ngq;  // wave-uniform
-        const int gg = isk[u] ? gu - p.ngq : gu;
-        rs[u] = head_rsrc(isk[u] ? krow + gg * p.k_grp : qrow + gg * p.q_grp);
-        off[u] = isk[u] ? k_off : q_off;
-        ok[u] = in_head && gu < g_end && gg * G + sub < (isk[u] ? p.Hkv : p.Hq);
-        if (ok[u]) {
-          raw[u] = load_io<NV>(rs[u], off[u]);
-        } else {
-#pragma unroll
-          for (int w = 0; w < NV; ++w) raw[u].w[w] = 0u;
-        }
-      }
-    };
-    issue(g_begin);
-
-    // cos / sin of this lane's dims at this token (loaded after the head data
-    // is in flight; kept in registers for every group of the item)
-    float cs[NCS], sn[NCS];
-    if constexpr (kRotate) {
-      const float* row = cache + pos * R;
-      if ((FULL || NEOX) && NCS % 4 == 0 && p.cs_vec) {
-#pragma unroll
-        for (int i = 0; i < NCS; i += 4) {
-          const float4 c4 = *reinterpret_cast<const float4*>(row + j0 + i);
-          const float4 s4 = *reinterpret_cast<const float4*>(row + half + j0 + i);
-          cs[i] = c4.x; cs[i + 1] = c4.y; cs[i + 2] = c4.z; cs[i + 3] = c4.w;
-          sn[i] = s4.x; sn[i + 1] = s4.y; sn[i + 2] = s4.z; sn[i + 3] = s4.w;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < NCS; ++i) {
-          const int j = (FULL || NEOX) ? j0 + i : min(j0 + i, half - 1);
-          cs[i] = row[j];
-          sn[i] = row[half + j];
-        }
-      }
-      if constexpr (NEOX) {
-#pragma unroll
-        for (int i = 0; i < NCS; ++i) sn[i] = lower ? -sn[i] : sn[i];
-      }
-    }
-
-    for (int g = g_begin; g < g_end; g += U) {
-      if (g != g_begin) issue(g);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float x[E];
-#pragma unroll
-        for (int w = 0; w < NV; ++w) IO::unpack(raw[u].w[w], x[2 * w], x[2 * w + 1]);
-        float n[E];
-        if constexpr (kLayer) {
-          // two passes in registers: mean, then the variance of the centred values
-          float sm = 0.0f;
-#pragma unroll
-          for (int i = 0; i < E; ++i) sm += x[i];
-          const float mean = group_sum<L>(sm) * (EXACT ? 1.0f / DMAX : p.inv_d);
-          float c[E], ss = 0.0f;
-#pragma unroll
-          for (int i = 0; i < E; ++i) {
-            c[i] = in_head ? x[i] - mean : 0.0f;
-            ss = fmaf(c[i], c[i], ss);
-          }
-          ss = group_sum<L>(ss);
-          const float r = __builtin_amdgcn_rsqf(fmaf(ss, EXACT ? 1.0f / DMAX : p.inv_d, p.eps));
-#pragma unroll
-          for (int w = 0; w < NV; ++w) {
-            float w0, w1, b0, b1;
-            IO::unpack(isk[u] ? wk_p.w[w] : wq_p.w[w], w0, w1);
-            IO::unpack(isk[u] ? bk_p.w[w] : bq_p.w[w], b0, b1);
-            n[2 * w] = fmaf(c[2 * w] * r, w0, b0);
-            n[2 * w + 1] = fmaf(c[2 * w + 1] * r, w1, b1);
-          }
-        } else if constexpr (kRms) {
-          float ss = 0.0f;
-#pragma unroll
-          for (int i = 0; i < E; ++i) ss = fmaf(x[i], x[i], ss);
-          ss = group_sum<L>(ss);
-          const float r = __builtin_amdgcn_rsqf(fmaf(ss, EXACT ? 1.0f / DMAX : p.inv_d, p.eps));
-#pragma unroll
-          for (int w = 0; w < NV; ++w) {
-            float w0, w1;
-            IO::unpack(isk[u] ? wk_p.w[w] : wq_p.w[w], w0, w1);
-            n[2 * w] = x[2 * w] * r * w0;
-            n[2 * w + 1] = x[2 * w + 1] * r * w1;
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < E; ++i) n[i] = x[i];
-        }
-        float o[E];
-        if constexpr (!kRotate) {
-#pragma unroll
-          for (int i = 0; i < E; ++i) o[i] = n[i];
-        } else if constexpr (NEOX) {
-#pragma unroll
-          for (int i = 0; i < E; ++i) {
-            const float pn = lane_fetch(partner_addr, n[i]);
-            const float v = fmaf(n[i], cs[i], pn * sn[i]);
-            o[i] = lane_rot ? v : n[i];
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < E / 2; ++kk) {
-            const float a = n[2 * kk], b = n[2 * kk + 1];
-            const float oa = fmaf(a, cs[kk], -(b * sn[kk]));
-            const float ob = fmaf(b, cs[kk], a * sn[kk]);
-            const bool rot = (FULL && EXACT) || (d0 + 2 * kk < R);
-            o[2 * kk] = rot ? oa : a;
-            o[2 * kk + 1] = rot ? ob : b;
-          }
-        }
-        Raw<NV> out;
-#pragma unroll
-        for (int w = 0; w < NV; ++w) out.w[w] = IO::pack(o[2 * w], o[2 * w + 1]);
-        if (ok[u]) store_io<NV>(rs[u], off[u], out);
-      }
-    }
-  }
-}
-
-// ==== fused-kernel device code end
+using namespace qknr_impl;
 
 // Measurement aids (see qknr_bench.h): one 16-byte element per thread, one
 // pass over the grid, nontemporal like the op's Q/K traffic.
@@ -459,108 +40,25 @@ __global__ void __launch_bounds__(256) rmw_kernel(u32x4_t* buf, int64_t n, uint3
   }
 }
 
-// ----------------------------------------------------------------------------
-// Kernel table
-// ----------------------------------------------------------------------------
-template <class IO, int D, int E, bool NEOX, bool FULL>
-const void* pick_unroll(int U, int mode) {
-  if (mode == kFused) {
-    switch (U) {
-      case 1: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 1, kFused, true>);
-      case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kFused, true>);
-      case 4: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 4, kFused, true>);
-      default: return nullptr;
-    }
-  }
-  // the unfused baseline steps and the LayerNorm sibling exist at unroll 2 only
-  if (U != 2) return nullptr;
-  if (mode == kRopeOnly)
-    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kRopeOnly, true>);
-  if (mode == kLayerRope)
-    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kLayerRope, true>);
-  if (!NEOX && FULL) {  // pairing and rope_dim play no part without a rotation
-    if (mode == kNormOnly)
-      return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kNormOnly, true>);
-    if (mode == kLayerOnly)
-      return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kLayerOnly, true>);
-  }
-  return nullptr;
-}
-
-template <class IO, int D, int E>
-const void* pick_pairing(bool neox, bool full, int U, int mode) {
-  if (neox) return full ? pick_unroll<IO, D, E, true, true>(U, mode) : pick_unroll<IO, D, E, true, false>(U, mode);
-  return full ? pick_unroll<IO, D, E, false, true>(U, mode) : pick_unroll<IO, D, E, false, false>(U, mode);
-}
-
-// Elements per lane: 8 (16-byte lanes), head_dim/32 (half a wave per head) and
-// head_dim/64 (a full wave per head; needs an even count, so not head_dim 64).
-template <class IO, int D>
-const void* pick_lanes(int E, bool neox, bool full, int U, int mode) {
-  if (E == 8) return pick_pairing<IO, D, 8>(neox, full, U, mode);
-  if constexpr (D / 32 != 8) {
-    if (E == D / 32) return pick_pairing<IO, D, D / 32>(neox, full, U, mode);
-  }
-  if constexpr (D / 64 >= 2 && D / 64 != 8) {
-    if (E == D / 64) return pick_pairing<IO, D, D / 64>(neox, full, U, mode);
-  }
-  return nullptr;
-}
-
-// Run-time head_dim instances: 16-byte lanes, lane group of DMAX/8 lanes, the
-// fused op and the LayerNorm sibling at unroll 2.
-template <class IO, int DMAX, int MODE>
-const void* pick_any_dim_mode(bool neox, bool full) {
-  if (neox) {
-    return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, true, 2, MODE, false>)
-                : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, false, 2, MODE, false>);
-  }
-  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, MODE, false>)
-              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, false, 2, MODE, false>);
-}
-
-template <class IO, int DMAX>
-const void* pick_any_dim(bool neox, bool full, int mode) {
-  switch (mode) {
-    case kFused: return pick_any_dim_mode<IO, DMAX, kFused>(neox, full);
-    case kLayerRope: return pick_any_dim_mode<IO, DMAX, kLayerRope>(neox, full);
-    case kLayerOnly:
-      return reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, kLayerOnly, false>);
-    default: return nullptr;
-  }
-}
-
-template <class IO>
-const void* pick_dim(int D, int E, bool neox, bool full, int U, int mode, bool exact) {
-  if (!exact) {
-    if (U != 2 || E != 8) return nullptr;
-    switch (D) {  // D is the lane-group capacity DMAX here
-      case 16: return pick_any_dim<IO, 16>(neox, full, mode);
-      case 32: return pick_any_dim<IO, 32>(neox, full, mode);
-      case 64: return pick_any_dim<IO, 64>(neox, full, mode);
-      case 128: return pick_any_dim<IO, 128>(neox, full, mode);
-      case 256: return pick_any_dim<IO, 256>(neox, full, mode);
-      case 512: return pick_any_dim<IO, 512>(neox, full, mode);
-      default: return nullptr;
-    }
-  }
-  switch (D) {
-    case 64: return pick_lanes<IO, 64>(E, neox, full, U, mode);
-    case 128: return pick_lanes<IO, 128>(E, neox, full, U, mode);
-    case 256: return pick_lanes<IO, 256>(E, neox, full, U, mode);
-    default: return nullptr;
-  }
-}
-
 const void* pick_kernel(int dtype, int D, int E, bool neox, bool full, int U, int mode, bool exact) {
-  return dtype == QKNR_BF16 ? pick_dim<Bf16>(D, E, neox, full, U, mode, exact)
-                            : pick_dim<Fp16>(D, E, neox, full, U, mode, exact);
+  const int group = !exact ? 2 : (mode == kFused ? 0 : 1);
+  if (dtype == QKNR_BF16) {
+    switch (group) {
+      case 0: return pick_group<Bf16, 0>(D, E, neox, full, U, mode);
+      case 1: return pick_group<Bf16, 1>(D, E, neox, full, U, mode);
+      default: return pick_group<Bf16, 2>(D, E, neox, full, U, mode);
+    }
+  }
+  switch (group) {
+    case 0: return pick_group<Fp16, 0>(D, E, neox, full, U, mode);
+    case 1: return pick_group<Fp16, 1>(D, E, neox, full, U, mode);
+    default: return pick_group<Fp16, 2>(D, E, neox, full, U, mode);
+  }
 }
 
 // ----------------------------------------------------------------------------
 // Host-side validation and planning (no HIP call before validation passes)
 // ----------------------------------------------------------------------------
-bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
 // head_dim with compile-time instances (every lane mapping)
 bool fast_head_dim(int32_t D) { return D == 64 || D == 128 || D == 256; }

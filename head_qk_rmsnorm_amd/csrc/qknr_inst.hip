@@ -1,0 +1,115 @@
+// qknr_inst.hip -- one instance group of the fused QK RMSNorm + RoPE kernel
+// table (see qknr_device.h). Built once per (I/O type, group) with
+// -DQKNR_INST_IO=Bf16|Fp16 -DQKNR_INST_GROUP=0|1|2, so the groups compile in
+// parallel; the host library (qknr.hip) calls pick_group<IO, GROUP>.
+
+#include "qknr_device.h"
+
+#ifndef QKNR_INST_IO
+#error "build with -DQKNR_INST_IO=Bf16 or Fp16"
+#endif
+#ifndef QKNR_INST_GROUP
+#error "build with -DQKNR_INST_GROUP=0, 1 or 2"
+#endif
+
+namespace qknr_impl {
+
+template <class IO, int D, int E, bool NEOX, bool FULL, int GROUP>
+const void* pick_unroll(int U, int mode) {
+  if constexpr (GROUP == 0) {
+    if (mode != kFused) return nullptr;
+    switch (U) {
+      case 1: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 1, kFused, true>);
+      case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kFused, true>);
+      case 4: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 4, kFused, true>);
+      default: return nullptr;
+    }
+  }
+  // the unfused baseline steps and the LayerNorm sibling exist at unroll 2 only
+  if (mode == kFused || U != 2) return nullptr;
+  if (mode == kRopeOnly)
+    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kRopeOnly, true>);
+  if (mode == kLayerRope)
+    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kLayerRope, true>);
+  if (!NEOX && FULL) {  // pairing and rope_dim play no part without a rotation
+    if (mode == kNormOnly)
+      return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kNormOnly, true>);
+    if (mode == kLayerOnly)
+      return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kLayerOnly, true>);
+  }
+  return nullptr;
+}
+
+template <class IO, int D, int E, int GROUP>
+const void* pick_pairing(bool neox, bool full, int U, int mode) {
+  if (neox) {
+    return full ? pick_unroll<IO, D, E, true, true, GROUP>(U, mode)
+                : pick_unroll<IO, D, E, true, false, GROUP>(U, mode);
+  }
+  return full ? pick_unroll<IO, D, E, false, true, GROUP>(U, mode)
+              : pick_unroll<IO, D, E, false, false, GROUP>(U, mode);
+}
+
+// Elements per lane: 8 (16-byte lanes), head_dim/32 (half a wave per head) and
+// head_dim/64 (a full wave per head; needs an even count, so not head_dim 64).
+template <class IO, int D, int GROUP>
+const void* pick_lanes(int E, bool neox, bool full, int U, int mode) {
+  if (E == 8) return pick_pairing<IO, D, 8, GROUP>(neox, full, U, mode);
+  if constexpr (D / 32 != 8) {
+    if (E == D / 32) return pick_pairing<IO, D, D / 32, GROUP>(neox, full, U, mode);
+  }
+  if constexpr (D / 64 >= 2 && D / 64 != 8) {
+    if (E == D / 64) return pick_pairing<IO, D, D / 64, GROUP>(neox, full, U, mode);
+  }
+  return nullptr;
+}
+
+// Run-time head_dim instances: 16-byte lanes, lane group of DMAX/8 lanes, the
+// fused op and the LayerNorm sibling at unroll 2.
+template <class IO, int DMAX, int MODE>
+const void* pick_any_dim_mode(bool neox, bool full) {
+  if (neox) {
+    return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, true, 2, MODE, false>)
+                : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, false, 2, MODE, false>);
+  }
+  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, MODE, false>)
+              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, false, 2, MODE, false>);
+}
+
+template <class IO, int DMAX>
+const void* pick_any_dim(bool neox, bool full, int mode) {
+  switch (mode) {
+    case kFused: return pick_any_dim_mode<IO, DMAX, kFused>(neox, full);
+    case kLayerRope: return pick_any_dim_mode<IO, DMAX, kLayerRope>(neox, full);
+    case kLayerOnly:
+      return reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, kLayerOnly, false>);
+    default: return nullptr;
+  }
+}
+
+template <class IO, int GROUP>
+const void* pick_group(int D, int E, bool neox, bool full, int U, int mode) {
+  if constexpr (GROUP == 2) {
+    if (U != 2 || E != 8) return nullptr;
+    switch (D) {  // D is the lane-group capacity DMAX here
+      case 16: return pick_any_dim<IO, 16>(neox, full, mode);
+      case 32: return pick_any_dim<IO, 32>(neox, full, mode);
+      case 64: return pick_any_dim<IO, 64>(neox, full, mode);
+      case 128: return pick_any_dim<IO, 128>(neox, full, mode);
+      case 256: return pick_any_dim<IO, 256>(neox, full, mode);
+      case 512: return pick_any_dim<IO, 512>(neox, full, mode);
+      default: return nullptr;
+    }
+  } else {
+    switch (D) {
+      case 64: return pick_lanes<IO, 64, GROUP>(E, neox, full, U, mode);
+      case 128: return pick_lanes<IO, 128, GROUP>(E, neox, full, U, mode);
+      case 256: return pick_lanes<IO, 256, GROUP>(E, neox, full, U, mode);
+      default: return nullptr;
+    }
+  }
+}
+
+template const void* pick_group<QKNR_INST_IO, QKNR_INST_GROUP>(int, int, bool, bool, int, int);
+
+}  // namespace qknr_impl
