@@ -1,0 +1,93 @@
+"""Seeded random cases over the whole supported set: head_dim, rope_dim,
+pairing, head counts, token counts, dtypes, layouts, eps and launch shapes,
+each checked against the fp64 oracle element by element (plus untouched bytes
+outside Q/K). The draw is fixed by the seed, so every run tests the same cases."""
+import numpy as np
+import pytest
+
+from head_qk_rmsnorm_amd import workloads as W
+from tests import qknr_harness as Hn
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 160
+
+
+def _draw(i):
+    from head_qk_rmsnorm_amd import binding as B
+
+    g = np.random.default_rng([2026, i])
+    fast = g.random() < 0.7
+    D = int(g.choice([64, 128, 256])) if fast else int(8 * g.integers(2, 65))
+    neox = bool(g.random() < 0.5)
+    for _ in range(100):
+        R = int(2 * g.integers(1, D // 2 + 1)) if g.random() < 0.6 else D
+        if B.qknr_can_use(D, R, neox):
+            break
+    else:
+        R = D
+    Hq = int(g.integers(0, 13))
+    Hkv = int(g.integers(0 if Hq else 1, 7))
+    T = 1 if g.random() < 0.1 else int(g.integers(1, 301))
+    dt = W.BF16 if g.random() < 0.6 else W.FP16
+    pdt = W.I32 if g.random() < 0.5 else W.I64
+    layout = str(g.choice(["contiguous", "contiguous", "padded", "head_major", "qkv"]))
+    eps = float(g.choice([1e-6, 1e-5, 1e-3, 0.0]))
+    launch = None
+    if fast and g.random() < 0.5:
+        launch = {}
+        if g.random() < 0.5:
+            launch["unroll"] = int(g.choice([1, 2, 4]))
+        if g.random() < 0.5:
+            launch["groups_per_item"] = int(g.integers(1, 9))
+        if g.random() < 0.3:
+            launch["block_waves"] = int(g.integers(1, 9))
+        if g.random() < 0.3:
+            launch["max_blocks"] = int(g.choice([-1, 1, 3, 17]))
+        if g.random() < 0.3:
+            launch["lanes_per_head"] = int(g.choice([D // 8, 32, 64]))
+    cfg = W.case(T, Hq, Hkv, D, R, neox, dtype=dt, pos_dtype=pdt, eps=eps, seed=1000 + i,
+                 x_std=float(g.choice([0.5, 1.0, 4.0])))
+    return cfg, layout, launch
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    from head_qk_rmsnorm_amd import binding as B
+
+    B.lib()
+    yield
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_fuzz_case(i):
+    from head_qk_rmsnorm_amd import binding as B
+
+    cfg, layout, launch = _draw(i)
+    print("case", i, cfg.name, layout, launch, flush=True)
+    wl = W.make_workload(cfg)
+    if launch is not None:
+        # a drawn launch shape may not fit this shape (e.g. NeoX rotary lanes);
+        # such a shape must be refused before anything runs, then the default runs
+        dc = Hn.DeviceCase(wl, layout=layout)
+        try:
+            dc.run(launch=launch)
+        except RuntimeError as e:
+            assert "bad argument" in str(e), e
+            after = dc.fetch()
+            for b, a in zip(dc.storages_host, after):
+                assert np.array_equal(b, a)
+            launch = None
+        else:
+            after = dc.fetch()
+            dc.check_untouched(after)
+            gq, gk = dc.outputs(after)
+            rq, rk = Hn.oracle_ref(wl)
+            for g, r in ((gq, rq), (gk, rk)):
+                cmp = Hn.compare_bits(g, r, cfg.dtype)
+                assert cmp.bad == 0 and cmp.exact_frac >= 0.99, cmp
+            return
+    Hn.run_and_check(wl, layout=layout)
