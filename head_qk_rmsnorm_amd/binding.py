@@ -41,7 +41,7 @@ class LaunchCfg(ctypes.Structure):
 
     _fields_ = [("lanes_per_head", ctypes.c_int32), ("groups_per_item", ctypes.c_int32),
                 ("unroll", ctypes.c_int32), ("block_waves", ctypes.c_int32),
-                ("max_blocks", ctypes.c_int32)]
+                ("max_blocks", ctypes.c_int32), ("generic", ctypes.c_int32)]
 
 
 class LaunchInfo(ctypes.Structure):
@@ -51,7 +51,7 @@ class LaunchInfo(ctypes.Structure):
                 ("heads_per_wave", ctypes.c_int32), ("groups_per_token", ctypes.c_int32),
                 ("groups_per_item", ctypes.c_int32), ("unroll", ctypes.c_int32),
                 ("block_threads", ctypes.c_int32), ("grid_blocks", ctypes.c_int32),
-                ("items", ctypes.c_int64)]
+                ("items", ctypes.c_int64), ("generic", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {f: int(getattr(self, f)) for f, _ in self._fields_}

@@ -13,6 +13,7 @@
 #include <cstdint>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "qknr.h"
@@ -73,6 +74,10 @@ int any_dim_capacity(int32_t D) {
   return c;
 }
 
+const void* pick_elem_kernel(int dtype, int mode) {
+  return dtype == QKNR_BF16 ? pick_elem<Bf16>(mode) : pick_elem<Fp16>(mode);
+}
+
 // NeoX pairs (d, d + R/2): with E elements per lane the partner sits a fixed
 // m = (R/2)/E lanes away when R/2 is a multiple of E.
 bool lanes_fit(int32_t R, int32_t neox, int E) {
@@ -80,11 +85,21 @@ bool lanes_fit(int32_t R, int32_t neox, int E) {
   return (R / 2) % E == 0 && R / 2 >= E;
 }
 
-// The supported set: the page's rule (head_dim 64/128/256, rope_dim a
-// multiple of head_dim/32, NeoX rotary lanes a power of two) widened to every
-// even rope_dim for interleaved pairing, every NeoX rope_dim whose half is a
-// multiple of some lane width, and other head_dims that are multiples of 8.
-bool shape_supported(int32_t D, int32_t R, int32_t neox) {
+bool rotates(int mode) { return mode == kFused || mode == kRopeOnly || mode == kLayerRope; }
+
+// The supported set (every mode, on the element-granular kernel): head_dim
+// 2..512; with a rotation, rope_dim even in [2, head_dim].
+bool elem_supported(int mode, int32_t D, int32_t R) {
+  if (D < 2 || D > kElemMaxDim) return false;
+  return !rotates(mode) || (R >= 2 && R <= D && R % 2 == 0);
+}
+
+// Shapes of the vectorised kernel: the page's rule (head_dim 64/128/256,
+// rope_dim a multiple of head_dim/32, NeoX rotary lanes a power of two)
+// widened to every even rope_dim for interleaved pairing, every NeoX rope_dim
+// whose half is a multiple of some lane width, and other head_dims that are
+// multiples of 8.
+bool vector_shape(int32_t D, int32_t R, int32_t neox) {
   if (!fast_head_dim(D) && !any_head_dim(D)) return false;
   if (R <= 0 || R > D || R % 2) return false;
   if (!neox) return true;
@@ -110,6 +125,13 @@ bool views_ok(int64_t T, int64_t H, int64_t tok, int64_t head, int64_t vec_bytes
   return s_out >= s_in * n_in;
 }
 
+// Vectorised instances exist for every mode at head_dim 64/128/256 and for the
+// fused op and the LayerNorm sibling at the other multiples of 8.
+bool vector_mode(int mode, int32_t D) {
+  return fast_head_dim(D) ||
+         (any_head_dim(D) && (mode == kFused || mode == kLayerRope || mode == kLayerOnly));
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Launch defaults, chosen by measurement on MI355X (launch-shape sweeps over
@@ -119,6 +141,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 constexpr int kDefaultGroupsPerItem = 2;
 constexpr int kDefaultUnroll = 2;
 constexpr int kDefaultBlockWaves = 4;
+constexpr int kDefaultElemHeadsPerItem = 4;  // element-granular kernel
+// Work items per launch stay below 2^30 so a wave's item index plus the grid's
+// wave count never overflows 32 bits.
+constexpr int64_t kMaxItems = int64_t{1} << 30;
 
 struct Plan {
   const void* fn = nullptr;
@@ -128,6 +154,8 @@ struct Plan {
   int max_blocks = 0;  // 0: one workgroup per wpb items; -1: occupancy x CUs; > 0: explicit cap
   int dmax = 0;        // head_dim of the instance (lane-group capacity)
   bool exact = true;   // head_dim == dmax
+  bool elem = false;   // element-granular kernel (G = 1: a group is one head)
+  size_t lds = 0;      // dynamic LDS bytes per workgroup
 };
 
 // A lane's byte offset inside its head group, (heads-1)*head_stride + 2*D at
@@ -142,10 +170,12 @@ bool lane_offsets_fit(int G, int32_t H, int64_t head_stride, int32_t D) {
   return true;
 }
 
+// Plan of the vectorised kernel; the launch configuration's fields are
+// already range-checked. QKNR_E_SHAPE: no lane mapping keeps the lane offsets
+// of a head group below 2^31 (or too many work items).
 int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t R,
                   int32_t neox, int32_t dtype, int64_t q_head, int64_t k_head,
-                  const qknr_launch_cfg* cfg, Plan* pl) {
-  qknr_launch_cfg c = cfg ? *cfg : qknr_launch_cfg{0, 0, 0, 0, 0};
+                  const qknr_launch_cfg& c, Plan* pl) {
   auto fits = [&](int E) {
     const int G = kWave / (D / E);
     return lane_offsets_fit(G, Hq, q_head, D) && lane_offsets_fit(G, Hkv, k_head, D);
@@ -169,19 +199,16 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
     }
     if (E == 0) return QKNR_E_SHAPE;
   } else {
-    if (c.lanes_per_head <= 0 || c.lanes_per_head > kWave || D % c.lanes_per_head != 0)
-      return QKNR_E_ARG;
+    if (c.lanes_per_head > kWave || D % c.lanes_per_head != 0) return QKNR_E_ARG;
     E = D / c.lanes_per_head;
     if (E != 8 && E != D / 32 && !(E == D / 64 && E >= 2)) return QKNR_E_ARG;
     if (!lanes_fit(R, neox, E) || !fits(E)) return QKNR_E_ARG;
   }
   // the unfused baseline steps and the run-time head_dim instances exist at unroll 2 only
   const int U = (mode != kFused || !exact) ? 2 : (c.unroll == 0 ? kDefaultUnroll : c.unroll);
-  if (U != 1 && U != 2 && U != 4) return QKNR_E_ARG;
-  const int wpb = c.block_waves == 0 ? kDefaultBlockWaves : c.block_waves;
-  if (wpb < 1 || wpb > kMaxBlockWaves) return QKNR_E_ARG;
-  if (c.groups_per_item < 0 || c.max_blocks < -1) return QKNR_E_ARG;
 
+  pl->elem = false;
+  pl->lds = 0;
   pl->E = E;
   pl->L = dmax / E;
   pl->dmax = dmax;
@@ -193,18 +220,45 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   pl->gpi = std::max(1, std::min(want_gpi, pl->ng));
   pl->nc = (pl->ng + pl->gpi - 1) / pl->gpi;
   pl->items = T * pl->nc;
-  if (pl->items > INT32_MAX) return QKNR_E_SHAPE;
+  if (pl->items > kMaxItems) return QKNR_E_SHAPE;
   pl->U = U;
-  pl->wpb = wpb;
+  pl->wpb = c.block_waves == 0 ? kDefaultBlockWaves : c.block_waves;
   pl->max_blocks = c.max_blocks;
   pl->fn = pick_kernel(dtype, dmax, E, neox != 0, R == D, U, mode, exact);
+  return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
+}
+
+// Plan of the element-granular kernel: one head per wave instruction, a work
+// item is a run of heads (Q, then K) of one token.
+int32_t make_elem_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t neox,
+                       int32_t dtype, const qknr_launch_cfg& c, Plan* pl) {
+  const int H = Hq + Hkv;
+  pl->elem = true;
+  pl->E = (D + kWave - 1) / kWave;
+  pl->L = kWave;
+  pl->dmax = D;
+  pl->exact = false;
+  pl->G = 1;
+  pl->ngq = Hq;
+  pl->ng = H;
+  const int want = c.groups_per_item == 0 ? kDefaultElemHeadsPerItem : c.groups_per_item;
+  pl->gpi = std::max(1, std::min(want, H));
+  pl->nc = (H + pl->gpi - 1) / pl->gpi;
+  pl->items = T * pl->nc;
+  if (pl->items > kMaxItems) return QKNR_E_SHAPE;
+  pl->U = 2;
+  pl->wpb = c.block_waves == 0 ? kDefaultBlockWaves : c.block_waves;
+  pl->max_blocks = c.max_blocks;
+  // NeoX rotation exchanges partners through one LDS row of head_dim floats per wave
+  pl->lds = (rotates(mode) && neox) ? static_cast<size_t>(pl->wpb) * D * sizeof(float) : 0;
+  pl->fn = pick_elem_kernel(dtype, mode);
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
 }
 
 // Per-device CU count and per-kernel occupancy, computed once.
 std::mutex g_cache_mu;
 std::map<int, int> g_cus;
-std::map<std::pair<const void*, int>, int> g_occ;
+std::map<std::tuple<const void*, int, size_t>, int> g_occ;
 
 int32_t device_limits(const void* fn, int threads, size_t lds, int* cus, int* blocks_per_cu) {
   int dev = 0;
@@ -218,7 +272,7 @@ int32_t device_limits(const void* fn, int threads, size_t lds, int* cus, int* bl
     it = g_cus.emplace(dev, n).first;
   }
   *cus = it->second;
-  auto key = std::make_pair(fn, threads);
+  auto key = std::make_tuple(fn, threads, lds);
   auto jt = g_occ.find(key);
   if (jt == g_occ.end()) {
     int nb = 0;
@@ -248,19 +302,72 @@ struct Call {
   hipStream_t stream;
 };
 
+// q or k side of a call: base, weight and bias rows and the strides that are
+// used (the token stride only with T > 1, the head stride only with H > 1)
+// are multiples of `a` bytes.
+bool side_aligned(const void* x, const void* w, const void* b, int64_t T, int32_t H, int64_t tok,
+                  int64_t head, bool need_w, bool bias, uintptr_t a) {
+  if (H == 0) return true;
+  if (!aligned(x, a) || (need_w && !aligned(w, a)) || (bias && !aligned(b, a))) return false;
+  return (T <= 1 || tok % static_cast<int64_t>(a) == 0) && (H <= 1 || head % static_cast<int64_t>(a) == 0);
+}
+
 // Validation (no HIP call) and planning. For kNormOnly the rotation arguments
 // are ignored (pass rope_dim = head_dim); for kRopeOnly the weights and eps.
+// The vectorised kernel is taken when the shape, the alignment and the lane
+// offsets allow it (and the launch configuration does not ask for the
+// element-granular kernel); every other supported case runs element-granular.
 int32_t prepare(int mode, const Call& c, const qknr_launch_cfg* cfg, Plan* pl,
                 qknr_launch_info* info) {
   if (c.T < 0 || c.Hq < 0 || c.Hkv < 0) return QKNR_E_SHAPE;
   if (c.dtype != QKNR_BF16 && c.dtype != QKNR_FP16) return QKNR_E_DTYPE;
   if (c.pdt != QKNR_I32 && c.pdt != QKNR_I64) return QKNR_E_DTYPE;
-  if (!shape_supported(c.D, c.R, c.neox)) return QKNR_E_UNSUPPORTED;
+  if (!elem_supported(mode, c.D, c.R)) return QKNR_E_UNSUPPORTED;
   if (!std::isfinite(c.eps) || c.eps < 0.0f) return QKNR_E_ARG;
   if (c.T > INT32_MAX || c.T * (static_cast<int64_t>(c.Hq) + c.Hkv) > INT32_MAX) return QKNR_E_SHAPE;
+  const qknr_launch_cfg lc = cfg ? *cfg : qknr_launch_cfg{0, 0, 0, 0, 0, 0};
+  if (lc.lanes_per_head < 0 || lc.groups_per_item < 0 || lc.max_blocks < -1 ||
+      lc.block_waves < 0 || lc.block_waves > kMaxBlockWaves ||
+      (lc.unroll != 0 && lc.unroll != 1 && lc.unroll != 2 && lc.unroll != 4) ||
+      (lc.generic != 0 && lc.generic != 1) || (lc.generic && lc.lanes_per_head))
+    return QKNR_E_ARG;
 
-  const int32_t prc = make_plan(mode, c.T, c.Hq, c.Hkv, c.D, c.R, c.neox, c.dtype, c.qh, c.kh, cfg, pl);
-  if (prc != QKNR_OK) return prc;
+  const bool empty = c.T == 0 || c.Hq + c.Hkv == 0;
+  const bool need_w = mode != kRopeOnly;
+  const bool need_rot = rotates(mode);
+  const bool bias = (mode == kLayerRope || mode == kLayerOnly) && (c.bq || c.bk);
+  bool vec_aligned = true;
+  if (!empty) {
+    if ((c.Hq > 0 && (!c.q || (need_w && !c.wq) || (bias && !c.bq))) ||
+        (c.Hkv > 0 && (!c.k || (need_w && !c.wk) || (bias && !c.bk))) ||
+        (need_rot && (!c.cache || !c.pos)))
+      return QKNR_E_NULL;
+    const int64_t vec = 2 * static_cast<int64_t>(c.D);
+    if (c.Hq > 0 && !views_ok(c.T, c.Hq, c.qt, c.qh, vec)) return QKNR_E_SHAPE;
+    if (c.Hkv > 0 && !views_ok(c.T, c.Hkv, c.kt, c.kh, vec)) return QKNR_E_SHAPE;
+    if (!side_aligned(c.q, c.wq, c.bq, c.T, c.Hq, c.qt, c.qh, need_w, bias, 2) ||
+        !side_aligned(c.k, c.wk, c.bk, c.T, c.Hkv, c.kt, c.kh, need_w, bias, 2))
+      return QKNR_E_ALIGN;
+    if (need_rot && (!aligned(c.cache, 4) || !aligned(c.pos, c.pdt == QKNR_I64 ? 8 : 4)))
+      return QKNR_E_ALIGN;
+    vec_aligned = side_aligned(c.q, c.wq, c.bq, c.T, c.Hq, c.qt, c.qh, need_w, bias, 16) &&
+                  side_aligned(c.k, c.wk, c.bk, c.T, c.Hkv, c.kt, c.kh, need_w, bias, 16);
+  }
+
+  const bool vector = !lc.generic && vec_aligned && vector_mode(mode, c.D) &&
+                      vector_shape(c.D, c.R, c.neox);
+  int32_t rc = QKNR_E_UNSUPPORTED;
+  if (vector) {
+    rc = make_plan(mode, c.T, c.Hq, c.Hkv, c.D, c.R, c.neox, c.dtype, c.qh, c.kh, lc, pl);
+    // an explicit lane mapping is honoured or refused, never replaced
+    if (rc != QKNR_OK && (lc.lanes_per_head != 0 || rc != QKNR_E_SHAPE)) return rc;
+  } else if (lc.lanes_per_head != 0) {
+    return QKNR_E_ARG;
+  }
+  if (rc != QKNR_OK) {
+    rc = make_elem_plan(mode, c.T, c.Hq, c.Hkv, c.D, c.neox, c.dtype, lc, pl);
+    if (rc != QKNR_OK) return rc;
+  }
   if (info) {
     info->lanes_per_head = pl->L;
     info->elems_per_lane = pl->E;
@@ -271,28 +378,8 @@ int32_t prepare(int mode, const Call& c, const qknr_launch_cfg* cfg, Plan* pl,
     info->block_threads = pl->wpb * kWave;
     info->grid_blocks = 0;
     info->items = pl->items;
+    info->generic = pl->elem ? 1 : 0;
   }
-  if (c.T == 0 || c.Hq + c.Hkv == 0) return QKNR_OK;
-
-  const bool need_w = mode != kRopeOnly;
-  const bool need_rot = mode == kFused || mode == kRopeOnly || mode == kLayerRope;
-  const bool bias = (mode == kLayerRope || mode == kLayerOnly) && (c.bq || c.bk);
-  if ((c.Hq > 0 && (!c.q || (need_w && !c.wq) || (bias && !c.bq))) ||
-      (c.Hkv > 0 && (!c.k || (need_w && !c.wk) || (bias && !c.bk))) ||
-      (need_rot && (!c.cache || !c.pos)))
-    return QKNR_E_NULL;
-  if (bias && ((c.bq && !aligned(c.bq, 16)) || (c.bk && !aligned(c.bk, 16)))) return QKNR_E_ALIGN;
-  const int64_t vec = 2 * static_cast<int64_t>(c.D);
-  if (c.Hq > 0 && !views_ok(c.T, c.Hq, c.qt, c.qh, vec)) return QKNR_E_SHAPE;
-  if (c.Hkv > 0 && !views_ok(c.T, c.Hkv, c.kt, c.kh, vec)) return QKNR_E_SHAPE;
-  if (c.Hq > 0 && (!aligned(c.q, 16) || (need_w && !aligned(c.wq, 16)) || (c.T > 1 && c.qt % 16) ||
-                   (c.Hq > 1 && c.qh % 16)))
-    return QKNR_E_ALIGN;
-  if (c.Hkv > 0 && (!aligned(c.k, 16) || (need_w && !aligned(c.wk, 16)) || (c.T > 1 && c.kt % 16) ||
-                    (c.Hkv > 1 && c.kh % 16)))
-    return QKNR_E_ALIGN;
-  if (need_rot && (!aligned(c.cache, 4) || !aligned(c.pos, c.pdt == QKNR_I64 ? 8 : 4)))
-    return QKNR_E_ALIGN;
   return QKNR_OK;
 }
 
@@ -301,7 +388,7 @@ int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
   if (c.T == 0 || c.Hq + c.Hkv == 0) return QKNR_OK;
   const int threads = pl.wpb * kWave;
   int cus = 0, per_cu = 0;
-  const int32_t drc = device_limits(pl.fn, threads, 0, &cus, &per_cu);
+  const int32_t drc = device_limits(pl.fn, threads, pl.lds, &cus, &per_cu);
   if (drc != QKNR_OK) return drc;
   const int64_t needed = (pl.items + pl.wpb - 1) / pl.wpb;
   int64_t cap = needed;
@@ -310,7 +397,6 @@ int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min(needed, cap)));
   if (info) info->grid_blocks = grid;
 
-  Params prm;
   char* qarg = static_cast<char*>(c.q);
   char* karg = static_cast<char*>(c.k);
   const void* wqarg = c.wq ? c.wq : c.wk;  // the side with 0 heads still gets a readable row
@@ -319,10 +405,36 @@ int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
   const void* parg = c.pos;
   const void* bqarg = c.bq ? c.bq : c.bk;  // the side with 0 heads still gets a readable row
   const void* bkarg = c.bk ? c.bk : c.bq;
-  prm.has_bias = (c.bq || c.bk) ? 1 : 0;
-  prm.cs_vec = (reinterpret_cast<uintptr_t>(c.cache) % 16 == 0) && ((c.R / 2) % 4 == 0);
   // head strides only matter for views with more than one head
   const int64_t qh = c.Hq > 1 ? c.qh : 0, kh = c.Hkv > 1 ? c.kh : 0;
+
+  if (pl.elem) {
+    ElemParams ep;
+    ep.q_tok = c.qt;
+    ep.k_tok = c.kt;
+    ep.q_head = qh;
+    ep.k_head = kh;
+    ep.Hq = c.Hq;
+    ep.H = c.Hq + c.Hkv;
+    ep.D = c.D;
+    ep.R = c.R;
+    ep.inv_d = static_cast<float>(1.0 / c.D);
+    ep.eps = c.eps;
+    ep.neox = c.neox ? 1 : 0;
+    ep.pos64 = c.pdt == QKNR_I64;
+    ep.has_bias = (c.bq || c.bk) ? 1 : 0;
+    ep.hpi = pl.gpi;
+    ep.nc = pl.nc;
+    ep.n_items = static_cast<int32_t>(pl.items);
+    void* args[] = {&qarg, &karg, &wqarg, &wkarg, &carg, &parg, &bqarg, &bkarg, &ep};
+    if (hipLaunchKernel(pl.fn, dim3(grid), dim3(threads), args, pl.lds, c.stream) != hipSuccess)
+      return QKNR_E_LAUNCH;
+    return QKNR_OK;
+  }
+
+  Params prm;
+  prm.has_bias = (c.bq || c.bk) ? 1 : 0;
+  prm.cs_vec = (reinterpret_cast<uintptr_t>(c.cache) % 16 == 0) && ((c.R / 2) % 4 == 0);
   prm.q_tok = c.qt;
   prm.k_tok = c.kt;
   prm.q_grp = qh * pl.G;
@@ -358,7 +470,8 @@ QKNR_API int32_t qknr_can_use(int32_t head_dim, int32_t rope_dim, int32_t is_neo
                               int32_t pos_dtype) {
   if (dtype != QKNR_BF16 && dtype != QKNR_FP16) return 0;
   if (pos_dtype != QKNR_I32 && pos_dtype != QKNR_I64) return 0;
-  return shape_supported(head_dim, rope_dim, is_neox) ? 1 : 0;
+  (void)is_neox;  // both pairings, every supported width
+  return elem_supported(kFused, head_dim, rope_dim) ? 1 : 0;
 }
 
 QKNR_API const char* qknr_status_string(int32_t status) {
@@ -367,13 +480,11 @@ QKNR_API const char* qknr_status_string(int32_t status) {
     case QKNR_E_NULL: return "qknr: a required pointer is NULL";
     case QKNR_E_SHAPE: return "qknr: bad shape or strides (negative, overlapping head vectors, or too large)";
     case QKNR_E_UNSUPPORTED:
-      return "qknr: unsupported (head_dim, rope_dim, is_neox): need head_dim a multiple of 8 in "
-             "[16, 512], rope_dim even in (0, head_dim], and for NeoX rope_dim/2 a multiple of 8 "
-             "(for head_dim 64/128/256 a multiple of 2, 2 or 4); the unfused steps take head_dim "
-             "64/128/256 only";
+      return "qknr: unsupported (head_dim, rope_dim): need head_dim in [2, 512] and, with a "
+             "rotation, rope_dim even in [2, head_dim]";
     case QKNR_E_ALIGN:
-      return "qknr: misaligned: q, k, weights and q/k strides need 16-byte alignment, the cache 4 bytes, "
-             "positions their element size";
+      return "qknr: misaligned: q, k, weights, biases and q/k strides need 2-byte alignment, the "
+             "cache 4 bytes, positions their element size";
     case QKNR_E_DTYPE: return "qknr: unknown dtype or pos_dtype code";
     case QKNR_E_ARG: return "qknr: bad argument (eps must be finite and >= 0; launch configuration invalid)";
     case QKNR_E_LAUNCH: return "qknr: the HIP runtime rejected the kernel launch";

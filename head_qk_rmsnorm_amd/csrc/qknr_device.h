@@ -443,6 +443,234 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 
 // ==== fused-kernel device code end
 
+// ----------------------------------------------------------------------------
+// Element-granular kernel: the shapes and layouts the vectorised kernel above
+// cannot take (head_dims that are not multiples of 8, NeoX halves that are not
+// a multiple of any lane width, pointers or strides that are only element
+// aligned, head strides beyond 32-bit lane offsets). Same operation, same fp32
+// formulas and FMA forms, same rounding; only the order of the sums differs.
+//
+// One head vector per wave instruction: element e sits in lane e % 64, slot
+// e / 64 (head_dim <= 512, so at most 8 slots). Every access is a 2-byte
+// buffer access relative to the head's own base address, which is wave-uniform
+// (64-bit, no limit on strides); lane offsets stay below 1 KiB and the
+// descriptor covers exactly the head vector. Interleaved partners (e, e ^ 1)
+// are neighbouring lanes of one slot (DPP); NeoX partners (e, e +- R/2) can
+// sit in any lane and slot, so the normalised row goes through a per-wave row
+// of LDS. A work item is a run of heads (Q then K) of one token.
+// ----------------------------------------------------------------------------
+constexpr int kElemSlots = 8;
+constexpr int kElemMaxDim = kElemSlots * kWave;  // 512
+
+struct ElemParams {
+  int64_t q_tok, k_tok, q_head, k_head;  // byte strides
+  int32_t Hq, H;                         // Q heads; Q + K heads (K heads follow Q heads)
+  int32_t D, R;
+  float inv_d, eps;
+  int32_t neox, pos64, has_bias;
+  int32_t hpi, nc, n_items;              // heads per item, items per token, items
+};
+
+// Order this wave's LDS accesses around a row exchange (a wave's LDS accesses
+// execute in order; the fences keep the compiler from moving them).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// one I/O element <-> fp32 (the low half of the packed conversions above)
+template <class IO>
+__device__ __forceinline__ float widen1(uint32_t bits) {
+  float lo, hi;
+  IO::unpack(bits, lo, hi);
+  return lo;
+}
+
+template <class IO>
+__device__ __forceinline__ uint16_t narrow1(float v) {
+  return static_cast<uint16_t>(IO::pack(v, 0.0f) & 0xffffu);
+}
+
+template <class IO, int MODE>
+__global__ void __launch_bounds__(kMaxBlockWaves * kWave)
+qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict__ wqp,
+                 const void* __restrict__ wkp, const float* __restrict__ cache,
+                 const void* __restrict__ posp, const void* __restrict__ bqp,
+                 const void* __restrict__ bkp, const ElemParams p) {
+  constexpr int S = kElemSlots;
+  constexpr int U = 2;  // heads loaded before the first is computed
+  constexpr bool kRotate = MODE == kFused || MODE == kRopeOnly || MODE == kLayerRope;
+  constexpr bool kRms = MODE == kFused || MODE == kNormOnly;
+  constexpr bool kLayer = MODE == kLayerRope || MODE == kLayerOnly;
+  extern __shared__ float elem_rows[];  // NeoX rotation: head_dim floats per wave
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wpb = blockDim.x / kWave;
+  const int D = p.D, R = p.R, half = R / 2;
+  const bool neox = p.neox != 0;  // wave-uniform
+  float* const row = elem_rows + wib * D;
+
+  // weights, biases and rotation roles of this lane's elements
+  const uint16_t* const wq16 = static_cast<const uint16_t*>(wqp);
+  const uint16_t* const wk16 = static_cast<const uint16_t*>(wkp);
+  const uint16_t* const bq16 = static_cast<const uint16_t*>(bqp);
+  const uint16_t* const bk16 = static_cast<const uint16_t*>(bkp);
+  float wq[S], wk[S], bq[S], bk[S];
+  int col[S], partner[S];  // cos/sin column, partner element
+  bool rot[S], neg[S];     // rotated element; partner term subtracted
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int e = s * kWave + lane;
+    const bool act = e < D;
+    wq[s] = wk[s] = bq[s] = bk[s] = 0.0f;
+    if constexpr (kRms || kLayer) {
+      if (act) {
+        wq[s] = widen1<IO>(wq16[e]);
+        wk[s] = widen1<IO>(wk16[e]);
+      }
+    }
+    if constexpr (kLayer) {
+      if (act && p.has_bias) {
+        bq[s] = widen1<IO>(bq16[e]);
+        bk[s] = widen1<IO>(bk16[e]);
+      }
+    }
+    rot[s] = kRotate && e < R;
+    if (neox) {
+      const bool lower = e < half;
+      col[s] = lower ? e : e - half;
+      partner[s] = lower ? e + half : e - half;
+      neg[s] = lower;
+    } else {
+      col[s] = e >> 1;
+      partner[s] = e ^ 1;
+      neg[s] = (e & 1) == 0;
+    }
+    if (!rot[s]) {
+      col[s] = 0;
+      partner[s] = 0;
+    }
+  }
+
+  const int total_waves = gridDim.x * wpb;
+  for (int item = blockIdx.x * wpb + wib; item < p.n_items; item += total_waves) {
+    const int t = item / p.nc;
+    const int h_begin = (item - t * p.nc) * p.hpi;
+    const int h_end = min(h_begin + p.hpi, p.H);
+
+    float x[U][S];
+    __amdgpu_buffer_rsrc_t rs[U];
+    bool ok[U], isk[U];
+    auto issue = [&](int h) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int hh = h + u;
+        ok[u] = hh < h_end;  // wave-uniform
+        isk[u] = hh >= p.Hq;
+        char* const base = isk[u] ? kb + t * p.k_tok + (hh - p.Hq) * p.k_head
+                                  : qb + t * p.q_tok + hh * p.q_head;
+        rs[u] = __builtin_amdgcn_make_buffer_rsrc(base, 0, 2 * D, kBufferFlags);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int e = s * kWave + lane;
+          x[u][s] = 0.0f;
+          if (ok[u] && s * kWave < D && e < D)
+            x[u][s] = widen1<IO>(__builtin_amdgcn_raw_buffer_load_b16(rs[u], 2 * e, 0, kCachePolicyNT));
+        }
+      }
+    };
+    issue(h_begin);
+
+    // cos / sin of this lane's elements at this token; the sign of the
+    // partner term folded into sin
+    float cs[S], sn[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      cs[s] = 1.0f;
+      sn[s] = 0.0f;
+    }
+    if constexpr (kRotate) {
+      const float* const crow = cache + token_position(posp, p.pos64, t) * R;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        if (s * kWave < R && rot[s]) {
+          cs[s] = crow[col[s]];
+          const float v = crow[half + col[s]];
+          sn[s] = neg[s] ? -v : v;
+        }
+      }
+    }
+
+    for (int h = h_begin; h < h_end; h += U) {
+      if (h != h_begin) issue(h);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!ok[u]) continue;
+        float n[S];
+        if constexpr (kLayer) {
+          float sm = 0.0f;
+#pragma unroll
+          for (int s = 0; s < S; ++s) sm += x[u][s];
+          const float mean = group_sum<kWave>(sm) * p.inv_d;
+          float c[S], ss = 0.0f;
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            c[s] = s * kWave + lane < D ? x[u][s] - mean : 0.0f;
+            ss = fmaf(c[s], c[s], ss);
+          }
+          ss = group_sum<kWave>(ss);
+          const float r = __builtin_amdgcn_rsqf(fmaf(ss, p.inv_d, p.eps));
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+            n[s] = fmaf(c[s] * r, isk[u] ? wk[s] : wq[s], isk[u] ? bk[s] : bq[s]);
+        } else if constexpr (kRms) {
+          float ss = 0.0f;
+#pragma unroll
+          for (int s = 0; s < S; ++s) ss = fmaf(x[u][s], x[u][s], ss);
+          ss = group_sum<kWave>(ss);
+          const float r = __builtin_amdgcn_rsqf(fmaf(ss, p.inv_d, p.eps));
+#pragma unroll
+          for (int s = 0; s < S; ++s) n[s] = x[u][s] * r * (isk[u] ? wk[s] : wq[s]);
+        } else {
+#pragma unroll
+          for (int s = 0; s < S; ++s) n[s] = x[u][s];
+        }
+
+        float o[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) o[s] = n[s];
+        if constexpr (kRotate) {
+          float pn[S];
+          if (neox) {
+            wave_lds_fence();  // the previous head's reads are done
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+              const int e = s * kWave + lane;
+              if (s * kWave < R && e < R) row[e] = n[s];
+            }
+            wave_lds_fence();
+#pragma unroll
+            for (int s = 0; s < S; ++s) pn[s] = (s * kWave < R && rot[s]) ? row[partner[s]] : 0.0f;
+          } else {
+#pragma unroll
+            for (int s = 0; s < S; ++s) pn[s] = dpp_mov<kDppQuadXor1>(n[s]);
+          }
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+            if (rot[s]) o[s] = fmaf(n[s], cs[s], pn[s] * sn[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int e = s * kWave + lane;
+          if (s * kWave < D && e < D)
+            __builtin_amdgcn_raw_buffer_store_b16(narrow1<IO>(o[s]), rs[u], 2 * e, 0, kCachePolicyNT);
+        }
+      }
+    }
+  }
+}
+
 // One instance group of the kernel table, defined in qknr_inst.hip and built
 // once per (I/O type, group): group 0 the fused op with compile-time head_dim,
 // group 1 the other modes with compile-time head_dim, group 2 every mode with a
@@ -450,5 +678,9 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 // host stub, or nullptr if no instance matches.
 template <class IO, int GROUP>
 const void* pick_group(int D, int E, bool neox, bool full, int U, int mode);
+
+// Group 3: the element-granular kernel of a mode (kFused ... kLayerOnly).
+template <class IO>
+const void* pick_elem(int mode);
 
 }  // namespace qknr_impl

@@ -1,7 +1,9 @@
 // qknr_inst.hip -- one instance group of the fused QK RMSNorm + RoPE kernel
 // table (see qknr_device.h). Built once per (I/O type, group) with
-// -DQKNR_INST_IO=Bf16|Fp16 -DQKNR_INST_GROUP=0|1|2, so the groups compile in
-// parallel; the host library (qknr.hip) calls pick_group<IO, GROUP>.
+// -DQKNR_INST_IO=Bf16|Fp16 -DQKNR_INST_GROUP=0|1|2|3, so the groups compile in
+// parallel; the host library (qknr.hip) calls pick_group<IO, GROUP> (groups
+// 0-2, the vectorised kernel) and pick_elem<IO> (group 3, the element-granular
+// kernel).
 
 #include "qknr_device.h"
 
@@ -9,7 +11,7 @@
 #error "build with -DQKNR_INST_IO=Bf16 or Fp16"
 #endif
 #ifndef QKNR_INST_GROUP
-#error "build with -DQKNR_INST_GROUP=0, 1 or 2"
+#error "build with -DQKNR_INST_GROUP=0, 1, 2 or 3"
 #endif
 
 namespace qknr_impl {
@@ -110,6 +112,22 @@ const void* pick_group(int D, int E, bool neox, bool full, int U, int mode) {
   }
 }
 
+#if QKNR_INST_GROUP == 3
+template <class IO>
+const void* pick_elem(int mode) {
+  switch (mode) {
+    case kFused: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, kFused>);
+    case kNormOnly: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, kNormOnly>);
+    case kRopeOnly: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, kRopeOnly>);
+    case kLayerRope: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, kLayerRope>);
+    case kLayerOnly: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, kLayerOnly>);
+    default: return nullptr;
+  }
+}
+
+template const void* pick_elem<QKNR_INST_IO>(int);
+#else
 template const void* pick_group<QKNR_INST_IO, QKNR_INST_GROUP>(int, int, bool, bool, int, int);
+#endif
 
 }  // namespace qknr_impl

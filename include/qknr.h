@@ -21,17 +21,23 @@
  *     dtype, the cos|sin cache [rows, R] fp32 row-contiguous, positions [T]
  *     int32 or int64.
  *
- * Supported shapes. Every shape the page accepts (section 4.6 compile-time
- * guards, section 5.2 predicate: head_dim in {64, 128, 256}, rope_dim a
- * multiple of head_dim/32, for NeoX rope_dim/(head_dim/32) a power of two >= 2),
- * widened to:
- *   head_dim a multiple of 8 in [16, 512] (64, 128 and 256 have compile-time
- *   instances with every lane mapping; the others run-time instances);
- *   rope_dim even with 0 < rope_dim <= head_dim;
- *   for NeoX, rope_dim/2 a multiple of a lane width E: 8 for any head_dim, or
- *   also head_dim/32 and head_dim/64 (>= 2) for head_dim 64, 128, 256.
- * qknr_can_use reports exactly this set. The unfused steps below exist for
- * head_dim 64, 128 and 256.
+ * Supported shapes: head_dim from 2 to 512 and rope_dim even with
+ * 2 <= rope_dim <= head_dim, either pairing; qknr_can_use reports exactly this
+ * set, a superset of the page's (section 4.6 compile-time guards, section 5.2
+ * predicate: head_dim in {64, 128, 256}, rope_dim a multiple of head_dim/32,
+ * for NeoX rope_dim/(head_dim/32) a power of two >= 2). Two kernels serve it:
+ *   - the vectorised kernel (16-, 8- or 4-byte lanes, several heads per wave
+ *     instruction), taken whenever all of these hold: head_dim a multiple of 8
+ *     in [16, 512]; for NeoX, rope_dim/2 a multiple of a lane width E (8 for
+ *     any head_dim; also head_dim/32 and head_dim/64 >= 2 for head_dim 64,
+ *     128, 256); q, k, weights (and biases) 16-byte aligned and every used q/k
+ *     stride a multiple of 16 bytes; lane offsets inside a head group below
+ *     2^31 bytes (a mapping with fewer heads per group is tried first); and,
+ *     for the unfused steps, head_dim 64, 128 or 256;
+ *   - the element-granular kernel (2-byte accesses, one head per wave
+ *     instruction) for every other supported case. It needs only element
+ *     alignment and has no stride limit; it computes the same formulas.
+ * qknr_inplace_ex reports which one a call takes (qknr_launch_info.generic).
  *
  * All entry points are thread-safe and keep no state besides small per-device
  * caches of the CU count and kernel occupancy.
@@ -54,8 +60,8 @@ enum {
   QKNR_OK = 0,
   QKNR_E_NULL = -1,        /* a required pointer is NULL */
   QKNR_E_SHAPE = -2,       /* negative size or stride, overlapping head views, size overflow */
-  QKNR_E_UNSUPPORTED = -3, /* (head_dim, rope_dim, is_neox) outside the supported set */
-  QKNR_E_ALIGN = -4,       /* q/k/weights or q/k strides not multiples of 16 bytes,
+  QKNR_E_UNSUPPORTED = -3, /* (head_dim, rope_dim) outside the supported set */
+  QKNR_E_ALIGN = -4,       /* q/k/weights/biases or q/k strides not multiples of 2 bytes,
                               cache not 4-byte aligned, positions not aligned to their type */
   QKNR_E_DTYPE = -5,       /* unknown dtype or pos_dtype code */
   QKNR_E_ARG = -6,         /* eps negative or not finite; bad launch configuration */
@@ -74,13 +80,15 @@ enum { QKNR_I32 = 0, QKNR_I64 = 1 };
  *   q, k            device pointers to element [0,0,0] of q and k. Element
  *                   (t, h, i) of q lives at  q + t*q_tok_stride_B
  *                   + h*q_head_stride_B + 2*i  (bytes); likewise for k.
- *                   Strides are in BYTES, must be >= 0, multiples of 16 and
- *                   describe non-overlapping head vectors. Any layout works
+ *                   Strides are in BYTES, must be >= 0, even (multiples of 16
+ *                   for the vectorised kernel) and describe non-overlapping
+ *                   head vectors. Any layout works
  *                   (contiguous [T,H,D], strided views into a fused qkv buffer,
  *                   head-major); only the T*(Hq+Hkv)*head_dim Q/K elements are
  *                   read and written, no other byte.
  *   wq, wk          device pointers to the [head_dim] RMSNorm weights of Q and
- *                   of K, in the I/O dtype, 16-byte aligned.
+ *                   of K, in the I/O dtype (16-byte aligned for the vectorised
+ *                   kernel).
  *   cos_sin_cache   device pointer to the fp32 table, row p at
  *                   cos_sin_cache + p*rope_dim; it must hold every row that
  *                   positions[] names (not checked: an out-of-range position
@@ -115,8 +123,9 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
  *   lanes_per_head   lanes of the 64-lane wavefront that share one head vector:
  *                    head_dim/8 (16-byte accesses per lane), 32 (half a wave)
  *                    or 64 (a full wave; head_dim 128 and 256 only). NeoX needs
- *                    rope_dim/(head_dim/lanes_per_head) to be a power of two
- *                    >= 2. [head_dim/8 when that holds, else 32]
+ *                    rope_dim/2 to be a multiple of head_dim/lanes_per_head.
+ *                    [the first of head_dim/8, 32, 64 that fits the pairing and
+ *                    the lane-offset limit; none: the element-granular kernel]
  *   groups_per_item  head groups (one per wave instruction: 64/lanes_per_head
  *                    heads of one token) that a wave handles per work item;
  *                    a work item never spans two tokens. [2]
@@ -126,6 +135,13 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
  *                    handles one item [default]; -1: a persistent grid of
  *                    (occupancy x CUs) workgroups striding over the items;
  *                    > 0: at most that many workgroups, striding.
+ *   generic          1: take the element-granular kernel even where the
+ *                    vectorised one applies (lanes_per_head must then be 0);
+ *                    0: choose [0].
+ * On the element-granular kernel a "group" is one head: groups_per_item is
+ * the heads per work item [4], block_waves and max_blocks apply as above,
+ * unroll is fixed at 2 (any valid value is accepted), and lanes_per_head must
+ * be 0 (an explicit lane mapping that the case cannot use is QKNR_E_ARG).
  */
 typedef struct qknr_launch_cfg {
   int32_t lanes_per_head;
@@ -133,9 +149,12 @@ typedef struct qknr_launch_cfg {
   int32_t unroll;
   int32_t block_waves;
   int32_t max_blocks;
+  int32_t generic;
 } qknr_launch_cfg;
 
-/* What a call launches (filled by qknr_inplace_ex / qknr_plan). */
+/* What a call launches (filled by qknr_inplace_ex, also for empty work, where
+ * grid_blocks stays 0). On the element-granular kernel (generic = 1) a lane
+ * owns elems_per_lane elements 64 apart, one head per wave instruction. */
 typedef struct qknr_launch_info {
   int32_t lanes_per_head;
   int32_t elems_per_lane;
@@ -146,6 +165,7 @@ typedef struct qknr_launch_info {
   int32_t block_threads;
   int32_t grid_blocks;
   int64_t items;
+  int32_t generic;
 } qknr_launch_info;
 
 /* qknr_inplace with an explicit launch configuration (cfg may be NULL) and an
@@ -169,7 +189,7 @@ QKNR_API int32_t qknr_inplace_ex(void* q, void* k, const void* wq, const void* w
  *
  * qknr_rmsnorm_inplace -- section 2.1 only: q and k (same layout rules as
  *   qknr_inplace) are replaced by x * rsqrt(mean(x^2) + eps) * w, rounded to the
- *   I/O type. No cache, positions or rotation arguments.
+ *   I/O type. No cache, positions or rotation arguments; head_dim 2..512.
  * qknr_rope_inplace -- section 2.2 only: the first rope_dim dims of every head
  *   of q and k are rotated by cache row positions[t] as stored (no norm); no
  *   weights or eps.
@@ -210,8 +230,9 @@ QKNR_API int32_t qknr_unfused_inplace(void* q, void* k, const void* wq, const vo
  * when rope_dim > 0, by the same rotation as qknr_inplace. rope_dim == 0 means
  * the norm alone (cos_sin_cache, positions, is_neox and pos_dtype are then
  * ignored and may be NULL/0). bq, bk: the [head_dim] bias rows of Q and K in
- * the I/O dtype, 16-byte aligned, or both NULL for no bias. Same layout rules,
- * supported shapes, status codes and ownership as qknr_inplace.
+ * the I/O dtype, or both NULL for no bias. Same layout rules,
+ * supported shapes, status codes and ownership as qknr_inplace (with
+ * rope_dim == 0, any head_dim from 2 to 512).
  */
 QKNR_API int32_t qknr_layernorm_rope_inplace(void* q, void* k, const void* wq, const void* wk,
                                              const void* bq, const void* bk,

@@ -32,6 +32,9 @@ def layout_views(T: int, Hq: int, Hkv: int, D: int, layout: str):
     padded:     [T, H, D] with 8 spare elements after each head and 16 after each token
     head_major: storage [H, T, D] seen as [T, H, D]
     qkv:        one storage [T, (Hq + 2*Hkv) * D]; q, k side by side, v untouched after them
+    shifted:    contiguous [T, H, D] starting 3 elements (6 bytes) past a 16-byte boundary
+    odd_pad:    [T, H, D] with 1 spare element after each head and 1 after each token
+                (strides of an odd number of elements)
     """
     if layout == "qkv":
         width = (Hq + 2 * Hkv) * D
@@ -47,6 +50,12 @@ def layout_views(T: int, Hq: int, Hkv: int, D: int, layout: str):
             out.append((T * ts, [View(0, (ts, hs, 1), (T, H, D))]))
         elif layout == "head_major":
             out.append((T * H * D, [View(0, (D, T * D, 1), (T, H, D))]))
+        elif layout == "shifted":
+            out.append((T * H * D + 3, [View(3, (H * D, D, 1), (T, H, D))]))
+        elif layout == "odd_pad":
+            hs = D + 1
+            ts = H * hs + 1
+            out.append((T * ts, [View(0, (ts, hs, 1), (T, H, D))]))
         else:
             raise ValueError(layout)
     return out
@@ -218,3 +227,75 @@ def run_and_check(wl: W.Workload, layout: Optional[str] = None, launch: Optional
         assert cmp.exact_frac >= min_exact, f"{wl.cfg.name} {name}: {cmp}"
         res.append(cmp)
     return res[0], res[1]
+
+
+def unfused_check(wl, which, layout=None, tokens=None):
+    """Run one unfused entry point on fresh device copies and compare with the
+    matching oracle function (every Q/K element; bytes outside untouched)."""
+    from head_qk_rmsnorm_amd import binding as B
+
+    c = wl.cfg
+    dc = DeviceCase(wl, layout=layout)
+    if which == "norm":
+        B.qknr_rmsnorm_inplace(dc.q, dc.k, dc.wq, dc.wk, eps=c.eps)
+        rq = O.rms_norm_io(wl.q, wl.wq, eps=c.eps, dtype=c.dtype)
+        rk = O.rms_norm_io(wl.k, wl.wk, eps=c.eps, dtype=c.dtype)
+    elif which == "rope":
+        B.qknr_rope_inplace(dc.q, dc.k, dc.cache, dc.positions, is_neox=c.is_neox)
+        rq = O.rope_io(wl.q, wl.cache, wl.positions, is_neox=c.is_neox, dtype=c.dtype)
+        rk = O.rope_io(wl.k, wl.cache, wl.positions, is_neox=c.is_neox, dtype=c.dtype)
+    else:
+        B.qknr_unfused_inplace(dc.q, dc.k, dc.wq, dc.wk, dc.cache, dc.positions,
+                               is_neox=c.is_neox, eps=c.eps)
+        rq, rk = O.qknorm_rope_unfused_io(wl.q, wl.k, wl.wq, wl.wk, wl.cache, wl.positions,
+                                          is_neox=c.is_neox, eps=c.eps, dtype=c.dtype)
+    after = dc.fetch()
+    dc.check_untouched(after)
+    dc.check_inputs_unchanged()
+    gq, gk = dc.outputs(after)
+    out = []
+    for name, g, r in (("q", gq, rq), ("k", gk, rk)):
+        cmp = compare_bits(g, r, c.dtype)
+        assert cmp.bad == 0, f"{which} {c.name} {name}: {cmp}"
+        # the rope step on stored values only adds one rounding of an fp32
+        # rotation; the norm step is the fused op's first half
+        assert cmp.exact_frac >= 0.99, f"{which} {c.name} {name}: {cmp}"
+        out.append(cmp)
+    return out
+
+
+def layernorm_check(wl, rope_dim, bias, layout=None, bias_seed=0):
+    from head_qk_rmsnorm_amd import binding as B
+
+    c = wl.cfg
+    dc = DeviceCase(wl, layout=layout)
+    bq_bits = bk_bits = None
+    bq = bk = None
+    if bias:
+        g = W.rng(c.seed + bias_seed, 77)
+        bq_bits = W.to_io_bits(g.standard_normal(c.head_dim) * 0.5, c.dtype)
+        bk_bits = W.to_io_bits(g.standard_normal(c.head_dim) * 0.5, c.dtype)
+        bq = torch_from_bits(bq_bits, dc)
+        bk = torch_from_bits(bk_bits, dc)
+    B.qknr_layernorm_rope_inplace(dc.q, dc.k, dc.wq, dc.wk, bq, bk,
+                                  dc.cache if rope_dim else None,
+                                  dc.positions if rope_dim else None,
+                                  is_neox=c.is_neox, eps=c.eps, rope_dim=rope_dim)
+    rq, rk = O.qk_layernorm_rope_io(wl.q, wl.k, wl.wq, wl.wk, bq_bits, bk_bits,
+                                    wl.cache[:, :rope_dim] if rope_dim else None, wl.positions,
+                                    is_neox=c.is_neox, eps=c.eps, dtype=c.dtype,
+                                    rope_dim=rope_dim)
+    after = dc.fetch()
+    dc.check_untouched(after)
+    dc.check_inputs_unchanged()
+    gq, gk = dc.outputs(after)
+    for name, g, r in (("q", gq, rq), ("k", gk, rk)):
+        cmp = compare_bits(g, r, c.dtype)
+        assert cmp.bad == 0, f"layernorm {c.name} {name}: {cmp}"
+        assert cmp.exact_frac >= 0.99, f"layernorm {c.name} {name}: {cmp}"
+
+
+def torch_from_bits(bits, dc):
+    import torch
+
+    return torch.from_numpy(bits.view(np.int16)).to(dc.device).view(dc.tdt)

@@ -54,13 +54,17 @@ def _page_predicate(D, R, neox):
 
 
 def _supported(D, R, neox):
-    """The library's documented set (include/qknr.h), restated: head_dim a
-    multiple of 8 in [16, 512]; rope_dim even in (0, head_dim]; NeoX needs
-    rope_dim/2 to be a multiple of a lane width E (8 for any head_dim; also
-    head_dim/32 and head_dim/64 >= 2 for head_dim 64, 128, 256)."""
-    if D % 8 or D < 16 or D > 512:
-        return False
-    if R <= 0 or R > D or R % 2:
+    """The library's documented set (include/qknr.h), restated: head_dim in
+    [2, 512], rope_dim even in [2, head_dim], either pairing."""
+    return 2 <= D <= 512 and 2 <= R <= D and R % 2 == 0
+
+
+def _vectorised(D, R, neox):
+    """Shapes of the vectorised kernel (include/qknr.h), restated: head_dim a
+    multiple of 8 in [16, 512]; NeoX needs rope_dim/2 to be a multiple of a
+    lane width E (8 for any head_dim; also head_dim/32 and head_dim/64 >= 2 for
+    head_dim 64, 128, 256)."""
+    if D % 8 or D < 16 or D > 512 or not _supported(D, R, neox):
         return False
     if not neox:
         return True
@@ -70,7 +74,8 @@ def _supported(D, R, neox):
 
 def test_can_use_covers_page_predicate_and_matches_documented_set():
     n_page = n_more = 0
-    for D in (0, 8, 16, 24, 32, 40, 64, 80, 96, 100, 128, 192, 256, 320, 512, 520, 1024):
+    for D in (0, 1, 2, 3, 8, 16, 24, 32, 40, 64, 80, 96, 100, 128, 192, 256, 320, 512, 513, 520,
+              1024):
         for R in range(-2, max(D, 8) + 3):
             for neox in (0, 1):
                 got = B.qknr_can_use(D, R, neox)
@@ -98,6 +103,10 @@ A = 0x10000  # a 16-byte aligned fake address; never dereferenced
 
 
 def _call(**kw):
+    return _call_info(**kw)[0]
+
+
+def _call_info(**kw):
     a = dict(q=P(A), k=P(A + 0x100000), wq=P(A), wk=P(A), cache=P(A), pos=P(A), T=5, Hq=4,
              Hkv=4, D=128, R=128, neox=1, eps=1e-6, qt=4 * 256, qh=256, kt=4 * 256, kh=256,
              dtype=0, pdt=0, stream=P(0), cfg=None)
@@ -106,7 +115,8 @@ def _call(**kw):
     info = B.LaunchInfo()
     args = [a[n] for n in ("q", "k", "wq", "wk", "cache", "pos", "T", "Hq", "Hkv", "D", "R",
                            "neox", "eps", "qt", "qh", "kt", "kh", "dtype", "pdt", "stream")]
-    return B.lib().qknr_inplace_ex(*args, ctypes.byref(cfg) if cfg else None, ctypes.byref(info))
+    rc = B.lib().qknr_inplace_ex(*args, ctypes.byref(cfg) if cfg else None, ctypes.byref(info))
+    return rc, info.as_dict()
 
 
 REJECT = [
@@ -114,12 +124,10 @@ REJECT = [
     (dict(T=1 << 31), B.QKNR_E_SHAPE), (dict(T=(1 << 28), Hq=8, Hkv=8), B.QKNR_E_SHAPE),
     (dict(dtype=2), B.QKNR_E_DTYPE), (dict(dtype=-1), B.QKNR_E_DTYPE),
     (dict(pdt=2), B.QKNR_E_DTYPE),
-    (dict(D=100, R=100), B.QKNR_E_UNSUPPORTED), (dict(D=1024, R=1024), B.QKNR_E_UNSUPPORTED),
-    (dict(D=8, R=8), B.QKNR_E_UNSUPPORTED), (dict(R=0), B.QKNR_E_UNSUPPORTED),
-    (dict(R=130), B.QKNR_E_UNSUPPORTED), (dict(R=6), B.QKNR_E_UNSUPPORTED),
-    (dict(R=7, neox=0), B.QKNR_E_UNSUPPORTED), (dict(R=98, neox=1), B.QKNR_E_UNSUPPORTED),
-    (dict(D=64, R=2, neox=1), B.QKNR_E_UNSUPPORTED),
-    (dict(D=96, R=40, neox=1, qt=4 * 192, qh=192, kt=4 * 192, kh=192), B.QKNR_E_UNSUPPORTED),
+    (dict(D=1024, R=1024), B.QKNR_E_UNSUPPORTED), (dict(D=514, R=2), B.QKNR_E_UNSUPPORTED),
+    (dict(D=1, R=0), B.QKNR_E_UNSUPPORTED), (dict(R=0), B.QKNR_E_UNSUPPORTED),
+    (dict(R=130), B.QKNR_E_UNSUPPORTED), (dict(R=-2), B.QKNR_E_UNSUPPORTED),
+    (dict(R=7, neox=0), B.QKNR_E_UNSUPPORTED), (dict(R=99, neox=1), B.QKNR_E_UNSUPPORTED),
     (dict(eps=-1e-6), B.QKNR_E_ARG), (dict(eps=float("nan")), B.QKNR_E_ARG),
     (dict(eps=float("inf")), B.QKNR_E_ARG),
     (dict(q=P(0)), B.QKNR_E_NULL), (dict(k=P(0)), B.QKNR_E_NULL), (dict(wq=P(0)), B.QKNR_E_NULL),
@@ -129,9 +137,9 @@ REJECT = [
     (dict(qt=3 * 256), B.QKNR_E_SHAPE),        # token rows overlap
     (dict(qh=-256), B.QKNR_E_SHAPE), (dict(kt=-1024), B.QKNR_E_SHAPE),
     (dict(qt=256, qh=256), B.QKNR_E_SHAPE),    # equal strides overlap
-    (dict(q=P(A + 8)), B.QKNR_E_ALIGN), (dict(k=P(A + 2)), B.QKNR_E_ALIGN),
-    (dict(wq=P(A + 4)), B.QKNR_E_ALIGN), (dict(wk=P(A + 8)), B.QKNR_E_ALIGN),
-    (dict(qh=264, qt=4 * 264), B.QKNR_E_ALIGN), (dict(kt=4 * 256 + 8), B.QKNR_E_ALIGN),
+    (dict(q=P(A + 1)), B.QKNR_E_ALIGN), (dict(k=P(A + 3)), B.QKNR_E_ALIGN),
+    (dict(wq=P(A + 1)), B.QKNR_E_ALIGN), (dict(wk=P(A + 7)), B.QKNR_E_ALIGN),
+    (dict(qh=257, qt=4 * 258), B.QKNR_E_ALIGN), (dict(kt=4 * 256 + 1), B.QKNR_E_ALIGN),
     (dict(cache=P(A + 2)), B.QKNR_E_ALIGN), (dict(pos=P(A + 2)), B.QKNR_E_ALIGN),
     (dict(pos=P(A + 4), pdt=1), B.QKNR_E_ALIGN),
     (dict(cfg=B.LaunchCfg(lanes_per_head=7)), B.QKNR_E_ARG),
@@ -143,8 +151,31 @@ REJECT = [
     (dict(cfg=B.LaunchCfg(block_waves=-1)), B.QKNR_E_ARG),
     (dict(cfg=B.LaunchCfg(max_blocks=-2)), B.QKNR_E_ARG),
     (dict(cfg=B.LaunchCfg(groups_per_item=-1)), B.QKNR_E_ARG),
-    # NeoX with 16-byte lanes needs rope_dim/8 rotary lanes, a power of two >= 2
+    # NeoX with 16-byte lanes needs rope_dim/2 to be a multiple of 8
     (dict(D=128, R=8, cfg=B.LaunchCfg(lanes_per_head=16)), B.QKNR_E_ARG),
+    (dict(cfg=B.LaunchCfg(generic=2)), B.QKNR_E_ARG),
+    (dict(cfg=B.LaunchCfg(generic=1, lanes_per_head=16)), B.QKNR_E_ARG),
+    # an explicit lane mapping on a case only the element-granular kernel takes
+    (dict(q=P(A + 8), cfg=B.LaunchCfg(lanes_per_head=16)), B.QKNR_E_ARG),
+    (dict(D=100, R=100, qt=4 * 200, qh=200, kt=4 * 200, kh=200,
+          cfg=B.LaunchCfg(lanes_per_head=16)), B.QKNR_E_ARG),
+]
+
+# Accepted on the element-granular kernel: shapes, alignments and strides the
+# vectorised kernel cannot take (valid otherwise, so the call reaches the HIP
+# runtime, which a GPU-less host does not have).
+GENERIC = [
+    dict(D=100, R=100, qt=4 * 200, qh=200, kt=4 * 200, kh=200),
+    dict(D=8, R=8, qt=4 * 16, qh=16, kt=4 * 16, kh=16),
+    dict(D=2, R=2, neox=0, qt=4 * 4, qh=4, kt=4 * 4, kh=4),
+    dict(D=3, R=2, neox=1, qt=4 * 6, qh=6, kt=4 * 6, kh=6),
+    dict(R=6), dict(R=98, neox=1), dict(D=64, R=2, neox=1, qt=4 * 128, qh=128, kt=4 * 128, kh=128),
+    dict(D=96, R=40, neox=1, qt=4 * 192, qh=192, kt=4 * 192, kh=192),
+    dict(D=512, R=510, neox=1, qt=4 * 1024, qh=1024, kt=4 * 1024, kh=1024),
+    dict(q=P(A + 8)), dict(k=P(A + 2)), dict(wq=P(A + 4)), dict(wk=P(A + 8)),
+    dict(qh=264, qt=4 * 264), dict(kt=4 * 256 + 8), dict(qh=258, qt=4 * 258),
+    dict(cfg=B.LaunchCfg(generic=1)),
+    dict(cfg=B.LaunchCfg(generic=1, groups_per_item=3, block_waves=8, unroll=4)),
 ]
 
 
@@ -161,6 +192,27 @@ def _no_gpu():
 @pytest.mark.parametrize("kw,code", REJECT, ids=lambda v: str(v))
 def test_rejections(kw, code):
     assert _call(**kw) == code
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: run on a host without a GPU")
+@pytest.mark.parametrize("kw", GENERIC, ids=lambda v: str(v))
+def test_element_granular_cases_are_accepted(kw):
+    rc, info = _call_info(**kw)
+    assert rc == B.QKNR_E_DEVICE, B.qknr_status_string(rc)
+    D = kw.get("D", 128)
+    assert info["generic"] == 1 and info["lanes_per_head"] == 64 and info["heads_per_wave"] == 1
+    assert info["elems_per_lane"] == -(-D // 64)
+    assert info["groups_per_token"] == 8  # one group per head
+    cfg = kw.get("cfg")
+    want = cfg.groups_per_item if cfg is not None and cfg.groups_per_item else 4
+    assert info["groups_per_item"] == want and info["unroll"] == 2
+    assert info["items"] == 5 * -(-8 // want)
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: run on a host without a GPU")
+def test_vectorised_cases_stay_vectorised():
+    rc, info = _call_info()
+    assert rc == B.QKNR_E_DEVICE and info["generic"] == 0 and info["lanes_per_head"] == 16
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: run on a host without a GPU")
@@ -190,6 +242,10 @@ def test_plan_lane_mapping(D):
             if not B.qknr_can_use(D, R, neox):
                 continue
             info = _plan(D, R, neox)
+            if not _vectorised(D, R, neox):
+                assert info["generic"] == 1 and info["lanes_per_head"] == 64, (D, R, neox)
+                continue
+            assert info["generic"] == 0
             fits = lambda e: (not neox) or ((R // 2) % e == 0 and R // 2 >= e)
             want_lanes = D // 8 if fits(8) else (32 if fits(D // 32) else 64)
             assert info["lanes_per_head"] == want_lanes, (D, R, neox, info)
@@ -236,7 +292,23 @@ def test_plan_explicit_cfg():
                                               block_waves=8))
     assert info == dict(lanes_per_head=32, elems_per_lane=4, heads_per_wave=2,
                         groups_per_token=24, groups_per_item=5, unroll=4, block_threads=512,
-                        grid_blocks=0, items=0)
+                        grid_blocks=0, items=0, generic=0)
+
+
+def test_plan_element_granular():
+    """head_dims the vectorised kernel does not take, NeoX halves that are not
+    a multiple of a lane width, and an explicit request, plan one head per
+    wave instruction with elements 64 apart."""
+    info = _plan(100, 100, 1, Hq=7, Hkv=3)
+    assert info == dict(lanes_per_head=64, elems_per_lane=2, heads_per_wave=1,
+                        groups_per_token=10, groups_per_item=4, unroll=2, block_threads=256,
+                        grid_blocks=0, items=0, generic=1)
+    assert _plan(72, 72, 1)["generic"] == 1          # NeoX half 36: no lane width divides it
+    assert _plan(72, 72, 0)["generic"] == 0          # interleaved: 16-byte lanes
+    assert _plan(130, 64, 0)["elems_per_lane"] == 3  # not a multiple of 8
+    forced = _plan(128, 128, 0, cfg=B.LaunchCfg(generic=1, groups_per_item=48, block_waves=2))
+    assert forced["generic"] == 1 and forced["groups_per_item"] == 48
+    assert forced["block_threads"] == 128
 
 
 def test_binding_rejects_host_tensors():
@@ -285,8 +357,8 @@ def test_plan_falls_back_to_fewer_heads_per_group_for_huge_head_strides():
     assert rc == 0 and info["lanes_per_head"] == 32
     rc, info = plan(128, 3 << 30)
     assert rc == 0 and info["lanes_per_head"] == 64
-    rc, _ = plan(64, 3 << 30)
-    assert rc == B.QKNR_E_SHAPE
+    rc, info = plan(64, 3 << 30)  # no vectorised mapping fits: element-granular
+    assert rc == 0 and info["generic"] == 1
     rc, info = plan(64, 3 << 30, Hq=1)  # one head: its stride is never used
     assert rc == 0 and info["lanes_per_head"] == 8
 
@@ -299,11 +371,13 @@ def test_unfused_entry_points_validate_before_launching():
     # the norm step needs no cache or positions; it does need the weights
     assert L.qknr_rmsnorm_inplace(a, a, z, a, 5, 4, 4, 128, 1e-6, 1024, 256, 1024, 256, 0,
                                   z) == B.QKNR_E_NULL
-    # the unfused steps exist for head_dim 64/128/256 only
+    # other head_dims run on the element-granular kernel
     assert L.qknr_rmsnorm_inplace(a, a, a, a, 5, 4, 4, 96, 1e-6, 4 * 192, 192, 4 * 192, 192, 0,
-                                  z) == B.QKNR_E_UNSUPPORTED
-    assert L.qknr_rmsnorm_inplace(a, a, a, a, 5, 4, 4, 100, 1e-6, 4 * 208, 208, 4 * 208, 208, 0,
-                                  z) == B.QKNR_E_UNSUPPORTED
+                                  z) == B.QKNR_E_DEVICE
+    assert L.qknr_rmsnorm_inplace(a, a, a, a, 5, 4, 4, 101, 1e-6, 4 * 208, 208, 4 * 208, 208, 0,
+                                  z) == B.QKNR_E_DEVICE
+    assert L.qknr_rmsnorm_inplace(a, a, a, a, 5, 4, 4, 600, 1e-6, 4 * 1200, 1200, 4 * 1200, 1200,
+                                  0, z) == B.QKNR_E_UNSUPPORTED
     assert L.qknr_rmsnorm_inplace(a, a, a, a, 5, 4, 4, 128, -1.0, 1024, 256, 1024, 256, 0,
                                   z) == B.QKNR_E_ARG
     assert L.qknr_rmsnorm_inplace(a, a, a, a, 5, 4, 4, 128, 1e-6, 1024, 256, 1024, 256, 0,
@@ -312,6 +386,8 @@ def test_unfused_entry_points_validate_before_launching():
     assert L.qknr_rope_inplace(a, a, z, a, 5, 4, 4, 128, 128, 1, 1024, 256, 1024, 256, 0, 0,
                                z) == B.QKNR_E_NULL
     assert L.qknr_rope_inplace(a, a, a, a, 5, 4, 4, 128, 98, 1, 1024, 256, 1024, 256, 0, 0,
+                               z) == B.QKNR_E_DEVICE
+    assert L.qknr_rope_inplace(a, a, a, a, 5, 4, 4, 128, 97, 1, 1024, 256, 1024, 256, 0, 0,
                                z) == B.QKNR_E_UNSUPPORTED
     assert L.qknr_rope_inplace(a, a, a, P(A + 4), 5, 4, 4, 128, 128, 1, 1024, 256, 1024, 256, 0,
                                1, z) == B.QKNR_E_ALIGN
@@ -320,7 +396,7 @@ def test_unfused_entry_points_validate_before_launching():
     # the unfused pair validates like the fused op, before either launch
     args = [a, a, a, a, a, a, 5, 4, 4, 128, 128, 1, 1e-6, 1024, 256, 1024, 256, 0, 0, z]
     assert L.qknr_unfused_inplace(*args) == B.QKNR_E_DEVICE
-    for i, bad, code in ((2, z, B.QKNR_E_NULL), (4, z, B.QKNR_E_NULL), (10, 98, B.QKNR_E_UNSUPPORTED),
+    for i, bad, code in ((2, z, B.QKNR_E_NULL), (4, z, B.QKNR_E_NULL), (10, 99, B.QKNR_E_UNSUPPORTED),
                          (12, float("nan"), B.QKNR_E_ARG), (14, 128, B.QKNR_E_SHAPE)):
         bad_args = list(args)
         bad_args[i] = bad
@@ -345,11 +421,14 @@ def test_layernorm_entry_point_validates_before_launching():
     assert call() == B.QKNR_E_DEVICE                       # valid: reaches the runtime
     assert call(bq=z, bk=z) == B.QKNR_E_DEVICE             # no bias is fine
     assert call(bk=z) == B.QKNR_E_NULL                     # one bias without the other
-    assert call(bq=P(A + 8)) == B.QKNR_E_ALIGN
+    assert call(bq=P(A + 8)) == B.QKNR_E_DEVICE            # element-granular
     assert call(wq=z) == B.QKNR_E_NULL
     assert call(cache=z) == B.QKNR_E_NULL                  # rotation asked, no table
     assert call(R=0, cache=z, pos=z, neox=0) == B.QKNR_E_DEVICE  # norm alone needs no table
-    assert call(R=98) == B.QKNR_E_UNSUPPORTED
-    assert call(D=100, qt=800, qh=200, kt=800, kh=200, R=0) == B.QKNR_E_UNSUPPORTED
+    assert call(R=98) == B.QKNR_E_DEVICE                   # element-granular
+    assert call(R=99) == B.QKNR_E_UNSUPPORTED
+    assert call(D=100, qt=800, qh=200, kt=800, kh=200, R=0) == B.QKNR_E_DEVICE
+    assert call(D=600, qt=4800, qh=1200, kt=4800, kh=1200, R=0) == B.QKNR_E_UNSUPPORTED
+    assert call(bq=P(A + 1)) == B.QKNR_E_ALIGN
     assert call(eps=-1.0) == B.QKNR_E_ARG
     assert call(T=0, q=z, k=z, wq=z, wk=z, bq=z, bk=z, cache=z, pos=z) == B.QKNR_OK

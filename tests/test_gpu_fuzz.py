@@ -1,5 +1,6 @@
-"""Seeded random cases over the whole supported set: head_dim, rope_dim,
-pairing, head counts, token counts, dtypes, layouts, eps and launch shapes,
+"""Seeded random cases over the whole supported set: head_dim (compile-time,
+run-time and element-granular), rope_dim, pairing, head counts, token counts,
+dtypes, layouts (element-aligned ones included), eps and launch shapes,
 each checked against the fp64 oracle element by element (plus untouched bytes
 outside Q/K). The draw is fixed by the seed, so every run tests the same cases."""
 import numpy as np
@@ -10,31 +11,31 @@ from tests import qknr_harness as Hn
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 160
+N_CASES = 240
 
 
 def _draw(i):
-    from head_qk_rmsnorm_amd import binding as B
-
     g = np.random.default_rng([2026, i])
-    fast = g.random() < 0.7
-    D = int(g.choice([64, 128, 256])) if fast else int(8 * g.integers(2, 65))
-    neox = bool(g.random() < 0.5)
-    for _ in range(100):
-        R = int(2 * g.integers(1, D // 2 + 1)) if g.random() < 0.6 else D
-        if B.qknr_can_use(D, R, neox):
-            break
+    u = g.random()
+    if u < 0.5:
+        D = int(g.choice([64, 128, 256]))  # compile-time instances
+    elif u < 0.75:
+        D = int(8 * g.integers(2, 65))     # run-time instances
     else:
-        R = D
+        D = int(g.integers(2, 513))        # any supported head_dim
+    fast = D in (64, 128, 256)
+    neox = bool(g.random() < 0.5)
+    R = D - D % 2 if g.random() < 0.4 else int(2 * g.integers(1, D // 2 + 1))
     Hq = int(g.integers(0, 13))
     Hkv = int(g.integers(0 if Hq else 1, 7))
     T = 1 if g.random() < 0.1 else int(g.integers(1, 301))
     dt = W.BF16 if g.random() < 0.6 else W.FP16
     pdt = W.I32 if g.random() < 0.5 else W.I64
-    layout = str(g.choice(["contiguous", "contiguous", "padded", "head_major", "qkv"]))
+    layout = str(g.choice(["contiguous", "contiguous", "padded", "head_major", "qkv", "shifted",
+                           "odd_pad"]))
     eps = float(g.choice([1e-6, 1e-5, 1e-3, 0.0]))
     launch = None
-    if fast and g.random() < 0.5:
+    if g.random() < 0.5:
         launch = {}
         if g.random() < 0.5:
             launch["unroll"] = int(g.choice([1, 2, 4]))
@@ -44,8 +45,10 @@ def _draw(i):
             launch["block_waves"] = int(g.integers(1, 9))
         if g.random() < 0.3:
             launch["max_blocks"] = int(g.choice([-1, 1, 3, 17]))
-        if g.random() < 0.3:
+        if fast and g.random() < 0.3:
             launch["lanes_per_head"] = int(g.choice([D // 8, 32, 64]))
+        elif g.random() < 0.2:
+            launch["generic"] = 1
     cfg = W.case(T, Hq, Hkv, D, R, neox, dtype=dt, pos_dtype=pdt, eps=eps, seed=1000 + i,
                  x_std=float(g.choice([0.5, 1.0, 4.0])))
     return cfg, layout, launch
@@ -64,14 +67,13 @@ def _gpu():
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_fuzz_case(i):
-    from head_qk_rmsnorm_amd import binding as B
-
     cfg, layout, launch = _draw(i)
     print("case", i, cfg.name, layout, launch, flush=True)
     wl = W.make_workload(cfg)
     if launch is not None:
-        # a drawn launch shape may not fit this shape (e.g. NeoX rotary lanes);
-        # such a shape must be refused before anything runs, then the default runs
+        # a drawn lane mapping may not fit this case (NeoX rotary lanes, a layout
+        # that only the element-granular kernel takes): it must be refused
+        # before anything runs, then the automatic choice runs
         dc = Hn.DeviceCase(wl, layout=layout)
         try:
             dc.run(launch=launch)

@@ -247,7 +247,7 @@ def test_rejections_leave_buffers_untouched():
     bad = [
         dict(eps=-1.0),
         dict(eps=float("nan")),
-        dict(rope_dim=98),  # NeoX: half of 98 is odd, no lane width divides it
+        dict(rope_dim=99),  # odd: no pairs
     ]
     for kw in bad:
         args = dict(is_neox=True, eps=1e-6)
@@ -257,11 +257,18 @@ def test_rejections_leave_buffers_untouched():
             B.qknr_inplace(dc.q, dc.k, dc.wq, dc.wk,
                            dc.cache if not rope else torch.zeros(rows, rope, device=dc.device),
                            dc.positions, rope_dim=rope, **args)
-    # misaligned q view (offset by one element)
-    q_mis = torch.as_strided(dc.storages_dev[0], dc.q.shape, dc.q.stride(),
-                             dc.q.storage_offset() + 1)
-    with pytest.raises(RuntimeError, match="misaligned"):
-        B.qknr_inplace(q_mis, dc.k, dc.wq, dc.wk, dc.cache, dc.positions, is_neox=True)
+    # q at an odd byte address (not even element aligned), through the C ABI
+    import ctypes
+
+    c = wl.cfg
+    P = ctypes.c_void_p
+    rc = B.lib().qknr_inplace(P(dc.q.data_ptr() + 1), P(dc.k.data_ptr()), P(dc.wq.data_ptr()),
+                              P(dc.wk.data_ptr()), P(dc.cache.data_ptr()),
+                              P(dc.positions.data_ptr()), c.T, c.Hq, c.Hkv, c.head_dim,
+                              c.rope_dim, 1, 1e-6, dc.q.stride(0) * 2, dc.q.stride(1) * 2,
+                              dc.k.stride(0) * 2, dc.k.stride(1) * 2, 0, 0, P(0))
+    assert rc == B.QKNR_E_ALIGN
+    torch.cuda.synchronize()
     after = dc.fetch()
     for b, a in zip(dc.storages_host, after):
         assert np.array_equal(b, a)
@@ -293,42 +300,6 @@ def test_copy_and_rmw_kernels():
 # The unfused baseline: norm step, rope step, and the two-launch chain
 # ---------------------------------------------------------------------------
 
-def _unfused_check(wl, which, layout=None, tokens=None):
-    """Run one unfused entry point on fresh device copies and compare with the
-    matching oracle function (every Q/K element; bytes outside untouched)."""
-    from head_qk_rmsnorm_amd import binding as B
-    from oracle import qknr_oracle as O
-
-    c = wl.cfg
-    dc = Hn.DeviceCase(wl, layout=layout)
-    if which == "norm":
-        B.qknr_rmsnorm_inplace(dc.q, dc.k, dc.wq, dc.wk, eps=c.eps)
-        rq = O.rms_norm_io(wl.q, wl.wq, eps=c.eps, dtype=c.dtype)
-        rk = O.rms_norm_io(wl.k, wl.wk, eps=c.eps, dtype=c.dtype)
-    elif which == "rope":
-        B.qknr_rope_inplace(dc.q, dc.k, dc.cache, dc.positions, is_neox=c.is_neox)
-        rq = O.rope_io(wl.q, wl.cache, wl.positions, is_neox=c.is_neox, dtype=c.dtype)
-        rk = O.rope_io(wl.k, wl.cache, wl.positions, is_neox=c.is_neox, dtype=c.dtype)
-    else:
-        B.qknr_unfused_inplace(dc.q, dc.k, dc.wq, dc.wk, dc.cache, dc.positions,
-                               is_neox=c.is_neox, eps=c.eps)
-        rq, rk = O.qknorm_rope_unfused_io(wl.q, wl.k, wl.wq, wl.wk, wl.cache, wl.positions,
-                                          is_neox=c.is_neox, eps=c.eps, dtype=c.dtype)
-    after = dc.fetch()
-    dc.check_untouched(after)
-    dc.check_inputs_unchanged()
-    gq, gk = dc.outputs(after)
-    out = []
-    for name, g, r in (("q", gq, rq), ("k", gk, rk)):
-        cmp = Hn.compare_bits(g, r, c.dtype)
-        assert cmp.bad == 0, f"{which} {c.name} {name}: {cmp}"
-        # the rope step on stored values only adds one rounding of an fp32
-        # rotation; the norm step is the fused op's first half
-        assert cmp.exact_frac >= 0.99, f"{which} {c.name} {name}: {cmp}"
-        out.append(cmp)
-    return out
-
-
 UNFUSED_GRID = [(D, R, neox, dt, pdt, T)
                 for D in (64, 128, 256) for R in (D, D // 2) for neox in (False, True)
                 for dt, pdt in ((W.BF16, W.I64), (W.FP16, W.I32)) for T in (1, 129)]
@@ -339,14 +310,14 @@ UNFUSED_GRID = [(D, R, neox, dt, pdt, T)
 def test_unfused_steps_grid(which, D, R, neox, dt, pdt, T):
     cfg = W.case(T, 5, 3, D, R, neox, dtype=dt, pos_dtype=pdt, seed=T + D + R + 1)
     _say("case", which, cfg.name)
-    _unfused_check(W.make_workload(cfg), which)
+    Hn.unfused_check(W.make_workload(cfg), which)
 
 
 @pytest.mark.parametrize("which", ["norm", "rope", "unfused"])
 @pytest.mark.parametrize("layout", ["padded", "qkv"])
 def test_unfused_steps_layouts(which, layout):
     cfg = W.case(33, 6, 2, 128, 64, True, dtype=W.FP16, seed=11)
-    _unfused_check(W.make_workload(cfg), which, layout=layout)
+    Hn.unfused_check(W.make_workload(cfg), which, layout=layout)
 
 
 @pytest.mark.parametrize("name", ["tiny", "dit", "gqa"])
@@ -354,7 +325,7 @@ def test_unfused_chain_on_workloads(name):
     """The two-launch chain on the workloads (full outputs for Tiny; DiT and GQA
     checked in full as well: the oracle handles them in seconds)."""
     _say("case unfused", name)
-    _unfused_check(W.make_workload(W.CONFIGS[name]), "unfused")
+    Hn.unfused_check(W.make_workload(W.CONFIGS[name]), "unfused")
 
 
 def test_fused_and_unfused_agree_within_page_tolerance():
@@ -380,44 +351,6 @@ def test_fused_and_unfused_agree_within_page_tolerance():
 # Sibling: per-head QK LayerNorm (+ optional rotation)
 # ---------------------------------------------------------------------------
 
-def _layernorm_check(wl, rope_dim, bias, layout=None, bias_seed=0):
-    from head_qk_rmsnorm_amd import binding as B
-    from oracle import qknr_oracle as O
-
-    c = wl.cfg
-    dc = Hn.DeviceCase(wl, layout=layout)
-    bq_bits = bk_bits = None
-    bq = bk = None
-    if bias:
-        g = W.rng(c.seed + bias_seed, 77)
-        bq_bits = W.to_io_bits(g.standard_normal(c.head_dim) * 0.5, c.dtype)
-        bk_bits = W.to_io_bits(g.standard_normal(c.head_dim) * 0.5, c.dtype)
-        bq = torch_from_bits(bq_bits, dc)
-        bk = torch_from_bits(bk_bits, dc)
-    B.qknr_layernorm_rope_inplace(dc.q, dc.k, dc.wq, dc.wk, bq, bk,
-                                  dc.cache if rope_dim else None,
-                                  dc.positions if rope_dim else None,
-                                  is_neox=c.is_neox, eps=c.eps, rope_dim=rope_dim)
-    rq, rk = O.qk_layernorm_rope_io(wl.q, wl.k, wl.wq, wl.wk, bq_bits, bk_bits,
-                                    wl.cache[:, :rope_dim] if rope_dim else None, wl.positions,
-                                    is_neox=c.is_neox, eps=c.eps, dtype=c.dtype,
-                                    rope_dim=rope_dim)
-    after = dc.fetch()
-    dc.check_untouched(after)
-    dc.check_inputs_unchanged()
-    gq, gk = dc.outputs(after)
-    for name, g, r in (("q", gq, rq), ("k", gk, rk)):
-        cmp = Hn.compare_bits(g, r, c.dtype)
-        assert cmp.bad == 0, f"layernorm {c.name} {name}: {cmp}"
-        assert cmp.exact_frac >= 0.99, f"layernorm {c.name} {name}: {cmp}"
-
-
-def torch_from_bits(bits, dc):
-    import torch
-
-    return torch.from_numpy(bits.view(np.int16)).to(dc.device).view(dc.tdt)
-
-
 LN_GRID = [(D, R, neox, dt, bias)
            for D in (64, 128, 256, 96, 192)
            for R, neox in ((0, False), (D, False), (D, True), (D // 2, True), (D // 2, False))
@@ -433,15 +366,15 @@ def test_layernorm_sibling(D, R, neox, dt, bias):
     from oracle import qknr_oracle as O
     wl.q[...] = O.round_to_io_bits(O.decode_io(wl.q, dt) + 1.5, dt)
     _say("case layernorm", cfg.name, R, bias)
-    _layernorm_check(wl, R, bias)
+    Hn.layernorm_check(wl, R, bias)
 
 
 @pytest.mark.parametrize("layout", ["padded", "qkv"])
 def test_layernorm_sibling_layouts(layout):
     cfg = W.case(33, 6, 2, 128, 64, True, seed=5)
-    _layernorm_check(W.make_workload(cfg), 64, True, layout=layout)
+    Hn.layernorm_check(W.make_workload(cfg), 64, True, layout=layout)
 
 
 def test_layernorm_sibling_on_dit_workload():
     """The DiT workload with LayerNorm instead of RMSNorm (all tokens)."""
-    _layernorm_check(W.make_workload(W.CONFIGS["dit"]), 128, True)
+    Hn.layernorm_check(W.make_workload(W.CONFIGS["dit"]), 128, True)
