@@ -74,8 +74,8 @@ int any_dim_capacity(int32_t D) {
   return c;
 }
 
-const void* pick_elem_kernel(int dtype, int mode) {
-  return dtype == QKNR_BF16 ? pick_elem<Bf16>(mode) : pick_elem<Fp16>(mode);
+const void* pick_elem_kernel(int dtype, int mode, int slots) {
+  return dtype == QKNR_BF16 ? pick_elem<Bf16>(mode, slots) : pick_elem<Fp16>(mode, slots);
 }
 
 // NeoX pairs (d, d + R/2): with E elements per lane the partner sits a fixed
@@ -141,7 +141,9 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 constexpr int kDefaultGroupsPerItem = 2;
 constexpr int kDefaultUnroll = 2;
 constexpr int kDefaultBlockWaves = 4;
-constexpr int kDefaultElemHeadsPerItem = 4;  // element-granular kernel
+// element-granular kernel: heads per work item, in units of the heads it loads
+// before computing the first (16 / slots)
+constexpr int kDefaultElemRounds = 2;
 // Work items per launch stay below 2^30 so a wave's item index plus the grid's
 // wave count never overflows 32 bits.
 constexpr int64_t kMaxItems = int64_t{1} << 30;
@@ -229,11 +231,15 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
 }
 
 // Plan of the element-granular kernel: one head per wave instruction, a work
-// item is a run of heads (Q, then K) of one token.
+// item is a run of heads (Q, then K) of one token; S slots per lane, the
+// smallest power of two with 64*S >= head_dim.
 int32_t make_elem_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t neox,
                        int32_t dtype, const qknr_launch_cfg& c, Plan* pl) {
   const int H = Hq + Hkv;
   pl->elem = true;
+  int slots = 1;
+  while (slots * kWave < D) slots *= 2;
+  const int U = 2 * kElemSlots / slots;
   pl->E = (D + kWave - 1) / kWave;
   pl->L = kWave;
   pl->dmax = D;
@@ -241,17 +247,17 @@ int32_t make_elem_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, 
   pl->G = 1;
   pl->ngq = Hq;
   pl->ng = H;
-  const int want = c.groups_per_item == 0 ? kDefaultElemHeadsPerItem : c.groups_per_item;
+  const int want = c.groups_per_item == 0 ? kDefaultElemRounds * U : c.groups_per_item;
   pl->gpi = std::max(1, std::min(want, H));
   pl->nc = (H + pl->gpi - 1) / pl->gpi;
   pl->items = T * pl->nc;
   if (pl->items > kMaxItems) return QKNR_E_SHAPE;
-  pl->U = 2;
+  pl->U = U;
   pl->wpb = c.block_waves == 0 ? kDefaultBlockWaves : c.block_waves;
   pl->max_blocks = c.max_blocks;
   // NeoX rotation exchanges partners through one LDS row of head_dim floats per wave
   pl->lds = (rotates(mode) && neox) ? static_cast<size_t>(pl->wpb) * D * sizeof(float) : 0;
-  pl->fn = pick_elem_kernel(dtype, mode);
+  pl->fn = pick_elem_kernel(dtype, mode, slots);
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
 }
 

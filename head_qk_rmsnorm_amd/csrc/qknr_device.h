@@ -451,13 +451,15 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 // formulas and FMA forms, same rounding; only the order of the sums differs.
 //
 // One head vector per wave instruction: element e sits in lane e % 64, slot
-// e / 64 (head_dim <= 512, so at most 8 slots). Every access is a 2-byte
+// e / 64 (S slots, a power of two covering head_dim <= 512). Every access is a 2-byte
 // buffer access relative to the head's own base address, which is wave-uniform
 // (64-bit, no limit on strides); lane offsets stay below 1 KiB and the
 // descriptor covers exactly the head vector. Interleaved partners (e, e ^ 1)
 // are neighbouring lanes of one slot (DPP); NeoX partners (e, e +- R/2) can
 // sit in any lane and slot, so the normalised row goes through a per-wave row
-// of LDS. A work item is a run of heads (Q then K) of one token.
+// of LDS. A work item is a run of heads (Q then K) of one token; 16/S heads are
+// loaded before the first is computed, so every instance keeps the same
+// number of bytes in flight per wave whatever its head_dim.
 // ----------------------------------------------------------------------------
 constexpr int kElemSlots = 8;
 constexpr int kElemMaxDim = kElemSlots * kWave;  // 512
@@ -492,14 +494,14 @@ __device__ __forceinline__ uint16_t narrow1(float v) {
   return static_cast<uint16_t>(IO::pack(v, 0.0f) & 0xffffu);
 }
 
-template <class IO, int MODE>
+template <class IO, int MODE, int S>
 __global__ void __launch_bounds__(kMaxBlockWaves * kWave)
 qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict__ wqp,
                  const void* __restrict__ wkp, const float* __restrict__ cache,
                  const void* __restrict__ posp, const void* __restrict__ bqp,
                  const void* __restrict__ bkp, const ElemParams p) {
-  constexpr int S = kElemSlots;
-  constexpr int U = 2;  // heads loaded before the first is computed
+  static_assert(S == 1 || S == 2 || S == 4 || S == 8, "slots per lane");
+  constexpr int U = 2 * kElemSlots / S;  // heads loaded before the first is computed
   constexpr bool kRotate = MODE == kFused || MODE == kRopeOnly || MODE == kLayerRope;
   constexpr bool kRms = MODE == kFused || MODE == kNormOnly;
   constexpr bool kLayer = MODE == kLayerRope || MODE == kLayerOnly;
@@ -679,8 +681,9 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
 template <class IO, int GROUP>
 const void* pick_group(int D, int E, bool neox, bool full, int U, int mode);
 
-// Group 3: the element-granular kernel of a mode (kFused ... kLayerOnly).
+// Group 3: the element-granular kernel of a mode (kFused ... kLayerOnly) with
+// S slots per lane (1, 2, 4 or 8).
 template <class IO>
-const void* pick_elem(int mode);
+const void* pick_elem(int mode, int slots);
 
 }  // namespace qknr_impl

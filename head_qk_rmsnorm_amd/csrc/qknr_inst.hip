@@ -113,19 +113,30 @@ const void* pick_group(int D, int E, bool neox, bool full, int U, int mode) {
 }
 
 #if QKNR_INST_GROUP == 3
-template <class IO>
-const void* pick_elem(int mode) {
-  switch (mode) {
-    case kFused: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, kFused>);
-    case kNormOnly: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, kNormOnly>);
-    case kRopeOnly: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, kRopeOnly>);
-    case kLayerRope: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, kLayerRope>);
-    case kLayerOnly: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, kLayerOnly>);
+template <class IO, int MODE>
+const void* pick_elem_slots(int slots) {
+  switch (slots) {
+    case 1: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 1>);
+    case 2: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 2>);
+    case 4: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 4>);
+    case 8: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 8>);
     default: return nullptr;
   }
 }
 
-template const void* pick_elem<QKNR_INST_IO>(int);
+template <class IO>
+const void* pick_elem(int mode, int slots) {
+  switch (mode) {
+    case kFused: return pick_elem_slots<IO, kFused>(slots);
+    case kNormOnly: return pick_elem_slots<IO, kNormOnly>(slots);
+    case kRopeOnly: return pick_elem_slots<IO, kRopeOnly>(slots);
+    case kLayerRope: return pick_elem_slots<IO, kLayerRope>(slots);
+    case kLayerOnly: return pick_elem_slots<IO, kLayerOnly>(slots);
+    default: return nullptr;
+  }
+}
+
+template const void* pick_elem<QKNR_INST_IO>(int, int);
 #else
 template const void* pick_group<QKNR_INST_IO, QKNR_INST_GROUP>(int, int, bool, bool, int, int);
 #endif

@@ -203,9 +203,15 @@ def test_element_granular_cases_are_accepted(kw):
     assert info["generic"] == 1 and info["lanes_per_head"] == 64 and info["heads_per_wave"] == 1
     assert info["elems_per_lane"] == -(-D // 64)
     assert info["groups_per_token"] == 8  # one group per head
+    # slots per lane: the smallest power of two covering head_dim / 64; 16/slots
+    # heads are loaded before the first is computed, two such rounds per item
+    slots = 1
+    while 64 * slots < D:
+        slots *= 2
+    U = 16 // slots
     cfg = kw.get("cfg")
-    want = cfg.groups_per_item if cfg is not None and cfg.groups_per_item else 4
-    assert info["groups_per_item"] == want and info["unroll"] == 2
+    want = min(cfg.groups_per_item if cfg is not None and cfg.groups_per_item else 2 * U, 8)
+    assert info["groups_per_item"] == want and info["unroll"] == U
     assert info["items"] == 5 * -(-8 // want)
 
 
@@ -301,8 +307,12 @@ def test_plan_element_granular():
     wave instruction with elements 64 apart."""
     info = _plan(100, 100, 1, Hq=7, Hkv=3)
     assert info == dict(lanes_per_head=64, elems_per_lane=2, heads_per_wave=1,
-                        groups_per_token=10, groups_per_item=4, unroll=2, block_threads=256,
+                        groups_per_token=10, groups_per_item=10, unroll=8, block_threads=256,
                         grid_blocks=0, items=0, generic=1)
+    big = _plan(300, 300, 1, Hq=30, Hkv=10)  # 8 slots: 2 heads in flight, 4 per item
+    assert (big["elems_per_lane"], big["unroll"], big["groups_per_item"]) == (5, 2, 4)
+    small = _plan(40, 40, 1, Hq=30, Hkv=10)  # 1 slot: 16 heads in flight, 32 per item
+    assert (small["elems_per_lane"], small["unroll"], small["groups_per_item"]) == (1, 16, 32)
     assert _plan(72, 72, 1)["generic"] == 1          # NeoX half 36: no lane width divides it
     assert _plan(72, 72, 0)["generic"] == 0          # interleaved: 16-byte lanes
     assert _plan(130, 64, 0)["elems_per_lane"] == 3  # not a multiple of 8
