@@ -25,19 +25,33 @@ namespace {
 using namespace qknr_impl;
 
 // Measurement aids (see qknr_bench.h): one 16-byte element per thread, one
-// pass over the grid, nontemporal like the op's Q/K traffic.
-__global__ void __launch_bounds__(256) copy_kernel(u32x4_t* __restrict__ dst,
-                                                   const u32x4_t* __restrict__ src, int64_t n) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
+// pass over the grid, with the op's Q/K cache policies (nontemporal loads;
+// nontemporal, agent-scope stores). Each workgroup addresses its own 4 KiB
+// chunk through a buffer descriptor.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 4096, kBufferFlags);
 }
 
-__global__ void __launch_bounds__(256) rmw_kernel(u32x4_t* buf, int64_t n, uint32_t key) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
-    const u32x4_t v = __builtin_nontemporal_load(&buf[i]);
-    __builtin_nontemporal_store(v ^ key, &buf[i]);
+__global__ void __launch_bounds__(256) copy_kernel(char* __restrict__ dst,
+                                                   const char* __restrict__ src, int64_t n) {
+  for (int64_t blk = blockIdx.x; blk * 256 < n; blk += gridDim.x) {
+    if (blk * 256 + threadIdx.x < n) {
+      const uint32_t off = threadIdx.x * 16;
+      const u32x4_t v = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(chunk_rsrc(src + blk * 4096), off, 0, kLoadPolicy));
+      __builtin_amdgcn_raw_buffer_store_b128(v, chunk_rsrc(dst + blk * 4096), off, 0, kStorePolicy);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) rmw_kernel(char* buf, int64_t n, uint32_t key) {
+  for (int64_t blk = blockIdx.x; blk * 256 < n; blk += gridDim.x) {
+    if (blk * 256 + threadIdx.x < n) {
+      const uint32_t off = threadIdx.x * 16;
+      const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(buf + blk * 4096);
+      const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kLoadPolicy));
+      __builtin_amdgcn_raw_buffer_store_b128(v ^ key, rs, off, 0, kStorePolicy);
+    }
   }
 }
 
@@ -611,8 +625,8 @@ QKNR_API int32_t qknr_copy(void* dst, const void* src, int64_t bytes, hipStream_
   if (bytes == 0) return QKNR_OK;
   if (!dst || !src) return QKNR_E_NULL;
   if (!aligned(dst, 16) || !aligned(src, 16) || bytes % 16) return QKNR_E_ALIGN;
-  u32x4_t* d = static_cast<u32x4_t*>(dst);
-  const u32x4_t* s = static_cast<const u32x4_t*>(src);
+  char* d = static_cast<char*>(dst);
+  const char* s = static_cast<const char*>(src);
   int64_t n = bytes / 16;
   void* args[] = {&d, &s, &n};
   return stream_launch(reinterpret_cast<const void*>(&copy_kernel), args, n, stream);
@@ -623,7 +637,7 @@ QKNR_API int32_t qknr_rmw(void* buf, int64_t bytes, uint32_t key, hipStream_t st
   if (bytes == 0) return QKNR_OK;
   if (!buf) return QKNR_E_NULL;
   if (!aligned(buf, 16) || bytes % 16) return QKNR_E_ALIGN;
-  u32x4_t* b = static_cast<u32x4_t*>(buf);
+  char* b = static_cast<char*>(buf);
   int64_t n = bytes / 16;
   void* args[] = {&b, &n, &key};
   return stream_launch(reinterpret_cast<const void*>(&rmw_kernel), args, n, stream);

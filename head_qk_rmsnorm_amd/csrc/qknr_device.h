@@ -164,13 +164,19 @@ __device__ __forceinline__ float lane_fetch(int byte_addr, float v) {
 // Kernel
 // ----------------------------------------------------------------------------
 // Q/K are read and written exactly once: nontemporal accesses keep them from
-// displacing the reused weights, positions and cos|sin rows in L2.
+// displacing the reused weights, positions and cos|sin rows in L2. Stores also
+// carry agent scope (sc1): they are written through to memory instead of
+// staying dirty in the XCD's L2 until the end-of-kernel write-back, which
+// shortens the drain of every launch (measured 0.4-2% faster across sizes).
 // Q/K accesses go through raw buffer instructions: a wave-uniform descriptor
-// (base address of the head group, in SGPRs) plus a 32-bit per-lane offset,
-// with the nontemporal cache policy. Offsets stay below 2^31 (checked on the
-// host), far inside the descriptor's range, so no access is out of range.
+// (base address of the head group, in SGPRs) plus a 32-bit per-lane offset.
+// Offsets stay below 2^31 (checked on the host), far inside the descriptor's
+// range, so no access is out of range.
 constexpr int kBufferFlags = 0x00020000;  // gfx9 raw-buffer descriptor word 3
-constexpr int kCachePolicyNT = 2;          // nontemporal
+constexpr int kCachePolicyNT = 2;          // cache-policy operand: nt
+constexpr int kCachePolicySC1 = 16;        // cache-policy operand: sc1 (agent scope)
+constexpr int kLoadPolicy = kCachePolicyNT;
+constexpr int kStorePolicy = kCachePolicyNT | kCachePolicySC1;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(char* base) {
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, kBufferFlags);
@@ -180,13 +186,13 @@ template <int NV>
 __device__ __forceinline__ Raw<NV> load_io(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   Raw<NV> r;
   if constexpr (NV == 4) {
-    const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCachePolicyNT));
+    const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kLoadPolicy));
     r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
   } else if constexpr (NV == 2) {
-    const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kCachePolicyNT));
+    const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kLoadPolicy));
     r.w[0] = v.x; r.w[1] = v.y;
   } else {
-    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kCachePolicyNT);
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kLoadPolicy);
   }
   return r;
 }
@@ -194,11 +200,11 @@ __device__ __forceinline__ Raw<NV> load_io(__amdgpu_buffer_rsrc_t rs, uint32_t o
 template <int NV>
 __device__ __forceinline__ void store_io(__amdgpu_buffer_rsrc_t rs, uint32_t off, const Raw<NV>& r) {
   if constexpr (NV == 4) {
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{r.w[0], r.w[1], r.w[2], r.w[3]}, rs, off, 0, kCachePolicyNT);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{r.w[0], r.w[1], r.w[2], r.w[3]}, rs, off, 0, kStorePolicy);
   } else if constexpr (NV == 2) {
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{r.w[0], r.w[1]}, rs, off, 0, kCachePolicyNT);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{r.w[0], r.w[1]}, rs, off, 0, kStorePolicy);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b32(r.w[0], rs, off, 0, kCachePolicyNT);
+    __builtin_amdgcn_raw_buffer_store_b32(r.w[0], rs, off, 0, kStorePolicy);
   }
 }
 
@@ -578,7 +584,7 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
           const int e = s * kWave + lane;
           x[u][s] = 0.0f;
           if (ok[u] && s * kWave < D && e < D)
-            x[u][s] = widen1<IO>(__builtin_amdgcn_raw_buffer_load_b16(rs[u], 2 * e, 0, kCachePolicyNT));
+            x[u][s] = widen1<IO>(__builtin_amdgcn_raw_buffer_load_b16(rs[u], 2 * e, 0, kLoadPolicy));
         }
       }
     };
@@ -666,7 +672,7 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
         for (int s = 0; s < S; ++s) {
           const int e = s * kWave + lane;
           if (s * kWave < D && e < D)
-            __builtin_amdgcn_raw_buffer_store_b16(narrow1<IO>(o[s]), rs[u], 2 * e, 0, kCachePolicyNT);
+            __builtin_amdgcn_raw_buffer_store_b16(narrow1<IO>(o[s]), rs[u], 2 * e, 0, kStorePolicy);
         }
       }
     }

@@ -10,7 +10,8 @@
  *     same read-then-overwrite pattern as the op with no arithmetic, i.e. the
  *     practical bandwidth ceiling of an in-place stream. key == 0 leaves the
  *     buffer's contents unchanged.
- * Both use 16-byte accesses: pointers must be 16-byte aligned and bytes a
+ * Both use 16-byte accesses with the op's cache policies (nontemporal loads;
+ * nontemporal, agent-scope stores): pointers must be 16-byte aligned and bytes a
  * multiple of 16 (else QKNR_E_ALIGN); bytes < 0 gives QKNR_E_SHAPE, bytes == 0
  * is a no-op. Asynchronous on `stream`; the caller owns all memory.
  */
