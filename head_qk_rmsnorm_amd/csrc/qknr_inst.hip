@@ -26,20 +26,21 @@ const void* pick_unroll(int U, int mode) {
       case 4: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 4, kFused, true>);
       default: return nullptr;
     }
+  } else {
+    // the unfused baseline steps and the LayerNorm sibling exist at unroll 2 only
+    if (mode == kFused || U != 2) return nullptr;
+    if (mode == kRopeOnly)
+      return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kRopeOnly, true>);
+    if (mode == kLayerRope)
+      return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kLayerRope, true>);
+    if (!NEOX && FULL) {  // pairing and rope_dim play no part without a rotation
+      if (mode == kNormOnly)
+        return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kNormOnly, true>);
+      if (mode == kLayerOnly)
+        return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kLayerOnly, true>);
+    }
+    return nullptr;
   }
-  // the unfused baseline steps and the LayerNorm sibling exist at unroll 2 only
-  if (mode == kFused || U != 2) return nullptr;
-  if (mode == kRopeOnly)
-    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kRopeOnly, true>);
-  if (mode == kLayerRope)
-    return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, NEOX, FULL, 2, kLayerRope, true>);
-  if (!NEOX && FULL) {  // pairing and rope_dim play no part without a rotation
-    if (mode == kNormOnly)
-      return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kNormOnly, true>);
-    if (mode == kLayerOnly)
-      return reinterpret_cast<const void*>(&qknr_kernel<IO, D, E, false, true, 2, kLayerOnly, true>);
-  }
-  return nullptr;
 }
 
 template <class IO, int D, int E, int GROUP>
