@@ -493,6 +493,26 @@ def test_brute_force_tiny(seed):
     np.testing.assert_allclose(ok, bk, rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_brute_force_any_head_dim(seed):
+    """Head_dims that are not multiples of 8 (odd ones included), any even
+    rope_dim, both pairings: the vectorised oracle equals the scalar loops."""
+    g = np.random.default_rng(300 + seed)
+    D = int(g.integers(2, 41))
+    R = 2 * int(g.integers(1, D // 2 + 1))
+    neox = bool(seed % 2)
+    T = int(g.integers(1, 8))
+    Hq, Hkv = int(g.integers(1, 4)), int(g.integers(1, 3))
+    q, k = _rand_heads(g, T, Hq, D), _rand_heads(g, T, Hkv, D)
+    wq, wk = g.uniform(0.5, 1.5, D), g.uniform(0.5, 1.5, D)
+    cache = _cache_formula(16, R)
+    pos = g.integers(0, 16, T)
+    oq, ok = O.qknorm_rope(q, k, wq, wk, cache, pos, is_neox=neox, eps=1e-6, rope_dim=R)
+    bq, bk = _brute(q, k, wq, wk, cache, pos, neox, 1e-6, R)
+    np.testing.assert_allclose(oq, bq, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(ok, bk, rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------------------------
 # The unfused chain (norm step, intermediate rounded to the I/O type, rope step)
 # ---------------------------------------------------------------------------
@@ -595,7 +615,7 @@ def test_layer_norm_matches_torch_layer_norm(eps, bias):
     """Library routine: torch's layer_norm in float64 (biased variance, weight, bias)."""
     torch = pytest.importorskip("torch")
     g = np.random.default_rng(13)
-    for D in (8, 64, 96, 128, 256):
+    for D in (2, 3, 8, 17, 64, 96, 100, 128, 256):
         x = g.standard_normal((5, 3, D)) * 3.0 + 1.5
         w = g.uniform(0.5, 1.5, D)
         b = g.standard_normal(D) if bias else None
