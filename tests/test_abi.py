@@ -442,3 +442,33 @@ def test_layernorm_entry_point_validates_before_launching():
     assert call(bq=P(A + 1)) == B.QKNR_E_ALIGN
     assert call(eps=-1.0) == B.QKNR_E_ARG
     assert call(T=0, q=z, k=z, wq=z, wk=z, bq=z, bk=z, cache=z, pos=z) == B.QKNR_OK
+
+
+def test_torch_custom_ops_are_registered_with_their_mutations():
+    """The ops are torch custom ops that declare q and k as mutated (what
+    torch.compile needs for an in-place op), with the page's capability query."""
+    torch = pytest.importorskip("torch")
+    from head_qk_rmsnorm_amd import torch_ops as T
+
+    s = str(torch.ops.qknr.fused_inplace_qknorm_rope.default._schema)
+    assert "Tensor(a0!) q" in s and "Tensor(a1!) k" in s and "Tensor q_weight" in s, s
+    assert "bool is_neox" in s and "-> ()" in s, s
+    s = str(torch.ops.qknr.fused_inplace_qk_layernorm_rope.default._schema)
+    assert "Tensor(a0!) q" in s and "Tensor(a1!) k" in s and "Tensor? q_bias" in s, s
+    assert T.can_use_fused_inplace_qknorm_rope(128, 128, True, torch.bfloat16)
+    assert T.can_use_fused_inplace_qknorm_rope(100, 98, True, torch.float16)
+    assert not T.can_use_fused_inplace_qknorm_rope(128, 128, True, torch.float32)
+    assert not T.can_use_fused_inplace_qknorm_rope(1024, 128, False, torch.bfloat16)
+    # the page's accepted shapes are all accepted
+    for D in (64, 128, 256):
+        for R in range(D // 32, D + 1, D // 32):
+            rl = R // (D // 32)
+            for neox in (False, True):
+                if neox and (rl < 2 or rl & (rl - 1)):
+                    continue
+                assert T.can_use_fused_inplace_qknorm_rope(D, R, neox, torch.bfloat16), (D, R)
+    q = torch.zeros(2, 2, 64, dtype=torch.bfloat16)
+    w = torch.ones(64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        torch.ops.qknr.fused_inplace_qknorm_rope(q, q.clone(), w, w, torch.zeros(4, 64),
+                                                 torch.zeros(2, dtype=torch.int32), is_neox=True)

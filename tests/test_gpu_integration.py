@@ -148,3 +148,42 @@ def test_concurrent_callers():
             # value and the next one starts from there: check the tolerance only
             cmp = Hn.compare_bits(g, r, c.dtype)
             assert cmp.bad == 0, (c.name, cmp)
+
+
+def test_torch_custom_ops_eager_and_compiled():
+    """torch.ops.qknr.* called directly matches the oracle; inside a compiled
+    function (aot_eager, full graph) the in-place updates of q and k survive and
+    equal the eager result bit for bit, for the fused op and the LayerNorm
+    sibling."""
+    import torch
+    from head_qk_rmsnorm_amd import torch_ops  # noqa: F401  (registers torch.ops.qknr)
+
+    cfg = W.case(33, 6, 2, 128, 64, True, pos_dtype=W.I64, seed=21)
+    wl = W.make_workload(cfg)
+    a = Hn.DeviceCase(wl)
+    torch.ops.qknr.fused_inplace_qknorm_rope(a.q, a.k, a.wq, a.wk, a.cache, a.positions,
+                                             is_neox=True, eps=cfg.eps)
+    gq, gk = a.outputs(a.fetch())
+    rq, rk = Hn.oracle_ref(wl)
+    for g, r in ((gq, rq), (gk, rk)):
+        cmp = Hn.compare_bits(g, r, cfg.dtype)
+        assert cmp.bad == 0 and cmp.exact_frac >= 0.99, cmp
+
+    def step(q, k, wq, wk, cache, pos, bq, bk):
+        torch.ops.qknr.fused_inplace_qknorm_rope(q, k, wq, wk, cache, pos, is_neox=True, eps=1e-6)
+        s = q.float().sum() + k.float().sum()
+        torch.ops.qknr.fused_inplace_qk_layernorm_rope(q, k, wq, wk, bq, bk, cache, pos,
+                                                       is_neox=True, eps=1e-6, rope_dim=64)
+        return s
+
+    compiled = torch.compile(step, backend="aot_eager", fullgraph=True)
+    e = Hn.DeviceCase(wl)
+    c = Hn.DeviceCase(wl)
+    bq = torch.linspace(-0.5, 0.5, 128, device=e.device).to(e.tdt)
+    bk = torch.linspace(0.5, -0.5, 128, device=e.device).to(e.tdt)
+    se = step(e.q, e.k, e.wq, e.wk, e.cache, e.positions, bq, bk)
+    sc = compiled(c.q, c.k, c.wq, c.wk, c.cache, c.positions, bq, bk)
+    torch.cuda.synchronize()
+    assert torch.equal(se, sc)
+    for x, y in zip(e.fetch(), c.fetch()):
+        assert np.array_equal(x, y)
