@@ -50,7 +50,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", default="dit", help="tiny | dit | gqa | partial | large")
+    ap.add_argument("--config", default="dit",
+                    help="tiny | dit | gqa | partial | large, or a one-GPU shard: gqa_tp8 | "
+                         "dit_hp8 | dit_sp8")
     ap.add_argument("--launch", default="", help="JSON launch configuration (qknr_launch_cfg fields)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle timing budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -62,6 +64,8 @@ def parse():
     ap.add_argument("--sweep-grid", action="store_true",
                     help="time every (grid kind, groups per item, unroll, block waves) combination")
     ap.add_argument("--all-configs", action="store_true", help="also time every workload")
+    ap.add_argument("--shards", action="store_true",
+                    help="also time the one-GPU shard workloads (gqa_tp8, dit_hp8, dit_sp8)")
     ap.add_argument("--extra-out", default="", help="file for per-config / sweep JSON lines")
     return ap.parse_args()
 
@@ -344,8 +348,9 @@ def main():
                 extra.write(json.dumps(r) + "\n")
                 extra.flush()
         del rig
-    if args.all_configs:
-        for name in W.CONFIG_ORDER:
+    if args.all_configs or args.shards:
+        names = (W.CONFIG_ORDER if args.all_configs else []) + (W.SHARD_ORDER if args.shards else [])
+        for name in names:
             r = measure(W.CONFIGS[name], dev, args.steps, args.warmup, launch,
                         want_yard=not args.no_yardstick, want_unfused=not args.no_unfused,
                         op=args.op)

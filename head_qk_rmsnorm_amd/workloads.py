@@ -53,7 +53,7 @@ class Config:
     cache_rows: int
     base: float
     x_std: float = 1.0
-    positions: str = "arange"  # arange | perm | uniform
+    positions: str = "arange"  # arange | perm | uniform | rows
     layout: str = "contiguous"  # contiguous | qkv (q,k strided views into [T,(Hq+2Hkv)*D])
     outlier_frac: float = 0.0  # fraction of (head, dim) channels scaled by outlier_scale
     outlier_scale: float = 1.0
@@ -106,6 +106,27 @@ CONFIGS = {
                     seed=5),
 }
 CONFIG_ORDER = ["tiny", "dit", "gqa", "partial", "large"]
+
+# One GPU's share of a sharded run, at its real shape (every (token, head) is
+# independent, so a shard is the same op on fewer tokens or fewer heads):
+#   gqa_tp8  the GQA workload under 8-way tensor (head) parallelism: each GPU
+#            holds 4 of the 32 Q heads and 1 of the 8 K heads, in its own qkv
+#            shard [T, (4 + 2*1) * 128];
+#   dit_hp8  the DiT workload after an 8-way head scatter (all tokens, 3 + 3 heads);
+#   dit_sp8  the DiT workload under 8-way sequence parallelism: 576 of the 4608
+#            tokens with their global positions (distinct rows of the full table).
+CONFIGS.update({
+    "gqa_tp8": Config("gqa_tp8", T=8192, Hq=4, Hkv=1, head_dim=128, rope_dim=128, is_neox=True,
+                      dtype=BF16, pos_dtype=I32, eps=1e-6, cache_rows=8192, base=1e6,
+                      positions="arange", layout="qkv", seed=13),
+    "dit_hp8": Config("dit_hp8", T=4608, Hq=3, Hkv=3, head_dim=128, rope_dim=128,
+                      is_neox=False, dtype=BF16, pos_dtype=I64, eps=1e-6, cache_rows=4608,
+                      base=1e4, x_std=2.0, positions="perm", seed=12),
+    "dit_sp8": Config("dit_sp8", T=576, Hq=24, Hkv=24, head_dim=128, rope_dim=128,
+                      is_neox=False, dtype=BF16, pos_dtype=I64, eps=1e-6, cache_rows=4608,
+                      base=1e4, x_std=2.0, positions="rows", seed=12),
+})
+SHARD_ORDER = ["gqa_tp8", "dit_hp8", "dit_sp8"]
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -163,6 +184,8 @@ def _positions(cfg: Config, g: np.random.Generator) -> np.ndarray:
         p = g.permutation(cfg.T).astype(np.int64)
     elif cfg.positions == "uniform":
         p = g.integers(0, cfg.cache_rows, size=cfg.T, dtype=np.int64)
+    elif cfg.positions == "rows":  # T distinct rows of the table (a shard of a permutation)
+        p = g.permutation(cfg.cache_rows)[:cfg.T].astype(np.int64)
     else:
         raise ValueError(cfg.positions)
     if cfg.T and (p.min() < 0 or p.max() >= cfg.cache_rows):
@@ -240,7 +263,7 @@ def theta(rope_dim: int, base: float) -> np.ndarray:
 
 
 __all__ = [
-    "BF16", "FP16", "I32", "I64", "Config", "CONFIGS", "CONFIG_ORDER", "Workload",
+    "BF16", "FP16", "I32", "I64", "Config", "CONFIGS", "CONFIG_ORDER", "SHARD_ORDER", "Workload",
     "make_workload", "case", "rope_cache", "to_io_bits", "rng", "sample_tokens",
     "describe", "theta",
 ]

@@ -57,6 +57,15 @@ def test_config_full_size_sampled(name):
     _say(name, cq, ck)
 
 
+@pytest.mark.parametrize("name", ["gqa_tp8", "dit_hp8", "dit_sp8"])
+def test_shard_workloads_full(name):
+    """One GPU's share of the sharded runs, every output element, in the launch
+    configuration the benchmark times."""
+    cfg = W.CONFIGS[name]
+    _say("case", name)
+    Hn.run_and_check(W.make_workload(cfg))
+
+
 # ---------------------------------------------------------------------------
 # Grid: head_dim x rope_dim x pairing x dtype x positions x T, with GQA
 # ---------------------------------------------------------------------------

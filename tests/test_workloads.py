@@ -90,3 +90,25 @@ def test_algorithmic_bytes_of_configs():
             "large": 1644299264}
     for n, b in want.items():
         assert W.CONFIGS[n].algorithmic_bytes() == b, n
+
+
+@pytest.mark.parametrize("name", ["gqa_tp8", "dit_hp8", "dit_sp8"])
+def test_shard_workloads(name):
+    """One GPU's share of the sharded runs: the heads or tokens of one shard, with
+    positions of the full sequence."""
+    c = W.CONFIGS[name]
+    assert name in W.SHARD_ORDER and name not in W.CONFIG_ORDER
+    wl = W.make_workload(c)
+    assert wl.q.shape == (c.T, c.Hq, c.head_dim) and wl.k.shape == (c.T, c.Hkv, c.head_dim)
+    assert wl.positions.min() >= 0 and wl.positions.max() < c.cache_rows
+    full = W.CONFIGS["gqa" if name.startswith("gqa") else "dit"]
+    assert (c.head_dim, c.rope_dim, c.is_neox, c.dtype, c.pos_dtype, c.base) == \
+        (full.head_dim, full.rope_dim, full.is_neox, full.dtype, full.pos_dtype, full.base)
+    if name == "gqa_tp8":
+        assert (c.Hq, c.Hkv, c.layout) == (full.Hq // 8, full.Hkv // 8, "qkv")
+        assert wl.qkv.shape == (c.T, (c.Hq + 2 * c.Hkv) * c.head_dim)
+    elif name == "dit_hp8":
+        assert (c.T, c.Hq, c.Hkv) == (full.T, full.Hq // 8, full.Hkv // 8)
+    else:
+        assert (c.T, c.Hq, c.Hkv, c.cache_rows) == (full.T // 8, full.Hq, full.Hkv, full.T)
+        assert len(set(wl.positions.tolist())) == c.T  # distinct global positions
