@@ -20,10 +20,9 @@
 //     half a wave also covers the NeoX rotary widths whose rotary lanes would
 //     not be a power of two with E = 8.
 //   * A wave's work item is a run of head groups of ONE token, so the position
-//     is wave-uniform and read with a scalar load (prefetched one item ahead
-//     when a wave strides);
-//     each lane loads the cos/sin values of its own dims once per item and keeps
-//     them in registers for every head of the item.
+//     is wave-uniform and read with a scalar load; each lane loads the cos/sin
+//     values of its own dims once per item and keeps them in registers for
+//     every head of the item.
 //   * The fp32 sum of squares is reduced over the L lanes of a head with DPP
 //     row operations (quad_perm, row_half_mirror, row_mirror), one ds_swizzle
 //     across 16-lane rows for L >= 32 and two readlanes across the wave halves
@@ -34,10 +33,12 @@
 //     both) of one token, so the group's base address is wave-uniform (an SGPR
 //     buffer descriptor) and each lane adds a fixed 32-bit offset. Only Q/K
 //     elements are loaded or stored.
-//   * The loads of `unroll` head groups are issued before the first is computed
-//     and before the position-dependent cos/sin fetch, so the data is in flight
-//     while the position -> cache-row chain resolves. Q/K traffic is streamed
-//     with nontemporal loads and stores (each byte is touched once).
+//   * A wave's first memory requests are the loads of `unroll` head groups;
+//     the weight rows, the position and the position-dependent cos/sin fetch
+//     follow, so the head data is in flight while that chain resolves (issuing
+//     the weights and the position first made every wave wait for them before
+//     its head loads: 0.5-2.6% slower). Q/K traffic is streamed with
+//     nontemporal loads and stores (each byte is touched once).
 //   * By default every wave takes one work item and exits (no persistent grid):
 //     the dispatcher back-fills CUs as waves finish, which balances the tail.
 // Nothing here is a contraction, so there is no MFMA.
@@ -271,19 +272,31 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   constexpr bool kRms = MODE == kFused || MODE == kNormOnly;
   constexpr bool kLayer = MODE == kLayerRope || MODE == kLayerOnly;
 
-  // Weights (and LayerNorm biases) of this lane's dims, kept packed.
+  // Weights (and LayerNorm biases) of this lane's dims, kept packed; loaded
+  // once, after the first head loads are in flight. The LayerNorm modes keep
+  // the other order (weights, biases and the position requested first, the
+  // position prefetched one item ahead): for them the late order costs
+  // registers, a wave per SIMD, and measured 1-3.5% slower on the NeoX
+  // workloads.
   Raw<NV> wq_p{}, wk_p{}, bq_p{}, bk_p{};
-  if constexpr (kRms || kLayer) {
-    if (in_head) {
-      wq_p = load_raw<NV>(static_cast<const char*>(wqp) + d0 * 2);
-      wk_p = load_raw<NV>(static_cast<const char*>(wkp) + d0 * 2);
+  bool have_w = false;
+  auto load_weights = [&]() {
+    if constexpr (kRms || kLayer) {
+      if (in_head) {
+        wq_p = load_raw<NV>(static_cast<const char*>(wqp) + d0 * 2);
+        wk_p = load_raw<NV>(static_cast<const char*>(wkp) + d0 * 2);
+      }
     }
-  }
+    if constexpr (kLayer) {
+      if (in_head && p.has_bias) {
+        bq_p = load_raw<NV>(static_cast<const char*>(bqp) + d0 * 2);
+        bk_p = load_raw<NV>(static_cast<const char*>(bkp) + d0 * 2);
+      }
+    }
+  };
   if constexpr (kLayer) {
-    if (in_head && p.has_bias) {
-      bq_p = load_raw<NV>(static_cast<const char*>(bqp) + d0 * 2);
-      bk_p = load_raw<NV>(static_cast<const char*>(bkp) + d0 * 2);
-    }
+    load_weights();
+    have_w = true;
   }
 
   // NeoX: this lane holds dims d0..d0+E-1. With m = (R/2)/E, lanes below m
@@ -307,15 +320,19 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   const int total_waves = gridDim.x * wpb;
   int item = blockIdx.x * wpb + wib;
   if (item >= p.n_items) return;
-  int64_t pos_next = kRotate ? token_position(posp, p.pos64, item / p.nc) : 0;
+  int64_t pos_next = 0;
+  if constexpr (kLayer && kRotate) pos_next = token_position(posp, p.pos64, item / p.nc);
 
   for (; item < p.n_items; item += total_waves) {
     const int t = item / p.nc;
     const int g_begin = (item - t * p.nc) * p.gpi;
     const int g_end = min(g_begin + p.gpi, p.ng);
-    const int64_t pos = pos_next;
-    if (kRotate && item + total_waves < p.n_items)
-      pos_next = token_position(posp, p.pos64, (item + total_waves) / p.nc);
+    int64_t pos = 0;
+    if constexpr (kLayer && kRotate) {
+      pos = pos_next;
+      if (item + total_waves < p.n_items)
+        pos_next = token_position(posp, p.pos64, (item + total_waves) / p.nc);
+    }
     char* const qrow = qb + t * p.q_tok;
     char* const krow = kb + t * p.k_tok;
 
@@ -341,6 +358,18 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
       }
     };
     issue(g_begin);
+    if constexpr (!kLayer) {
+      // Nothing above waits on memory: the head loads leave before the weight
+      // rows and the position (whose cos/sin fetch depends on it) are
+      // requested, and the barrier keeps the scheduler from hoisting those
+      // loads (and the waits they bring) above them.
+      __builtin_amdgcn_sched_barrier(0);
+      if (!have_w) {
+        load_weights();
+        have_w = true;
+      }
+      if constexpr (kRotate) pos = token_position(posp, p.pos64, t);
+    }
 
     // cos / sin of this lane's dims at this token (loaded after the head data
     // is in flight; kept in registers for every group of the item)
@@ -527,23 +556,30 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
   float wq[S], wk[S], bq[S], bk[S];
   int col[S], partner[S];  // cos/sin column, partner element
   bool rot[S], neg[S];     // rotated element; partner term subtracted
+  bool have_w = false;     // weights are loaded after the first head loads
+  auto load_weights = [&]() {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int e = s * kWave + lane;
+      const bool act = e < D;
+      wq[s] = wk[s] = bq[s] = bk[s] = 0.0f;
+      if constexpr (kRms || kLayer) {
+        if (act) {
+          wq[s] = widen1<IO>(wq16[e]);
+          wk[s] = widen1<IO>(wk16[e]);
+        }
+      }
+      if constexpr (kLayer) {
+        if (act && p.has_bias) {
+          bq[s] = widen1<IO>(bq16[e]);
+          bk[s] = widen1<IO>(bk16[e]);
+        }
+      }
+    }
+  };
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int e = s * kWave + lane;
-    const bool act = e < D;
-    wq[s] = wk[s] = bq[s] = bk[s] = 0.0f;
-    if constexpr (kRms || kLayer) {
-      if (act) {
-        wq[s] = widen1<IO>(wq16[e]);
-        wk[s] = widen1<IO>(wk16[e]);
-      }
-    }
-    if constexpr (kLayer) {
-      if (act && p.has_bias) {
-        bq[s] = widen1<IO>(bq16[e]);
-        bk[s] = widen1<IO>(bk16[e]);
-      }
-    }
     rot[s] = kRotate && e < R;
     if (neox) {
       const bool lower = e < half;
@@ -589,6 +625,11 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
       }
     };
     issue(h_begin);
+    __builtin_amdgcn_sched_barrier(0);  // the head loads leave first
+    if (!have_w) {
+      load_weights();
+      have_w = true;
+    }
 
     // cos / sin of this lane's elements at this token; the sign of the
     // partner term folded into sin
