@@ -130,7 +130,8 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
  *                    heads of one token) that a wave handles per work item;
  *                    a work item never spans two tokens. [2]
  *   unroll           head groups loaded before the first is computed: 1, 2 or 4. [2]
- *   block_waves      wavefronts per workgroup: 1..8. [4]
+ *   block_waves      wavefronts per workgroup: 1..8. [3 when a head takes at
+ *                    most 16 lanes, else 4; 4 on the element-granular kernel]
  *   max_blocks       0: one workgroup per block_waves work items, each wave
  *                    handles one item [default]; -1: a persistent grid of
  *                    (occupancy x CUs) workgroups striding over the items;

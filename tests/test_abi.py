@@ -275,10 +275,14 @@ def test_plan_run_time_head_dims(D, lanes):
 
 def test_plan_defaults():
     """Automatic launch: 2 head groups per work item, both loaded up front,
-    4 waves per workgroup."""
+    3 waves per workgroup when a head takes at most 16 lanes, else 4."""
     info = _plan(128, 128, 0)
     assert info["groups_per_item"] == 2 and info["unroll"] == 2
-    assert info["block_threads"] == 256
+    assert info["block_threads"] == 192
+    assert _plan(256, 256, 0)["block_threads"] == 256          # 32 lanes per head
+    assert _plan(64, 64, 1)["block_threads"] == 192            # 8 lanes per head
+    assert _plan(96, 96, 1)["block_threads"] == 192            # run-time head_dim, 16 lanes
+    assert _plan(128, 8, 1)["block_threads"] == 256            # NeoX 8: half a wave per head
     # head groups never mix Q and K heads: 4 Q + 4 K heads of head_dim 64 (8 per
     # wave instruction) are two half-filled groups, one work item
     tiny = _plan(64, 64, 1, Hq=4, Hkv=4)
