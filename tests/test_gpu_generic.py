@@ -187,3 +187,52 @@ def test_layernorm_sibling(D, R, neox, bias, layout):
     wl.q[...] = O.round_to_io_bits(O.decode_io(wl.q, W.BF16) + 1.5, W.BF16)
     print("case layernorm", cfg.name, layout, flush=True)
     Hn.layernorm_check(wl, R, bias, layout=layout)
+
+
+@pytest.mark.parametrize("D,R,neox,launch,want", [
+    (128, 128, True, None, dict(lanes_per_head=64, generic=0)),   # one head per group
+    (128, 64, False, None, dict(lanes_per_head=64, generic=0)),
+    (64, 64, True, None, dict(generic=1)),                        # no vectorised mapping fits
+    (128, 128, False, {"generic": 1}, dict(generic=1)),
+])
+def test_head_strides_beyond_32_bit_lane_offsets(D, R, neox, launch, want):
+    """Q heads 3 GiB apart in one device buffer: a head group of several heads
+    would need lane offsets above 2^31, so the planner takes one head per wave
+    instruction (or the element-granular kernel, whose head bases are 64-bit).
+    Every Q/K element matches the oracle and the bytes between the heads stay
+    untouched."""
+    import torch
+    from head_qk_rmsnorm_amd import binding as B
+
+    T, Hq, Hkv = 33, 2, 3
+    cfg = W.case(T, Hq, Hkv, D, R, neox, pos_dtype=W.I64, seed=D + R + 5)
+    wl = W.make_workload(cfg)
+    dev = torch.device("cuda:0")
+    hs = (3 << 30) // 2                  # head stride in elements (3 GiB)
+    fill = 0x5A5A
+    store = torch.full((hs * (Hq - 1) + T * D + 4096,), fill, dtype=torch.int16, device=dev)
+    q = torch.as_strided(store, (T, Hq, D), (D, hs, 1)).view(torch.bfloat16)
+    q.view(torch.int16).copy_(torch.from_numpy(wl.q.view(np.int16)).to(dev))
+    k = torch.from_numpy(wl.k.view(np.int16)).to(dev).view(torch.bfloat16)
+    wq = torch.from_numpy(wl.wq.view(np.int16)).to(dev).view(torch.bfloat16)
+    wk = torch.from_numpy(wl.wk.view(np.int16)).to(dev).view(torch.bfloat16)
+    cache = torch.from_numpy(wl.cache).to(dev)
+    pos = torch.from_numpy(wl.positions).to(dev)
+    print("case", cfg.name, launch, flush=True)
+    info = B.qknr_inplace_ex(q, k, wq, wk, cache, pos, is_neox=neox, eps=cfg.eps,
+                             launch=launch or {})
+    torch.cuda.synchronize()
+    for key, v in want.items():
+        assert info[key] == v, info
+    gq = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    gk = k.view(torch.int16).cpu().numpy().view(np.uint16)
+    rq, rk = Hn.oracle_ref(wl)
+    for g, r in ((gq, rq), (gk, rk)):
+        cmp = Hn.compare_bits(g, r, cfg.dtype)
+        assert cmp.bad == 0 and cmp.exact_frac >= 0.99, cmp
+    # the gap between the two heads and the tail: untouched
+    for start in (T * D, T * D + (1 << 20), hs - 4096, hs + T * D):
+        seg = store[start:start + 4096].cpu().numpy().view(np.uint16)
+        assert np.all(seg == fill), start
+    del store
+    torch.cuda.empty_cache()
