@@ -316,7 +316,7 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this op runs on one GPU; every (token, head) vector is "
                           "independent, so N GPUs would each run the same kernel on their own "
-                          "shard (see DESIGN.md). Run with --gpus 1."}), flush=True)
+                          "shard with no exchange step. Run with --gpus 1."}), flush=True)
         sys.exit(2)
     import torch
 
