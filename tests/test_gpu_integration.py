@@ -187,3 +187,72 @@ def test_torch_custom_ops_eager_and_compiled():
     assert torch.equal(se, sc)
     for x, y in zip(e.fetch(), c.fetch()):
         assert np.array_equal(x, y)
+
+
+def test_prepared_calls_equal_direct_calls():
+    """PreparedCall (arguments marshalled once, as the benchmark launches) gives
+    the same bits as the direct binding calls, for the fused op, the unfused
+    pair and the LayerNorm sibling."""
+    import torch
+    from head_qk_rmsnorm_amd import binding as B
+
+    cfg = W.case(47, 5, 3, 128, 64, True, pos_dtype=W.I64, seed=77)
+    wl = W.make_workload(cfg)
+    kw = dict(is_neox=True, eps=cfg.eps)
+    bias = (torch.linspace(-1, 1, 128, device="cuda").to(torch.bfloat16),
+            torch.linspace(1, -1, 128, device="cuda").to(torch.bfloat16))
+    cases = [
+        (lambda d: B.PreparedCall(d.q, d.k, d.wq, d.wk, d.cache, d.positions, **kw),
+         lambda d: B.qknr_inplace(d.q, d.k, d.wq, d.wk, d.cache, d.positions, **kw)),
+        (lambda d: B.PreparedCall(d.q, d.k, d.wq, d.wk, d.cache, d.positions, unfused=True, **kw),
+         lambda d: B.qknr_unfused_inplace(d.q, d.k, d.wq, d.wk, d.cache, d.positions, **kw)),
+        (lambda d: B.PreparedCall(d.q, d.k, d.wq, d.wk, d.cache, d.positions, layernorm_bias=bias,
+                                  **kw),
+         lambda d: B.qknr_layernorm_rope_inplace(d.q, d.k, d.wq, d.wk, bias[0], bias[1], d.cache,
+                                                 d.positions, **kw)),
+    ]
+    for make, direct in cases:
+        a, b = Hn.DeviceCase(wl), Hn.DeviceCase(wl)
+        call = make(a)
+        call()
+        call()  # twice in place
+        direct(b)
+        direct(b)
+        torch.cuda.synchronize()
+        for x, y in zip(a.fetch(), b.fetch()):
+            assert np.array_equal(x, y)
+
+
+def test_binding_rejects_bad_tensors_before_launching():
+    """The Python binding checks shapes, dtypes and layouts before any launch;
+    every rejection leaves q and k as they were."""
+    import torch
+    from head_qk_rmsnorm_amd import binding as B
+
+    cfg = W.case(9, 4, 2, 128, 128, False, seed=78)
+    wl = W.make_workload(cfg)
+    d = Hn.DeviceCase(wl)
+    q, k, wq, wk, cache, pos = d.q, d.k, d.wq, d.wk, d.cache, d.positions
+    bad = [
+        (ValueError, lambda: B.qknr_inplace(q[:, :, :64], k, wq, wk, cache, pos, is_neox=False)),
+        (ValueError, lambda: B.qknr_inplace(q, k[:5], wq, wk, cache, pos, is_neox=False)),
+        (ValueError, lambda: B.qknr_inplace(q[..., ::2], k[..., ::2], wq[::2], wk[::2],
+                                            cache[:, :64].contiguous(), pos, is_neox=False)),
+        (TypeError, lambda: B.qknr_inplace(q, k.half(), wq, wk, cache, pos, is_neox=False)),
+        (TypeError, lambda: B.qknr_inplace(q, k, wq.half(), wk, cache, pos, is_neox=False)),
+        (ValueError, lambda: B.qknr_inplace(q, k, wq[:64], wk, cache, pos, is_neox=False)),
+        (ValueError, lambda: B.qknr_inplace(q, k, wq, wk, cache.double(), pos, is_neox=False)),
+        (ValueError, lambda: B.qknr_inplace(q, k, wq, wk, cache, pos[:3], is_neox=False)),
+        (TypeError, lambda: B.qknr_inplace(q, k, wq, wk, cache, pos.float(), is_neox=False)),
+        (ValueError, lambda: B.qknr_inplace(q.reshape(9, 4 * 128), k, wq, wk, cache, pos,
+                                            is_neox=False)),
+        (ValueError, lambda: B.qknr_layernorm_rope_inplace(q, k, wq, wk, wq, None)),
+        (ValueError, lambda: B.PreparedCall(q, k, wq, wk, cache, pos, is_neox=False, unfused=True,
+                                            launch={"unroll": 1})),
+    ]
+    for i, (exc, fn) in enumerate(bad):
+        with pytest.raises(exc):
+            fn()
+        torch.cuda.synchronize()
+    for before, after in zip(d.storages_host, d.fetch()):
+        assert np.array_equal(before, after)
