@@ -3,12 +3,16 @@
  * no Python, no torch): reads a case file written by the test, copies the
  * inputs to the device, runs qknr_inplace on a stream of its own, copies q and
  * k back and writes them out for the test to compare with the fp64 oracle.
- * It also exercises qknr_can_use, qknr_status_string and one rejection.
+ * It then runs the same case again from the same inputs through qknr_inplace_ex
+ * with the element-granular kernel requested (qknr_launch_cfg.generic) and prints
+ * the launch report. It also exercises qknr_can_use, qknr_status_string and one
+ * rejection.
  *
  * Case file (little endian): int64 T, Hq, Hkv, head_dim, rope_dim, is_neox,
  * dtype, pos_dtype, cache_rows; float eps; then q (T*Hq*D u16), k (T*Hkv*D u16),
  * wq (D u16), wk (D u16), cache (cache_rows*R f32), positions (T i32 or i64).
- * Output file: q then k, as u16.
+ * Output file: q then k from qknr_inplace, then q and k from qknr_inplace_ex,
+ * as u16.
  * Exit status 0 on success; a message on stderr otherwise.
  */
 #include <stdio.h>
@@ -91,17 +95,44 @@ int main(int argc, char** argv) {
     return 5;
   }
   CHECK_HIP(hipStreamSynchronize(s));
-  CHECK_HIP(hipMemcpy(hq, dq, bytes_q, hipMemcpyDeviceToHost));
-  CHECK_HIP(hipMemcpy(hk, dk, bytes_k, hipMemcpyDeviceToHost));
+  char* out = (char*)malloc(2 * (bytes_q + bytes_k) + 2);
+  if (!out) return 1;
+  CHECK_HIP(hipMemcpy(out, dq, bytes_q, hipMemcpyDeviceToHost));
+  CHECK_HIP(hipMemcpy(out + bytes_q, dk, bytes_k, hipMemcpyDeviceToHost));
+
+  /* the same case from the same inputs, element-granular kernel requested */
+  CHECK_HIP(hipMemcpy(dq, hq, bytes_q, hipMemcpyHostToDevice));
+  CHECK_HIP(hipMemcpy(dk, hk, bytes_k, hipMemcpyHostToDevice));
+  qknr_launch_cfg cfg;
+  memset(&cfg, 0, sizeof cfg);
+  cfg.generic = 1;
+  qknr_launch_info info;
+  memset(&info, 0, sizeof info);
+  rc = qknr_inplace_ex(dq, dk, dwq, dwk, (const float*)dc, dp, T, (int32_t)Hq, (int32_t)Hkv,
+                       (int32_t)D, (int32_t)R, (int32_t)neox, eps, Hq * D * 2, D * 2,
+                       Hkv * D * 2, D * 2, (int32_t)dtype, (int32_t)pos_dtype, s, &cfg, &info);
+  if (rc != QKNR_OK) {
+    fprintf(stderr, "qknr_inplace_ex: %s\n", qknr_status_string(rc));
+    return 6;
+  }
+  CHECK_HIP(hipStreamSynchronize(s));
+  CHECK_HIP(hipMemcpy(out + bytes_q + bytes_k, dq, bytes_q, hipMemcpyDeviceToHost));
+  CHECK_HIP(hipMemcpy(out + 2 * bytes_q + bytes_k, dk, bytes_k, hipMemcpyDeviceToHost));
+  printf("launch: generic=%d lanes_per_head=%d elems_per_lane=%d groups_per_item=%d "
+         "block_threads=%d grid_blocks=%d items=%lld\n", info.generic, info.lanes_per_head,
+         info.elems_per_lane, info.groups_per_item, info.block_threads, info.grid_blocks,
+         (long long)info.items);
   CHECK_HIP(hipStreamDestroy(s));
   hipFree(dq); hipFree(dk); hipFree(dwq); hipFree(dwk); hipFree(dc); hipFree(dp);
 
   FILE* o = fopen(argv[2], "wb");
-  if (!o || fwrite(hq, 1, bytes_q, o) != bytes_q || fwrite(hk, 1, bytes_k, o) != bytes_k) {
+  const size_t n_out = 2 * (bytes_q + bytes_k);
+  if (!o || fwrite(out, 1, n_out, o) != n_out) {
     fprintf(stderr, "cannot write output\n");
     return 1;
   }
   fclose(o);
+  free(out);
   free(host);
   printf("qknr C ABI run ok: T=%lld Hq=%lld Hkv=%lld D=%lld R=%lld neox=%lld\n", (long long)T,
          (long long)Hq, (long long)Hkv, (long long)D, (long long)R, (long long)neox);

@@ -47,8 +47,9 @@ def _write_case(path, wl):
     W.case(23, 4, 4, 96, 96, True, seed=5),
 ], ids=lambda c: c.name)
 def test_plain_c_caller(cfg):
-    """libqknr.so driven from C through include/qknr.h only; output checked
-    against the fp64 oracle."""
+    """libqknr.so driven from C through include/qknr.h only (qknr_inplace, and
+    qknr_inplace_ex with the element-granular kernel requested); both outputs
+    checked against the fp64 oracle."""
     if not os.path.exists(CAPI_BIN):
         pytest.fail(f"{CAPI_BIN} missing: run __graft_entry__.build()")
     wl = W.make_workload(cfg)
@@ -59,13 +60,16 @@ def test_plain_c_caller(cfg):
         print(r.stdout, r.stderr, flush=True)
         assert r.returncode == 0, r.stderr
         got = np.fromfile(out, dtype=np.uint16)
-    nq = wl.q.size
-    gq = got[:nq].reshape(wl.q.shape)
-    gk = got[nq:].reshape(wl.k.shape)
+    assert "launch: generic=1 lanes_per_head=64" in r.stdout, r.stdout
+    nq, nk = wl.q.size, wl.k.size
+    assert got.size == 2 * (nq + nk)
     rq, rk = Hn.oracle_ref(wl)
-    for g, ref in ((gq, rq), (gk, rk)):
-        cmp = Hn.compare_bits(g, ref, cfg.dtype)
-        assert cmp.bad == 0 and cmp.exact_frac >= 0.99, cmp
+    for base in (0, nq + nk):  # qknr_inplace, then qknr_inplace_ex on the element kernel
+        gq = got[base:base + nq].reshape(wl.q.shape)
+        gk = got[base + nq:base + nq + nk].reshape(wl.k.shape)
+        for g, ref in ((gq, rq), (gk, rk)):
+            cmp = Hn.compare_bits(g, ref, cfg.dtype)
+            assert cmp.bad == 0 and cmp.exact_frac >= 0.99, (base, cmp)
 
 
 def test_hip_graph_capture_and_replay():
