@@ -476,3 +476,31 @@ def test_torch_custom_ops_are_registered_with_their_mutations():
     with pytest.raises(ValueError, match="HIP device"):
         torch.ops.qknr.fused_inplace_qknorm_rope(q, q.clone(), w, w, torch.zeros(4, 64),
                                                  torch.zeros(2, dtype=torch.int32), is_neox=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "dit", "gqa", "partial", "large", "gqa_tp8", "dit_hp8",
+                                  "dit_sp8"])
+def test_benchmark_workloads_plan_the_measured_launch(name):
+    """Every benchmark and shard workload, with the strides the benchmark uses
+    (contiguous or views into a fused qkv buffer), plans onto the vectorised
+    kernel with 16-byte lanes, 2 head groups per item loaded together, and 3
+    waves per workgroup (4 for the half-wave heads of head_dim 256)."""
+    from head_qk_rmsnorm_amd import workloads as W
+
+    c = W.CONFIGS[name]
+    D = c.head_dim
+    if c.layout == "qkv":
+        row = (c.Hq + 2 * c.Hkv) * D * 2
+        qt, qh, kt, kh = row, D * 2, row, D * 2
+    else:
+        qt, qh, kt, kh = c.Hq * D * 2, D * 2, c.Hkv * D * 2, D * 2
+    info = B.LaunchInfo()
+    z = P(0)
+    rc = B.lib().qknr_inplace_ex(z, z, z, z, z, z, 0, c.Hq, c.Hkv, D, c.rope_dim, int(c.is_neox),
+                                 c.eps, qt, qh, kt, kh, 0 if c.dtype == W.BF16 else 1,
+                                 0 if c.pos_dtype == W.I32 else 1, z, None, ctypes.byref(info))
+    assert rc == 0
+    i = info.as_dict()
+    assert i["generic"] == 0 and i["lanes_per_head"] == D // 8 and i["elems_per_lane"] == 8, i
+    assert i["groups_per_item"] == min(2, i["groups_per_token"]) and i["unroll"] == 2, i
+    assert i["block_threads"] == (256 if D // 8 > 16 else 192), i
