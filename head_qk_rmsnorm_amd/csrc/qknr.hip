@@ -99,6 +99,16 @@ bool lanes_fit(int32_t R, int32_t neox, int E) {
   return (R / 2) % E == 0 && R / 2 >= E;
 }
 
+// Elements per lane of a run-time head_dim instance (lane group capacity dmax):
+// 8 whenever the pairing allows it; for NeoX also 4 and 2 while the lane group
+// (dmax/E lanes) fits a wave. 0: none.
+int any_dim_lanes(int dmax, int32_t R, int32_t neox) {
+  if (lanes_fit(R, neox, 8)) return 8;
+  if (dmax / 4 <= kWave && lanes_fit(R, neox, 4)) return 4;
+  if (dmax / 2 <= kWave && lanes_fit(R, neox, 2)) return 2;
+  return 0;
+}
+
 bool rotates(int mode) { return mode == kFused || mode == kRopeOnly || mode == kLayerRope; }
 
 // The supported set (every mode, on the element-granular kernel): head_dim
@@ -121,7 +131,7 @@ bool vector_shape(int32_t D, int32_t R, int32_t neox) {
     if (lanes_fit(R, neox, 8) || lanes_fit(R, neox, D / 32)) return true;
     return D / 64 >= 2 && lanes_fit(R, neox, D / 64);
   }
-  return lanes_fit(R, neox, 8);
+  return any_dim_lanes(any_dim_capacity(D), R, neox) != 0;
 }
 
 // Head vectors of one tensor must not overlap: with the smaller of the two
@@ -203,11 +213,12 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   const bool exact = fast_head_dim(D);
   const int dmax = exact ? D : any_dim_capacity(D);
   if (!exact) {
-    // run-time head_dim: 16-byte lanes in a lane group of dmax/8 lanes
-    E = 8;
-    const int G = kWave / (dmax / 8);
-    if (!lanes_fit(R, neox, 8)) return QKNR_E_UNSUPPORTED;
-    if (c.lanes_per_head != 0 && c.lanes_per_head != dmax / 8) return QKNR_E_ARG;
+    // run-time head_dim: 16-byte lanes in a lane group of dmax/8 lanes; NeoX
+    // halves that no 16-byte lane divides take 8- or 4-byte lanes
+    E = any_dim_lanes(dmax, R, neox);
+    if (E == 0) return QKNR_E_UNSUPPORTED;
+    const int G = kWave / (dmax / E);
+    if (c.lanes_per_head != 0 && c.lanes_per_head != dmax / E) return QKNR_E_ARG;
     if (!lane_offsets_fit(G, Hq, q_head, D) || !lane_offsets_fit(G, Hkv, k_head, D))
       return QKNR_E_SHAPE;
   } else if (c.lanes_per_head == 0) {

@@ -67,40 +67,60 @@ const void* pick_lanes(int E, bool neox, bool full, int U, int mode) {
   return nullptr;
 }
 
-// Run-time head_dim instances: 16-byte lanes, lane group of DMAX/8 lanes, the
-// fused op and the LayerNorm sibling at unroll 2.
-template <class IO, int DMAX, int MODE>
+// Run-time head_dim instances, the fused op and the LayerNorm sibling at unroll
+// 2: 16-byte lanes (lane group of DMAX/8 lanes); for NeoX widths whose half no
+// 16-byte lane divides, also 8-byte and 4-byte lanes where the lane group still
+// fits a wave (DMAX/4 and DMAX/2 lanes).
+template <class IO, int DMAX, int E, int MODE>
 const void* pick_any_dim_mode(bool neox, bool full) {
-  if (neox) {
-    return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, true, 2, MODE, false>)
-                : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, false, 2, MODE, false>);
+  if constexpr (E == 8) {
+    if (!neox) {
+      return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, MODE, false>)
+                  : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, false, 2, MODE, false>);
+    }
+  } else {
+    if (!neox) return nullptr;
   }
-  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, MODE, false>)
-              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, false, 2, MODE, false>);
+  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, E, true, true, 2, MODE, false>)
+              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, E, true, false, 2, MODE, false>);
+}
+
+template <class IO, int DMAX, int E>
+const void* pick_any_dim(bool neox, bool full, int mode) {
+  switch (mode) {
+    case kFused: return pick_any_dim_mode<IO, DMAX, E, kFused>(neox, full);
+    case kLayerRope: return pick_any_dim_mode<IO, DMAX, E, kLayerRope>(neox, full);
+    case kLayerOnly:
+      if constexpr (E == 8)
+        return reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, kLayerOnly, false>);
+      return nullptr;
+    default: return nullptr;
+  }
 }
 
 template <class IO, int DMAX>
-const void* pick_any_dim(bool neox, bool full, int mode) {
-  switch (mode) {
-    case kFused: return pick_any_dim_mode<IO, DMAX, kFused>(neox, full);
-    case kLayerRope: return pick_any_dim_mode<IO, DMAX, kLayerRope>(neox, full);
-    case kLayerOnly:
-      return reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, kLayerOnly, false>);
-    default: return nullptr;
+const void* pick_any_dim_lanes(int E, bool neox, bool full, int mode) {
+  if (E == 8) return pick_any_dim<IO, DMAX, 8>(neox, full, mode);
+  if constexpr (DMAX / 4 <= kWave) {
+    if (E == 4) return pick_any_dim<IO, DMAX, 4>(neox, full, mode);
   }
+  if constexpr (DMAX / 2 <= kWave) {
+    if (E == 2) return pick_any_dim<IO, DMAX, 2>(neox, full, mode);
+  }
+  return nullptr;
 }
 
 template <class IO, int GROUP>
 const void* pick_group(int D, int E, bool neox, bool full, int U, int mode) {
   if constexpr (GROUP == 2) {
-    if (U != 2 || E != 8) return nullptr;
+    if (U != 2) return nullptr;
     switch (D) {  // D is the lane-group capacity DMAX here
-      case 16: return pick_any_dim<IO, 16>(neox, full, mode);
-      case 32: return pick_any_dim<IO, 32>(neox, full, mode);
-      case 64: return pick_any_dim<IO, 64>(neox, full, mode);
-      case 128: return pick_any_dim<IO, 128>(neox, full, mode);
-      case 256: return pick_any_dim<IO, 256>(neox, full, mode);
-      case 512: return pick_any_dim<IO, 512>(neox, full, mode);
+      case 16: return pick_any_dim_lanes<IO, 16>(E, neox, full, mode);
+      case 32: return pick_any_dim_lanes<IO, 32>(E, neox, full, mode);
+      case 64: return pick_any_dim_lanes<IO, 64>(E, neox, full, mode);
+      case 128: return pick_any_dim_lanes<IO, 128>(E, neox, full, mode);
+      case 256: return pick_any_dim_lanes<IO, 256>(E, neox, full, mode);
+      case 512: return pick_any_dim_lanes<IO, 512>(E, neox, full, mode);
       default: return nullptr;
     }
   } else {

@@ -63,12 +63,19 @@ def _vectorised(D, R, neox):
     """Shapes of the vectorised kernel (include/qknr.h), restated: head_dim a
     multiple of 8 in [16, 512]; NeoX needs rope_dim/2 to be a multiple of a
     lane width E (8 for any head_dim; also head_dim/32 and head_dim/64 >= 2 for
-    head_dim 64, 128, 256)."""
+    head_dim 64, 128, 256; also 4 and 2 for the other head_dims while the lane
+    group of capacity/E lanes fits a wave)."""
     if D % 8 or D < 16 or D > 512 or not _supported(D, R, neox):
         return False
     if not neox:
         return True
-    widths = [8] + ([D // 32] + ([D // 64] if D // 64 >= 2 else []) if D in (64, 128, 256) else [])
+    if D in (64, 128, 256):
+        widths = [8, D // 32] + ([D // 64] if D // 64 >= 2 else [])
+    else:  # lane group capacity: the next power of two >= max(16, D)
+        cap = 16
+        while cap < D:
+            cap *= 2
+        widths = [8] + ([4] if cap <= 256 else []) + ([2] if cap <= 128 else [])
     return any((R // 2) % e == 0 and R // 2 >= e for e in widths)
 
 
@@ -170,7 +177,7 @@ GENERIC = [
     dict(D=2, R=2, neox=0, qt=4 * 4, qh=4, kt=4 * 4, kh=4),
     dict(D=3, R=2, neox=1, qt=4 * 6, qh=6, kt=4 * 6, kh=6),
     dict(R=6), dict(R=98, neox=1), dict(D=64, R=2, neox=1, qt=4 * 128, qh=128, kt=4 * 128, kh=128),
-    dict(D=96, R=40, neox=1, qt=4 * 192, qh=192, kt=4 * 192, kh=192),
+    dict(D=96, R=6, neox=1, qt=4 * 192, qh=192, kt=4 * 192, kh=192),
     dict(D=512, R=510, neox=1, qt=4 * 1024, qh=1024, kt=4 * 1024, kh=1024),
     dict(q=P(A + 8)), dict(k=P(A + 2)), dict(wq=P(A + 4)), dict(wk=P(A + 8)),
     dict(qh=264, qt=4 * 264), dict(kt=4 * 256 + 8), dict(qh=258, qt=4 * 258),
@@ -273,6 +280,25 @@ def test_plan_run_time_head_dims(D, lanes):
     assert _plan(D, D - (D % 16), 1)["lanes_per_head"] == lanes
 
 
+@pytest.mark.parametrize("D,R,E", [(96, 24, 4), (80, 40, 4), (112, 56, 4), (80, 20, 2),
+                                   (72, 72, 4), (40, 12, 2), (120, 60, 2), (160, 40, 4)])
+def test_plan_run_time_head_dims_narrow_lanes(D, R, E):
+    """NeoX halves that no 16-byte lane divides take 8- or 4-byte lanes when the
+    lane group still fits a wave (e.g. head_dim 96 with rope_dim 24)."""
+    cap = 16
+    while cap < D:
+        cap *= 2
+    info = _plan(D, R, 1)
+    assert info["generic"] == 0 and info["elems_per_lane"] == E, info
+    assert info["lanes_per_head"] == cap // E and info["heads_per_wave"] == 64 // (cap // E)
+
+
+@pytest.mark.parametrize("D,R", [(200, 20), (200, 100), (320, 20), (320, 40), (96, 6), (504, 12)])
+def test_plan_run_time_head_dims_without_a_lane_width_use_the_element_kernel(D, R):
+    info = _plan(D, R, 1)
+    assert info["generic"] == 1, info
+
+
 def test_plan_defaults():
     """Automatic launch: 2 head groups per work item, both loaded up front,
     3 waves per workgroup when a head takes at most 16 lanes, else 4."""
@@ -315,9 +341,10 @@ def test_plan_element_granular():
                         grid_blocks=0, items=0, generic=1)
     big = _plan(300, 300, 1, Hq=30, Hkv=10)  # 8 slots: 2 heads in flight, 4 per item
     assert (big["elems_per_lane"], big["unroll"], big["groups_per_item"]) == (5, 2, 4)
-    small = _plan(40, 40, 1, Hq=30, Hkv=10)  # 1 slot: 16 heads in flight, 32 per item
+    small = _plan(40, 6, 1, Hq=30, Hkv=10)   # 1 slot: 16 heads in flight, 32 per item
     assert (small["elems_per_lane"], small["unroll"], small["groups_per_item"]) == (1, 16, 32)
-    assert _plan(72, 72, 1)["generic"] == 1          # NeoX half 36: no lane width divides it
+    assert _plan(72, 70, 1)["generic"] == 1          # NeoX half 35: no lane width divides it
+    assert _plan(72, 72, 1)["elems_per_lane"] == 4   # NeoX half 36: 8-byte lanes
     assert _plan(72, 72, 0)["generic"] == 0          # interleaved: 16-byte lanes
     assert _plan(130, 64, 0)["elems_per_lane"] == 3  # not a multiple of 8
     forced = _plan(128, 128, 0, cfg=B.LaunchCfg(generic=1, groups_per_item=48, block_waves=2))

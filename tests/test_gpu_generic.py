@@ -58,7 +58,13 @@ def _vectorised(D, R, neox):
         return False
     if not neox:
         return True
-    widths = [8] + ([D // 32] + ([D // 64] if D // 64 >= 2 else []) if D in (64, 128, 256) else [])
+    if D in (64, 128, 256):
+        widths = [8, D // 32] + ([D // 64] if D // 64 >= 2 else [])
+    else:  # lane group capacity: the next power of two >= max(16, D)
+        cap = 16
+        while cap < D:
+            cap *= 2
+        widths = [8] + ([4] if cap <= 256 else []) + ([2] if cap <= 128 else [])
     return any((R // 2) % e == 0 and R // 2 >= e for e in widths)
 
 
