@@ -303,15 +303,18 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   // hold first-half dims and find their partners d + R/2 at the same offsets
   // in lane + m; lanes m..2m-1 hold the second half and look m lanes down.
   // Lanes from 2m on hold pass-through dims. Lower-half lanes subtract.
+  // With rope_dim == head_dim every lane rotates: the spare lanes of a
+  // run-time head_dim compute values that are never stored, and read cos/sin
+  // column 0 so they stay inside the row.
   int partner_addr = lane << 2, j0 = 0;
   bool lower = false, lane_rot = true;
   if constexpr (NEOX) {
     const int m = half / E;
-    lane_rot = (FULL && EXACT) || li < 2 * m;
+    lane_rot = FULL || li < 2 * m;
     lower = li < m;
     if (lane_rot) {
       partner_addr = (lower ? lane + m : lane - m) << 2;
-      j0 = lower ? d0 : d0 - half;
+      j0 = !in_head ? 0 : (lower ? d0 : d0 - half);
     }
   } else {
     j0 = in_head ? d0 / 2 : 0;
@@ -462,7 +465,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
             const float a = n[2 * kk], b = n[2 * kk + 1];
             const float oa = fmaf(a, cs[kk], -(b * sn[kk]));
             const float ob = fmaf(b, cs[kk], a * sn[kk]);
-            const bool rot = (FULL && EXACT) || (d0 + 2 * kk < R);
+            const bool rot = FULL || (d0 + 2 * kk < R);
             o[2 * kk] = rot ? oa : a;
             o[2 * kk + 1] = rot ? ob : b;
           }
