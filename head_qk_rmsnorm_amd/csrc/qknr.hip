@@ -168,6 +168,18 @@ constexpr int kDefaultGroupsPerItem = 2;
 constexpr int kDefaultUnroll = 2;
 constexpr int kDefaultBlockWaves = 4;
 constexpr int kDefaultBlockWavesNarrow = 3;  // lane groups of at most 16 lanes
+// Run-time head_dim instances of the fused op with NeoX pairing whose head group
+// carries at most 768 bytes (spare lanes in the padded lane group, or few heads
+// per wave instruction) take longer work items on smaller workgroups: 4 groups
+// per item and 2 waves per workgroup. At the same bytes per launch that
+// measured faster for head_dim 24, 40, 80, 96, 160, 192 and 320 (NeoX: +2 to
+// +24%, +8-9% at 80, 160 and 320, level at 48), and slower where it is not
+// used: groups of 896 bytes (head_dim 112, 224: -2.5%), 4- or 2-element lanes
+// in lane groups of 32 or 64 lanes (-6 to -15%), interleaved pairing (-4%) and
+// the compile-time head_dims (-3.5 to -7.4%).
+constexpr int kLongItemGroupBytes = 768;
+constexpr int kLongItemGroups = 4;
+constexpr int kLongItemBlockWaves = 2;
 // element-granular kernel: heads per work item, in units of the heads it loads
 // before computing the first (16 / slots)
 constexpr int kDefaultElemRounds = 2;
@@ -246,14 +258,20 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   pl->G = kWave / pl->L;
   pl->ngq = (Hq + pl->G - 1) / pl->G;
   pl->ng = pl->ngq + (Hkv + pl->G - 1) / pl->G;
-  const int want_gpi = c.groups_per_item == 0 ? kDefaultGroupsPerItem : c.groups_per_item;
+  const bool long_items = mode == kFused && !exact && neox &&
+                          pl->G * 2 * D <= kLongItemGroupBytes && (E == 8 || pl->L <= 16);
+  const int want_gpi = c.groups_per_item != 0 ? c.groups_per_item
+                       : long_items          ? kLongItemGroups
+                                             : kDefaultGroupsPerItem;
   pl->gpi = std::max(1, std::min(want_gpi, pl->ng));
   pl->nc = (pl->ng + pl->gpi - 1) / pl->gpi;
   pl->items = T * pl->nc;
   if (pl->items > kMaxItems) return QKNR_E_SHAPE;
   pl->U = U;
   pl->wpb = c.block_waves != 0 ? c.block_waves
-                               : (pl->L <= 16 ? kDefaultBlockWavesNarrow : kDefaultBlockWaves);
+            : long_items       ? kLongItemBlockWaves
+            : pl->L <= 16      ? kDefaultBlockWavesNarrow
+                               : kDefaultBlockWaves;
   pl->max_blocks = c.max_blocks;
   pl->fn = pick_kernel(dtype, dmax, E, neox != 0, R == D, U, mode, exact);
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;

@@ -307,12 +307,37 @@ def test_plan_defaults():
     assert info["block_threads"] == 192
     assert _plan(256, 256, 0)["block_threads"] == 256          # 32 lanes per head
     assert _plan(64, 64, 1)["block_threads"] == 192            # 8 lanes per head
-    assert _plan(96, 96, 1)["block_threads"] == 192            # run-time head_dim, 16 lanes
+    assert _plan(96, 96, 0)["block_threads"] == 192            # run-time head_dim, 16 lanes
     assert _plan(128, 8, 1)["block_threads"] == 256            # NeoX 8: half a wave per head
     # head groups never mix Q and K heads: 4 Q + 4 K heads of head_dim 64 (8 per
     # wave instruction) are two half-filled groups, one work item
     tiny = _plan(64, 64, 1, Hq=4, Hkv=4)
     assert tiny["groups_per_token"] == 2 and tiny["groups_per_item"] == 2
+
+
+@pytest.mark.parametrize("D,R,long_items", [
+    (80, 80, True), (96, 96, True), (80, 32, True), (160, 160, True), (192, 64, True),
+    (320, 320, True), (48, 48, True), (40, 40, True), (24, 24, True),
+    (112, 112, False), (224, 224, False), (72, 72, False), (136, 136, False), (104, 52, False),
+    (128, 128, False), (64, 64, False), (256, 256, False)])
+def test_plan_defaults_run_time_neox(D, R, long_items):
+    """Run-time head_dims with NeoX pairing whose head group holds at most 768
+    bytes (and whose lanes hold 8 elements, or whose lane group has at most 16
+    lanes) default to 4 groups per item on 2-wave workgroups; interleaved
+    pairing, explicit settings and every other shape keep the usual defaults."""
+    info = _plan(D, R, 1)
+    assert info["generic"] == 0, info
+    G, E, L = info["heads_per_wave"], info["elems_per_lane"], info["lanes_per_head"]
+    assert long_items == (D not in (64, 128, 256) and G * 2 * D <= 768 and (E == 8 or L <= 16))
+    if long_items:
+        assert (info["groups_per_item"], info["block_threads"]) == (4, 128), info
+    else:
+        assert info["groups_per_item"] == 2, info
+        assert info["block_threads"] == (192 if L <= 16 else 256), info
+    il = _plan(D, R, 0)
+    assert il["groups_per_item"] == 2 and il["block_threads"] == (192 if il["lanes_per_head"] <= 16 else 256)
+    explicit = _plan(D, R, 1, cfg=B.LaunchCfg(groups_per_item=3, block_waves=5))
+    assert (explicit["groups_per_item"], explicit["block_threads"]) == (3, 320)
 
 
 @pytest.mark.parametrize("D,lanes,E", [(128, 64, 2), (256, 64, 4), (128, 32, 4), (64, 32, 2),
