@@ -56,18 +56,20 @@ __global__ void __launch_bounds__(256) rmw_kernel(char* buf, int64_t n, uint32_t
 }
 
 const void* pick_kernel(int dtype, int D, int E, bool neox, bool full, int U, int mode, bool exact) {
-  const int group = !exact ? 2 : (mode == kFused ? 0 : 1);
+  const int group = !exact ? (U == 4 ? 4 : 2) : (mode == kFused ? 0 : 1);
   if (dtype == QKNR_BF16) {
     switch (group) {
       case 0: return pick_group<Bf16, 0>(D, E, neox, full, U, mode);
       case 1: return pick_group<Bf16, 1>(D, E, neox, full, U, mode);
-      default: return pick_group<Bf16, 2>(D, E, neox, full, U, mode);
+      case 2: return pick_group<Bf16, 2>(D, E, neox, full, U, mode);
+      default: return pick_group<Bf16, 4>(D, E, neox, full, U, mode);
     }
   }
   switch (group) {
     case 0: return pick_group<Fp16, 0>(D, E, neox, full, U, mode);
     case 1: return pick_group<Fp16, 1>(D, E, neox, full, U, mode);
-    default: return pick_group<Fp16, 2>(D, E, neox, full, U, mode);
+    case 2: return pick_group<Fp16, 2>(D, E, neox, full, U, mode);
+    default: return pick_group<Fp16, 4>(D, E, neox, full, U, mode);
   }
 }
 
@@ -168,16 +170,17 @@ constexpr int kDefaultGroupsPerItem = 2;
 constexpr int kDefaultUnroll = 2;
 constexpr int kDefaultBlockWaves = 4;
 constexpr int kDefaultBlockWavesNarrow = 3;  // lane groups of at most 16 lanes
-// Run-time head_dim instances of the fused op with NeoX pairing whose head group
-// carries at most 768 bytes (spare lanes in the padded lane group, or few heads
-// per wave instruction) take longer work items on smaller workgroups: 4 groups
-// per item and 2 waves per workgroup. At the same bytes per launch that
-// measured faster for head_dim 24, 40, 80, 96, 160, 192 and 320 (NeoX: +2 to
-// +24%, +8-9% at 80, 160 and 320, level at 48), and slower where it is not
-// used: groups of 896 bytes (head_dim 112, 224: -2.5%), 4- or 2-element lanes
-// in lane groups of 32 or 64 lanes (-6 to -15%), interleaved pairing (-4%) and
-// the compile-time head_dims (-3.5 to -7.4%).
-constexpr int kLongItemGroupBytes = 768;
+// Run-time head_dim instances of the fused op take longer work items with NeoX
+// pairing, or when a head group holds at most 640 bytes (spare lanes in the
+// padded lane group, or few heads per wave instruction): 4 head groups loaded
+// together (unroll 4), 4 groups per item, 2 waves per workgroup. At the same
+// bytes per launch that measured faster on every run-time NeoX shape (head_dim
+// 24-320: +2.5 to +33%, the most with 8-byte lanes) and on interleaved groups of
+// at most 640 bytes (head_dim 40, 80, 144, 160, 320: +1 to +8%); interleaved
+// groups of 768-896 bytes lose 1.4-3.4% with it, and the compile-time head_dims
+// 3.5-7.4% (4 groups per item at unroll 2), so they keep the usual defaults.
+constexpr int kLongItemGroupBytes = 640;
+constexpr int kLongItemUnroll = 4;
 constexpr int kLongItemGroups = 4;
 constexpr int kLongItemBlockWaves = 2;
 // element-granular kernel: heads per work item, in units of the heads it loads
@@ -246,20 +249,25 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
     if (E != 8 && E != D / 32 && !(E == D / 64 && E >= 2)) return QKNR_E_ARG;
     if (!lanes_fit(R, neox, E) || !fits(E)) return QKNR_E_ARG;
   }
-  // the unfused baseline steps and the run-time head_dim instances exist at unroll 2 only
-  const int U = (mode != kFused || !exact) ? 2 : (c.unroll == 0 ? kDefaultUnroll : c.unroll);
+  const int L = dmax / E, G = kWave / L;
+  const bool long_items =
+      mode == kFused && !exact && (neox || G * 2 * D <= kLongItemGroupBytes);
+  // the unfused baseline steps and the LayerNorm sibling exist at unroll 2;
+  // the run-time head_dims of the fused op at unroll 2 and 4 (1 runs as 2)
+  int U = 2;
+  if (mode == kFused && exact) U = c.unroll == 0 ? kDefaultUnroll : c.unroll;
+  if (mode == kFused && !exact && (c.unroll == 4 || (c.unroll == 0 && long_items)))
+    U = kLongItemUnroll;
 
   pl->elem = false;
   pl->lds = 0;
   pl->E = E;
-  pl->L = dmax / E;
+  pl->L = L;
   pl->dmax = dmax;
   pl->exact = exact;
-  pl->G = kWave / pl->L;
+  pl->G = G;
   pl->ngq = (Hq + pl->G - 1) / pl->G;
   pl->ng = pl->ngq + (Hkv + pl->G - 1) / pl->G;
-  const bool long_items = mode == kFused && !exact && neox &&
-                          pl->G * 2 * D <= kLongItemGroupBytes && (E == 8 || pl->L <= 16);
   const int want_gpi = c.groups_per_item != 0 ? c.groups_per_item
                        : long_items          ? kLongItemGroups
                                              : kDefaultGroupsPerItem;

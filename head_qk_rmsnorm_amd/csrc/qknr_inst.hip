@@ -1,9 +1,10 @@
 // qknr_inst.hip -- one instance group of the fused QK RMSNorm + RoPE kernel
 // table (see qknr_device.h). Built once per (I/O type, group) with
-// -DQKNR_INST_IO=Bf16|Fp16 -DQKNR_INST_GROUP=0|1|2|3, so the groups compile in
-// parallel; the host library (qknr.hip) calls pick_group<IO, GROUP> (groups
-// 0-2, the vectorised kernel) and pick_elem<IO> (group 3, the element-granular
-// kernel).
+// -DQKNR_INST_IO=Bf16|Fp16 -DQKNR_INST_GROUP=0..4, so the groups compile in
+// parallel; the host library (qknr.hip) calls pick_group<IO, GROUP> (the
+// vectorised kernel: group 0 the fused op at head_dim 64/128/256, group 1 the
+// other modes there, groups 2 and 4 the run-time head_dims at unroll 2 and 4)
+// and pick_elem<IO> (group 3, the element-granular kernel).
 
 #include "qknr_device.h"
 
@@ -11,7 +12,7 @@
 #error "build with -DQKNR_INST_IO=Bf16 or Fp16"
 #endif
 #ifndef QKNR_INST_GROUP
-#error "build with -DQKNR_INST_GROUP=0, 1, 2 or 3"
+#error "build with -DQKNR_INST_GROUP=0, 1, 2, 3 or 4"
 #endif
 
 namespace qknr_impl {
@@ -67,60 +68,61 @@ const void* pick_lanes(int E, bool neox, bool full, int U, int mode) {
   return nullptr;
 }
 
-// Run-time head_dim instances, the fused op and the LayerNorm sibling at unroll
-// 2: 16-byte lanes (lane group of DMAX/8 lanes); for NeoX widths whose half no
-// 16-byte lane divides, also 8-byte and 4-byte lanes where the lane group still
-// fits a wave (DMAX/4 and DMAX/2 lanes).
-template <class IO, int DMAX, int E, int MODE>
+// Run-time head_dim instances: the fused op at unroll UU (2 or 4), the
+// LayerNorm sibling at unroll 2. 16-byte lanes (lane group of DMAX/8 lanes);
+// for NeoX widths whose half no 16-byte lane divides, also 8-byte and 4-byte
+// lanes where the lane group still fits a wave (DMAX/4 and DMAX/2 lanes).
+template <class IO, int DMAX, int E, int MODE, int UU>
 const void* pick_any_dim_mode(bool neox, bool full) {
   if constexpr (E == 8) {
     if (!neox) {
-      return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, MODE, false>)
-                  : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, false, 2, MODE, false>);
+      return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, UU, MODE, false>)
+                  : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, false, UU, MODE, false>);
     }
   } else {
     if (!neox) return nullptr;
   }
-  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, E, true, true, 2, MODE, false>)
-              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, E, true, false, 2, MODE, false>);
+  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, E, true, true, UU, MODE, false>)
+              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, E, true, false, UU, MODE, false>);
 }
 
-template <class IO, int DMAX, int E>
+template <class IO, int DMAX, int E, int UU>
 const void* pick_any_dim(bool neox, bool full, int mode) {
-  switch (mode) {
-    case kFused: return pick_any_dim_mode<IO, DMAX, E, kFused>(neox, full);
-    case kLayerRope: return pick_any_dim_mode<IO, DMAX, E, kLayerRope>(neox, full);
-    case kLayerOnly:
-      if constexpr (E == 8)
+  if (mode == kFused) return pick_any_dim_mode<IO, DMAX, E, kFused, UU>(neox, full);
+  if constexpr (UU == 2) {
+    if (mode == kLayerRope) return pick_any_dim_mode<IO, DMAX, E, kLayerRope, 2>(neox, full);
+    if constexpr (E == 8) {
+      if (mode == kLayerOnly)
         return reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, kLayerOnly, false>);
-      return nullptr;
-    default: return nullptr;
+    }
   }
+  return nullptr;
 }
 
-template <class IO, int DMAX>
+template <class IO, int DMAX, int UU>
 const void* pick_any_dim_lanes(int E, bool neox, bool full, int mode) {
-  if (E == 8) return pick_any_dim<IO, DMAX, 8>(neox, full, mode);
+  if (E == 8) return pick_any_dim<IO, DMAX, 8, UU>(neox, full, mode);
   if constexpr (DMAX / 4 <= kWave) {
-    if (E == 4) return pick_any_dim<IO, DMAX, 4>(neox, full, mode);
+    if (E == 4) return pick_any_dim<IO, DMAX, 4, UU>(neox, full, mode);
   }
   if constexpr (DMAX / 2 <= kWave) {
-    if (E == 2) return pick_any_dim<IO, DMAX, 2>(neox, full, mode);
+    if (E == 2) return pick_any_dim<IO, DMAX, 2, UU>(neox, full, mode);
   }
   return nullptr;
 }
 
 template <class IO, int GROUP>
 const void* pick_group(int D, int E, bool neox, bool full, int U, int mode) {
-  if constexpr (GROUP == 2) {
-    if (U != 2) return nullptr;
+  if constexpr (GROUP == 2 || GROUP == 4) {
+    constexpr int UU = GROUP == 2 ? 2 : 4;
+    if (U != UU) return nullptr;
     switch (D) {  // D is the lane-group capacity DMAX here
-      case 16: return pick_any_dim_lanes<IO, 16>(E, neox, full, mode);
-      case 32: return pick_any_dim_lanes<IO, 32>(E, neox, full, mode);
-      case 64: return pick_any_dim_lanes<IO, 64>(E, neox, full, mode);
-      case 128: return pick_any_dim_lanes<IO, 128>(E, neox, full, mode);
-      case 256: return pick_any_dim_lanes<IO, 256>(E, neox, full, mode);
-      case 512: return pick_any_dim_lanes<IO, 512>(E, neox, full, mode);
+      case 16: return pick_any_dim_lanes<IO, 16, UU>(E, neox, full, mode);
+      case 32: return pick_any_dim_lanes<IO, 32, UU>(E, neox, full, mode);
+      case 64: return pick_any_dim_lanes<IO, 64, UU>(E, neox, full, mode);
+      case 128: return pick_any_dim_lanes<IO, 128, UU>(E, neox, full, mode);
+      case 256: return pick_any_dim_lanes<IO, 256, UU>(E, neox, full, mode);
+      case 512: return pick_any_dim_lanes<IO, 512, UU>(E, neox, full, mode);
       default: return nullptr;
     }
   } else {

@@ -130,14 +130,15 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
  *                    the lane-offset limit; none: the element-granular kernel]
  *   groups_per_item  head groups (one per wave instruction: 64/lanes_per_head
  *                    heads of one token) that a wave handles per work item;
- *                    a work item never spans two tokens. [2; 4 for NeoX
- *                    pairing on a head_dim other than 64/128/256 whose head
- *                    group holds at most 768 bytes, unless its lanes hold
- *                    fewer than 8 elements in a lane group of over 16 lanes]
- *   unroll           head groups loaded before the first is computed: 1, 2 or 4. [2]
+ *                    a work item never spans two tokens. [2; 4 for "long
+ *                    items": a head_dim other than 64/128/256 with NeoX
+ *                    pairing, or whose head group holds at most 640 bytes]
+ *   unroll           head groups loaded before the first is computed: 1, 2 or 4.
+ *                    [2; 4 for long items] A head_dim other than 64/128/256
+ *                    runs at 2 or 4 (1 runs as 2).
  *   block_waves      wavefronts per workgroup: 1..8. [3 when a head takes at
- *                    most 16 lanes, else 4; 2 where groups_per_item defaults
- *                    to 4; 4 on the element-granular kernel]
+ *                    most 16 lanes, else 4; 2 for long items; 4 on the
+ *                    element-granular kernel]
  *   max_blocks       0: one workgroup per block_waves work items, each wave
  *                    handles one item [default]; -1: a persistent grid of
  *                    (occupancy x CUs) workgroups striding over the items;

@@ -276,7 +276,9 @@ def test_plan_run_time_head_dims(D, lanes):
     """Other head_dims use 16-byte lanes in a lane group padded to a power of two."""
     info = _plan(D, D, 0)
     assert (info["lanes_per_head"], info["elems_per_lane"]) == (lanes, 8)
-    assert info["heads_per_wave"] == 64 // lanes and info["unroll"] == 2
+    G = 64 // lanes
+    assert info["heads_per_wave"] == G
+    assert info["unroll"] == (4 if G * 2 * D <= 640 else 2)   # long items: small head groups
     assert _plan(D, D - (D % 16), 1)["lanes_per_head"] == lanes
 
 
@@ -315,29 +317,36 @@ def test_plan_defaults():
     assert tiny["groups_per_token"] == 2 and tiny["groups_per_item"] == 2
 
 
-@pytest.mark.parametrize("D,R,long_items", [
-    (80, 80, True), (96, 96, True), (80, 32, True), (160, 160, True), (192, 64, True),
-    (320, 320, True), (48, 48, True), (40, 40, True), (24, 24, True),
-    (112, 112, False), (224, 224, False), (72, 72, False), (136, 136, False), (104, 52, False),
-    (128, 128, False), (64, 64, False), (256, 256, False)])
-def test_plan_defaults_run_time_neox(D, R, long_items):
-    """Run-time head_dims with NeoX pairing whose head group holds at most 768
-    bytes (and whose lanes hold 8 elements, or whose lane group has at most 16
-    lanes) default to 4 groups per item on 2-wave workgroups; interleaved
-    pairing, explicit settings and every other shape keep the usual defaults."""
-    info = _plan(D, R, 1)
+@pytest.mark.parametrize("D,R,neox,long_items", [
+    (80, 80, 1, True), (96, 96, 1, True), (80, 32, 1, True), (160, 160, 1, True),
+    (192, 64, 1, True), (320, 320, 1, True), (48, 48, 1, True), (40, 40, 1, True),
+    (24, 24, 1, True), (112, 112, 1, True), (224, 224, 1, True), (72, 72, 1, True),
+    (136, 136, 1, True), (104, 52, 1, True),
+    (40, 40, 0, True), (80, 80, 0, True), (144, 144, 0, True), (160, 160, 0, True),
+    (320, 320, 0, True), (24, 24, 0, False), (48, 48, 0, False), (56, 56, 0, False),
+    (96, 96, 0, False), (112, 112, 0, False), (192, 192, 0, False), (200, 200, 0, False),
+    (128, 128, 1, False), (64, 64, 1, False), (256, 256, 1, False), (128, 128, 0, False)])
+def test_plan_defaults_long_items(D, R, neox, long_items):
+    """Head_dims other than 64/128/256 default to long work items (unroll 4,
+    4 groups per item, 2-wave workgroups) with NeoX pairing or when a head group
+    holds at most 640 bytes; every other shape keeps unroll 2, 2 groups per
+    item and 3 or 4 waves. Explicit settings are honoured; a run-time head_dim
+    runs unroll 1 as 2."""
+    info = _plan(D, R, neox)
     assert info["generic"] == 0, info
-    G, E, L = info["heads_per_wave"], info["elems_per_lane"], info["lanes_per_head"]
-    assert long_items == (D not in (64, 128, 256) and G * 2 * D <= 768 and (E == 8 or L <= 16))
+    G, L = info["heads_per_wave"], info["lanes_per_head"]
+    assert long_items == (D not in (64, 128, 256) and (neox == 1 or G * 2 * D <= 640))
     if long_items:
-        assert (info["groups_per_item"], info["block_threads"]) == (4, 128), info
+        assert (info["unroll"], info["groups_per_item"], info["block_threads"]) == (4, 4, 128), info
     else:
-        assert info["groups_per_item"] == 2, info
+        assert (info["unroll"], info["groups_per_item"]) == (2, 2), info
         assert info["block_threads"] == (192 if L <= 16 else 256), info
-    il = _plan(D, R, 0)
-    assert il["groups_per_item"] == 2 and il["block_threads"] == (192 if il["lanes_per_head"] <= 16 else 256)
-    explicit = _plan(D, R, 1, cfg=B.LaunchCfg(groups_per_item=3, block_waves=5))
-    assert (explicit["groups_per_item"], explicit["block_threads"]) == (3, 320)
+    explicit = _plan(D, R, neox, cfg=B.LaunchCfg(groups_per_item=3, block_waves=5, unroll=2))
+    assert (explicit["unroll"], explicit["groups_per_item"], explicit["block_threads"]) == (2, 3, 320)
+    four = _plan(D, R, neox, cfg=B.LaunchCfg(unroll=4))
+    assert four["unroll"] == 4
+    one = _plan(D, R, neox, cfg=B.LaunchCfg(unroll=1))
+    assert one["unroll"] == (1 if D in (64, 128, 256) else 2)
 
 
 @pytest.mark.parametrize("D,lanes,E", [(128, 64, 2), (256, 64, 4), (128, 32, 4), (64, 32, 2),

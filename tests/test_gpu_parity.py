@@ -129,6 +129,28 @@ def test_run_time_head_dim_layouts(layout, D, R, neox):
     Hn.run_and_check(W.make_workload(cfg), layout=layout)
 
 
+RT_LAUNCHES = [
+    dict(unroll=2), dict(unroll=4), dict(unroll=1, groups_per_item=3),
+    dict(unroll=4, groups_per_item=1), dict(unroll=4, groups_per_item=3),
+    dict(unroll=4, groups_per_item=5, block_waves=1), dict(unroll=4, max_blocks=-1),
+    dict(unroll=2, groups_per_item=4, block_waves=2), dict(unroll=4, groups_per_item=9, max_blocks=5),
+]
+
+
+@pytest.mark.parametrize("launch", RT_LAUNCHES, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+@pytest.mark.parametrize("D,R,neox", [(80, 80, False), (96, 96, True), (72, 72, True), (104, 52, True),
+                                      (40, 40, False), (160, 64, True), (320, 320, False)])
+def test_run_time_launch_variants(launch, D, R, neox):
+    """Run-time head_dims at unroll 2 and 4 (1 runs as 2), with work items that
+    end inside an unrolled batch of head groups and Q/K straddling items."""
+    cfg = W.case(29, 7, 3, D, R, neox, dtype=W.FP16, pos_dtype=W.I32, seed=D + 3 * R)
+    _say("case", cfg.name, launch)
+    Hn.run_and_check(W.make_workload(cfg), launch=launch)
+    dc = Hn.DeviceCase(W.make_workload(cfg))
+    info = dc.run(launch=launch)
+    assert info["unroll"] == (4 if launch.get("unroll") == 4 else 2), info
+
+
 # ---------------------------------------------------------------------------
 # Launch configurations (all must give the same, correct result)
 # ---------------------------------------------------------------------------
