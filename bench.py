@@ -49,7 +49,8 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed launches before the timed ones (1000 lets the clocks settle)")
     ap.add_argument("--config", default="dit",
                     help="tiny | dit | gqa | partial | large, or a one-GPU shard: gqa_tp8 | "
                          "dit_hp8 | dit_sp8")
@@ -66,6 +67,13 @@ def parse():
     ap.add_argument("--all-configs", action="store_true", help="also time every workload")
     ap.add_argument("--shards", action="store_true",
                     help="also time the one-GPU shard workloads (gqa_tp8, dit_hp8, dit_sp8)")
+    ap.add_argument("--case", default="",
+                    help="JSON keyword arguments of workloads.case (T, Hq, Hkv, head_dim, "
+                         "rope_dim, is_neox, dtype, pos_dtype, ...): time that shape instead "
+                         "of --config")
+    ap.add_argument("--head-dim-scan", action="store_true",
+                    help="also time head_dims other than 128 at the DiT workload's bytes per "
+                         "launch (24+24 heads, int64 positions), automatic launch")
     ap.add_argument("--extra-out", default="", help="file for per-config / sweep JSON lines")
     return ap.parse_args()
 
@@ -294,6 +302,26 @@ def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None, want_unfu
     return out
 
 
+# (head_dim, rope_dim, NeoX) shapes of the head_dim scan: the compile-time 128
+# for reference, run-time head_dims with 16-byte lanes, NeoX halves that need
+# 8-byte lanes (72, 88, 136, and 96 with rope_dim 24), and small heads.
+HEAD_DIM_SCAN = [(128, 128, False), (128, 128, True), (96, 96, False), (96, 96, True),
+                 (80, 80, False), (80, 80, True), (112, 112, False), (112, 112, True),
+                 (160, 160, False), (160, 160, True), (192, 192, False), (192, 192, True),
+                 (40, 40, False), (40, 40, True), (72, 72, True), (88, 88, True),
+                 (136, 136, True), (96, 24, True)]
+
+
+def head_dim_scan_case(D, R, neox):
+    """24+24 heads and as many tokens as give the DiT workload's Q/K bytes
+    (4608 tokens at head_dim 128); int64 positions drawn uniformly from a cache of
+    T rows."""
+    from head_qk_rmsnorm_amd import workloads as W
+
+    T = int(4608 * 128 / D)
+    return W.case(T, 24, 24, D, R, neox, pos_dtype=W.I64, seed=D + R, cache_rows=T)
+
+
 SWEEP = [
     dict(), dict(unroll=1), dict(unroll=4),
     dict(groups_per_item=1), dict(groups_per_item=2), dict(groups_per_item=3), dict(groups_per_item=4),
@@ -328,7 +356,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     launch = json.loads(args.launch) if args.launch else None
-    cfg = W.CONFIGS[args.config]
+    cfg = W.case(**json.loads(args.case)) if args.case else W.CONFIGS[args.config]
     extra = open(args.extra_out, "a") if args.extra_out else None
 
     calib = calibration_copy(dev)
@@ -362,6 +390,18 @@ def main():
                 msg += (f", unfused pair {r['unfused']['ms_per_step'] * 1e3:.2f} us "
                         f"(fused {r['unfused']['speedup_fused_over_unfused']:.2f}x faster)")
             print(msg, file=sys.stderr, flush=True)
+            if extra:
+                extra.write(json.dumps(r) + "\n")
+                extra.flush()
+
+    if args.head_dim_scan:
+        for D, R, neox in HEAD_DIM_SCAN:
+            c = head_dim_scan_case(D, R, neox)
+            r = measure(c, dev, args.steps, args.warmup, None, want_yard=False,
+                        want_unfused=False, op=args.op)
+            r["scan"] = {"head_dim": D, "rope_dim": R, "pairing": "neox" if neox else "interleaved"}
+            print(f"[bench] scan {c.name}: {r['GB_s']:.1f} GB/s, launch {r['launch']}",
+                  file=sys.stderr, flush=True)
             if extra:
                 extra.write(json.dumps(r) + "\n")
                 extra.flush()

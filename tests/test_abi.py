@@ -565,3 +565,18 @@ def test_benchmark_workloads_plan_the_measured_launch(name):
     assert i["generic"] == 0 and i["lanes_per_head"] == D // 8 and i["elems_per_lane"] == 8, i
     assert i["groups_per_item"] == min(2, i["groups_per_token"]) and i["unroll"] == 2, i
     assert i["block_threads"] == (256 if D // 8 > 16 else 192), i
+
+
+def test_head_dim_scan_shapes_are_vectorised():
+    """Every shape of bench.py's head_dim scan runs on the vectorised kernel and
+    moves the DiT workload's Q/K bytes to within one token row."""
+    import bench
+    from head_qk_rmsnorm_amd import workloads as W
+
+    dit = W.CONFIGS["dit"]
+    for D, R, neox in bench.HEAD_DIM_SCAN:
+        c = bench.head_dim_scan_case(D, R, neox)
+        assert (c.head_dim, c.rope_dim, c.is_neox, c.Hq, c.Hkv) == (D, R, neox, 24, 24)
+        assert abs(c.units * D - dit.units * dit.head_dim) <= 48 * D
+        info = _plan(D, R, neox)
+        assert info["generic"] == 0, (D, R, neox, info)
