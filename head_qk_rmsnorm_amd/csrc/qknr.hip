@@ -55,21 +55,22 @@ __global__ void __launch_bounds__(256) rmw_kernel(char* buf, int64_t n, uint32_t
   }
 }
 
-const void* pick_kernel(int dtype, int D, int E, bool neox, bool full, int U, int mode, bool exact) {
+const void* pick_kernel(int dtype, int D, int E, bool neox, bool full, int U, int mode, bool exact,
+                        int shift) {
   const int group = !exact ? (U == 4 ? 4 : 2) : (mode == kFused ? 0 : 1);
   if (dtype == QKNR_BF16) {
     switch (group) {
-      case 0: return pick_group<Bf16, 0>(D, E, neox, full, U, mode);
-      case 1: return pick_group<Bf16, 1>(D, E, neox, full, U, mode);
-      case 2: return pick_group<Bf16, 2>(D, E, neox, full, U, mode);
-      default: return pick_group<Bf16, 4>(D, E, neox, full, U, mode);
+      case 0: return pick_group<Bf16, 0>(D, E, neox, full, U, mode, shift);
+      case 1: return pick_group<Bf16, 1>(D, E, neox, full, U, mode, shift);
+      case 2: return pick_group<Bf16, 2>(D, E, neox, full, U, mode, shift);
+      default: return pick_group<Bf16, 4>(D, E, neox, full, U, mode, shift);
     }
   }
   switch (group) {
-    case 0: return pick_group<Fp16, 0>(D, E, neox, full, U, mode);
-    case 1: return pick_group<Fp16, 1>(D, E, neox, full, U, mode);
-    case 2: return pick_group<Fp16, 2>(D, E, neox, full, U, mode);
-    default: return pick_group<Fp16, 4>(D, E, neox, full, U, mode);
+    case 0: return pick_group<Fp16, 0>(D, E, neox, full, U, mode, shift);
+    case 1: return pick_group<Fp16, 1>(D, E, neox, full, U, mode, shift);
+    case 2: return pick_group<Fp16, 2>(D, E, neox, full, U, mode, shift);
+    default: return pick_group<Fp16, 4>(D, E, neox, full, U, mode, shift);
   }
 }
 
@@ -101,11 +102,23 @@ bool lanes_fit(int32_t R, int32_t neox, int E) {
   return (R / 2) % E == 0 && R / 2 >= E;
 }
 
+// The fused op also pairs NeoX halves of 8m + 4 dims on 16-byte lanes: each
+// partner sits 4 slots over in one of two neighbouring lanes (SHIFT 4).
+bool shift4_fits(int mode, int32_t R, int32_t neox) {
+  return mode == kFused && neox && (R / 2) % 8 == 4;
+}
+
+// Partner slot shift of a lane mapping with E elements per lane: 0, or 4 where
+// only the shifted pairing fits.
+int lane_shift(int mode, int32_t R, int32_t neox, int E) {
+  return (E == 8 && !lanes_fit(R, neox, 8) && shift4_fits(mode, R, neox)) ? 4 : 0;
+}
+
 // Elements per lane of a run-time head_dim instance (lane group capacity dmax):
-// 8 whenever the pairing allows it; for NeoX also 4 and 2 while the lane group
-// (dmax/E lanes) fits a wave. 0: none.
-int any_dim_lanes(int dmax, int32_t R, int32_t neox) {
-  if (lanes_fit(R, neox, 8)) return 8;
+// 8 whenever the pairing allows it (shifted partners included); for NeoX also
+// 4 and 2 while the lane group (dmax/E lanes) fits a wave. 0: none.
+int any_dim_lanes(int mode, int dmax, int32_t R, int32_t neox) {
+  if (lanes_fit(R, neox, 8) || shift4_fits(mode, R, neox)) return 8;
   if (dmax / 4 <= kWave && lanes_fit(R, neox, 4)) return 4;
   if (dmax / 2 <= kWave && lanes_fit(R, neox, 2)) return 2;
   return 0;
@@ -120,20 +133,21 @@ bool elem_supported(int mode, int32_t D, int32_t R) {
   return !rotates(mode) || (R >= 2 && R <= D && R % 2 == 0);
 }
 
-// Shapes of the vectorised kernel: the page's rule (head_dim 64/128/256,
-// rope_dim a multiple of head_dim/32, NeoX rotary lanes a power of two)
-// widened to every even rope_dim for interleaved pairing, every NeoX rope_dim
-// whose half is a multiple of some lane width, and other head_dims that are
-// multiples of 8.
-bool vector_shape(int32_t D, int32_t R, int32_t neox) {
+// Shapes of the vectorised kernel in a mode: the page's rule (head_dim
+// 64/128/256, rope_dim a multiple of head_dim/32, NeoX rotary lanes a power of
+// two) widened to every even rope_dim for interleaved pairing, every NeoX
+// rope_dim whose half is a multiple of some lane width (or, for the fused op,
+// 4 more than a multiple of 8), and other head_dims that are multiples of 8.
+bool vector_shape(int mode, int32_t D, int32_t R, int32_t neox) {
   if (!fast_head_dim(D) && !any_head_dim(D)) return false;
   if (R <= 0 || R > D || R % 2) return false;
   if (!neox) return true;
   if (fast_head_dim(D)) {
-    if (lanes_fit(R, neox, 8) || lanes_fit(R, neox, D / 32)) return true;
+    if (lanes_fit(R, neox, 8) || shift4_fits(mode, R, neox) || lanes_fit(R, neox, D / 32))
+      return true;
     return D / 64 >= 2 && lanes_fit(R, neox, D / 64);
   }
-  return any_dim_lanes(any_dim_capacity(D), R, neox) != 0;
+  return any_dim_lanes(mode, any_dim_capacity(D), R, neox) != 0;
 }
 
 // Head vectors of one tensor must not overlap: with the smaller of the two
@@ -199,6 +213,7 @@ struct Plan {
   int dmax = 0;        // head_dim of the instance (lane-group capacity)
   bool exact = true;   // head_dim == dmax
   bool elem = false;   // element-granular kernel (G = 1: a group is one head)
+  int shift = 0;       // NeoX partner slot shift (0 or 4)
   size_t lds = 0;      // dynamic LDS bytes per workgroup
 };
 
@@ -230,7 +245,7 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   if (!exact) {
     // run-time head_dim: 16-byte lanes in a lane group of dmax/8 lanes; NeoX
     // halves that no 16-byte lane divides take 8- or 4-byte lanes
-    E = any_dim_lanes(dmax, R, neox);
+    E = any_dim_lanes(mode, dmax, R, neox);
     if (E == 0) return QKNR_E_UNSUPPORTED;
     const int G = kWave / (dmax / E);
     if (c.lanes_per_head != 0 && c.lanes_per_head != dmax / E) return QKNR_E_ARG;
@@ -240,14 +255,16 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
     // 16-byte lanes first; then half a wave and a full wave per head
     const int cand[3] = {8, D / 32, D / 64};
     for (int e : cand) {
-      if (e >= 2 && lanes_fit(R, neox, e) && fits(e)) { E = e; break; }
+      const bool pairs = lanes_fit(R, neox, e) || (e == 8 && shift4_fits(mode, R, neox));
+      if (e >= 2 && pairs && fits(e)) { E = e; break; }
     }
     if (E == 0) return QKNR_E_SHAPE;
   } else {
     if (c.lanes_per_head > kWave || D % c.lanes_per_head != 0) return QKNR_E_ARG;
     E = D / c.lanes_per_head;
     if (E != 8 && E != D / 32 && !(E == D / 64 && E >= 2)) return QKNR_E_ARG;
-    if (!lanes_fit(R, neox, E) || !fits(E)) return QKNR_E_ARG;
+    if (!(lanes_fit(R, neox, E) || (E == 8 && shift4_fits(mode, R, neox))) || !fits(E))
+      return QKNR_E_ARG;
   }
   const int L = dmax / E, G = kWave / L;
   const bool long_items =
@@ -261,6 +278,7 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
 
   pl->elem = false;
   pl->lds = 0;
+  pl->shift = lane_shift(mode, R, neox, E);
   pl->E = E;
   pl->L = L;
   pl->dmax = dmax;
@@ -281,7 +299,7 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
             : pl->L <= 16      ? kDefaultBlockWavesNarrow
                                : kDefaultBlockWaves;
   pl->max_blocks = c.max_blocks;
-  pl->fn = pick_kernel(dtype, dmax, E, neox != 0, R == D, U, mode, exact);
+  pl->fn = pick_kernel(dtype, dmax, E, neox != 0, R == D, U, mode, exact, pl->shift);
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
 }
 
@@ -292,6 +310,7 @@ int32_t make_elem_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, 
                        int32_t dtype, const qknr_launch_cfg& c, Plan* pl) {
   const int H = Hq + Hkv;
   pl->elem = true;
+  pl->shift = 0;
   int slots = 1;
   while (slots * kWave < D) slots *= 2;
   const int U = 2 * kElemSlots / slots;
@@ -416,7 +435,7 @@ int32_t prepare(int mode, const Call& c, const qknr_launch_cfg* cfg, Plan* pl,
   }
 
   const bool vector = !lc.generic && vec_aligned && vector_mode(mode, c.D) &&
-                      vector_shape(c.D, c.R, c.neox);
+                      vector_shape(mode, c.D, c.R, c.neox);
   int32_t rc = QKNR_E_UNSUPPORTED;
   if (vector) {
     rc = make_plan(mode, c.T, c.Hq, c.Hkv, c.D, c.R, c.neox, c.dtype, c.qh, c.kh, lc, pl);

@@ -244,7 +244,10 @@ enum : int { kFused = 0, kNormOnly = 1, kRopeOnly = 2, kLayerRope = 3, kLayerOnl
 // DMAX is the head_dim the instance is built for. EXACT instances have
 // head_dim == DMAX; the others take any multiple of E up to DMAX at run time
 // (each head keeps a lane group of DMAX/E lanes, the spare ones masked).
-template <class IO, int DMAX, int E, bool NEOX, bool FULL, int U, int MODE, bool EXACT>
+// SHIFT 4 (NeoX, 8 elements per lane): rope_dim/2 is 4 more than a multiple of
+// 8, so a partner sits 4 slots over in one of two neighbouring lanes.
+template <class IO, int DMAX, int E, bool NEOX, bool FULL, int U, int MODE, bool EXACT,
+          int SHIFT = 0>
 __global__ void __launch_bounds__(kMaxBlockWaves * kWave)
 qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict__ wqp,
             const void* __restrict__ wkp, const float* __restrict__ cache,
@@ -255,6 +258,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   constexpr int NV = E / 2;     // packed dwords per lane
   constexpr int NCS = NEOX ? E : E / 2;  // cos (and sin) values per lane
   static_assert(DMAX % E == 0 && E % 2 == 0 && G >= 1, "lane mapping");
+  static_assert(SHIFT == 0 || (SHIFT == 4 && NEOX && E == 8), "partner slot shift");
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
@@ -308,7 +312,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   // column 0 so they stay inside the row.
   int partner_addr = lane << 2, j0 = 0;
   bool lower = false, lane_rot = true;
-  if constexpr (NEOX) {
+  if constexpr (NEOX && SHIFT == 0) {
     const int m = half / E;
     lane_rot = FULL || li < 2 * m;
     lower = li < m;
@@ -318,6 +322,29 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
     }
   } else {
     j0 = in_head ? d0 / 2 : 0;
+  }
+  // SHIFT 4, with R/2 = 8m + 4: slots 0-3 and 4-7 of a lane are runs of 4
+  // dims that each lie in one half (R/2 is a multiple of 4), and the rotated
+  // dims end on a lane boundary (R = 16m + 8). A first-half run k pairs with
+  // slots (i+4)&7 of lane li+m+k, a second-half run with lane li-m-1+k, so
+  // partner lane, cos/sin column and sign are kept per run. Lanes that do not
+  // rotate (pass-through dims, spare lanes) fetch from themselves and read
+  // columns 0-3, which keeps every access inside the head and the row.
+  int pa_s[2] = {lane << 2, lane << 2}, jc_s[2] = {0, 0};
+  bool lo_s[2] = {false, false}, ro_s = false;
+  if constexpr (SHIFT == 4) {
+    const int m = half >> 3;
+    const int head_lane0 = lane - li;
+    ro_s = in_head && d0 < 2 * half;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int d = d0 + 4 * k;
+      const bool lo = d < half;
+      const int pl = lo ? li + m + k : li - m - 1 + k;
+      pa_s[k] = (ro_s ? head_lane0 + pl : lane) << 2;
+      jc_s[k] = ro_s ? (lo ? d : d - half) : 0;
+      lo_s[k] = lo;
+    }
   }
 
   const int total_waves = gridDim.x * wpb;
@@ -379,7 +406,25 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
     float cs[NCS], sn[NCS];
     if constexpr (kRotate) {
       const float* row = cache + pos * R;
-      if ((FULL || NEOX) && NCS % 4 == 0 && p.cs_vec) {
+      if constexpr (SHIFT == 4) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          if (p.cs_vec) {
+            const float4 c4 = *reinterpret_cast<const float4*>(row + jc_s[k]);
+            const float4 s4 = *reinterpret_cast<const float4*>(row + half + jc_s[k]);
+            cs[4 * k] = c4.x; cs[4 * k + 1] = c4.y; cs[4 * k + 2] = c4.z; cs[4 * k + 3] = c4.w;
+            sn[4 * k] = s4.x; sn[4 * k + 1] = s4.y; sn[4 * k + 2] = s4.z; sn[4 * k + 3] = s4.w;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              cs[4 * k + i] = row[jc_s[k] + i];
+              sn[4 * k + i] = row[half + jc_s[k] + i];
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sn[4 * k + i] = lo_s[k] ? -sn[4 * k + i] : sn[4 * k + i];
+        }
+      } else if ((FULL || NEOX) && NCS % 4 == 0 && p.cs_vec) {
 #pragma unroll
         for (int i = 0; i < NCS; i += 4) {
           const float4 c4 = *reinterpret_cast<const float4*>(row + j0 + i);
@@ -395,7 +440,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
           sn[i] = row[half + j];
         }
       }
-      if constexpr (NEOX) {
+      if constexpr (NEOX && SHIFT == 0) {
 #pragma unroll
         for (int i = 0; i < NCS; ++i) sn[i] = lower ? -sn[i] : sn[i];
       }
@@ -452,6 +497,13 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
         if constexpr (!kRotate) {
 #pragma unroll
           for (int i = 0; i < E; ++i) o[i] = n[i];
+        } else if constexpr (SHIFT == 4) {
+#pragma unroll
+          for (int i = 0; i < E; ++i) {
+            const float pn = lane_fetch(pa_s[i >> 2], n[(i + 4) & 7]);
+            const float v = fmaf(n[i], cs[i], pn * sn[i]);
+            o[i] = (FULL || ro_s) ? v : n[i];
+          }
         } else if constexpr (NEOX) {
 #pragma unroll
           for (int i = 0; i < E; ++i) {
@@ -725,11 +777,13 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
 
 // One instance group of the kernel table, defined in qknr_inst.hip and built
 // once per (I/O type, group): group 0 the fused op with compile-time head_dim,
-// group 1 the other modes with compile-time head_dim, group 2 every mode with a
-// run-time head_dim (D is then the lane-group capacity). Returns the kernel's
-// host stub, or nullptr if no instance matches.
+// group 1 the other modes with compile-time head_dim, groups 2 and 4 the
+// run-time head_dims at unroll 2 (every mode) and 4 (the fused op); D is then
+// the lane-group capacity. shift 4 selects the NeoX instances whose partners
+// sit 4 slots over (fused op, 8 elements per lane). Returns the kernel's host
+// stub, or nullptr if no instance matches.
 template <class IO, int GROUP>
-const void* pick_group(int D, int E, bool neox, bool full, int U, int mode);
+const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int shift);
 
 // Group 3: the element-granular kernel of a mode (kFused ... kLayerOnly) with
 // S slots per lane (1, 2, 4 or 8).

@@ -111,8 +111,56 @@ const void* pick_any_dim_lanes(int E, bool neox, bool full, int mode) {
   return nullptr;
 }
 
+// NeoX instances whose partners sit 4 slots over (SHIFT 4; fused op, 16-byte
+// lanes): head_dim 64/128/256 with a partial rotation (a full one has
+// rope_dim/2 a multiple of 8) at unroll 1, 2 and 4 in group 0, the run-time
+// head_dims at unroll 2 in group 2 and 4 in group 4.
+template <class IO, int D>
+const void* pick_shift4_exact(int U) {
+  switch (U) {
+    case 1: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, 8, true, false, 1, kFused, true, 4>);
+    case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, 8, true, false, 2, kFused, true, 4>);
+    case 4: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, 8, true, false, 4, kFused, true, 4>);
+    default: return nullptr;
+  }
+}
+
+template <class IO, int DMAX, int UU>
+const void* pick_shift4_any(bool full) {
+  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, true, UU, kFused, false, 4>)
+              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, false, UU, kFused, false, 4>);
+}
+
 template <class IO, int GROUP>
-const void* pick_group(int D, int E, bool neox, bool full, int U, int mode) {
+const void* pick_shift4(int D, bool full, int U, int mode) {
+  if (mode != kFused) return nullptr;
+  if constexpr (GROUP == 0) {
+    if (full) return nullptr;
+    switch (D) {
+      case 64: return pick_shift4_exact<IO, 64>(U);
+      case 128: return pick_shift4_exact<IO, 128>(U);
+      case 256: return pick_shift4_exact<IO, 256>(U);
+      default: return nullptr;
+    }
+  } else if constexpr (GROUP == 2 || GROUP == 4) {
+    constexpr int UU = GROUP == 2 ? 2 : 4;
+    if (U != UU) return nullptr;
+    switch (D) {  // the lane-group capacity DMAX
+      case 16: return pick_shift4_any<IO, 16, UU>(full);
+      case 32: return pick_shift4_any<IO, 32, UU>(full);
+      case 64: return pick_shift4_any<IO, 64, UU>(full);
+      case 128: return pick_shift4_any<IO, 128, UU>(full);
+      case 256: return pick_shift4_any<IO, 256, UU>(full);
+      case 512: return pick_shift4_any<IO, 512, UU>(full);
+      default: return nullptr;
+    }
+  }
+  return nullptr;
+}
+
+template <class IO, int GROUP>
+const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int shift) {
+  if (shift != 0) return (shift == 4 && neox && E == 8) ? pick_shift4<IO, GROUP>(D, full, U, mode) : nullptr;
   if constexpr (GROUP == 2 || GROUP == 4) {
     constexpr int UU = GROUP == 2 ? 2 : 4;
     if (U != UU) return nullptr;
@@ -161,7 +209,7 @@ const void* pick_elem(int mode, int slots) {
 
 template const void* pick_elem<QKNR_INST_IO>(int, int);
 #else
-template const void* pick_group<QKNR_INST_IO, QKNR_INST_GROUP>(int, int, bool, bool, int, int);
+template const void* pick_group<QKNR_INST_IO, QKNR_INST_GROUP>(int, int, bool, bool, int, int, int);
 #endif
 
 }  // namespace qknr_impl

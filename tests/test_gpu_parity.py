@@ -151,6 +151,34 @@ def test_run_time_launch_variants(launch, D, R, neox):
     assert info["unroll"] == (4 if launch.get("unroll") == 4 else 2), info
 
 
+# NeoX halves of 8m + 4 dims on 16-byte lanes: partners 4 slots over, in one of
+# two neighbouring lanes (compile-time head_dims with a partial rotation,
+# run-time head_dims with a full or partial one, half 4 pairing inside a lane)
+SHIFTED = [(96, 24), (72, 72), (40, 40), (88, 88), (136, 136), (264, 264), (200, 200), (120, 8),
+           (16, 8), (64, 24), (128, 40), (128, 8), (256, 104), (256, 24)]
+SHIFTED_LAUNCHES = [None, dict(unroll=4, groups_per_item=3), dict(unroll=2, groups_per_item=1, block_waves=1)]
+
+
+@pytest.mark.parametrize("launch", SHIFTED_LAUNCHES,
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()) if d else "auto")
+@pytest.mark.parametrize("dt", [W.BF16, W.FP16])
+@pytest.mark.parametrize("D,R", SHIFTED)
+def test_neox_shifted_partners(D, R, dt, launch):
+    cfg = W.case(29, 7, 3, D, R, True, dtype=dt, pos_dtype=W.I64, seed=3 * D + R)
+    _say("case", cfg.name, launch)
+    wl = W.make_workload(cfg)
+    info = Hn.DeviceCase(wl).run(launch=launch or {})
+    assert info["generic"] == 0 and info["elems_per_lane"] == 8, info
+    Hn.run_and_check(wl, launch=launch)
+
+
+@pytest.mark.parametrize("layout", ["padded", "head_major", "qkv"])
+@pytest.mark.parametrize("D,R", [(96, 24), (128, 40), (72, 72)])
+def test_neox_shifted_partners_layouts(layout, D, R):
+    cfg = W.case(23, 5, 2, D, R, True, seed=D + 7 * R)
+    Hn.run_and_check(W.make_workload(cfg), layout=layout)
+
+
 # ---------------------------------------------------------------------------
 # Launch configurations (all must give the same, correct result)
 # ---------------------------------------------------------------------------
