@@ -184,15 +184,17 @@ constexpr int kDefaultGroupsPerItem = 2;
 constexpr int kDefaultUnroll = 2;
 constexpr int kDefaultBlockWaves = 4;
 constexpr int kDefaultBlockWavesNarrow = 3;  // lane groups of at most 16 lanes
-// Run-time head_dim instances of the fused op take longer work items with NeoX
-// pairing, or when a head group holds at most 640 bytes (spare lanes in the
-// padded lane group, or few heads per wave instruction): 4 head groups loaded
-// together (unroll 4), 4 groups per item, 2 waves per workgroup. At the same
-// bytes per launch that measured faster on every run-time NeoX shape (head_dim
-// 24-320: +2.5 to +33%, the most with 8-byte lanes) and on interleaved groups of
-// at most 640 bytes (head_dim 40, 80, 144, 160, 320: +1 to +8%); interleaved
-// groups of 768-896 bytes lose 1.4-3.4% with it, and the compile-time head_dims
-// 3.5-7.4% (4 groups per item at unroll 2), so they keep the usual defaults.
+// Run-time head_dim instances of the fused op and of the LayerNorm sibling take
+// longer work items with NeoX pairing, or when a head group holds at most 640
+// bytes (spare lanes in the padded lane group, or few heads per wave
+// instruction): 4 head groups loaded together (unroll 4), 4 groups per item, 2
+// waves per workgroup. At the same bytes per launch that measured faster on
+// every run-time NeoX shape (fused op, head_dim 24-320: +2.5 to +33%, the most
+// with 8-byte lanes) and on interleaved groups of at most 640 bytes (head_dim
+// 40, 80, 144, 160, 320: +1 to +8%); the LayerNorm sibling gained 8-27% on the
+// same shapes. Interleaved groups of 768-896 bytes lose 1.4-3.4% with it, and
+// the compile-time head_dims 3.5-7.4% (4 groups per item at unroll 2), so they
+// keep the usual defaults.
 constexpr int kLongItemGroupBytes = 640;
 constexpr int kLongItemUnroll = 4;
 constexpr int kLongItemGroups = 4;
@@ -267,13 +269,15 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
       return QKNR_E_ARG;
   }
   const int L = dmax / E, G = kWave / L;
+  const bool layer = mode == kLayerRope || mode == kLayerOnly;
   const bool long_items =
-      mode == kFused && !exact && (neox || G * 2 * D <= kLongItemGroupBytes);
-  // the unfused baseline steps and the LayerNorm sibling exist at unroll 2;
-  // the run-time head_dims of the fused op at unroll 2 and 4 (1 runs as 2)
+      (mode == kFused || layer) && !exact && (neox || G * 2 * D <= kLongItemGroupBytes);
+  // the unfused baseline steps, and the LayerNorm sibling at head_dim
+  // 64/128/256, exist at unroll 2; the run-time head_dims of the fused op and
+  // the LayerNorm sibling at unroll 2 and 4 (1 runs as 2)
   int U = 2;
   if (mode == kFused && exact) U = c.unroll == 0 ? kDefaultUnroll : c.unroll;
-  if (mode == kFused && !exact && (c.unroll == 4 || (c.unroll == 0 && long_items)))
+  if ((mode == kFused || layer) && !exact && (c.unroll == 4 || (c.unroll == 0 && long_items)))
     U = kLongItemUnroll;
 
   pl->elem = false;

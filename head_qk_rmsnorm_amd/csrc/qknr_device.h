@@ -777,9 +777,9 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
 
 // One instance group of the kernel table, defined in qknr_inst.hip and built
 // once per (I/O type, group): group 0 the fused op with compile-time head_dim,
-// group 1 the other modes with compile-time head_dim, groups 2 and 4 the
-// run-time head_dims at unroll 2 (every mode) and 4 (the fused op); D is then
-// the lane-group capacity. shift 4 selects the NeoX instances whose partners
+// group 1 the other modes with compile-time head_dim, groups 2 and 4 the fused
+// op and the LayerNorm sibling with a run-time head_dim at unroll 2 and 4 (D is
+// then the lane-group capacity). shift 4 selects the NeoX instances whose partners
 // sit 4 slots over (fused op, 8 elements per lane). Returns the kernel's host
 // stub, or nullptr if no instance matches.
 template <class IO, int GROUP>

@@ -68,8 +68,8 @@ const void* pick_lanes(int E, bool neox, bool full, int U, int mode) {
   return nullptr;
 }
 
-// Run-time head_dim instances: the fused op at unroll UU (2 or 4), the
-// LayerNorm sibling at unroll 2. 16-byte lanes (lane group of DMAX/8 lanes);
+// Run-time head_dim instances: the fused op and the LayerNorm sibling at
+// unroll UU (2 or 4). 16-byte lanes (lane group of DMAX/8 lanes);
 // for NeoX widths whose half no 16-byte lane divides, also 8-byte and 4-byte
 // lanes where the lane group still fits a wave (DMAX/4 and DMAX/2 lanes).
 template <class IO, int DMAX, int E, int MODE, int UU>
@@ -89,12 +89,10 @@ const void* pick_any_dim_mode(bool neox, bool full) {
 template <class IO, int DMAX, int E, int UU>
 const void* pick_any_dim(bool neox, bool full, int mode) {
   if (mode == kFused) return pick_any_dim_mode<IO, DMAX, E, kFused, UU>(neox, full);
-  if constexpr (UU == 2) {
-    if (mode == kLayerRope) return pick_any_dim_mode<IO, DMAX, E, kLayerRope, 2>(neox, full);
-    if constexpr (E == 8) {
-      if (mode == kLayerOnly)
-        return reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, 2, kLayerOnly, false>);
-    }
+  if (mode == kLayerRope) return pick_any_dim_mode<IO, DMAX, E, kLayerRope, UU>(neox, full);
+  if constexpr (E == 8) {
+    if (mode == kLayerOnly)
+      return reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, UU, kLayerOnly, false>);
   }
   return nullptr;
 }

@@ -411,7 +411,7 @@ def test_fused_and_unfused_agree_within_page_tolerance():
 # ---------------------------------------------------------------------------
 
 LN_GRID = [(D, R, neox, dt, bias)
-           for D in (64, 128, 256, 96, 192)
+           for D in (64, 128, 256, 96, 192, 80, 160)
            for R, neox in ((0, False), (D, False), (D, True), (D // 2, True), (D // 2, False))
            for dt in (W.BF16, W.FP16) for bias in (False, True)]
 
