@@ -11,7 +11,7 @@ from tests import qknr_harness as Hn
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 240
+N_CASES = 400
 
 
 def _draw(i):
