@@ -102,23 +102,25 @@ bool lanes_fit(int32_t R, int32_t neox, int E) {
   return (R / 2) % E == 0 && R / 2 >= E;
 }
 
-// The fused op also pairs NeoX halves of 8m + 4 dims on 16-byte lanes: each
-// partner sits 4 slots over in one of two neighbouring lanes (SHIFT 4).
-bool shift4_fits(int mode, int32_t R, int32_t neox) {
-  return mode == kFused && neox && (R / 2) % 8 == 4;
+// The fused op also pairs NeoX halves of 8m + 2, 8m + 4 and 8m + 6 dims on
+// 16-byte lanes: each partner sits 2, 4 or 6 slots over in a neighbouring lane.
+bool shifted_fits(int mode, int32_t R, int32_t neox) {
+  const int s = (R / 2) % 8;
+  return mode == kFused && neox && (s == 2 || s == 4 || s == 6);
 }
 
-// Partner slot shift of a lane mapping with E elements per lane: 0, or 4 where
-// only the shifted pairing fits.
+// Partner slot shift of a lane mapping with E elements per lane: 0, or
+// rope_dim/2 mod 8 where only the shifted pairing fits.
 int lane_shift(int mode, int32_t R, int32_t neox, int E) {
-  return (E == 8 && !lanes_fit(R, neox, 8) && shift4_fits(mode, R, neox)) ? 4 : 0;
+  return (E == 8 && !lanes_fit(R, neox, 8) && shifted_fits(mode, R, neox)) ? (R / 2) % 8 : 0;
 }
 
 // Elements per lane of a run-time head_dim instance (lane group capacity dmax):
-// 8 whenever the pairing allows it (shifted partners included); for NeoX also
-// 4 and 2 while the lane group (dmax/E lanes) fits a wave. 0: none.
+// 8 whenever the pairing allows it (shifted partners included); for NeoX in
+// the other modes also 4 and 2 while the lane group (dmax/E lanes) fits a
+// wave. 0: none.
 int any_dim_lanes(int mode, int dmax, int32_t R, int32_t neox) {
-  if (lanes_fit(R, neox, 8) || shift4_fits(mode, R, neox)) return 8;
+  if (lanes_fit(R, neox, 8) || shifted_fits(mode, R, neox)) return 8;
   if (dmax / 4 <= kWave && lanes_fit(R, neox, 4)) return 4;
   if (dmax / 2 <= kWave && lanes_fit(R, neox, 2)) return 2;
   return 0;
@@ -136,14 +138,14 @@ bool elem_supported(int mode, int32_t D, int32_t R) {
 // Shapes of the vectorised kernel in a mode: the page's rule (head_dim
 // 64/128/256, rope_dim a multiple of head_dim/32, NeoX rotary lanes a power of
 // two) widened to every even rope_dim for interleaved pairing, every NeoX
-// rope_dim whose half is a multiple of some lane width (or, for the fused op,
-// 4 more than a multiple of 8), and other head_dims that are multiples of 8.
+// rope_dim whose half is a multiple of some lane width (for the fused op: every
+// even half), and other head_dims that are multiples of 8.
 bool vector_shape(int mode, int32_t D, int32_t R, int32_t neox) {
   if (!fast_head_dim(D) && !any_head_dim(D)) return false;
   if (R <= 0 || R > D || R % 2) return false;
   if (!neox) return true;
   if (fast_head_dim(D)) {
-    if (lanes_fit(R, neox, 8) || shift4_fits(mode, R, neox) || lanes_fit(R, neox, D / 32))
+    if (lanes_fit(R, neox, 8) || shifted_fits(mode, R, neox) || lanes_fit(R, neox, D / 32))
       return true;
     return D / 64 >= 2 && lanes_fit(R, neox, D / 64);
   }
@@ -257,7 +259,7 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
     // 16-byte lanes first; then half a wave and a full wave per head
     const int cand[3] = {8, D / 32, D / 64};
     for (int e : cand) {
-      const bool pairs = lanes_fit(R, neox, e) || (e == 8 && shift4_fits(mode, R, neox));
+      const bool pairs = lanes_fit(R, neox, e) || (e == 8 && shifted_fits(mode, R, neox));
       if (e >= 2 && pairs && fits(e)) { E = e; break; }
     }
     if (E == 0) return QKNR_E_SHAPE;
@@ -265,7 +267,7 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
     if (c.lanes_per_head > kWave || D % c.lanes_per_head != 0) return QKNR_E_ARG;
     E = D / c.lanes_per_head;
     if (E != 8 && E != D / 32 && !(E == D / 64 && E >= 2)) return QKNR_E_ARG;
-    if (!(lanes_fit(R, neox, E) || (E == 8 && shift4_fits(mode, R, neox))) || !fits(E))
+    if (!(lanes_fit(R, neox, E) || (E == 8 && shifted_fits(mode, R, neox))) || !fits(E))
       return QKNR_E_ARG;
   }
   const int L = dmax / E, G = kWave / L;

@@ -244,8 +244,8 @@ enum : int { kFused = 0, kNormOnly = 1, kRopeOnly = 2, kLayerRope = 3, kLayerOnl
 // DMAX is the head_dim the instance is built for. EXACT instances have
 // head_dim == DMAX; the others take any multiple of E up to DMAX at run time
 // (each head keeps a lane group of DMAX/E lanes, the spare ones masked).
-// SHIFT 4 (NeoX, 8 elements per lane): rope_dim/2 is 4 more than a multiple of
-// 8, so a partner sits 4 slots over in one of two neighbouring lanes.
+// SHIFT 2, 4 or 6 (NeoX, 8 elements per lane): rope_dim/2 is that much more than
+// a multiple of 8, so a partner sits SHIFT slots over in a neighbouring lane.
 template <class IO, int DMAX, int E, bool NEOX, bool FULL, int U, int MODE, bool EXACT,
           int SHIFT = 0>
 __global__ void __launch_bounds__(kMaxBlockWaves * kWave)
@@ -258,7 +258,9 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   constexpr int NV = E / 2;     // packed dwords per lane
   constexpr int NCS = NEOX ? E : E / 2;  // cos (and sin) values per lane
   static_assert(DMAX % E == 0 && E % 2 == 0 && G >= 1, "lane mapping");
-  static_assert(SHIFT == 0 || (SHIFT == 4 && NEOX && E == 8), "partner slot shift");
+  static_assert(SHIFT == 0 || ((SHIFT == 2 || SHIFT == 4 || SHIFT == 6) && NEOX && E == 8),
+                "partner slot shift");
+  constexpr bool kShift26 = SHIFT == 2 || SHIFT == 6;
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
@@ -346,6 +348,25 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
       lo_s[k] = lo;
     }
   }
+  // SHIFT 2 or 6, with R/2 = 8m + SHIFT: a first-half element i pairs with slot
+  // (i+SHIFT)&7 of lane li+m (i < 8-SHIFT) or li+m+1, a second-half element
+  // with slot (i-SHIFT)&7 of lane li-m-1 (i < SHIFT) or li-m. The two halves
+  // read different source registers, so every element takes both fetches and
+  // keeps the one its half needs. Partner lanes outside the head (never needed
+  // by the element that computes them) fall back to the lane itself. Pairs of
+  // dims (2p, 2p+1) lie in one half and on one side of the rotation end (R/2
+  // and R are even), so cos/sin are read in aligned pairs.
+  int pb_lo[2] = {lane << 2, lane << 2}, pb_up[2] = {lane << 2, lane << 2};
+  if constexpr (kShift26) {
+    const int m = half >> 3;
+    const int head_lane0 = lane - li;
+    auto addr = [&](int pl) { return ((in_head && pl >= 0 && pl < L) ? head_lane0 + pl : lane) << 2; };
+    pb_lo[0] = addr(li + m);
+    pb_lo[1] = addr(li + m + 1);
+    pb_up[0] = addr(li - m - 1);
+    pb_up[1] = addr(li - m);
+  }
+  const bool cs_pairs = kShift26 && (reinterpret_cast<uintptr_t>(cache) & 7) == 0;
 
   const int total_waves = gridDim.x * wpb;
   int item = blockIdx.x * wpb + wib;
@@ -406,7 +427,24 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
     float cs[NCS], sn[NCS];
     if constexpr (kRotate) {
       const float* row = cache + pos * R;
-      if constexpr (SHIFT == 4) {
+      if constexpr (kShift26) {
+#pragma unroll
+        for (int q2 = 0; q2 < E / 2; ++q2) {
+          const int d = d0 + 2 * q2;
+          const bool lo = d < half;
+          const int j = (in_head && d < 2 * half) ? (lo ? d : d - half) : 0;
+          if (cs_pairs) {
+            const float2 c2 = *reinterpret_cast<const float2*>(row + j);
+            const float2 s2 = *reinterpret_cast<const float2*>(row + half + j);
+            cs[2 * q2] = c2.x; cs[2 * q2 + 1] = c2.y;
+            sn[2 * q2] = lo ? -s2.x : s2.x; sn[2 * q2 + 1] = lo ? -s2.y : s2.y;
+          } else {
+            cs[2 * q2] = row[j]; cs[2 * q2 + 1] = row[j + 1];
+            sn[2 * q2] = lo ? -row[half + j] : row[half + j];
+            sn[2 * q2 + 1] = lo ? -row[half + j + 1] : row[half + j + 1];
+          }
+        }
+      } else if constexpr (SHIFT == 4) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           if (p.cs_vec) {
@@ -497,6 +535,15 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
         if constexpr (!kRotate) {
 #pragma unroll
           for (int i = 0; i < E; ++i) o[i] = n[i];
+        } else if constexpr (kShift26) {
+#pragma unroll
+          for (int i = 0; i < E; ++i) {
+            const float a = lane_fetch(pb_lo[i >= 8 - SHIFT ? 1 : 0], n[(i + SHIFT) & 7]);
+            const float b = lane_fetch(pb_up[i >= SHIFT ? 1 : 0], n[(i + 8 - SHIFT) & 7]);
+            const float pn = (d0 + i < half) ? a : b;
+            const float v = fmaf(n[i], cs[i], pn * sn[i]);
+            o[i] = (FULL || (in_head && d0 + i < 2 * half)) ? v : n[i];
+          }
         } else if constexpr (SHIFT == 4) {
 #pragma unroll
           for (int i = 0; i < E; ++i) {
@@ -779,8 +826,8 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
 // once per (I/O type, group): group 0 the fused op with compile-time head_dim,
 // group 1 the other modes with compile-time head_dim, groups 2 and 4 the fused
 // op and the LayerNorm sibling with a run-time head_dim at unroll 2 and 4 (D is
-// then the lane-group capacity). shift 4 selects the NeoX instances whose partners
-// sit 4 slots over (fused op, 8 elements per lane). Returns the kernel's host
+// then the lane-group capacity). shift 2, 4 or 6 selects the NeoX instances whose
+// partners sit that many slots over (fused op, 8 elements per lane). Returns the kernel's host
 // stub, or nullptr if no instance matches.
 template <class IO, int GROUP>
 const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int shift);

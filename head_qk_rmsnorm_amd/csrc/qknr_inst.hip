@@ -109,47 +109,46 @@ const void* pick_any_dim_lanes(int E, bool neox, bool full, int mode) {
   return nullptr;
 }
 
-// NeoX instances whose partners sit 4 slots over (SHIFT 4; fused op, 16-byte
-// lanes): head_dim 64/128/256 with a partial rotation (a full one has
+// NeoX instances whose partners sit S = 2, 4 or 6 slots over (fused op,
+// 16-byte lanes): head_dim 64/128/256 with a partial rotation (a full one has
 // rope_dim/2 a multiple of 8) at unroll 1, 2 and 4 in group 0, the run-time
 // head_dims at unroll 2 in group 2 and 4 in group 4.
-template <class IO, int D>
-const void* pick_shift4_exact(int U) {
+template <class IO, int D, int S>
+const void* pick_shift_exact(int U) {
   switch (U) {
-    case 1: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, 8, true, false, 1, kFused, true, 4>);
-    case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, 8, true, false, 2, kFused, true, 4>);
-    case 4: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, 8, true, false, 4, kFused, true, 4>);
+    case 1: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, 8, true, false, 1, kFused, true, S>);
+    case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, 8, true, false, 2, kFused, true, S>);
+    case 4: return reinterpret_cast<const void*>(&qknr_kernel<IO, D, 8, true, false, 4, kFused, true, S>);
     default: return nullptr;
   }
 }
 
-template <class IO, int DMAX, int UU>
-const void* pick_shift4_any(bool full) {
-  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, true, UU, kFused, false, 4>)
-              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, false, UU, kFused, false, 4>);
+template <class IO, int DMAX, int UU, int S>
+const void* pick_shift_any(bool full) {
+  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, true, UU, kFused, false, S>)
+              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, false, UU, kFused, false, S>);
 }
 
-template <class IO, int GROUP>
-const void* pick_shift4(int D, bool full, int U, int mode) {
-  if (mode != kFused) return nullptr;
+template <class IO, int GROUP, int S>
+const void* pick_shift_of(int D, bool full, int U) {
   if constexpr (GROUP == 0) {
     if (full) return nullptr;
     switch (D) {
-      case 64: return pick_shift4_exact<IO, 64>(U);
-      case 128: return pick_shift4_exact<IO, 128>(U);
-      case 256: return pick_shift4_exact<IO, 256>(U);
+      case 64: return pick_shift_exact<IO, 64, S>(U);
+      case 128: return pick_shift_exact<IO, 128, S>(U);
+      case 256: return pick_shift_exact<IO, 256, S>(U);
       default: return nullptr;
     }
   } else if constexpr (GROUP == 2 || GROUP == 4) {
     constexpr int UU = GROUP == 2 ? 2 : 4;
     if (U != UU) return nullptr;
     switch (D) {  // the lane-group capacity DMAX
-      case 16: return pick_shift4_any<IO, 16, UU>(full);
-      case 32: return pick_shift4_any<IO, 32, UU>(full);
-      case 64: return pick_shift4_any<IO, 64, UU>(full);
-      case 128: return pick_shift4_any<IO, 128, UU>(full);
-      case 256: return pick_shift4_any<IO, 256, UU>(full);
-      case 512: return pick_shift4_any<IO, 512, UU>(full);
+      case 16: return pick_shift_any<IO, 16, UU, S>(full);
+      case 32: return pick_shift_any<IO, 32, UU, S>(full);
+      case 64: return pick_shift_any<IO, 64, UU, S>(full);
+      case 128: return pick_shift_any<IO, 128, UU, S>(full);
+      case 256: return pick_shift_any<IO, 256, UU, S>(full);
+      case 512: return pick_shift_any<IO, 512, UU, S>(full);
       default: return nullptr;
     }
   }
@@ -157,8 +156,19 @@ const void* pick_shift4(int D, bool full, int U, int mode) {
 }
 
 template <class IO, int GROUP>
+const void* pick_shift(int D, bool full, int U, int mode, int shift) {
+  if (mode != kFused) return nullptr;
+  switch (shift) {
+    case 2: return pick_shift_of<IO, GROUP, 2>(D, full, U);
+    case 4: return pick_shift_of<IO, GROUP, 4>(D, full, U);
+    case 6: return pick_shift_of<IO, GROUP, 6>(D, full, U);
+    default: return nullptr;
+  }
+}
+
+template <class IO, int GROUP>
 const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int shift) {
-  if (shift != 0) return (shift == 4 && neox && E == 8) ? pick_shift4<IO, GROUP>(D, full, U, mode) : nullptr;
+  if (shift != 0) return (neox && E == 8) ? pick_shift<IO, GROUP>(D, full, U, mode, shift) : nullptr;
   if constexpr (GROUP == 2 || GROUP == 4) {
     constexpr int UU = GROUP == 2 ? 2 : 4;
     if (U != UU) return nullptr;

@@ -62,22 +62,11 @@ def _supported(D, R, neox):
 def _vectorised(D, R, neox):
     """Shapes of the vectorised kernel for the fused op (include/qknr.h),
     restated: head_dim a multiple of 8 in [16, 512]; NeoX needs rope_dim/2 to be
-    a multiple of a lane width E (8 for any head_dim; also head_dim/32 and
-    head_dim/64 >= 2 for head_dim 64, 128, 256; also 4 and 2 for the other
-    head_dims while the lane group of capacity/E lanes fits a wave), or 4 more
-    than a multiple of 8 (16-byte lanes, partners 4 slots over)."""
+    even (16-byte lanes; partners 2, 4 or 6 slots over when it is not a
+    multiple of 8). An odd half fits no lane width of 2 or more elements."""
     if D % 8 or D < 16 or D > 512 or not _supported(D, R, neox):
         return False
-    if not neox:
-        return True
-    if D in (64, 128, 256):
-        widths = [8, D // 32] + ([D // 64] if D // 64 >= 2 else [])
-    else:  # lane group capacity: the next power of two >= max(16, D)
-        cap = 16
-        while cap < D:
-            cap *= 2
-        widths = [8] + ([4] if cap <= 256 else []) + ([2] if cap <= 128 else [])
-    return (R // 2) % 8 == 4 or any((R // 2) % e == 0 and R // 2 >= e for e in widths)
+    return not neox or (R // 2) % 2 == 0
 
 
 def test_can_use_covers_page_predicate_and_matches_documented_set():
@@ -159,8 +148,8 @@ REJECT = [
     (dict(cfg=B.LaunchCfg(block_waves=-1)), B.QKNR_E_ARG),
     (dict(cfg=B.LaunchCfg(max_blocks=-2)), B.QKNR_E_ARG),
     (dict(cfg=B.LaunchCfg(groups_per_item=-1)), B.QKNR_E_ARG),
-    # NeoX with 16-byte lanes needs rope_dim/2 to be a multiple of 8, or 4 more
-    (dict(D=128, R=12, cfg=B.LaunchCfg(lanes_per_head=16)), B.QKNR_E_ARG),
+    # NeoX with 16-byte lanes needs rope_dim/2 to be even
+    (dict(D=128, R=10, cfg=B.LaunchCfg(lanes_per_head=16)), B.QKNR_E_ARG),
     (dict(cfg=B.LaunchCfg(generic=2)), B.QKNR_E_ARG),
     (dict(cfg=B.LaunchCfg(generic=1, lanes_per_head=16)), B.QKNR_E_ARG),
     # an explicit lane mapping on a case only the element-granular kernel takes
@@ -261,7 +250,7 @@ def test_plan_lane_mapping(D):
                 continue
             assert info["generic"] == 0
             fits = lambda e: (not neox) or ((R // 2) % e == 0 and R // 2 >= e)
-            shifted = neox and (R // 2) % 8 == 4   # 16-byte lanes, partners 4 slots over
+            shifted = neox and (R // 2) % 2 == 0   # 16-byte lanes, partners 2/4/6 slots over
             want_lanes = D // 8 if fits(8) or shifted else (32 if fits(D // 32) else 64)
             assert info["lanes_per_head"] == want_lanes, (D, R, neox, info)
             assert info["elems_per_lane"] * info["lanes_per_head"] == D
@@ -284,24 +273,24 @@ def test_plan_run_time_head_dims(D, lanes):
     assert _plan(D, D - (D % 16), 1)["lanes_per_head"] == lanes
 
 
-@pytest.mark.parametrize("D,R,E", [(96, 24, 8), (80, 40, 8), (112, 56, 8), (80, 20, 2),
-                                   (72, 72, 8), (40, 12, 2), (120, 60, 2), (160, 40, 8),
-                                   (96, 12, 2), (56, 20, 2), (104, 52, 2), (264, 264, 8)])
-def test_plan_run_time_head_dims_narrow_lanes(D, R, E):
-    """NeoX halves that no 16-byte lane divides: 4 more than a multiple of 8
-    keeps 16-byte lanes (partners 4 slots over, e.g. head_dim 96 with rope_dim
-    24); other even halves take 4-byte lanes when the lane group still fits a
-    wave."""
+@pytest.mark.parametrize("D,R", [(96, 24), (80, 40), (112, 56), (80, 20), (72, 72), (40, 12),
+                                 (120, 60), (160, 40), (96, 12), (56, 20), (104, 52), (264, 264),
+                                 (200, 20), (320, 36), (504, 12), (128, 20), (64, 12), (256, 44)])
+def test_plan_neox_halves_off_the_lane_width_take_shifted_partners(D, R):
+    """NeoX halves that no 16-byte lane divides keep 16-byte lanes for the fused
+    op: each partner sits (rope_dim/2 mod 8) slots over in a neighbouring lane
+    (e.g. head_dim 96 with rope_dim 24, head_dim 80 with rope_dim 20)."""
     cap = 16
     while cap < D:
         cap *= 2
     info = _plan(D, R, 1)
-    assert info["generic"] == 0 and info["elems_per_lane"] == E, info
-    assert info["lanes_per_head"] == cap // E and info["heads_per_wave"] == 64 // (cap // E)
+    assert info["generic"] == 0 and info["elems_per_lane"] == 8, info
+    assert info["lanes_per_head"] == (D if D in (64, 128, 256) else cap) // 8
 
 
-@pytest.mark.parametrize("D,R", [(200, 20), (200, 100), (320, 20), (320, 36), (96, 6), (504, 12)])
-def test_plan_run_time_head_dims_without_a_lane_width_use_the_element_kernel(D, R):
+@pytest.mark.parametrize("D,R", [(200, 22), (320, 30), (96, 6), (504, 10), (72, 70), (200, 2),
+                                 (128, 10), (64, 6)])
+def test_plan_odd_neox_halves_use_the_element_kernel(D, R):
     info = _plan(D, R, 1)
     assert info["generic"] == 1, info
 
@@ -315,7 +304,7 @@ def test_plan_defaults():
     assert _plan(256, 256, 0)["block_threads"] == 256          # 32 lanes per head
     assert _plan(64, 64, 1)["block_threads"] == 192            # 8 lanes per head
     assert _plan(96, 96, 0)["block_threads"] == 192            # run-time head_dim, 16 lanes
-    assert _plan(128, 12, 1)["block_threads"] == 256           # NeoX 12: a full wave per head
+    assert _plan(128, 12, 1)["lanes_per_head"] == 16            # NeoX 12: shifted partners
     # head groups never mix Q and K heads: 4 Q + 4 K heads of head_dim 64 (8 per
     # wave instruction) are two half-filled groups, one work item
     tiny = _plan(64, 64, 1, Hq=4, Hkv=4)
@@ -384,7 +373,7 @@ def test_plan_element_granular():
     assert (small["elems_per_lane"], small["unroll"], small["groups_per_item"]) == (1, 16, 32)
     assert _plan(72, 70, 1)["generic"] == 1          # NeoX half 35: no lane width divides it
     assert _plan(72, 72, 1)["elems_per_lane"] == 8   # NeoX half 36 = 8*4 + 4: 16-byte lanes
-    assert _plan(72, 68, 1)["elems_per_lane"] == 2   # NeoX half 34: 4-byte lanes
+    assert _plan(72, 68, 1)["elems_per_lane"] == 8   # NeoX half 34 = 8*4 + 2: shifted partners
     assert _plan(72, 72, 0)["generic"] == 0          # interleaved: 16-byte lanes
     assert _plan(130, 64, 0)["elems_per_lane"] == 3  # not a multiple of 8
     forced = _plan(128, 128, 0, cfg=B.LaunchCfg(generic=1, groups_per_item=48, block_waves=2))

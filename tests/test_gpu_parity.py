@@ -151,11 +151,14 @@ def test_run_time_launch_variants(launch, D, R, neox):
     assert info["unroll"] == (4 if launch.get("unroll") == 4 else 2), info
 
 
-# NeoX halves of 8m + 4 dims on 16-byte lanes: partners 4 slots over, in one of
-# two neighbouring lanes (compile-time head_dims with a partial rotation,
-# run-time head_dims with a full or partial one, half 4 pairing inside a lane)
+# NeoX halves of 8m + 2, 8m + 4 and 8m + 6 dims on 16-byte lanes: partners 2, 4
+# or 6 slots over in a neighbouring lane (compile-time head_dims with a partial
+# rotation, run-time head_dims with a full or partial one, halves of 2, 4 and 6
+# that pair inside a lane)
 SHIFTED = [(96, 24), (72, 72), (40, 40), (88, 88), (136, 136), (264, 264), (200, 200), (120, 8),
-           (16, 8), (64, 24), (128, 40), (128, 8), (256, 104), (256, 24)]
+           (16, 8), (64, 24), (128, 40), (128, 8), (256, 104), (256, 24),
+           (80, 20), (96, 12), (40, 12), (56, 20), (104, 52), (120, 60), (200, 100), (504, 12),
+           (16, 4), (24, 12), (128, 20), (64, 12), (256, 44), (128, 4), (64, 60)]
 SHIFTED_LAUNCHES = [None, dict(unroll=4, groups_per_item=3), dict(unroll=2, groups_per_item=1, block_waves=1)]
 
 
@@ -173,7 +176,7 @@ def test_neox_shifted_partners(D, R, dt, launch):
 
 
 @pytest.mark.parametrize("layout", ["padded", "head_major", "qkv"])
-@pytest.mark.parametrize("D,R", [(96, 24), (128, 40), (72, 72)])
+@pytest.mark.parametrize("D,R", [(96, 24), (128, 40), (72, 72), (80, 20), (128, 12)])
 def test_neox_shifted_partners_layouts(layout, D, R):
     cfg = W.case(23, 5, 2, D, R, True, seed=D + 7 * R)
     Hn.run_and_check(W.make_workload(cfg), layout=layout)
