@@ -303,13 +303,14 @@ def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None, want_unfu
 
 
 # (head_dim, rope_dim, NeoX) shapes of the head_dim scan: the compile-time 128
-# for reference, run-time head_dims with 16-byte lanes, NeoX halves that need
-# 8-byte lanes (72, 88, 136, and 96 with rope_dim 24), and small heads.
+# for reference, run-time head_dims, small heads, and NeoX halves no 16-byte
+# lane divides (partners 4 slots over: 72, 88, 136, 96 with rope_dim 24;
+# 2 or 6 slots over: 80 with rope_dim 20, 128 with rope_dim 20).
 HEAD_DIM_SCAN = [(128, 128, False), (128, 128, True), (96, 96, False), (96, 96, True),
                  (80, 80, False), (80, 80, True), (112, 112, False), (112, 112, True),
                  (160, 160, False), (160, 160, True), (192, 192, False), (192, 192, True),
                  (40, 40, False), (40, 40, True), (72, 72, True), (88, 88, True),
-                 (136, 136, True), (96, 24, True)]
+                 (136, 136, True), (96, 24, True), (80, 20, True), (128, 20, True)]
 
 
 def head_dim_scan_case(D, R, neox):

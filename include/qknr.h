@@ -32,8 +32,9 @@
  *     any head_dim; also head_dim/32 and head_dim/64 >= 2 for head_dim 64,
  *     128, 256; also 4 and 2 for the other head_dims while a head's lane group,
  *     capacity/E lanes with capacity the next power of two >= head_dim, fits
- *     the 64-lane wave), or, for the fused op, 4 more than a multiple of 8
- *     (16-byte lanes whose partners sit 4 slots over in a neighbouring lane);
+ *     the 64-lane wave); for the fused op any even rope_dim/2 (16-byte lanes
+ *     whose partners sit 2, 4 or 6 slots over in a neighbouring lane when
+ *     rope_dim/2 is not a multiple of 8);
  *     q, k, weights (and biases) 16-byte aligned and every used q/k
  *     stride a multiple of 16 bytes; lane offsets inside a head group below
  *     2^31 bytes (a mapping with fewer heads per group is tried first); and,
