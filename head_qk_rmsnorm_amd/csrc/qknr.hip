@@ -247,8 +247,10 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   const bool exact = fast_head_dim(D);
   const int dmax = exact ? D : any_dim_capacity(D);
   if (!exact) {
-    // run-time head_dim: 16-byte lanes in a lane group of dmax/8 lanes; NeoX
-    // halves that no 16-byte lane divides take 8- or 4-byte lanes
+    // run-time head_dim: 16-byte lanes in a lane group of dmax/8 lanes (the
+    // fused op pairs every even NeoX half there, with shifted partners); in
+    // the LayerNorm sibling NeoX halves that no 16-byte lane divides take 8-
+    // or 4-byte lanes
     E = any_dim_lanes(mode, dmax, R, neox);
     if (E == 0) return QKNR_E_UNSUPPORTED;
     const int G = kWave / (dmax / E);

@@ -69,9 +69,10 @@ const void* pick_lanes(int E, bool neox, bool full, int U, int mode) {
 }
 
 // Run-time head_dim instances: the fused op and the LayerNorm sibling at
-// unroll UU (2 or 4). 16-byte lanes (lane group of DMAX/8 lanes);
-// for NeoX widths whose half no 16-byte lane divides, also 8-byte and 4-byte
-// lanes where the lane group still fits a wave (DMAX/4 and DMAX/2 lanes).
+// unroll UU (2 or 4). 16-byte lanes (lane group of DMAX/8 lanes); for the
+// LayerNorm sibling's NeoX widths whose half no 16-byte lane divides, also
+// 8-byte and 4-byte lanes where the lane group still fits a wave (DMAX/4 and
+// DMAX/2 lanes).
 template <class IO, int DMAX, int E, int MODE, int UU>
 const void* pick_any_dim_mode(bool neox, bool full) {
   if constexpr (E == 8) {
@@ -88,7 +89,11 @@ const void* pick_any_dim_mode(bool neox, bool full) {
 
 template <class IO, int DMAX, int E, int UU>
 const void* pick_any_dim(bool neox, bool full, int mode) {
-  if (mode == kFused) return pick_any_dim_mode<IO, DMAX, E, kFused, UU>(neox, full);
+  // the fused op pairs every even NeoX half on 16-byte lanes (shifted partners
+  // where needed), so it has no 8- or 4-byte-lane instances
+  if constexpr (E == 8) {
+    if (mode == kFused) return pick_any_dim_mode<IO, DMAX, 8, kFused, UU>(neox, full);
+  }
   if (mode == kLayerRope) return pick_any_dim_mode<IO, DMAX, E, kLayerRope, UU>(neox, full);
   if constexpr (E == 8) {
     if (mode == kLayerOnly)
