@@ -575,3 +575,32 @@ def test_head_dim_scan_shapes_are_vectorised():
         assert abs(c.units * D - dit.units * dit.head_dim) <= 48 * D
         info = _plan(D, R, neox)
         assert info["generic"] == 0, (D, R, neox, info)
+
+
+def test_every_supported_shape_plans_an_existing_instance():
+    """For every head_dim 2..512, every even rope_dim and both pairings, the
+    planner lands on a kernel instance that exists (with empty work a missing
+    one would be QKNR_E_UNSUPPORTED before any HIP call): the fused op at each
+    unroll (vectorised exactly on the documented set), the LayerNorm sibling
+    with and without the rotation, and the unfused chain."""
+    lib = B.lib()
+    z = P(0)
+    cfgs = [B.LaunchCfg(unroll=u) for u in (1, 2, 4)]
+    n = 0
+    for D in range(2, 513):
+        assert lib.qknr_layernorm_rope_inplace(z, z, z, z, z, z, z, z, 0, 4, 4, D, 0, 0, 1e-6,
+                                               0, 0, 0, 0, 0, 0, z) == 0, D
+        for R in range(2, D + 1, 2):
+            for neox in (0, 1):
+                info = B.LaunchInfo()
+                for cfg in cfgs:
+                    rc = lib.qknr_inplace_ex(z, z, z, z, z, z, 0, 24, 8, D, R, neox, 1e-6, 0, 0,
+                                             0, 0, 0, 0, z, ctypes.byref(cfg), ctypes.byref(info))
+                    assert rc == 0, (D, R, neox, cfg.unroll, rc)
+                    assert info.generic == (0 if _vectorised(D, R, neox) else 1), (D, R, neox)
+                assert lib.qknr_layernorm_rope_inplace(z, z, z, z, z, z, z, z, 0, 4, 4, D, R, neox,
+                                                       1e-6, 0, 0, 0, 0, 0, 0, z) == 0, (D, R, neox)
+                assert lib.qknr_unfused_inplace(z, z, z, z, z, z, 0, 4, 4, D, R, neox, 1e-6, 0, 0,
+                                                0, 0, 0, 0, z) == 0, (D, R, neox)
+                n += 1
+    assert n == 2 * sum(D // 2 for D in range(2, 513))
