@@ -102,11 +102,12 @@ bool lanes_fit(int32_t R, int32_t neox, int E) {
   return (R / 2) % E == 0 && R / 2 >= E;
 }
 
-// The fused op also pairs NeoX halves of 8m + 2, 8m + 4 and 8m + 6 dims on
-// 16-byte lanes: each partner sits 2, 4 or 6 slots over in a neighbouring lane.
+// The fused op and the LayerNorm sibling also pair NeoX halves of 8m + 2,
+// 8m + 4 and 8m + 6 dims on 16-byte lanes: each partner sits 2, 4 or 6 slots
+// over in a neighbouring lane.
 bool shifted_fits(int mode, int32_t R, int32_t neox) {
   const int s = (R / 2) % 8;
-  return mode == kFused && neox && (s == 2 || s == 4 || s == 6);
+  return (mode == kFused || mode == kLayerRope) && neox && (s == 2 || s == 4 || s == 6);
 }
 
 // Partner slot shift of a lane mapping with E elements per lane: 0, or
@@ -115,15 +116,11 @@ int lane_shift(int mode, int32_t R, int32_t neox, int E) {
   return (E == 8 && !lanes_fit(R, neox, 8) && shifted_fits(mode, R, neox)) ? (R / 2) % 8 : 0;
 }
 
-// Elements per lane of a run-time head_dim instance (lane group capacity dmax):
-// 8 whenever the pairing allows it (shifted partners included); for NeoX in
-// the other modes also 4 and 2 while the lane group (dmax/E lanes) fits a
-// wave. 0: none.
-int any_dim_lanes(int mode, int dmax, int32_t R, int32_t neox) {
-  if (lanes_fit(R, neox, 8) || shifted_fits(mode, R, neox)) return 8;
-  if (dmax / 4 <= kWave && lanes_fit(R, neox, 4)) return 4;
-  if (dmax / 2 <= kWave && lanes_fit(R, neox, 2)) return 2;
-  return 0;
+// Elements per lane of a run-time head_dim instance: 8 whenever the pairing
+// allows it (shifted NeoX partners included, which covers every even NeoX
+// half in the modes that take run-time head_dims). 0: none.
+int any_dim_lanes(int mode, int32_t R, int32_t neox) {
+  return (lanes_fit(R, neox, 8) || shifted_fits(mode, R, neox)) ? 8 : 0;
 }
 
 bool rotates(int mode) { return mode == kFused || mode == kRopeOnly || mode == kLayerRope; }
@@ -149,7 +146,7 @@ bool vector_shape(int mode, int32_t D, int32_t R, int32_t neox) {
       return true;
     return D / 64 >= 2 && lanes_fit(R, neox, D / 64);
   }
-  return any_dim_lanes(mode, any_dim_capacity(D), R, neox) != 0;
+  return any_dim_lanes(mode, R, neox) != 0;
 }
 
 // Head vectors of one tensor must not overlap: with the smaller of the two
@@ -217,7 +214,7 @@ struct Plan {
   int dmax = 0;        // head_dim of the instance (lane-group capacity)
   bool exact = true;   // head_dim == dmax
   bool elem = false;   // element-granular kernel (G = 1: a group is one head)
-  int shift = 0;       // NeoX partner slot shift (0 or 4)
+  int shift = 0;       // NeoX partner slot shift (0, 2, 4 or 6)
   size_t lds = 0;      // dynamic LDS bytes per workgroup
 };
 
@@ -247,11 +244,9 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   const bool exact = fast_head_dim(D);
   const int dmax = exact ? D : any_dim_capacity(D);
   if (!exact) {
-    // run-time head_dim: 16-byte lanes in a lane group of dmax/8 lanes (the
-    // fused op pairs every even NeoX half there, with shifted partners); in
-    // the LayerNorm sibling NeoX halves that no 16-byte lane divides take 8-
-    // or 4-byte lanes
-    E = any_dim_lanes(mode, dmax, R, neox);
+    // run-time head_dim: 16-byte lanes in a lane group of dmax/8 lanes (every
+    // even NeoX half pairs there, with shifted partners where needed)
+    E = any_dim_lanes(mode, R, neox);
     if (E == 0) return QKNR_E_UNSUPPORTED;
     const int G = kWave / (dmax / E);
     if (c.lanes_per_head != 0 && c.lanes_per_head != dmax / E) return QKNR_E_ARG;

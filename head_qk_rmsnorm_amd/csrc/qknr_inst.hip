@@ -69,55 +69,34 @@ const void* pick_lanes(int E, bool neox, bool full, int U, int mode) {
 }
 
 // Run-time head_dim instances: the fused op and the LayerNorm sibling at
-// unroll UU (2 or 4). 16-byte lanes (lane group of DMAX/8 lanes); for the
-// LayerNorm sibling's NeoX widths whose half no 16-byte lane divides, also
-// 8-byte and 4-byte lanes where the lane group still fits a wave (DMAX/4 and
-// DMAX/2 lanes).
-template <class IO, int DMAX, int E, int MODE, int UU>
+// unroll UU (2 or 4), 16-byte lanes in a lane group of DMAX/8 lanes. Every even
+// NeoX half pairs on them (shifted partners, below, where no lane divides it),
+// so there are no narrower lanes.
+template <class IO, int DMAX, int MODE, int UU>
 const void* pick_any_dim_mode(bool neox, bool full) {
-  if constexpr (E == 8) {
-    if (!neox) {
-      return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, UU, MODE, false>)
-                  : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, false, UU, MODE, false>);
-    }
-  } else {
-    if (!neox) return nullptr;
+  if (neox) {
+    return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, true, UU, MODE, false>)
+                : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, false, UU, MODE, false>);
   }
-  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, E, true, true, UU, MODE, false>)
-              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, E, true, false, UU, MODE, false>);
-}
-
-template <class IO, int DMAX, int E, int UU>
-const void* pick_any_dim(bool neox, bool full, int mode) {
-  // the fused op pairs every even NeoX half on 16-byte lanes (shifted partners
-  // where needed), so it has no 8- or 4-byte-lane instances
-  if constexpr (E == 8) {
-    if (mode == kFused) return pick_any_dim_mode<IO, DMAX, 8, kFused, UU>(neox, full);
-  }
-  if (mode == kLayerRope) return pick_any_dim_mode<IO, DMAX, E, kLayerRope, UU>(neox, full);
-  if constexpr (E == 8) {
-    if (mode == kLayerOnly)
-      return reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, UU, kLayerOnly, false>);
-  }
-  return nullptr;
+  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, UU, MODE, false>)
+              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, false, UU, MODE, false>);
 }
 
 template <class IO, int DMAX, int UU>
 const void* pick_any_dim_lanes(int E, bool neox, bool full, int mode) {
-  if (E == 8) return pick_any_dim<IO, DMAX, 8, UU>(neox, full, mode);
-  if constexpr (DMAX / 4 <= kWave) {
-    if (E == 4) return pick_any_dim<IO, DMAX, 4, UU>(neox, full, mode);
-  }
-  if constexpr (DMAX / 2 <= kWave) {
-    if (E == 2) return pick_any_dim<IO, DMAX, 2, UU>(neox, full, mode);
-  }
+  if (E != 8) return nullptr;
+  if (mode == kFused) return pick_any_dim_mode<IO, DMAX, kFused, UU>(neox, full);
+  if (mode == kLayerRope) return pick_any_dim_mode<IO, DMAX, kLayerRope, UU>(neox, full);
+  if (mode == kLayerOnly)
+    return reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, false, true, UU, kLayerOnly, false>);
   return nullptr;
 }
 
-// NeoX instances whose partners sit S = 2, 4 or 6 slots over (fused op,
-// 16-byte lanes): head_dim 64/128/256 with a partial rotation (a full one has
-// rope_dim/2 a multiple of 8) at unroll 1, 2 and 4 in group 0, the run-time
-// head_dims at unroll 2 in group 2 and 4 in group 4.
+// NeoX instances whose partners sit S = 2, 4 or 6 slots over (16-byte
+// lanes): head_dim 64/128/256 with a partial rotation (a full one has
+// rope_dim/2 a multiple of 8), the fused op at unroll 1, 2 and 4 in group 0 and
+// the LayerNorm sibling at unroll 2 in group 1; the run-time head_dims of both
+// at unroll 2 in group 2 and 4 in group 4.
 template <class IO, int D, int S>
 const void* pick_shift_exact(int U) {
   switch (U) {
@@ -128,32 +107,46 @@ const void* pick_shift_exact(int U) {
   }
 }
 
-template <class IO, int DMAX, int UU, int S>
+template <class IO, int DMAX, int UU, int MODE, int S>
 const void* pick_shift_any(bool full) {
-  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, true, UU, kFused, false, S>)
-              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, false, UU, kFused, false, S>);
+  return full ? reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, true, UU, MODE, false, S>)
+              : reinterpret_cast<const void*>(&qknr_kernel<IO, DMAX, 8, true, false, UU, MODE, false, S>);
+}
+
+template <class IO, int DMAX, int UU, int S>
+const void* pick_shift_mode(bool full, int mode) {
+  return mode == kFused ? pick_shift_any<IO, DMAX, UU, kFused, S>(full)
+                        : pick_shift_any<IO, DMAX, UU, kLayerRope, S>(full);
 }
 
 template <class IO, int GROUP, int S>
-const void* pick_shift_of(int D, bool full, int U) {
+const void* pick_shift_of(int D, bool full, int U, int mode) {
   if constexpr (GROUP == 0) {
-    if (full) return nullptr;
+    if (full || mode != kFused) return nullptr;
     switch (D) {
       case 64: return pick_shift_exact<IO, 64, S>(U);
       case 128: return pick_shift_exact<IO, 128, S>(U);
       case 256: return pick_shift_exact<IO, 256, S>(U);
       default: return nullptr;
     }
+  } else if constexpr (GROUP == 1) {
+    if (full || mode != kLayerRope || U != 2) return nullptr;
+    switch (D) {
+      case 64: return reinterpret_cast<const void*>(&qknr_kernel<IO, 64, 8, true, false, 2, kLayerRope, true, S>);
+      case 128: return reinterpret_cast<const void*>(&qknr_kernel<IO, 128, 8, true, false, 2, kLayerRope, true, S>);
+      case 256: return reinterpret_cast<const void*>(&qknr_kernel<IO, 256, 8, true, false, 2, kLayerRope, true, S>);
+      default: return nullptr;
+    }
   } else if constexpr (GROUP == 2 || GROUP == 4) {
     constexpr int UU = GROUP == 2 ? 2 : 4;
     if (U != UU) return nullptr;
     switch (D) {  // the lane-group capacity DMAX
-      case 16: return pick_shift_any<IO, 16, UU, S>(full);
-      case 32: return pick_shift_any<IO, 32, UU, S>(full);
-      case 64: return pick_shift_any<IO, 64, UU, S>(full);
-      case 128: return pick_shift_any<IO, 128, UU, S>(full);
-      case 256: return pick_shift_any<IO, 256, UU, S>(full);
-      case 512: return pick_shift_any<IO, 512, UU, S>(full);
+      case 16: return pick_shift_mode<IO, 16, UU, S>(full, mode);
+      case 32: return pick_shift_mode<IO, 32, UU, S>(full, mode);
+      case 64: return pick_shift_mode<IO, 64, UU, S>(full, mode);
+      case 128: return pick_shift_mode<IO, 128, UU, S>(full, mode);
+      case 256: return pick_shift_mode<IO, 256, UU, S>(full, mode);
+      case 512: return pick_shift_mode<IO, 512, UU, S>(full, mode);
       default: return nullptr;
     }
   }
@@ -162,11 +155,11 @@ const void* pick_shift_of(int D, bool full, int U) {
 
 template <class IO, int GROUP>
 const void* pick_shift(int D, bool full, int U, int mode, int shift) {
-  if (mode != kFused) return nullptr;
+  if (mode != kFused && mode != kLayerRope) return nullptr;
   switch (shift) {
-    case 2: return pick_shift_of<IO, GROUP, 2>(D, full, U);
-    case 4: return pick_shift_of<IO, GROUP, 4>(D, full, U);
-    case 6: return pick_shift_of<IO, GROUP, 6>(D, full, U);
+    case 2: return pick_shift_of<IO, GROUP, 2>(D, full, U, mode);
+    case 4: return pick_shift_of<IO, GROUP, 4>(D, full, U, mode);
+    case 6: return pick_shift_of<IO, GROUP, 6>(D, full, U, mode);
     default: return nullptr;
   }
 }

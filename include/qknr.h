@@ -26,15 +26,14 @@
  * set, a superset of the page's (section 4.6 compile-time guards, section 5.2
  * predicate: head_dim in {64, 128, 256}, rope_dim a multiple of head_dim/32,
  * for NeoX rope_dim/(head_dim/32) a power of two >= 2). Two kernels serve it:
- *   - the vectorised kernel (16-, 8- or 4-byte lanes, several heads per wave
- *     instruction), taken whenever all of these hold: head_dim a multiple of 8
- *     in [16, 512]; for NeoX, rope_dim/2 a multiple of a lane width E (8 for
- *     any head_dim; also head_dim/32 and head_dim/64 >= 2 for head_dim 64,
- *     128, 256; also 4 and 2 for the other head_dims while a head's lane group,
- *     capacity/E lanes with capacity the next power of two >= head_dim, fits
- *     the 64-lane wave); for the fused op any even rope_dim/2 (16-byte lanes
- *     whose partners sit 2, 4 or 6 slots over in a neighbouring lane when
- *     rope_dim/2 is not a multiple of 8);
+ *   - the vectorised kernel (16-byte lanes, or half or a full wave per head,
+ *     several heads per wave instruction), taken whenever all of these hold:
+ *     head_dim a multiple of 8 in [16, 512]; for NeoX, rope_dim/2 a multiple
+ *     of a lane width E (8 for any head_dim; also head_dim/32 and
+ *     head_dim/64 >= 2 for head_dim 64, 128, 256), or, for the fused op and
+ *     the LayerNorm sibling, any even rope_dim/2 (16-byte lanes whose partners
+ *     sit 2, 4 or 6 slots over in a neighbouring lane when rope_dim/2 is not a
+ *     multiple of 8);
  *     q, k, weights (and biases) 16-byte aligned and every used q/k
  *     stride a multiple of 16 bytes; lane offsets inside a head group below
  *     2^31 bytes (a mapping with fewer heads per group is tried first); and,

@@ -431,6 +431,28 @@ def test_layernorm_sibling(D, R, neox, dt, bias):
     Hn.layernorm_check(wl, R, bias)
 
 
+# the LayerNorm sibling pairs the same NeoX halves on 16-byte lanes with
+# shifted partners (compile-time and run-time head_dims)
+@pytest.mark.parametrize("bias", [False, True])
+@pytest.mark.parametrize("dt", [W.BF16, W.FP16])
+@pytest.mark.parametrize("D,R", SHIFTED)
+def test_layernorm_sibling_shifted_partners(D, R, dt, bias):
+    from oracle import qknr_oracle as O
+
+    cfg = W.case(29, 7, 3, D, R, True, dtype=dt, pos_dtype=W.I64, seed=5 * D + R, x_std=2.0)
+    wl = W.make_workload(cfg)
+    wl.q[...] = O.round_to_io_bits(O.decode_io(wl.q, dt) + 1.5, dt)
+    _say("case layernorm shifted", cfg.name, bias)
+    Hn.layernorm_check(wl, R, bias)
+
+
+@pytest.mark.parametrize("layout", ["padded", "head_major", "qkv"])
+@pytest.mark.parametrize("D,R", [(96, 24), (128, 40), (80, 20), (128, 12)])
+def test_layernorm_sibling_shifted_partners_layouts(layout, D, R):
+    cfg = W.case(23, 5, 2, D, R, True, seed=D + 11 * R)
+    Hn.layernorm_check(W.make_workload(cfg), R, True, layout=layout)
+
+
 @pytest.mark.parametrize("layout", ["padded", "qkv"])
 def test_layernorm_sibling_layouts(layout):
     cfg = W.case(33, 6, 2, 128, 64, True, seed=5)
