@@ -366,6 +366,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
     pb_up[0] = addr(li - m - 1);
     pb_up[1] = addr(li - m);
   }
+  const bool ro_26[2] = {in_head && d0 < 2 * half, in_head && d0 + 4 < 2 * half};
   const bool cs_pairs = kShift26 && (reinterpret_cast<uintptr_t>(cache) & 7) == 0;
 
   const int total_waves = gridDim.x * wpb;
@@ -424,7 +425,10 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 
     // cos / sin of this lane's dims at this token (loaded after the head data
     // is in flight; kept in registers for every group of the item)
-    float cs[NCS], sn[NCS];
+    // SHIFT 2/6: sn weighs the fetch from d + R/2 (first-half dims, negated)
+    // and sb the fetch from d - R/2 (second-half dims); the other one is 0, so
+    // no element selects between its two fetches.
+    float cs[NCS], sn[NCS], sb[kShift26 ? NCS : 1];
     if constexpr (kRotate) {
       const float* row = cache + pos * R;
       if constexpr (kShift26) {
@@ -433,16 +437,17 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
           const int d = d0 + 2 * q2;
           const bool lo = d < half;
           const int j = (in_head && d < 2 * half) ? (lo ? d : d - half) : 0;
+          float c0, c1, s0, s1;
           if (cs_pairs) {
             const float2 c2 = *reinterpret_cast<const float2*>(row + j);
             const float2 s2 = *reinterpret_cast<const float2*>(row + half + j);
-            cs[2 * q2] = c2.x; cs[2 * q2 + 1] = c2.y;
-            sn[2 * q2] = lo ? -s2.x : s2.x; sn[2 * q2 + 1] = lo ? -s2.y : s2.y;
+            c0 = c2.x; c1 = c2.y; s0 = s2.x; s1 = s2.y;
           } else {
-            cs[2 * q2] = row[j]; cs[2 * q2 + 1] = row[j + 1];
-            sn[2 * q2] = lo ? -row[half + j] : row[half + j];
-            sn[2 * q2 + 1] = lo ? -row[half + j + 1] : row[half + j + 1];
+            c0 = row[j]; c1 = row[j + 1]; s0 = row[half + j]; s1 = row[half + j + 1];
           }
+          cs[2 * q2] = c0; cs[2 * q2 + 1] = c1;
+          sn[2 * q2] = lo ? -s0 : 0.0f; sn[2 * q2 + 1] = lo ? -s1 : 0.0f;
+          sb[2 * q2] = lo ? 0.0f : s0; sb[2 * q2 + 1] = lo ? 0.0f : s1;
         }
       } else if constexpr (SHIFT == 4) {
 #pragma unroll
@@ -536,13 +541,14 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 #pragma unroll
           for (int i = 0; i < E; ++i) o[i] = n[i];
         } else if constexpr (kShift26) {
+          // R = 16m + 2*SHIFT ends on slot 4 of a lane: each run of 4 slots is
+          // rotated as a whole or passed through
 #pragma unroll
           for (int i = 0; i < E; ++i) {
             const float a = lane_fetch(pb_lo[i >= 8 - SHIFT ? 1 : 0], n[(i + SHIFT) & 7]);
             const float b = lane_fetch(pb_up[i >= SHIFT ? 1 : 0], n[(i + 8 - SHIFT) & 7]);
-            const float pn = (d0 + i < half) ? a : b;
-            const float v = fmaf(n[i], cs[i], pn * sn[i]);
-            o[i] = (FULL || (in_head && d0 + i < 2 * half)) ? v : n[i];
+            const float v = fmaf(n[i], cs[i], fmaf(a, sn[i], b * sb[i]));
+            o[i] = (FULL || ro_26[i >> 2]) ? v : n[i];
           }
         } else if constexpr (SHIFT == 4) {
 #pragma unroll
