@@ -51,7 +51,8 @@ class LaunchInfo(ctypes.Structure):
                 ("heads_per_wave", ctypes.c_int32), ("groups_per_token", ctypes.c_int32),
                 ("groups_per_item", ctypes.c_int32), ("unroll", ctypes.c_int32),
                 ("block_threads", ctypes.c_int32), ("grid_blocks", ctypes.c_int32),
-                ("items", ctypes.c_int64), ("generic", ctypes.c_int32)]
+                ("items", ctypes.c_int64), ("generic", ctypes.c_int32),
+                ("access_bytes", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {f: int(getattr(self, f)) for f, _ in self._fields_}

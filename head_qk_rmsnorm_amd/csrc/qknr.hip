@@ -91,8 +91,8 @@ int any_dim_capacity(int32_t D) {
   return c;
 }
 
-const void* pick_elem_kernel(int dtype, int mode, int slots) {
-  return dtype == QKNR_BF16 ? pick_elem<Bf16>(mode, slots) : pick_elem<Fp16>(mode, slots);
+const void* pick_elem_kernel(int dtype, int mode, int slots, int pw) {
+  return dtype == QKNR_BF16 ? pick_elem<Bf16>(mode, slots, pw) : pick_elem<Fp16>(mode, slots, pw);
 }
 
 // NeoX pairs (d, d + R/2): with E elements per lane the partner sits a fixed
@@ -214,6 +214,7 @@ struct Plan {
   int dmax = 0;        // head_dim of the instance (lane-group capacity)
   bool exact = true;   // head_dim == dmax
   bool elem = false;   // element-granular kernel (G = 1: a group is one head)
+  int pw = 1;          // element-granular kernel: elements per lane slot (2-byte accesses x pw)
   int shift = 0;       // NeoX partner slot shift (0, 2, 4 or 6)
   size_t lds = 0;      // dynamic LDS bytes per workgroup
 };
@@ -307,17 +308,32 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
 }
 
 // Plan of the element-granular kernel: one head per wave instruction, a work
-// item is a run of heads (Q, then K) of one token; S slots per lane, the
-// smallest power of two with 64*S >= head_dim.
+// item is a run of heads (Q, then K) of one token; S slots of pw elements per
+// lane (accesses of 2*pw bytes), S the smallest power of two with
+// 64*S*pw >= head_dim. The widest pw (4, 2 or 1) that divides head_dim and
+// whose access size divides every pointer and stride (align: their common
+// alignment, 8 at most) gives the fewest slots; the narrowest pw with that many
+// slots is taken, which keeps the most lanes busy and 16/(S*pw) heads in
+// flight (measured: head_dim 100 and 128 run fastest with 4-byte accesses, 200
+// and 256 with 8-byte ones).
+int elem_slots(int32_t D, int pw) {
+  int s = 1;
+  while (s * kWave * pw < D) s *= 2;
+  return s;
+}
+
 int32_t make_elem_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t neox,
-                       int32_t dtype, const qknr_launch_cfg& c, Plan* pl) {
+                       int32_t dtype, int align, const qknr_launch_cfg& c, Plan* pl) {
   const int H = Hq + Hkv;
   pl->elem = true;
   pl->shift = 0;
-  int slots = 1;
-  while (slots * kWave < D) slots *= 2;
-  const int U = 2 * kElemSlots / slots;
-  pl->E = (D + kWave - 1) / kWave;
+  int pw = (align >= 8 && D % 4 == 0) ? 4 : (align >= 4 && D % 2 == 0) ? 2 : 1;
+  const int fewest = elem_slots(D, pw);
+  while (pw > 1 && elem_slots(D, pw / 2) <= fewest) pw /= 2;
+  pl->pw = pw;
+  const int slots = fewest;
+  const int U = 2 * kElemSlots / (slots * pl->pw);
+  pl->E = pl->pw * ((D + kWave * pl->pw - 1) / (kWave * pl->pw));
   pl->L = kWave;
   pl->dmax = D;
   pl->exact = false;
@@ -334,7 +350,7 @@ int32_t make_elem_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, 
   pl->max_blocks = c.max_blocks;
   // NeoX rotation exchanges partners through one LDS row of head_dim floats per wave
   pl->lds = (rotates(mode) && neox) ? static_cast<size_t>(pl->wpb) * D * sizeof(float) : 0;
-  pl->fn = pick_elem_kernel(dtype, mode, slots);
+  pl->fn = pick_elem_kernel(dtype, mode, slots, pl->pw);
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
 }
 
@@ -420,6 +436,7 @@ int32_t prepare(int mode, const Call& c, const qknr_launch_cfg* cfg, Plan* pl,
   const bool need_rot = rotates(mode);
   const bool bias = (mode == kLayerRope || mode == kLayerOnly) && (c.bq || c.bk);
   bool vec_aligned = true;
+  int elem_align = 8;  // common alignment of the views (2, 4 or 8 bytes) for the element-granular kernel
   if (!empty) {
     if ((c.Hq > 0 && (!c.q || (need_w && !c.wq) || (bias && !c.bq))) ||
         (c.Hkv > 0 && (!c.k || (need_w && !c.wk) || (bias && !c.bk))) ||
@@ -435,6 +452,10 @@ int32_t prepare(int mode, const Call& c, const qknr_launch_cfg* cfg, Plan* pl,
       return QKNR_E_ALIGN;
     vec_aligned = side_aligned(c.q, c.wq, c.bq, c.T, c.Hq, c.qt, c.qh, need_w, bias, 16) &&
                   side_aligned(c.k, c.wk, c.bk, c.T, c.Hkv, c.kt, c.kh, need_w, bias, 16);
+    while (elem_align > 2 &&
+           !(side_aligned(c.q, c.wq, c.bq, c.T, c.Hq, c.qt, c.qh, need_w, bias, elem_align) &&
+             side_aligned(c.k, c.wk, c.bk, c.T, c.Hkv, c.kt, c.kh, need_w, bias, elem_align)))
+      elem_align /= 2;
   }
 
   const bool vector = !lc.generic && vec_aligned && vector_mode(mode, c.D) &&
@@ -448,7 +469,7 @@ int32_t prepare(int mode, const Call& c, const qknr_launch_cfg* cfg, Plan* pl,
     return QKNR_E_ARG;
   }
   if (rc != QKNR_OK) {
-    rc = make_elem_plan(mode, c.T, c.Hq, c.Hkv, c.D, c.neox, c.dtype, lc, pl);
+    rc = make_elem_plan(mode, c.T, c.Hq, c.Hkv, c.D, c.neox, c.dtype, elem_align, lc, pl);
     if (rc != QKNR_OK) return rc;
   }
   if (info) {
@@ -462,6 +483,7 @@ int32_t prepare(int mode, const Call& c, const qknr_launch_cfg* cfg, Plan* pl,
     info->grid_blocks = 0;
     info->items = pl->items;
     info->generic = pl->elem ? 1 : 0;
+    info->access_bytes = 2 * (pl->elem ? pl->pw : pl->E);
   }
   return QKNR_OK;
 }

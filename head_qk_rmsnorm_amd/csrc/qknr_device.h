@@ -589,20 +589,25 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 // ----------------------------------------------------------------------------
 // Element-granular kernel: the shapes and layouts the vectorised kernel above
 // cannot take (head_dims that are not multiples of 8, NeoX halves that are not
-// a multiple of any lane width, pointers or strides that are only element
-// aligned, head strides beyond 32-bit lane offsets). Same operation, same fp32
-// formulas and FMA forms, same rounding; only the order of the sums differs.
+// a multiple of any lane width, pointers or strides that are only 2- or
+// 4-byte aligned, head strides beyond 32-bit lane offsets). Same operation,
+// same fp32 formulas and FMA forms, same rounding; only the order of the sums
+// differs.
 //
-// One head vector per wave instruction: element e sits in lane e % 64, slot
-// e / 64 (S slots, a power of two covering head_dim <= 512). Every access is a 2-byte
-// buffer access relative to the head's own base address, which is wave-uniform
-// (64-bit, no limit on strides); lane offsets stay below 1 KiB and the
-// descriptor covers exactly the head vector. Interleaved partners (e, e ^ 1)
-// are neighbouring lanes of one slot (DPP); NeoX partners (e, e +- R/2) can
+// One head vector per wave instruction. A lane slot holds PW consecutive
+// elements: PW = 4 (8-byte accesses) when head_dim is a multiple of 4 and every
+// pointer and stride is 8-byte aligned, PW = 2 (4-byte accesses) when head_dim
+// is even and they are 4-byte aligned, else PW = 1 (2-byte accesses). Element e sits
+// in lane (e / PW) % 64, slot e / (64 PW), S slots (a power of two covering
+// head_dim <= 512). Every access is a buffer access relative to the head's own
+// base address, which is wave-uniform (64-bit, no limit on strides); lane
+// offsets stay below 1 KiB and the descriptor covers exactly the head vector.
+// Interleaved partners (e, e ^ 1) lie in one slot (PW = 2, 4) or in
+// neighbouring lanes of one slot (PW = 1, DPP); NeoX partners (e, e +- R/2) can
 // sit in any lane and slot, so the normalised row goes through a per-wave row
-// of LDS. A work item is a run of heads (Q then K) of one token; 16/S heads are
-// loaded before the first is computed, so every instance keeps the same
-// number of bytes in flight per wave whatever its head_dim.
+// of LDS. A work item is a run of heads (Q then K) of one token; 16/(S PW)
+// heads are loaded before the first is computed, so every instance keeps the
+// same number of bytes in flight per wave whatever its head_dim.
 // ----------------------------------------------------------------------------
 constexpr int kElemSlots = 8;
 constexpr int kElemMaxDim = kElemSlots * kWave;  // 512
@@ -637,14 +642,33 @@ __device__ __forceinline__ uint16_t narrow1(float v) {
   return static_cast<uint16_t>(IO::pack(v, 0.0f) & 0xffffu);
 }
 
-template <class IO, int MODE, int S>
+// PW elements of a row of I/O values starting at element e (e a multiple of
+// PW, the row 2*PW-byte aligned) -> fp32
+template <class IO, int PW>
+__device__ __forceinline__ void load_row_elems(const uint16_t* r, int e, float* v) {
+  if constexpr (PW == 4) {
+    const u32x2_t w = *reinterpret_cast<const u32x2_t*>(r + e);
+    IO::unpack(w.x, v[0], v[1]);
+    IO::unpack(w.y, v[2], v[3]);
+  } else if constexpr (PW == 2) {
+    IO::unpack(*reinterpret_cast<const uint32_t*>(r + e), v[0], v[1]);
+  } else {
+    v[0] = widen1<IO>(r[e]);
+  }
+}
+
+template <class IO, int MODE, int S, int PW>
 __global__ void __launch_bounds__(kMaxBlockWaves * kWave)
 qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict__ wqp,
                  const void* __restrict__ wkp, const float* __restrict__ cache,
                  const void* __restrict__ posp, const void* __restrict__ bqp,
                  const void* __restrict__ bkp, const ElemParams p) {
   static_assert(S == 1 || S == 2 || S == 4 || S == 8, "slots per lane");
-  constexpr int U = 2 * kElemSlots / S;  // heads loaded before the first is computed
+  static_assert(PW == 1 || PW == 2 || PW == 4, "elements per lane slot");
+  static_assert(S * PW <= kElemSlots, "at most 512 elements");
+  constexpr int NE = S * PW;                  // elements per lane
+  constexpr int U = 2 * kElemSlots / NE;      // heads loaded before the first is computed
+  constexpr int SPAN = kWave * PW;            // elements per slot of the wave
   constexpr bool kRotate = MODE == kFused || MODE == kRopeOnly || MODE == kLayerRope;
   constexpr bool kRms = MODE == kFused || MODE == kNormOnly;
   constexpr bool kLayer = MODE == kLayerRope || MODE == kLayerOnly;
@@ -655,53 +679,57 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
   const int D = p.D, R = p.R, half = R / 2;
   const bool neox = p.neox != 0;  // wave-uniform
   float* const row = elem_rows + wib * D;
+  // element of slot s, position i in the slot; head_dim is a multiple of PW,
+  // so the elements of a slot are all in the head or none is
+  auto elem = [&](int s, int i) { return (s * kWave + lane) * PW + i; };
 
-  // weights, biases and rotation roles of this lane's elements
+  // weights, biases and rotation roles of this lane's elements (index s*PW + i)
   const uint16_t* const wq16 = static_cast<const uint16_t*>(wqp);
   const uint16_t* const wk16 = static_cast<const uint16_t*>(wkp);
   const uint16_t* const bq16 = static_cast<const uint16_t*>(bqp);
   const uint16_t* const bk16 = static_cast<const uint16_t*>(bkp);
-  float wq[S], wk[S], bq[S], bk[S];
-  int col[S], partner[S];  // cos/sin column, partner element
-  bool rot[S], neg[S];     // rotated element; partner term subtracted
-  bool have_w = false;     // weights are loaded after the first head loads
+  float wq[NE], wk[NE], bq[NE], bk[NE];
+  int col[NE], partner[NE];  // cos/sin column, partner element
+  bool rot[NE], neg[NE];     // rotated element; partner term subtracted
+  bool have_w = false;       // weights are loaded after the first head loads
   auto load_weights = [&]() {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const int e = s * kWave + lane;
+      const int e = elem(s, 0);
       const bool act = e < D;
-      wq[s] = wk[s] = bq[s] = bk[s] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < PW; ++i) wq[s * PW + i] = wk[s * PW + i] = bq[s * PW + i] = bk[s * PW + i] = 0.0f;
       if constexpr (kRms || kLayer) {
         if (act) {
-          wq[s] = widen1<IO>(wq16[e]);
-          wk[s] = widen1<IO>(wk16[e]);
+          load_row_elems<IO, PW>(wq16, e, &wq[s * PW]);
+          load_row_elems<IO, PW>(wk16, e, &wk[s * PW]);
         }
       }
       if constexpr (kLayer) {
         if (act && p.has_bias) {
-          bq[s] = widen1<IO>(bq16[e]);
-          bk[s] = widen1<IO>(bk16[e]);
+          load_row_elems<IO, PW>(bq16, e, &bq[s * PW]);
+          load_row_elems<IO, PW>(bk16, e, &bk[s * PW]);
         }
       }
     }
   };
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int e = s * kWave + lane;
-    rot[s] = kRotate && e < R;
+  for (int j = 0; j < NE; ++j) {
+    const int e = elem(j / PW, j % PW);
+    rot[j] = kRotate && e < R;
     if (neox) {
       const bool lower = e < half;
-      col[s] = lower ? e : e - half;
-      partner[s] = lower ? e + half : e - half;
-      neg[s] = lower;
+      col[j] = lower ? e : e - half;
+      partner[j] = lower ? e + half : e - half;
+      neg[j] = lower;
     } else {
-      col[s] = e >> 1;
-      partner[s] = e ^ 1;
-      neg[s] = (e & 1) == 0;
+      col[j] = e >> 1;
+      partner[j] = e ^ 1;
+      neg[j] = (e & 1) == 0;
     }
-    if (!rot[s]) {
-      col[s] = 0;
-      partner[s] = 0;
+    if (!rot[j]) {
+      col[j] = 0;
+      partner[j] = 0;
     }
   }
 
@@ -711,7 +739,7 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
     const int h_begin = (item - t * p.nc) * p.hpi;
     const int h_end = min(h_begin + p.hpi, p.H);
 
-    float x[U][S];
+    float x[U][NE];
     __amdgpu_buffer_rsrc_t rs[U];
     bool ok[U], isk[U];
     auto issue = [&](int h) {
@@ -725,10 +753,22 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
         rs[u] = __builtin_amdgcn_make_buffer_rsrc(base, 0, 2 * D, kBufferFlags);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          const int e = s * kWave + lane;
-          x[u][s] = 0.0f;
-          if (ok[u] && s * kWave < D && e < D)
-            x[u][s] = widen1<IO>(__builtin_amdgcn_raw_buffer_load_b16(rs[u], 2 * e, 0, kLoadPolicy));
+          const int e = elem(s, 0);
+#pragma unroll
+          for (int i = 0; i < PW; ++i) x[u][s * PW + i] = 0.0f;
+          if (ok[u] && s * SPAN < D && e < D) {
+            if constexpr (PW == 4) {
+              const u32x2_t w = __builtin_bit_cast(
+                  u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs[u], 2 * e, 0, kLoadPolicy));
+              IO::unpack(w.x, x[u][s * PW], x[u][s * PW + 1]);
+              IO::unpack(w.y, x[u][s * PW + 2], x[u][s * PW + 3]);
+            } else if constexpr (PW == 2) {
+              IO::unpack(__builtin_amdgcn_raw_buffer_load_b32(rs[u], 2 * e, 0, kLoadPolicy),
+                         x[u][s * PW], x[u][s * PW + 1]);
+            } else {
+              x[u][s] = widen1<IO>(__builtin_amdgcn_raw_buffer_load_b16(rs[u], 2 * e, 0, kLoadPolicy));
+            }
+          }
         }
       }
     };
@@ -741,20 +781,20 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
 
     // cos / sin of this lane's elements at this token; the sign of the
     // partner term folded into sin
-    float cs[S], sn[S];
+    float cs[NE], sn[NE];
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      cs[s] = 1.0f;
-      sn[s] = 0.0f;
+    for (int j = 0; j < NE; ++j) {
+      cs[j] = 1.0f;
+      sn[j] = 0.0f;
     }
     if constexpr (kRotate) {
       const float* const crow = cache + token_position(posp, p.pos64, t) * R;
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        if (s * kWave < R && rot[s]) {
-          cs[s] = crow[col[s]];
-          const float v = crow[half + col[s]];
-          sn[s] = neg[s] ? -v : v;
+      for (int j = 0; j < NE; ++j) {
+        if ((j / PW) * SPAN < R && rot[j]) {
+          cs[j] = crow[col[j]];
+          const float v = crow[half + col[j]];
+          sn[j] = neg[j] ? -v : v;
         }
       }
     }
@@ -764,64 +804,77 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (!ok[u]) continue;
-        float n[S];
+        float n[NE];
         if constexpr (kLayer) {
           float sm = 0.0f;
 #pragma unroll
-          for (int s = 0; s < S; ++s) sm += x[u][s];
+          for (int j = 0; j < NE; ++j) sm += x[u][j];
           const float mean = group_sum<kWave>(sm) * p.inv_d;
-          float c[S], ss = 0.0f;
+          float c[NE], ss = 0.0f;
 #pragma unroll
-          for (int s = 0; s < S; ++s) {
-            c[s] = s * kWave + lane < D ? x[u][s] - mean : 0.0f;
-            ss = fmaf(c[s], c[s], ss);
+          for (int j = 0; j < NE; ++j) {
+            c[j] = elem(j / PW, j % PW) < D ? x[u][j] - mean : 0.0f;
+            ss = fmaf(c[j], c[j], ss);
           }
           ss = group_sum<kWave>(ss);
           const float r = __builtin_amdgcn_rsqf(fmaf(ss, p.inv_d, p.eps));
 #pragma unroll
-          for (int s = 0; s < S; ++s)
-            n[s] = fmaf(c[s] * r, isk[u] ? wk[s] : wq[s], isk[u] ? bk[s] : bq[s]);
+          for (int j = 0; j < NE; ++j)
+            n[j] = fmaf(c[j] * r, isk[u] ? wk[j] : wq[j], isk[u] ? bk[j] : bq[j]);
         } else if constexpr (kRms) {
           float ss = 0.0f;
 #pragma unroll
-          for (int s = 0; s < S; ++s) ss = fmaf(x[u][s], x[u][s], ss);
+          for (int j = 0; j < NE; ++j) ss = fmaf(x[u][j], x[u][j], ss);
           ss = group_sum<kWave>(ss);
           const float r = __builtin_amdgcn_rsqf(fmaf(ss, p.inv_d, p.eps));
 #pragma unroll
-          for (int s = 0; s < S; ++s) n[s] = x[u][s] * r * (isk[u] ? wk[s] : wq[s]);
+          for (int j = 0; j < NE; ++j) n[j] = x[u][j] * r * (isk[u] ? wk[j] : wq[j]);
         } else {
 #pragma unroll
-          for (int s = 0; s < S; ++s) n[s] = x[u][s];
+          for (int j = 0; j < NE; ++j) n[j] = x[u][j];
         }
 
-        float o[S];
+        float o[NE];
 #pragma unroll
-        for (int s = 0; s < S; ++s) o[s] = n[s];
+        for (int j = 0; j < NE; ++j) o[j] = n[j];
         if constexpr (kRotate) {
-          float pn[S];
+          float pn[NE];
           if (neox) {
             wave_lds_fence();  // the previous head's reads are done
 #pragma unroll
-            for (int s = 0; s < S; ++s) {
-              const int e = s * kWave + lane;
-              if (s * kWave < R && e < R) row[e] = n[s];
+            for (int j = 0; j < NE; ++j) {
+              const int e = elem(j / PW, j % PW);
+              if ((j / PW) * SPAN < R && e < R) row[e] = n[j];
             }
             wave_lds_fence();
 #pragma unroll
-            for (int s = 0; s < S; ++s) pn[s] = (s * kWave < R && rot[s]) ? row[partner[s]] : 0.0f;
+            for (int j = 0; j < NE; ++j) pn[j] = ((j / PW) * SPAN < R && rot[j]) ? row[partner[j]] : 0.0f;
+          } else if constexpr (PW >= 2) {
+#pragma unroll
+            for (int j = 0; j < NE; ++j) pn[j] = n[j ^ 1];
           } else {
 #pragma unroll
-            for (int s = 0; s < S; ++s) pn[s] = dpp_mov<kDppQuadXor1>(n[s]);
+            for (int j = 0; j < NE; ++j) pn[j] = dpp_mov<kDppQuadXor1>(n[j]);
           }
 #pragma unroll
-          for (int s = 0; s < S; ++s)
-            if (rot[s]) o[s] = fmaf(n[s], cs[s], pn[s] * sn[s]);
+          for (int j = 0; j < NE; ++j)
+            if (rot[j]) o[j] = fmaf(n[j], cs[j], pn[j] * sn[j]);
         }
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          const int e = s * kWave + lane;
-          if (s * kWave < D && e < D)
-            __builtin_amdgcn_raw_buffer_store_b16(narrow1<IO>(o[s]), rs[u], 2 * e, 0, kStorePolicy);
+          const int e = elem(s, 0);
+          if (s * SPAN < D && e < D) {
+            if constexpr (PW == 4) {
+              __builtin_amdgcn_raw_buffer_store_b64(
+                  u32x2_t{IO::pack(o[s * PW], o[s * PW + 1]), IO::pack(o[s * PW + 2], o[s * PW + 3])},
+                  rs[u], 2 * e, 0, kStorePolicy);
+            } else if constexpr (PW == 2) {
+              __builtin_amdgcn_raw_buffer_store_b32(IO::pack(o[s * PW], o[s * PW + 1]), rs[u], 2 * e, 0,
+                                                    kStorePolicy);
+            } else {
+              __builtin_amdgcn_raw_buffer_store_b16(narrow1<IO>(o[s]), rs[u], 2 * e, 0, kStorePolicy);
+            }
+          }
         }
       }
     }
@@ -839,8 +892,8 @@ template <class IO, int GROUP>
 const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int shift);
 
 // Group 3: the element-granular kernel of a mode (kFused ... kLayerOnly) with
-// S slots per lane (1, 2, 4 or 8).
+// S slots per lane (1, 2, 4 or 8) of pw elements each (1, 2 or 4; S * pw <= 8).
 template <class IO>
-const void* pick_elem(int mode, int slots);
+const void* pick_elem(int mode, int slots, int pw);
 
 }  // namespace qknr_impl

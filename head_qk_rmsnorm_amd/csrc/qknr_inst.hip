@@ -4,7 +4,8 @@
 // parallel; the host library (qknr.hip) calls pick_group<IO, GROUP> (the
 // vectorised kernel: group 0 the fused op at head_dim 64/128/256, group 1 the
 // other modes there, groups 2 and 4 the run-time head_dims at unroll 2 and 4)
-// and pick_elem<IO> (group 3, the element-granular kernel).
+// and pick_elem<IO> (group 3, the element-granular kernel with 2-, 4- or
+// 8-byte accesses).
 
 #include "qknr_device.h"
 
@@ -190,30 +191,44 @@ const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int 
 }
 
 #if QKNR_INST_GROUP == 3
-template <class IO, int MODE>
+template <class IO, int MODE, int PW>
 const void* pick_elem_slots(int slots) {
   switch (slots) {
-    case 1: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 1>);
-    case 2: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 2>);
-    case 4: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 4>);
-    case 8: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 8>);
+    case 1: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 1, PW>);
+    case 2: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 2, PW>);
+    case 4:
+      if constexpr (PW <= 2) return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 4, PW>);
+      return nullptr;
+    case 8:
+      if constexpr (PW == 1) return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 8, 1>);
+      return nullptr;
+    default: return nullptr;
+  }
+}
+
+template <class IO, int MODE>
+const void* pick_elem_pw(int slots, int pw) {
+  switch (pw) {
+    case 1: return pick_elem_slots<IO, MODE, 1>(slots);
+    case 2: return pick_elem_slots<IO, MODE, 2>(slots);
+    case 4: return pick_elem_slots<IO, MODE, 4>(slots);
     default: return nullptr;
   }
 }
 
 template <class IO>
-const void* pick_elem(int mode, int slots) {
+const void* pick_elem(int mode, int slots, int pw) {
   switch (mode) {
-    case kFused: return pick_elem_slots<IO, kFused>(slots);
-    case kNormOnly: return pick_elem_slots<IO, kNormOnly>(slots);
-    case kRopeOnly: return pick_elem_slots<IO, kRopeOnly>(slots);
-    case kLayerRope: return pick_elem_slots<IO, kLayerRope>(slots);
-    case kLayerOnly: return pick_elem_slots<IO, kLayerOnly>(slots);
+    case kFused: return pick_elem_pw<IO, kFused>(slots, pw);
+    case kNormOnly: return pick_elem_pw<IO, kNormOnly>(slots, pw);
+    case kRopeOnly: return pick_elem_pw<IO, kRopeOnly>(slots, pw);
+    case kLayerRope: return pick_elem_pw<IO, kLayerRope>(slots, pw);
+    case kLayerOnly: return pick_elem_pw<IO, kLayerOnly>(slots, pw);
     default: return nullptr;
   }
 }
 
-template const void* pick_elem<QKNR_INST_IO>(int, int);
+template const void* pick_elem<QKNR_INST_IO>(int, int, int);
 #else
 template const void* pick_group<QKNR_INST_IO, QKNR_INST_GROUP>(int, int, bool, bool, int, int, int);
 #endif

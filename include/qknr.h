@@ -38,9 +38,13 @@
  *     stride a multiple of 16 bytes; lane offsets inside a head group below
  *     2^31 bytes (a mapping with fewer heads per group is tried first); and,
  *     for the unfused steps, head_dim 64, 128 or 256;
- *   - the element-granular kernel (2-byte accesses, one head per wave
- *     instruction) for every other supported case. It needs only element
- *     alignment and has no stride limit; it computes the same formulas.
+ *   - the element-granular kernel (one head per wave instruction) for every
+ *     other supported case, with 2-, 4- or 8-byte accesses: 8 (4) bytes need
+ *     head_dim a multiple of 4 (2) and q, k, weights (and biases) and every
+ *     used stride 8 (4)-byte aligned; of the allowed widths it takes the
+ *     narrowest that still needs no more accesses per head than the widest.
+ *     It needs only element alignment and has no stride limit; it computes
+ *     the same formulas.
  * qknr_inplace_ex reports which one a call takes (qknr_launch_info.generic).
  *
  * All entry points are thread-safe and keep no state besides small per-device
@@ -164,7 +168,10 @@ typedef struct qknr_launch_cfg {
 
 /* What a call launches (filled by qknr_inplace_ex, also for empty work, where
  * grid_blocks stays 0). On the element-granular kernel (generic = 1) a lane
- * owns elems_per_lane elements 64 apart, one head per wave instruction. */
+ * owns elems_per_lane elements in runs of access_bytes/2 (1, 2 or 4), runs 64
+ * apart, one head per wave instruction. access_bytes was added in the struct's
+ * former tail padding: the size (48 bytes) and the other offsets are
+ * unchanged. */
 typedef struct qknr_launch_info {
   int32_t lanes_per_head;
   int32_t elems_per_lane;
@@ -176,6 +183,7 @@ typedef struct qknr_launch_info {
   int32_t grid_blocks;
   int64_t items;
   int32_t generic;
+  int32_t access_bytes; /* bytes per Q/K load or store of a lane */
 } qknr_launch_info;
 
 /* qknr_inplace with an explicit launch configuration (cfg may be NULL) and an

@@ -33,6 +33,7 @@ def layout_views(T: int, Hq: int, Hkv: int, D: int, layout: str):
     head_major: storage [H, T, D] seen as [T, H, D]
     qkv:        one storage [T, (Hq + 2*Hkv) * D]; q, k side by side, v untouched after them
     shifted:    contiguous [T, H, D] starting 3 elements (6 bytes) past a 16-byte boundary
+    shifted4:   contiguous [T, H, D] starting 2 elements (4 bytes) past a 16-byte boundary
     odd_pad:    [T, H, D] with 1 spare element after each head and 1 after each token
                 (strides of an odd number of elements)
     """
@@ -52,6 +53,8 @@ def layout_views(T: int, Hq: int, Hkv: int, D: int, layout: str):
             out.append((T * H * D, [View(0, (D, T * D, 1), (T, H, D))]))
         elif layout == "shifted":
             out.append((T * H * D + 3, [View(3, (H * D, D, 1), (T, H, D))]))
+        elif layout == "shifted4":
+            out.append((T * H * D + 2, [View(2, (H * D, D, 1), (T, H, D))]))
         elif layout == "odd_pad":
             hs = D + 1
             ts = H * hs + 1

@@ -191,21 +191,63 @@ def test_rejections(kw, code):
     assert _call(**kw) == code
 
 
+def _elem_width(kw):
+    """Elements per access of the element-granular kernel: 4 (8-byte accesses)
+    when head_dim is a multiple of 4 and q, k, the weights and the used strides
+    are 8-byte aligned, 2 when head_dim is even and they are 4-byte aligned,
+    else 1."""
+    a = dict(q=P(A), k=P(A + 0x100000), wq=P(A), wk=P(A), D=128, qt=4 * 256, qh=256, kt=4 * 256,
+             kh=256)
+    a.update({n: v for n, v in kw.items() if n in a})
+
+    def aligned(b):
+        return (all(a[n].value % b == 0 for n in ("q", "k", "wq", "wk"))
+                and all(a[n] % b == 0 for n in ("qt", "qh", "kt", "kh")))
+
+    return elem_width(a["D"], 8 if aligned(8) else 4 if aligned(4) else 2)
+
+
+def elem_width(D, align):
+    """The widest run length the alignment allows gives the fewest slots per
+    lane; the narrowest run length with that many slots is taken."""
+    def slots(pw):
+        s = 1
+        while 64 * s * pw < D:
+            s *= 2
+        return s
+
+    pw = 4 if D % 4 == 0 and align >= 8 else 2 if D % 2 == 0 and align >= 4 else 1
+    fewest = slots(pw)
+    while pw > 1 and slots(pw // 2) <= fewest:
+        pw //= 2
+    return pw
+
+
+def test_element_width_rule_covers_every_width():
+    assert {_elem_width(kw) for kw in GENERIC} == {1, 2, 4}
+    # head_dim 100 and 128 take pairs, 200 and 256 runs of 4, 64 and 40 single elements
+    assert [elem_width(D, 8) for D in (100, 128, 200, 256, 64, 40, 300, 512)] == [2, 2, 4, 4, 1, 1, 4, 4]
+    assert [elem_width(D, 4) for D in (100, 200, 130, 45)] == [2, 2, 2, 1]
+
+
 @pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: run on a host without a GPU")
 @pytest.mark.parametrize("kw", GENERIC, ids=lambda v: str(v))
 def test_element_granular_cases_are_accepted(kw):
     rc, info = _call_info(**kw)
     assert rc == B.QKNR_E_DEVICE, B.qknr_status_string(rc)
     D = kw.get("D", 128)
+    pw = _elem_width(kw)
     assert info["generic"] == 1 and info["lanes_per_head"] == 64 and info["heads_per_wave"] == 1
-    assert info["elems_per_lane"] == -(-D // 64)
+    assert info["access_bytes"] == 2 * pw
+    assert info["elems_per_lane"] == pw * -(-D // (64 * pw))
     assert info["groups_per_token"] == 8  # one group per head
-    # slots per lane: the smallest power of two covering head_dim / 64; 16/slots
-    # heads are loaded before the first is computed, two such rounds per item
+    # slots per lane: the smallest power of two covering head_dim / (64 pw);
+    # 16/(slots pw) heads are loaded before the first is computed, two such
+    # rounds per item
     slots = 1
-    while 64 * slots < D:
+    while 64 * slots * pw < D:
         slots *= 2
-    U = 16 // slots
+    U = 16 // (slots * pw)
     cfg = kw.get("cfg")
     want = min(cfg.groups_per_item if cfg is not None and cfg.groups_per_item else 2 * U, 8)
     assert info["groups_per_item"] == want and info["unroll"] == U
@@ -356,26 +398,32 @@ def test_plan_explicit_cfg():
                                               block_waves=8))
     assert info == dict(lanes_per_head=32, elems_per_lane=4, heads_per_wave=2,
                         groups_per_token=24, groups_per_item=5, unroll=4, block_threads=512,
-                        grid_blocks=0, items=0, generic=0)
+                        grid_blocks=0, items=0, generic=0, access_bytes=8)
 
 
 def test_plan_element_granular():
     """head_dims the vectorised kernel does not take, NeoX halves that are not
     a multiple of a lane width, and an explicit request, plan one head per
-    wave instruction with elements 64 apart."""
-    info = _plan(100, 100, 1, Hq=7, Hkv=3)
+    wave instruction; a lane slot holds a run of 1, 2 or 4 elements (2-, 4- or
+    8-byte accesses; contiguous aligned views here), runs 64 apart."""
+    info = _plan(100, 100, 1, Hq=7, Hkv=3)   # 1 slot of pairs: 8 heads in flight
     assert info == dict(lanes_per_head=64, elems_per_lane=2, heads_per_wave=1,
                         groups_per_token=10, groups_per_item=10, unroll=8, block_threads=256,
-                        grid_blocks=0, items=0, generic=1)
-    big = _plan(300, 300, 1, Hq=30, Hkv=10)  # 8 slots: 2 heads in flight, 4 per item
-    assert (big["elems_per_lane"], big["unroll"], big["groups_per_item"]) == (5, 2, 4)
-    small = _plan(40, 6, 1, Hq=30, Hkv=10)   # 1 slot: 16 heads in flight, 32 per item
+                        grid_blocks=0, items=0, generic=1, access_bytes=4)
+    big = _plan(300, 300, 1, Hq=30, Hkv=10)  # 2 slots of 4: 2 heads in flight, 4 per item
+    assert (big["elems_per_lane"], big["unroll"], big["groups_per_item"]) == (8, 2, 4)
+    wide = _plan(200, 98, 1, Hq=30, Hkv=10)  # 1 slot of 4: 4 heads in flight, 8 per item
+    assert (wide["elems_per_lane"], wide["unroll"], wide["access_bytes"]) == (4, 4, 8)
+    small = _plan(40, 6, 1, Hq=30, Hkv=10)   # 1 slot of 1: 16 heads in flight, 32 per item
     assert (small["elems_per_lane"], small["unroll"], small["groups_per_item"]) == (1, 16, 32)
+    odd = _plan(45, 6, 1, Hq=30, Hkv=10)     # odd head_dim: 2-byte accesses, 1 slot, 16 heads
+    assert (odd["elems_per_lane"], odd["unroll"], odd["access_bytes"]) == (1, 16, 2)
     assert _plan(72, 70, 1)["generic"] == 1          # NeoX half 35: no lane width divides it
     assert _plan(72, 72, 1)["elems_per_lane"] == 8   # NeoX half 36 = 8*4 + 4: 16-byte lanes
     assert _plan(72, 68, 1)["elems_per_lane"] == 8   # NeoX half 34 = 8*4 + 2: shifted partners
     assert _plan(72, 72, 0)["generic"] == 0          # interleaved: 16-byte lanes
-    assert _plan(130, 64, 0)["elems_per_lane"] == 3  # not a multiple of 8
+    assert _plan(130, 64, 0)["elems_per_lane"] == 4  # not a multiple of 8: pairs in 2 slots
+    assert _plan(132, 64, 0)["access_bytes"] == 8    # a multiple of 4: runs of 4
     forced = _plan(128, 128, 0, cfg=B.LaunchCfg(generic=1, groups_per_item=48, block_waves=2))
     assert forced["generic"] == 1 and forced["groups_per_item"] == 48
     assert forced["block_threads"] == 128

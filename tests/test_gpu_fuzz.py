@@ -32,7 +32,7 @@ def _draw(i):
     dt = W.BF16 if g.random() < 0.6 else W.FP16
     pdt = W.I32 if g.random() < 0.5 else W.I64
     layout = str(g.choice(["contiguous", "contiguous", "padded", "head_major", "qkv", "shifted",
-                           "odd_pad"]))
+                           "odd_pad", "shifted4"]))
     eps = float(g.choice([1e-6, 1e-5, 1e-3, 0.0]))
     launch = None
     if g.random() < 0.5:

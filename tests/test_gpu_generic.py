@@ -9,6 +9,7 @@ import pytest
 
 from head_qk_rmsnorm_amd import workloads as W
 from tests import qknr_harness as Hn
+from tests.test_abi import elem_width
 
 pytestmark = pytest.mark.gpu
 
@@ -71,9 +72,11 @@ def test_shapes(D, R, neox):
     print("case", cfg.name, flush=True)
     info, _, _ = _check(W.make_workload(cfg))
     assert info["generic"] == (0 if _vectorised(D, R, neox) else 1), info
+    if info["generic"]:  # contiguous, aligned views: the access width follows head_dim
+        assert info["access_bytes"] == 2 * elem_width(D, 8), info
 
 
-@pytest.mark.parametrize("layout", ["shifted", "odd_pad", "padded", "head_major", "qkv"])
+@pytest.mark.parametrize("layout", ["shifted", "shifted4", "odd_pad", "padded", "head_major", "qkv"])
 @pytest.mark.parametrize("D,R,neox", [(128, 128, False), (128, 64, True), (100, 100, True),
                                       (72, 72, True), (64, 2, True), (3, 2, False)])
 def test_layouts(layout, D, R, neox):
@@ -81,8 +84,11 @@ def test_layouts(layout, D, R, neox):
     print("case", cfg.name, layout, flush=True)
     info, _, _ = _check(W.make_workload(cfg), layout=layout)
     element_aligned_only = layout in ("shifted", "odd_pad")
-    want = 0 if (_vectorised(D, R, neox) and not element_aligned_only) else 1
+    want = 0 if (_vectorised(D, R, neox) and layout not in ("shifted", "shifted4", "odd_pad")) else 1
     assert info["generic"] == want, (layout, info)
+    if want:  # 8-byte (4-byte) accesses need head_dim % 4 (% 2) == 0 and 8 (4)-byte aligned views
+        view_align = 2 if element_aligned_only else 4 if layout == "shifted4" else 8
+        assert info["access_bytes"] == 2 * elem_width(D, view_align), (layout, info)
 
 
 @pytest.mark.parametrize("D,R,neox", [(64, 64, True), (64, 32, False), (128, 128, False),
@@ -166,7 +172,8 @@ def test_deterministic_and_side_stream():
 @pytest.mark.parametrize("which", ["norm", "rope", "unfused"])
 @pytest.mark.parametrize("D,R,neox,layout", [(100, 100, True, None), (72, 72, True, "odd_pad"),
                                              (3, 2, False, None), (130, 64, True, "shifted"),
-                                             (128, 128, True, "shifted"), (512, 510, True, None)])
+                                             (128, 128, True, "shifted"), (512, 510, True, None),
+                                             (130, 64, True, "shifted4"), (100, 26, True, "shifted4")])
 def test_unfused_steps(which, D, R, neox, layout):
     cfg = W.case(33, 5, 3, D, R, neox, dtype=W.FP16, pos_dtype=W.I64, seed=D + R + 3)
     print("case", which, cfg.name, layout, flush=True)
@@ -176,7 +183,7 @@ def test_unfused_steps(which, D, R, neox, layout):
 @pytest.mark.parametrize("D,R,neox,bias,layout", [
     (100, 0, False, True, None), (100, 100, True, True, None), (72, 72, True, False, "odd_pad"),
     (3, 2, True, True, None), (130, 0, False, False, "shifted"), (128, 64, True, True, "shifted"),
-    (512, 510, False, True, None)])
+    (512, 510, False, True, None), (128, 64, True, True, "shifted4"), (100, 26, True, True, None)])
 def test_layernorm_sibling(D, R, neox, bias, layout):
     cfg = W.case(41, 5, 3, D, R if R else D - D % 2, neox, dtype=W.BF16, pos_dtype=W.I64,
                  seed=D + R + 11, x_std=2.0)
