@@ -652,3 +652,12 @@ def test_every_supported_shape_plans_an_existing_instance():
                                                 0, 0, 0, 0, z) == 0, (D, R, neox)
                 n += 1
     assert n == 2 * sum(D // 2 for D in range(2, 513))
+
+
+def test_launch_info_layout():
+    """qknr_launch_info keeps its 48-byte size: access_bytes sits in what was
+    the tail padding after generic, so callers built with the earlier layout
+    are not written past."""
+    assert ctypes.sizeof(B.LaunchInfo) == 48
+    assert B.LaunchInfo.items.offset == 32 and B.LaunchInfo.generic.offset == 40
+    assert B.LaunchInfo.access_bytes.offset == 44
