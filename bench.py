@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--head-dim-scan", action="store_true",
                     help="also time head_dims other than 128 at the DiT workload's bytes per "
                          "launch (24+24 heads, int64 positions), automatic launch")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP-graph replays of one pass over the rotated copies instead of "
+                         "launches from Python (for workloads shorter than the host's launch time)")
     ap.add_argument("--extra-out", default="", help="file for per-config / sweep JSON lines")
     return ap.parse_args()
 
@@ -81,7 +84,7 @@ def parse():
 class Rig:
     """Device copies of one workload and prepared launches over them."""
 
-    def __init__(self, cfg, dev, launch=None, n_rot=None):
+    def __init__(self, cfg, dev, launch=None, n_rot=None, graph=False):
         import numpy as np
         import torch
 
@@ -89,6 +92,10 @@ class Rig:
 
         self.cfg = cfg
         self.dev = dev
+        # graph mode: one pass over the rotated copies captured in a HIP graph
+        # and replayed, so host launch overhead stays out of the timing
+        self.gstream = torch.cuda.Stream(device=dev) if graph else None
+        self.graph = None
         wl = W.make_workload(cfg)
         tdt = torch.bfloat16 if cfg.dtype == W.BF16 else torch.float16
 
@@ -143,15 +150,44 @@ class Rig:
             q, k = self.views(bufs)
             self.calls.append(B.PreparedCall(q, k, self.wq, self.wk, self.cache, pos,
                                              is_neox=c.is_neox, eps=c.eps, launch=launch,
-                                             unfused=unfused, layernorm_bias=bias))
+                                             unfused=unfused, layernorm_bias=bias,
+                                             stream=self.gstream))
         self.calls[0]()
         torch.cuda.synchronize(self.dev)
         self.info = self.calls[0].info.as_dict()
+        self.graph = None
+        if self.gstream is not None:
+            for call in self.calls:  # one eager pass on the capture stream first
+                call()
+            torch.cuda.synchronize(self.dev)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=self.gstream):
+                for call in self.calls:
+                    call()
+            torch.cuda.synchronize(self.dev)
+            self.graph = g
 
     def time(self, steps, warmup):
         import torch
 
         n = self.n_rot
+        if self.graph is not None:
+            # whole passes over the copies: steps and warmup rounded up to multiples of n
+            reps, wreps = max(1, -(-steps // n)), max(1, -(-warmup // n))
+            for _ in range(wreps):
+                self.graph.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            h0 = time.perf_counter()
+            e0.record()
+            for _ in range(reps):
+                self.graph.replay()
+            e1.record()
+            host_s = time.perf_counter() - h0
+            torch.cuda.synchronize()
+            wall_s = time.perf_counter() - h0
+            return e0.elapsed_time(e1) / (reps * n), host_s / (reps * n) * 1e3, wall_s
         for i in range(warmup):
             self.calls[i % n]()
         torch.cuda.synchronize()
@@ -264,11 +300,11 @@ def unfused_bytes(cfg):
 
 
 def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None, want_unfused=True,
-            op="fused"):
+            op="fused", graph=False):
     own = rig is None
     layernorm = op == "layernorm"
     if own:
-        rig = Rig(cfg, dev, launch=launch)
+        rig = Rig(cfg, dev, launch=launch, graph=graph)
     if layernorm:
         rig.prepare(layernorm=True)
     elif not own:
@@ -281,7 +317,7 @@ def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None, want_unfu
         "workload": cfg.name, "ms_per_step": ms, "GB_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
         "gheads_per_s": cfg.units / (ms * 1e-3) / 1e9, "host_ms_per_launch": host_ms,
         "algorithmic_bytes": B, "n_rot": rig.n_rot, "footprint_bytes": rig.footprint,
-        "launch": rig.info, "op": op,
+        "launch": rig.info, "op": op, "graph": rig.gstream is not None,
     }
     if want_unfused and not layernorm:
         rig.prepare(unfused=True)
@@ -364,7 +400,7 @@ def main():
     print(f"[bench] calibration copies done: {calib}", file=sys.stderr, flush=True)
 
     if args.sweep or args.sweep_grid:
-        rig = Rig(cfg, dev)
+        rig = Rig(cfg, dev, graph=args.graph)
         for lc in (SWEEP_GRID if args.sweep_grid else SWEEP):
             try:
                 r = measure(cfg, dev, args.steps, args.warmup, lc, want_yard=False, rig=rig,
@@ -382,7 +418,7 @@ def main():
         for name in names:
             r = measure(W.CONFIGS[name], dev, args.steps, args.warmup, launch,
                         want_yard=not args.no_yardstick, want_unfused=not args.no_unfused,
-                        op=args.op)
+                        op=args.op, graph=args.graph)
             msg = (f"[bench] {name}: {r['GB_s']:.1f} GB/s ({r['frac_of_peak'] * 100:.1f}% of peak), "
                    f"{r['gheads_per_s']:.2f} Gheads/s")
             if "yardstick_GB_s" in r:
@@ -399,7 +435,7 @@ def main():
         for D, R, neox in HEAD_DIM_SCAN:
             c = head_dim_scan_case(D, R, neox)
             r = measure(c, dev, args.steps, args.warmup, None, want_yard=False,
-                        want_unfused=False, op=args.op)
+                        want_unfused=False, op=args.op, graph=args.graph)
             r["scan"] = {"head_dim": D, "rope_dim": R, "pairing": "neox" if neox else "interleaved"}
             print(f"[bench] scan {c.name}: {r['GB_s']:.1f} GB/s, launch {r['launch']}",
                   file=sys.stderr, flush=True)
@@ -408,7 +444,7 @@ def main():
                 extra.flush()
 
     r = measure(cfg, dev, args.steps, args.warmup, launch, want_yard=not args.no_yardstick,
-                want_unfused=not args.no_unfused, op=args.op)
+                want_unfused=not args.no_unfused, op=args.op, graph=args.graph)
     print(f"[bench] {cfg.name}: {r['GB_s']:.1f} GB/s, {r['ms_per_step'] * 1e3:.2f} us/launch",
           file=sys.stderr, flush=True)
     ent, why = counters_for(cfg.name) if args.op == "fused" else (None, "counters cover the fused op")
@@ -433,6 +469,7 @@ def main():
                    "rotated_copies": r["n_rot"]},
         "gheads_per_s": round(r["gheads_per_s"], 4),
         "frac_of_hbm_peak": round(r["frac_of_peak"], 5),
+        "launch_mode": "hip graph replay" if args.graph else "eager launches from python",
         "roofline": roof,
     }
     if ent is None:
