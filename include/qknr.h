@@ -153,9 +153,12 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
  *                    vectorised one applies (lanes_per_head must then be 0);
  *                    0: choose [0].
  * On the element-granular kernel a "group" is one head: groups_per_item is
- * the heads per work item [4], block_waves and max_blocks apply as above,
- * unroll is fixed at 2 (any valid value is accepted), and lanes_per_head must
- * be 0 (an explicit lane mapping that the case cannot use is QKNR_E_ARG).
+ * the heads per work item [twice the heads loaded together], block_waves and
+ * max_blocks apply as above, unroll is set by the kernel instance (16/(S*r)
+ * heads loaded before the first is computed, with S slots of r elements per
+ * lane; reported in qknr_launch_info.unroll; any valid value is accepted), and
+ * lanes_per_head must be 0 (an explicit lane mapping that the case cannot use
+ * is QKNR_E_ARG).
  */
 typedef struct qknr_launch_cfg {
   int32_t lanes_per_head;
