@@ -303,6 +303,10 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
             : pl->L <= 16      ? kDefaultBlockWavesNarrow
                                : kDefaultBlockWaves;
   pl->max_blocks = c.max_blocks;
+  // partners 2 or 6 slots over are exchanged through a per-wave LDS row of
+  // 64 lanes x E floats
+  if (pl->shift == 2 || pl->shift == 6)
+    pl->lds = static_cast<size_t>(pl->wpb) * kWave * E * sizeof(float);
   pl->fn = pick_kernel(dtype, dmax, E, neox != 0, R == D, U, mode, exact, pl->shift);
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
 }
@@ -559,7 +563,7 @@ int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
   prm.nc = pl.nc;
   prm.n_items = static_cast<int32_t>(pl.items);
   void* args[] = {&qarg, &karg, &wqarg, &wkarg, &carg, &parg, &bqarg, &bkarg, &prm};
-  if (hipLaunchKernel(pl.fn, dim3(grid), dim3(threads), args, 0, c.stream) != hipSuccess)
+  if (hipLaunchKernel(pl.fn, dim3(grid), dim3(threads), args, pl.lds, c.stream) != hipSuccess)
     return QKNR_E_LAUNCH;
   return QKNR_OK;
 }

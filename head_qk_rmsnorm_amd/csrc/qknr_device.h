@@ -161,6 +161,14 @@ __device__ __forceinline__ float lane_fetch(int byte_addr, float v) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(byte_addr, __float_as_int(v)));
 }
 
+// Order this wave's LDS accesses around a row exchange (a wave's LDS accesses
+// execute in order; the fences keep the compiler from moving them).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // ----------------------------------------------------------------------------
 // Kernel
 // ----------------------------------------------------------------------------
@@ -261,6 +269,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   static_assert(SHIFT == 0 || ((SHIFT == 2 || SHIFT == 4 || SHIFT == 6) && NEOX && E == 8),
                 "partner slot shift");
   constexpr bool kShift26 = SHIFT == 2 || SHIFT == 6;
+  extern __shared__ float shift_rows[];  // SHIFT 2/6: kWave * E floats per wave
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
@@ -348,23 +357,23 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
       lo_s[k] = lo;
     }
   }
-  // SHIFT 2 or 6, with R/2 = 8m + SHIFT: a first-half element i pairs with slot
-  // (i+SHIFT)&7 of lane li+m (i < 8-SHIFT) or li+m+1, a second-half element
-  // with slot (i-SHIFT)&7 of lane li-m-1 (i < SHIFT) or li-m. The two halves
-  // read different source registers, so every element takes both fetches and
-  // keeps the one its half needs. Partner lanes outside the head (never needed
-  // by the element that computes them) fall back to the lane itself. Pairs of
-  // dims (2p, 2p+1) lie in one half and on one side of the rotation end (R/2
-  // and R are even), so cos/sin are read in aligned pairs.
-  int pb_lo[2] = {lane << 2, lane << 2}, pb_up[2] = {lane << 2, lane << 2};
+  // SHIFT 2 or 6, with R/2 = 8m + SHIFT: a partner sits 2 or 6 slots over, and
+  // the first and second halves of a lane would need different source
+  // registers, so the normalised values go through this wave's row of LDS
+  // instead (E floats per lane, lane-major: a head's dims are contiguous from
+  // its first lane's slot). Pair (2p, 2p+1) of this lane reads the pair at its
+  // partner dims, 8-byte aligned: R/2 and R are even, so a pair lies in one
+  // half and on one side of the rotation end. Pairs that do not rotate (pass-
+  // through dims, spare lanes) read themselves; cos/sin come as aligned pairs.
+  int pidx[kShift26 ? E / 2 : 1];
   if constexpr (kShift26) {
-    const int m = half >> 3;
-    const int head_lane0 = lane - li;
-    auto addr = [&](int pl) { return ((in_head && pl >= 0 && pl < L) ? head_lane0 + pl : lane) << 2; };
-    pb_lo[0] = addr(li + m);
-    pb_lo[1] = addr(li + m + 1);
-    pb_up[0] = addr(li - m - 1);
-    pb_up[1] = addr(li - m);
+    const int head0 = (lane - li) * E;
+#pragma unroll
+    for (int q2 = 0; q2 < E / 2; ++q2) {
+      const int d = d0 + 2 * q2;
+      const bool rot = in_head && d < 2 * half;
+      pidx[q2] = rot ? head0 + (d < half ? d + half : d - half) : lane * E + 2 * q2;
+    }
   }
   const bool ro_26[2] = {in_head && d0 < 2 * half, in_head && d0 + 4 < 2 * half};
   const bool cs_pairs = kShift26 && (reinterpret_cast<uintptr_t>(cache) & 7) == 0;
@@ -425,10 +434,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 
     // cos / sin of this lane's dims at this token (loaded after the head data
     // is in flight; kept in registers for every group of the item)
-    // SHIFT 2/6: sn weighs the fetch from d + R/2 (first-half dims, negated)
-    // and sb the fetch from d - R/2 (second-half dims); the other one is 0, so
-    // no element selects between its two fetches.
-    float cs[NCS], sn[NCS], sb[kShift26 ? NCS : 1];
+    float cs[NCS], sn[NCS];
     if constexpr (kRotate) {
       const float* row = cache + pos * R;
       if constexpr (kShift26) {
@@ -446,8 +452,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
             c0 = row[j]; c1 = row[j + 1]; s0 = row[half + j]; s1 = row[half + j + 1];
           }
           cs[2 * q2] = c0; cs[2 * q2 + 1] = c1;
-          sn[2 * q2] = lo ? -s0 : 0.0f; sn[2 * q2 + 1] = lo ? -s1 : 0.0f;
-          sb[2 * q2] = lo ? 0.0f : s0; sb[2 * q2 + 1] = lo ? 0.0f : s1;
+          sn[2 * q2] = lo ? -s0 : s0; sn[2 * q2 + 1] = lo ? -s1 : s1;
         }
       } else if constexpr (SHIFT == 4) {
 #pragma unroll
@@ -543,12 +548,19 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
         } else if constexpr (kShift26) {
           // R = 16m + 2*SHIFT ends on slot 4 of a lane: each run of 4 slots is
           // rotated as a whole or passed through
+          float* const xrow = shift_rows + wib * (kWave * E);
+          wave_lds_fence();  // the previous group's reads are done
+          *reinterpret_cast<float4*>(xrow + lane * E) = make_float4(n[0], n[1], n[2], n[3]);
+          *reinterpret_cast<float4*>(xrow + lane * E + 4) = make_float4(n[4], n[5], n[6], n[7]);
+          wave_lds_fence();
 #pragma unroll
-          for (int i = 0; i < E; ++i) {
-            const float a = lane_fetch(pb_lo[i >= 8 - SHIFT ? 1 : 0], n[(i + SHIFT) & 7]);
-            const float b = lane_fetch(pb_up[i >= SHIFT ? 1 : 0], n[(i + 8 - SHIFT) & 7]);
-            const float v = fmaf(n[i], cs[i], fmaf(a, sn[i], b * sb[i]));
-            o[i] = (FULL || ro_26[i >> 2]) ? v : n[i];
+          for (int q2 = 0; q2 < E / 2; ++q2) {
+            const float2 pn = *reinterpret_cast<const float2*>(xrow + pidx[q2]);
+            const int i = 2 * q2;
+            const float v0 = fmaf(n[i], cs[i], pn.x * sn[i]);
+            const float v1 = fmaf(n[i + 1], cs[i + 1], pn.y * sn[i + 1]);
+            o[i] = (FULL || ro_26[i >> 2]) ? v0 : n[i];
+            o[i + 1] = (FULL || ro_26[i >> 2]) ? v1 : n[i + 1];
           }
         } else if constexpr (SHIFT == 4) {
 #pragma unroll
@@ -620,14 +632,6 @@ struct ElemParams {
   int32_t neox, pos64, has_bias;
   int32_t hpi, nc, n_items;              // heads per item, items per token, items
 };
-
-// Order this wave's LDS accesses around a row exchange (a wave's LDS accesses
-// execute in order; the fences keep the compiler from moving them).
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
 // one I/O element <-> fp32 (the low half of the packed conversions above)
 template <class IO>
