@@ -607,11 +607,10 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 // differs.
 //
 // One head vector per wave instruction. A lane slot holds PW consecutive
-// elements: PW = 4 (8-byte accesses) when head_dim is a multiple of 4 and every
-// pointer and stride is 8-byte aligned, PW = 2 (4-byte accesses) when head_dim
-// is even and they are 4-byte aligned, else PW = 1 (2-byte accesses). Element e sits
-// in lane (e / PW) % 64, slot e / (64 PW), S slots (a power of two covering
-// head_dim <= 512). Every access is a buffer access relative to the head's own
+// elements (PW = 1, 2 or 4: 2-, 4- or 8-byte accesses); PW divides head_dim and
+// every pointer and used stride is 2*PW-byte aligned (the host picks PW).
+// Element e sits in lane (e / PW) % 64, slot e / (64 PW), S slots (a power of
+// two covering head_dim <= 512). Every access is a buffer access relative to the head's own
 // base address, which is wave-uniform (64-bit, no limit on strides); lane
 // offsets stay below 1 KiB and the descriptor covers exactly the head vector.
 // Interleaved partners (e, e ^ 1) lie in one slot (PW = 2, 4) or in
