@@ -66,6 +66,7 @@ constexpr int kMaxBlockWaves = 8;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 struct Bf16 {
@@ -103,25 +104,17 @@ __device__ __forceinline__ Raw<NV> load_raw(const char* p) {
   if constexpr (NV == 4) {
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
     r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  } else if constexpr (NV == 3) {
+    const uint32_t* const d = reinterpret_cast<const uint32_t*>(p);
+    r.w[0] = d[0]; r.w[1] = d[1]; r.w[2] = d[2];
   } else if constexpr (NV == 2) {
     const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
     r.w[0] = v.x; r.w[1] = v.y;
   } else {
-    static_assert(NV == 1, "1, 2 or 4 dwords per lane");
+    static_assert(NV == 1, "1, 2, 3 or 4 dwords per lane");
     r.w[0] = *reinterpret_cast<const uint32_t*>(p);
   }
   return r;
-}
-
-template <int NV>
-__device__ __forceinline__ void store_raw(char* p, const Raw<NV>& r) {
-  if constexpr (NV == 4) {
-    *reinterpret_cast<u32x4_t*>(p) = u32x4_t{r.w[0], r.w[1], r.w[2], r.w[3]};
-  } else if constexpr (NV == 2) {
-    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{r.w[0], r.w[1]};
-  } else {
-    *reinterpret_cast<uint32_t*>(p) = r.w[0];
-  }
 }
 
 // ----------------------------------------------------------------------------
@@ -197,6 +190,9 @@ __device__ __forceinline__ Raw<NV> load_io(__amdgpu_buffer_rsrc_t rs, uint32_t o
   if constexpr (NV == 4) {
     const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kLoadPolicy));
     r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  } else if constexpr (NV == 3) {
+    const u32x3_t v = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(rs, off, 0, kLoadPolicy));
+    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z;
   } else if constexpr (NV == 2) {
     const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kLoadPolicy));
     r.w[0] = v.x; r.w[1] = v.y;
@@ -210,6 +206,8 @@ template <int NV>
 __device__ __forceinline__ void store_io(__amdgpu_buffer_rsrc_t rs, uint32_t off, const Raw<NV>& r) {
   if constexpr (NV == 4) {
     __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{r.w[0], r.w[1], r.w[2], r.w[3]}, rs, off, 0, kStorePolicy);
+  } else if constexpr (NV == 3) {
+    __builtin_amdgcn_raw_buffer_store_b96(u32x3_t{r.w[0], r.w[1], r.w[2]}, rs, off, 0, kStorePolicy);
   } else if constexpr (NV == 2) {
     __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{r.w[0], r.w[1]}, rs, off, 0, kStorePolicy);
   } else {
@@ -472,11 +470,15 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 #pragma unroll
           for (int i = 0; i < 4; ++i) sn[4 * k + i] = lo_s[k] ? -sn[4 * k + i] : sn[4 * k + i];
         }
-      } else if ((FULL || NEOX) && NCS % 4 == 0 && p.cs_vec) {
+      } else if (NCS % 4 == 0 && p.cs_vec) {
+        // interleaved with a partial rotation: R/2 is a multiple of 4 here, so a
+        // lane's runs of 4 pairs are rotated whole or not at all; lanes past the
+        // rotation read columns 0-3 (unused), which keeps the access in the row
+        const int jv = (FULL || NEOX || j0 < half) ? j0 : 0;
 #pragma unroll
         for (int i = 0; i < NCS; i += 4) {
-          const float4 c4 = *reinterpret_cast<const float4*>(row + j0 + i);
-          const float4 s4 = *reinterpret_cast<const float4*>(row + half + j0 + i);
+          const float4 c4 = *reinterpret_cast<const float4*>(row + jv + i);
+          const float4 s4 = *reinterpret_cast<const float4*>(row + half + jv + i);
           cs[i] = c4.x; cs[i + 1] = c4.y; cs[i + 2] = c4.z; cs[i + 3] = c4.w;
           sn[i] = s4.x; sn[i + 1] = s4.y; sn[i + 2] = s4.z; sn[i + 3] = s4.w;
         }

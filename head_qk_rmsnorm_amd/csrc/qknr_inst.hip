@@ -185,6 +185,11 @@ const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int 
       case 64: return pick_lanes<IO, 64, GROUP>(E, neox, full, U, mode);
       case 128: return pick_lanes<IO, 128, GROUP>(E, neox, full, U, mode);
       case 256: return pick_lanes<IO, 256, GROUP>(E, neox, full, U, mode);
+      case 96:  // the fused op on 12-byte lanes
+        if constexpr (GROUP == 0) {
+          if (E == 6) return pick_pairing<IO, 96, 6, GROUP>(neox, full, U, mode);
+        }
+        return nullptr;
       default: return nullptr;
     }
   }

@@ -303,7 +303,7 @@ def test_plan_lane_mapping(D):
             assert gqa["groups_per_token"] == -(-7 // gqa["heads_per_wave"]) + -(-3 // gqa["heads_per_wave"])
 
 
-@pytest.mark.parametrize("D,lanes", [(16, 2), (24, 4), (40, 8), (80, 16), (96, 16), (112, 16),
+@pytest.mark.parametrize("D,lanes", [(16, 2), (24, 4), (40, 8), (80, 16), (112, 16),
                                      (160, 32), (192, 32), (320, 64), (512, 64)])
 def test_plan_run_time_head_dims(D, lanes):
     """Other head_dims use 16-byte lanes in a lane group padded to a power of two."""
@@ -315,13 +315,13 @@ def test_plan_run_time_head_dims(D, lanes):
     assert _plan(D, D - (D % 16), 1)["lanes_per_head"] == lanes
 
 
-@pytest.mark.parametrize("D,R", [(96, 24), (80, 40), (112, 56), (80, 20), (72, 72), (40, 12),
-                                 (120, 60), (160, 40), (96, 12), (56, 20), (104, 52), (264, 264),
+@pytest.mark.parametrize("D,R", [(96, 40), (80, 40), (112, 56), (80, 20), (72, 72), (40, 12),
+                                 (120, 60), (160, 40), (96, 20), (56, 20), (104, 52), (264, 264),
                                  (200, 20), (320, 36), (504, 12), (128, 20), (64, 12), (256, 44)])
 def test_plan_neox_halves_off_the_lane_width_take_shifted_partners(D, R):
     """NeoX halves that no 16-byte lane divides keep 16-byte lanes for the fused
     op: each partner sits (rope_dim/2 mod 8) slots over in a neighbouring lane
-    (e.g. head_dim 96 with rope_dim 24, head_dim 80 with rope_dim 20)."""
+    (e.g. head_dim 96 with rope_dim 40, head_dim 80 with rope_dim 20)."""
     cap = 16
     while cap < D:
         cap *= 2
@@ -335,6 +335,35 @@ def test_plan_neox_halves_off_the_lane_width_take_shifted_partners(D, R):
 def test_plan_odd_neox_halves_use_the_element_kernel(D, R):
     info = _plan(D, R, 1)
     assert info["generic"] == 1, info
+
+
+def _fit96(D, R, neox):
+    """head_dim 96 of the fused op on 12-byte lanes: a NeoX half that is a
+    multiple of 6 but not of 8."""
+    return D == 96 and bool(neox) and (R // 2) % 6 == 0 and R // 2 >= 6 and (R // 2) % 8 != 0
+
+
+def test_plan_head_dim_96_takes_12_byte_lanes():
+    """The fused op at head_dim 96 with a NeoX half that is a multiple of 6 but
+    not of 8: 16 lanes of 6 elements (12-byte accesses, no spare lanes,
+    compile-time defaults). Every other pairing keeps the padded 16-byte-lane
+    mapping (shifted partners where needed), odd halves the element kernel.
+    Explicit unroll 1, 2 and 4 are honoured."""
+    for R in (24, 12, 72, 60, 84, 36):   # NeoX halves 12, 6, 36, 30, 42, 18
+        assert _fit96(96, R, 1)
+        i = _plan(96, R, 1)
+        assert (i["lanes_per_head"], i["elems_per_lane"], i["access_bytes"],
+                i["heads_per_wave"]) == (16, 6, 12, 4), (R, i)
+        assert (i["unroll"], i["groups_per_item"], i["block_threads"]) == (2, 2, 192), i
+    for R, neox in ((20, 1), (40, 1), (32, 1), (16, 1), (8, 1), (96, 1), (48, 1), (96, 0),
+                    (24, 0), (30, 0)):
+        assert not _fit96(96, R, neox)
+        i = _plan(96, R, neox)
+        assert (i["generic"], i["lanes_per_head"], i["elems_per_lane"]) == (0, 16, 8), (R, i)
+    assert _plan(96, 6, 1)["generic"] == 1   # odd half
+    for u in (1, 2, 4):
+        assert _plan(96, 24, 1, cfg=B.LaunchCfg(unroll=u))["unroll"] == u
+    assert _plan(96, 24, 1, cfg=B.LaunchCfg(lanes_per_head=16))["elems_per_lane"] == 6
 
 
 def test_plan_defaults():
@@ -354,7 +383,7 @@ def test_plan_defaults():
 
 
 @pytest.mark.parametrize("D,R,neox,long_items", [
-    (80, 80, 1, True), (96, 96, 1, True), (80, 32, 1, True), (160, 160, 1, True),
+    (80, 80, 1, True), (96, 96, 1, True), (96, 24, 1, False), (80, 32, 1, True), (160, 160, 1, True),
     (192, 64, 1, True), (320, 320, 1, True), (48, 48, 1, True), (40, 40, 1, True),
     (24, 24, 1, True), (112, 112, 1, True), (224, 224, 1, True), (72, 72, 1, True),
     (136, 136, 1, True), (104, 52, 1, True),
@@ -371,7 +400,8 @@ def test_plan_defaults_long_items(D, R, neox, long_items):
     info = _plan(D, R, neox)
     assert info["generic"] == 0, info
     G, L = info["heads_per_wave"], info["lanes_per_head"]
-    assert long_items == (D not in (64, 128, 256) and (neox == 1 or G * 2 * D <= 640))
+    assert long_items == (D not in (64, 128, 256) and not _fit96(D, R, neox)
+                          and (neox == 1 or G * 2 * D <= 640))
     if long_items:
         assert (info["unroll"], info["groups_per_item"], info["block_threads"]) == (4, 4, 128), info
     else:
@@ -382,7 +412,7 @@ def test_plan_defaults_long_items(D, R, neox, long_items):
     four = _plan(D, R, neox, cfg=B.LaunchCfg(unroll=4))
     assert four["unroll"] == 4
     one = _plan(D, R, neox, cfg=B.LaunchCfg(unroll=1))
-    assert one["unroll"] == (1 if D in (64, 128, 256) else 2)
+    assert one["unroll"] == (1 if D in (64, 128, 256) or _fit96(D, R, neox) else 2)
 
 
 @pytest.mark.parametrize("D,lanes,E", [(128, 64, 2), (256, 64, 4), (128, 32, 4), (64, 32, 2),

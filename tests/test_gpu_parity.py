@@ -138,7 +138,7 @@ RT_LAUNCHES = [
 
 
 @pytest.mark.parametrize("launch", RT_LAUNCHES, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
-@pytest.mark.parametrize("D,R,neox", [(80, 80, False), (96, 96, True), (72, 72, True), (104, 52, True),
+@pytest.mark.parametrize("D,R,neox", [(80, 80, False), (96, 40, True), (72, 72, True), (104, 52, True),
                                       (40, 40, False), (160, 64, True), (320, 320, False)])
 def test_run_time_launch_variants(launch, D, R, neox):
     """Run-time head_dims at unroll 2 and 4 (1 runs as 2), with work items that
@@ -171,7 +171,9 @@ def test_neox_shifted_partners(D, R, dt, launch):
     _say("case", cfg.name, launch)
     wl = W.make_workload(cfg)
     info = Hn.DeviceCase(wl).run(launch=launch or {})
-    assert info["generic"] == 0 and info["elems_per_lane"] == 8, info
+    # head_dim 96 with a NeoX half that is a multiple of 6 takes 12-byte lanes
+    twelve = D == 96 and (R // 2) % 6 == 0 and (R // 2) % 8 != 0
+    assert info["generic"] == 0 and info["elems_per_lane"] == (6 if twelve else 8), info
     Hn.run_and_check(wl, launch=launch)
 
 
@@ -208,6 +210,29 @@ def test_launch_variants(launch, D, R, neox):
     cfg = W.case(33, 7, 3, D, R, neox, dtype=W.BF16, pos_dtype=W.I64, seed=D + R)
     _say("case", cfg.name, launch)
     Hn.run_and_check(W.make_workload(cfg), launch=launch)
+
+
+# head_dim 96 of the fused op with a NeoX half that is a multiple of 6 but not
+# of 8: 12-byte lanes (16 lanes of 6 elements)
+@pytest.mark.parametrize("launch", [l for l in LAUNCHES if "lanes_per_head" not in l],
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()) or "auto")
+@pytest.mark.parametrize("D,R,neox,dt", [(96, 24, True, W.FP16), (96, 12, True, W.BF16),
+                                         (96, 72, True, W.BF16), (96, 60, True, W.FP16),
+                                         (96, 84, True, W.BF16)])
+def test_head_dim_96_twelve_byte_lanes(launch, D, R, neox, dt):
+    cfg = W.case(33, 7, 3, D, R, neox, dtype=dt, pos_dtype=W.I64, seed=D + 5 * R)
+    _say("case", cfg.name, launch)
+    wl = W.make_workload(cfg)
+    info = Hn.DeviceCase(wl).run(launch=launch)
+    assert (info["generic"], info["elems_per_lane"], info["access_bytes"]) == (0, 6, 12), info
+    Hn.run_and_check(wl, launch=launch)
+
+
+@pytest.mark.parametrize("layout", ["padded", "head_major", "qkv"])
+@pytest.mark.parametrize("D,R,neox", [(96, 72, True), (96, 36, True)])
+def test_head_dim_96_layouts(layout, D, R, neox):
+    cfg = W.case(21, 5, 3, D, R, neox, seed=D + R + 1)
+    Hn.run_and_check(W.make_workload(cfg), layout=layout)
 
 
 # ---------------------------------------------------------------------------
