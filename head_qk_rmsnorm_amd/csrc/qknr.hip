@@ -242,12 +242,14 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
     return lane_offsets_fit(G, Hq, q_head, D) && lane_offsets_fit(G, Hkv, k_head, D);
   };
   int E = 0;
-  // head_dim 96 of the fused op with a NeoX half that is a multiple of 6 but
-  // not of 8: 12-byte lanes (16 lanes of 6 elements, no spare lanes) pair it at
-  // a whole-lane distance, where 16-byte lanes would need shifted partners
-  // (measured 4-17% faster; with other pairings the 16-byte lanes are 4% faster)
-  const bool fit96 = D == 96 && mode == kFused && neox && lanes_fit(R, neox, 6) &&
-                     (R / 2) % 8 != 0 && (c.lanes_per_head == 0 || c.lanes_per_head == 16);
+  // head_dim 96 of the fused op (or the LayerNorm sibling) with a NeoX half
+  // that is a multiple of 6 but not of 8: 12-byte lanes (16 lanes of 6
+  // elements, no spare lanes) pair it at a whole-lane distance, where 16-byte
+  // lanes would need shifted partners (measured 4-17% faster; with other
+  // pairings the 16-byte lanes are 4% faster)
+  const bool fit96 = D == 96 && (mode == kFused || mode == kLayerRope) && neox &&
+                     lanes_fit(R, neox, 6) && (R / 2) % 8 != 0 &&
+                     (c.lanes_per_head == 0 || c.lanes_per_head == 16);
   const bool exact = fast_head_dim(D) || fit96;
   const int dmax = exact ? D : any_dim_capacity(D);
   if (fit96) {

@@ -185,9 +185,12 @@ const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int 
       case 64: return pick_lanes<IO, 64, GROUP>(E, neox, full, U, mode);
       case 128: return pick_lanes<IO, 128, GROUP>(E, neox, full, U, mode);
       case 256: return pick_lanes<IO, 256, GROUP>(E, neox, full, U, mode);
-      case 96:  // the fused op on 12-byte lanes
+      case 96:  // 12-byte lanes: the fused op, and the LayerNorm sibling (partial NeoX)
         if constexpr (GROUP == 0) {
           if (E == 6) return pick_pairing<IO, 96, 6, GROUP>(neox, full, U, mode);
+        } else if constexpr (GROUP == 1) {
+          if (E == 6 && neox && !full && mode == kLayerRope && U == 2)
+            return reinterpret_cast<const void*>(&qknr_kernel<IO, 96, 6, true, false, 2, kLayerRope, true>);
         }
         return nullptr;
       default: return nullptr;

@@ -33,8 +33,8 @@
  *     head_dim/64 >= 2 for head_dim 64, 128, 256), or, for the fused op and
  *     the LayerNorm sibling, any even rope_dim/2 (16-byte lanes whose partners
  *     sit 2, 4 or 6 slots over in a neighbouring lane when rope_dim/2 is not a
- *     multiple of 8; for the fused op at head_dim 96 with rope_dim/2 a
- *     multiple of 6 but not of 8, 12-byte lanes, 16 per head, instead);
+ *     multiple of 8; at head_dim 96 with rope_dim/2 a multiple of 6 but
+ *     not of 8, 12-byte lanes, 16 per head, instead);
  *     q, k, weights (and biases) 16-byte aligned and every used q/k
  *     stride a multiple of 16 bytes; lane offsets inside a head group below
  *     2^31 bytes (a mapping with fewer heads per group is tried first); and,
