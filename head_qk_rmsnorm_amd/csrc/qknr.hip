@@ -91,6 +91,12 @@ int any_dim_capacity(int32_t D) {
   return c;
 }
 
+const void* pick_seg_kernel(int dtype, bool full, int U, int mode, int shift) {
+  if (dtype == QKNR_BF16)
+    return U == 4 ? pick_seg<Bf16, 4>(full, U, mode, shift) : pick_seg<Bf16, 2>(full, U, mode, shift);
+  return U == 4 ? pick_seg<Fp16, 4>(full, U, mode, shift) : pick_seg<Fp16, 2>(full, U, mode, shift);
+}
+
 const void* pick_elem_kernel(int dtype, int mode, int slots, int pw) {
   return dtype == QKNR_BF16 ? pick_elem<Bf16>(mode, slots, pw) : pick_elem<Fp16>(mode, slots, pw);
 }
@@ -215,6 +221,7 @@ struct Plan {
   bool exact = true;   // head_dim == dmax
   bool elem = false;   // element-granular kernel (G = 1: a group is one head)
   int pw = 1;          // element-granular kernel: elements per lane slot (2-byte accesses x pw)
+  bool seg = false;    // exact-fit lane groups of a run-time head_dim (L lanes, G heads)
   int shift = 0;       // NeoX partner slot shift (0, 2, 4 or 6)
   size_t lds = 0;      // dynamic LDS bytes per workgroup
 };
@@ -242,6 +249,7 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
     return lane_offsets_fit(G, Hq, q_head, D) && lane_offsets_fit(G, Hkv, k_head, D);
   };
   int E = 0;
+  bool seg = false;
   // head_dim 96 of the fused op (or the LayerNorm sibling) with a NeoX half
   // that is a multiple of 6 but not of 8: 12-byte lanes (16 lanes of 6
   // elements, no spare lanes) pair it at a whole-lane distance, where 16-byte
@@ -260,8 +268,16 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
     // even NeoX half pairs there, with shifted partners where needed)
     E = any_dim_lanes(mode, R, neox);
     if (E == 0) return QKNR_E_UNSUPPORTED;
-    const int G = kWave / (dmax / E);
-    if (c.lanes_per_head != 0 && c.lanes_per_head != dmax / E) return QKNR_E_ARG;
+    // NeoX partners 2 or 6 slots over (an LDS exchange per head group): the
+    // fused op packs heads into exact-fit lane groups of head_dim/8 lanes (up
+    // to 32) when that fits at least 25% more heads into a wave instruction
+    // than the padded groups (measured +2 to +18%; at fewer extra heads the
+    // tree reduction it needs costs more than it saves)
+    const int lanes = D / E, sh = lane_shift(mode, R, neox, E);
+    const int g_pad = kWave / (dmax / E), g_fit = kWave / lanes;
+    seg = mode == kFused && (sh == 2 || sh == 6) && lanes <= 32 && 4 * g_fit >= 5 * g_pad;
+    const int G = kWave / (seg ? lanes : dmax / E);
+    if (c.lanes_per_head != 0 && c.lanes_per_head != (seg ? lanes : dmax / E)) return QKNR_E_ARG;
     if (!lane_offsets_fit(G, Hq, q_head, D) || !lane_offsets_fit(G, Hkv, k_head, D))
       return QKNR_E_SHAPE;
   } else if (c.lanes_per_head == 0) {
@@ -279,7 +295,7 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
     if (!(lanes_fit(R, neox, E) || (E == 8 && shifted_fits(mode, R, neox))) || !fits(E))
       return QKNR_E_ARG;
   }
-  const int L = dmax / E, G = kWave / L;
+  const int L = seg ? D / E : dmax / E, G = kWave / L;
   const bool layer = mode == kLayerRope || mode == kLayerOnly;
   const bool long_items =
       (mode == kFused || layer) && !exact && (neox || G * 2 * D <= kLongItemGroupBytes);
@@ -318,7 +334,9 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   // 64 lanes x E floats
   if (pl->shift == 2 || pl->shift == 6)
     pl->lds = static_cast<size_t>(pl->wpb) * kWave * E * sizeof(float);
-  pl->fn = pick_kernel(dtype, dmax, E, neox != 0, R == D, U, mode, exact, pl->shift);
+  pl->seg = seg;
+  pl->fn = seg ? pick_seg_kernel(dtype, R == D, U, mode, pl->shift)
+               : pick_kernel(dtype, dmax, E, neox != 0, R == D, U, mode, exact, pl->shift);
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
 }
 
@@ -573,6 +591,8 @@ int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
   prm.gpi = pl.gpi;
   prm.nc = pl.nc;
   prm.n_items = static_cast<int32_t>(pl.items);
+  prm.seg_l = pl.L;
+  prm.seg_g = pl.G;
   void* args[] = {&qarg, &karg, &wqarg, &wkarg, &carg, &parg, &bqarg, &bkarg, &prm};
   if (hipLaunchKernel(pl.fn, dim3(grid), dim3(threads), args, pl.lds, c.stream) != hipSuccess)
     return QKNR_E_LAUNCH;

@@ -131,6 +131,19 @@ constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 constexpr int kSwizzleXor16 = 0x401F;  // ds_swizzle bit mode: and 0x1f, xor 0x10
 
+// Sum over the L consecutive lanes of each head, for any L up to 32 with heads
+// packed from lane 0 (exact-fit lane groups): a tree of partial sums toward
+// the head's first lane, then a broadcast from it, so every lane of a head
+// gets the same bits. Lanes past the last head compute unused values.
+__device__ __forceinline__ float seg_sum(float v, int lane, int li, int L) {
+  for (int s = 1; s < L; s <<= 1) {
+    const float o = __int_as_float(
+        __builtin_amdgcn_ds_bpermute(((lane + s) & 63) << 2, __float_as_int(v)));
+    v += (li + s < L) ? o : 0.0f;
+  }
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane - li) << 2, __float_as_int(v)));
+}
+
 // Sum over aligned groups of L lanes; every lane of a group gets the same bits.
 // After the two quad steps a quad is uniform, so a mirror inside 8 (16) lanes
 // adds exactly the other quad (half row).
@@ -235,6 +248,7 @@ struct Params {
   int32_t has_bias;              // LayerNorm sibling: bias rows given
   float eps;
   int32_t ng, gpi, nc, n_items;  // groups per token, groups per item, items per token, items
+  int32_t seg_l, seg_g;          // exact-fit lane groups: lanes per head, heads per wave instruction
 };
 
 // What a launch computes: the fused op, one of the two steps of the unfused
@@ -253,17 +267,18 @@ enum : int { kFused = 0, kNormOnly = 1, kRopeOnly = 2, kLayerRope = 3, kLayerOnl
 // SHIFT 2, 4 or 6 (NeoX, 8 elements per lane): rope_dim/2 is that much more than
 // a multiple of 8, so a partner sits SHIFT slots over in a neighbouring lane.
 template <class IO, int DMAX, int E, bool NEOX, bool FULL, int U, int MODE, bool EXACT,
-          int SHIFT = 0>
+          int SHIFT = 0, bool SEG = false>
 __global__ void __launch_bounds__(kMaxBlockWaves * kWave)
 qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict__ wqp,
             const void* __restrict__ wkp, const float* __restrict__ cache,
             const void* __restrict__ posp, const void* __restrict__ bqp,
             const void* __restrict__ bkp, const Params p) {
-  constexpr int L = DMAX / E;   // lanes per head (lane group)
-  constexpr int G = kWave / L;  // heads per wave instruction
+  constexpr int LC = DMAX / E;    // lanes per head (lane group)
+  constexpr int GC = kWave / LC;  // heads per wave instruction
   constexpr int NV = E / 2;     // packed dwords per lane
   constexpr int NCS = NEOX ? E : E / 2;  // cos (and sin) values per lane
-  static_assert(DMAX % E == 0 && E % 2 == 0 && G >= 1, "lane mapping");
+  static_assert(DMAX % E == 0 && E % 2 == 0 && GC >= 1, "lane mapping");
+  static_assert(!SEG || (!EXACT && E == 8), "exact-fit lane groups: run-time head_dims");
   static_assert(SHIFT == 0 || ((SHIFT == 2 || SHIFT == 4 || SHIFT == 6) && NEOX && E == 8),
                 "partner slot shift");
   constexpr bool kShift26 = SHIFT == 2 || SHIFT == 6;
@@ -271,11 +286,15 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
-  const int sub = lane / L;  // head slot in the group
-  const int li = lane % L;   // lane inside the head
+  // SEG: exact-fit lane groups of head_dim/E lanes (p.seg_l, any count up to
+  // 32), p.seg_g heads per wave instruction, the lanes past them idle
+  const int L = SEG ? p.seg_l : LC;
+  const int G = SEG ? p.seg_g : GC;
+  const int sub = SEG ? lane / L : lane / LC;  // head slot in the group
+  const int li = lane - sub * L;               // lane inside the head
   const int d0 = li * E;     // first dim owned by this lane
   const int D = EXACT ? DMAX : p.D;
-  const bool in_head = EXACT || d0 < D;  // spare lanes of a run-time head_dim
+  const bool in_head = SEG ? sub < G : (EXACT || d0 < D);  // spare lanes
   const int R = FULL ? D : p.R;
   const int half = R / 2;
   const uint32_t q_off = static_cast<uint32_t>(sub) * p.q_head + d0 * 2;
@@ -375,6 +394,14 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   }
   const bool ro_26[2] = {in_head && d0 < 2 * half, in_head && d0 + 4 < 2 * half};
   const bool cs_pairs = kShift26 && (reinterpret_cast<uintptr_t>(cache) & 7) == 0;
+
+  auto head_sum = [&](float v) {
+    if constexpr (SEG) {
+      return seg_sum(v, lane, li, L);
+    } else {
+      return group_sum<LC>(v);
+    }
+  };
 
   const int total_waves = gridDim.x * wpb;
   int item = blockIdx.x * wpb + wib;
@@ -509,14 +536,14 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
           float sm = 0.0f;
 #pragma unroll
           for (int i = 0; i < E; ++i) sm += x[i];
-          const float mean = group_sum<L>(sm) * (EXACT ? 1.0f / DMAX : p.inv_d);
+          const float mean = head_sum(sm) * (EXACT ? 1.0f / DMAX : p.inv_d);
           float c[E], ss = 0.0f;
 #pragma unroll
           for (int i = 0; i < E; ++i) {
             c[i] = in_head ? x[i] - mean : 0.0f;
             ss = fmaf(c[i], c[i], ss);
           }
-          ss = group_sum<L>(ss);
+          ss = head_sum(ss);
           const float r = __builtin_amdgcn_rsqf(fmaf(ss, EXACT ? 1.0f / DMAX : p.inv_d, p.eps));
 #pragma unroll
           for (int w = 0; w < NV; ++w) {
@@ -530,7 +557,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
           float ss = 0.0f;
 #pragma unroll
           for (int i = 0; i < E; ++i) ss = fmaf(x[i], x[i], ss);
-          ss = group_sum<L>(ss);
+          ss = head_sum(ss);
           const float r = __builtin_amdgcn_rsqf(fmaf(ss, EXACT ? 1.0f / DMAX : p.inv_d, p.eps));
 #pragma unroll
           for (int w = 0; w < NV; ++w) {
@@ -895,6 +922,12 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
 // stub, or nullptr if no instance matches.
 template <class IO, int GROUP>
 const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int shift);
+
+// Groups 2 and 4 (unroll 2 and 4): the fused op with exact-fit lane groups
+// (SEG) of a run-time head_dim whose NeoX partners sit 2 or 6 slots over;
+// nullptr elsewhere.
+template <class IO, int GROUP>
+const void* pick_seg(bool full, int U, int mode, int shift);
 
 // Group 3: the element-granular kernel of a mode (kFused ... kLayerOnly) with
 // S slots per lane (1, 2, 4 or 8) of pw elements each (1, 2 or 4; S * pw <= 8).

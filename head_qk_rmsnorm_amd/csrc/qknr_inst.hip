@@ -198,6 +198,29 @@ const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int 
   }
 }
 
+// Exact-fit lane groups (SEG) for NeoX partners 2 or 6 slots over: lanes per
+// head and heads per wave instruction are run-time values, so DMAX plays no
+// part (fixed at 256).
+template <class IO, int UU, bool FULL>
+const void* pick_seg_shift(int shift) {
+  switch (shift) {
+    case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, 256, 8, true, FULL, UU, kFused, false, 2, true>);
+    case 6: return reinterpret_cast<const void*>(&qknr_kernel<IO, 256, 8, true, FULL, UU, kFused, false, 6, true>);
+    default: return nullptr;
+  }
+}
+
+template <class IO, int GROUP>
+const void* pick_seg(bool full, int U, int mode, int shift) {
+  if constexpr (GROUP == 2 || GROUP == 4) {
+    constexpr int UU = GROUP == 2 ? 2 : 4;
+    if (U != UU || mode != kFused) return nullptr;
+    return full ? pick_seg_shift<IO, UU, true>(shift) : pick_seg_shift<IO, UU, false>(shift);
+  } else {
+    return nullptr;
+  }
+}
+
 #if QKNR_INST_GROUP == 3
 template <class IO, int MODE, int PW>
 const void* pick_elem_slots(int slots) {
@@ -239,6 +262,7 @@ const void* pick_elem(int mode, int slots, int pw) {
 template const void* pick_elem<QKNR_INST_IO>(int, int, int);
 #else
 template const void* pick_group<QKNR_INST_IO, QKNR_INST_GROUP>(int, int, bool, bool, int, int, int);
+template const void* pick_seg<QKNR_INST_IO, QKNR_INST_GROUP>(bool, int, int, int);
 #endif
 
 }  // namespace qknr_impl

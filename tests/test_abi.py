@@ -327,7 +327,7 @@ def test_plan_neox_halves_off_the_lane_width_take_shifted_partners(D, R):
         cap *= 2
     info = _plan(D, R, 1)
     assert info["generic"] == 0 and info["elems_per_lane"] == 8, info
-    assert info["lanes_per_head"] == (D if D in (64, 128, 256) else cap) // 8
+    assert info["lanes_per_head"] == (D // 8 if _seg(D, R) else (D if D in (64, 128, 256) else cap) // 8)
 
 
 @pytest.mark.parametrize("D,R", [(200, 22), (320, 30), (96, 6), (504, 10), (72, 70), (200, 2),
@@ -335,6 +335,39 @@ def test_plan_neox_halves_off_the_lane_width_take_shifted_partners(D, R):
 def test_plan_odd_neox_halves_use_the_element_kernel(D, R):
     info = _plan(D, R, 1)
     assert info["generic"] == 1, info
+
+
+def _seg(D, R):
+    """Exact-fit lane groups of head_dim/8 lanes (fused op, NeoX): partners 2 or
+    6 slots over, and at least 25% more heads per wave instruction than the
+    lane group padded to a power of two."""
+    if D in (64, 128, 256) or D % 8 or D < 16 or (R // 2) % 8 not in (2, 6):
+        return False
+    lanes, cap = D // 8, 16
+    while cap < D:
+        cap *= 2
+    return lanes <= 32 and 4 * (64 // lanes) >= 5 * (64 // (cap // 8))
+
+
+@pytest.mark.parametrize("D,R,seg", [(80, 20, True), (72, 20, True), (152, 44, True), (96, 20, True),
+                                     (88, 28, True), (40, 12, True), (104, 52, False),
+                                     (120, 60, False), (200, 100, False), (56, 20, False),
+                                     (128, 20, False), (80, 40, False), (72, 72, False),
+                                     (264, 4, False)])
+def test_plan_exact_fit_lane_groups(D, R, seg):
+    """NeoX halves of 8m + 2 or 8m + 6 dims (partners through the LDS row) pack
+    heads into exact-fit groups of head_dim/8 lanes when that fits at least 25%
+    more heads into a wave instruction; otherwise the padded group stays."""
+    assert _seg(D, R) == seg
+    info = _plan(D, R, 1)
+    cap = 16
+    while cap < D:
+        cap *= 2
+    lanes = D // 8 if seg else (D if D in (64, 128, 256) else cap) // 8
+    assert (info["generic"], info["elems_per_lane"], info["lanes_per_head"]) == (0, 8, lanes), info
+    assert info["heads_per_wave"] == 64 // lanes
+    G = 64 // lanes
+    assert info["groups_per_token"] == -(-24 // G) * 2
 
 
 def _fit96(D, R, neox):
@@ -359,7 +392,8 @@ def test_plan_head_dim_96_takes_12_byte_lanes():
                     (24, 0), (30, 0)):
         assert not _fit96(96, R, neox)
         i = _plan(96, R, neox)
-        assert (i["generic"], i["lanes_per_head"], i["elems_per_lane"]) == (0, 16, 8), (R, i)
+        lanes = 12 if neox and _seg(96, R) else 16   # 96/20: exact-fit groups of 12 lanes
+        assert (i["generic"], i["lanes_per_head"], i["elems_per_lane"]) == (0, lanes, 8), (R, i)
     assert _plan(96, 6, 1)["generic"] == 1   # odd half
     for u in (1, 2, 4):
         assert _plan(96, 24, 1, cfg=B.LaunchCfg(unroll=u))["unroll"] == u

@@ -158,7 +158,8 @@ def test_run_time_launch_variants(launch, D, R, neox):
 SHIFTED = [(96, 24), (72, 72), (40, 40), (88, 88), (136, 136), (264, 264), (200, 200), (120, 8),
            (16, 8), (64, 24), (128, 40), (128, 8), (256, 104), (256, 24),
            (80, 20), (96, 12), (40, 12), (56, 20), (104, 52), (120, 60), (200, 100), (504, 12),
-           (16, 4), (24, 12), (128, 20), (64, 12), (256, 44), (128, 4), (64, 60)]
+           (16, 4), (24, 12), (128, 20), (64, 12), (256, 44), (128, 4), (64, 60),
+           (72, 20), (152, 44), (88, 28), (96, 20), (168, 44)]
 SHIFTED_LAUNCHES = [None, dict(unroll=4, groups_per_item=3), dict(unroll=2, groups_per_item=1, block_waves=1)]
 
 
