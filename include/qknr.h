@@ -135,6 +135,10 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
  *                    rope_dim/2 to be a multiple of head_dim/lanes_per_head.
  *                    [the first of head_dim/8, 32, 64 that fits the pairing and
  *                    the lane-offset limit; none: the element-granular kernel]
+ *                    Other head_dims take only their automatic mapping (0, or
+ *                    its lane count as qknr_launch_info reports it): head_dim/8
+ *                    lanes padded to a power of two, or exact-fit groups of
+ *                    head_dim/8 lanes, or 16 lanes of 12 bytes at head_dim 96.
  *   groups_per_item  head groups (one per wave instruction: 64/lanes_per_head
  *                    heads of one token) that a wave handles per work item;
  *                    a work item never spans two tokens. [2; 4 for "long
