@@ -268,14 +268,17 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
     // even NeoX half pairs there, with shifted partners where needed)
     E = any_dim_lanes(mode, R, neox);
     if (E == 0) return QKNR_E_UNSUPPORTED;
-    // NeoX partners 2 or 6 slots over (an LDS exchange per head group): the
-    // fused op packs heads into exact-fit lane groups of head_dim/8 lanes (up
-    // to 32) when that fits at least 25% more heads into a wave instruction
-    // than the padded groups (measured +2 to +18%; at fewer extra heads the
-    // tree reduction it needs costs more than it saves)
+    // NeoX partners 2 or 6 slots over (an LDS exchange per head group): heads
+    // go into exact-fit lane groups of head_dim/8 lanes (up to 32) when that
+    // fits at least 25% more heads into a wave instruction than the padded
+    // groups (fused op: measured +2 to +18%; at fewer extra heads the tree
+    // reduction it needs costs more than it saves), or 50% more for the
+    // LayerNorm sibling, which reduces twice (+8 to +12% there; -8% at 25%)
     const int lanes = D / E, sh = lane_shift(mode, R, neox, E);
     const int g_pad = kWave / (dmax / E), g_fit = kWave / lanes;
-    seg = mode == kFused && (sh == 2 || sh == 6) && lanes <= 32 && 4 * g_fit >= 5 * g_pad;
+    const bool more = mode == kFused ? 4 * g_fit >= 5 * g_pad
+                                     : mode == kLayerRope && 2 * g_fit >= 3 * g_pad;
+    seg = (sh == 2 || sh == 6) && lanes <= 32 && more;
     const int G = kWave / (seg ? lanes : dmax / E);
     if (c.lanes_per_head != 0 && c.lanes_per_head != (seg ? lanes : dmax / E)) return QKNR_E_ARG;
     if (!lane_offsets_fit(G, Hq, q_head, D) || !lane_offsets_fit(G, Hkv, k_head, D))

@@ -923,9 +923,9 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
 template <class IO, int GROUP>
 const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int shift);
 
-// Groups 2 and 4 (unroll 2 and 4): the fused op with exact-fit lane groups
-// (SEG) of a run-time head_dim whose NeoX partners sit 2 or 6 slots over;
-// nullptr elsewhere.
+// Groups 2 and 4 (unroll 2 and 4): the fused op and the LayerNorm sibling
+// with exact-fit lane groups (SEG) of a run-time head_dim whose NeoX partners
+// sit 2 or 6 slots over; nullptr elsewhere.
 template <class IO, int GROUP>
 const void* pick_seg(bool full, int U, int mode, int shift);
 

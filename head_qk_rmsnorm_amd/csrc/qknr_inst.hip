@@ -198,14 +198,15 @@ const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int 
   }
 }
 
-// Exact-fit lane groups (SEG) for NeoX partners 2 or 6 slots over: lanes per
+// Exact-fit lane groups (SEG) for NeoX partners 2 or 6 slots over (the fused
+// op and the LayerNorm sibling): lanes per
 // head and heads per wave instruction are run-time values, so DMAX plays no
 // part (fixed at 256).
-template <class IO, int UU, bool FULL>
+template <class IO, int UU, bool FULL, int MODE>
 const void* pick_seg_shift(int shift) {
   switch (shift) {
-    case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, 256, 8, true, FULL, UU, kFused, false, 2, true>);
-    case 6: return reinterpret_cast<const void*>(&qknr_kernel<IO, 256, 8, true, FULL, UU, kFused, false, 6, true>);
+    case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, 256, 8, true, FULL, UU, MODE, false, 2, true>);
+    case 6: return reinterpret_cast<const void*>(&qknr_kernel<IO, 256, 8, true, FULL, UU, MODE, false, 6, true>);
     default: return nullptr;
   }
 }
@@ -214,8 +215,13 @@ template <class IO, int GROUP>
 const void* pick_seg(bool full, int U, int mode, int shift) {
   if constexpr (GROUP == 2 || GROUP == 4) {
     constexpr int UU = GROUP == 2 ? 2 : 4;
-    if (U != UU || mode != kFused) return nullptr;
-    return full ? pick_seg_shift<IO, UU, true>(shift) : pick_seg_shift<IO, UU, false>(shift);
+    if (U != UU) return nullptr;
+    if (mode == kFused)
+      return full ? pick_seg_shift<IO, UU, true, kFused>(shift) : pick_seg_shift<IO, UU, false, kFused>(shift);
+    if (mode == kLayerRope)
+      return full ? pick_seg_shift<IO, UU, true, kLayerRope>(shift)
+                  : pick_seg_shift<IO, UU, false, kLayerRope>(shift);
+    return nullptr;
   } else {
     return nullptr;
   }
