@@ -256,7 +256,11 @@ def cpu_baseline(cfg, seconds):
     from oracle import qknr_oracle as O
 
     wl = W.make_workload(cfg)
-    workers = max(1, min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16")), 16))
+    try:
+        omp = int(os.environ.get("OMP_NUM_THREADS", "16").split(",")[0])
+    except ValueError:
+        omp = 16
+    workers = max(1, min(os.cpu_count() or 1, omp, 16))
     chunk = max(1, min(cfg.T, 16384 // max(cfg.heads, 1)))
     lock = threading.Lock()
     state = {"next": 0, "done": 0}
