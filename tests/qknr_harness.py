@@ -167,14 +167,40 @@ class DeviceCase:
         assert np.array_equal(self.positions.cpu().numpy(), self.wl.positions)
 
 
-def oracle_ref(wl: W.Workload, tokens: Optional[np.ndarray] = None):
-    """Oracle output bits for all tokens, or for the given token subset."""
+def oracle_ref(wl: W.Workload, tokens: Optional[np.ndarray] = None, chunk: int = 1024,
+               workers: int = 0):
+    """Oracle output bits for all tokens, or for the given token subset. Large
+    workloads are split into chunks of whole tokens that run on a thread pool
+    (NumPy releases the GIL in its array loops); every token is computed by the
+    same oracle call it would get in one piece, so the result does not depend
+    on the chunking."""
+    import concurrent.futures as cf
+    import os
+
     c = wl.cfg
     q, k, pos = wl.q, wl.k, wl.positions
     if tokens is not None:
         q, k, pos = q[tokens], k[tokens], pos[tokens]
-    rq, rk, _, _ = O.qknorm_rope_io(q, k, wl.wq, wl.wk, wl.cache, pos, is_neox=c.is_neox,
-                                    eps=c.eps, dtype=c.dtype, rope_dim=c.rope_dim)
+    T = q.shape[0]
+    rq = np.empty_like(q)
+    rk = np.empty_like(k)
+
+    def run(start):
+        sl = slice(start, min(start + chunk, T))
+        a, b, _, _ = O.qknorm_rope_io(q[sl], k[sl], wl.wq, wl.wk, wl.cache, pos[sl],
+                                      is_neox=c.is_neox, eps=c.eps, dtype=c.dtype,
+                                      rope_dim=c.rope_dim)
+        rq[sl] = a
+        rk[sl] = b
+
+    starts = range(0, T, chunk)
+    if len(starts) <= 1:
+        for s0 in starts:
+            run(s0)
+    else:
+        n = workers or max(1, min(16, os.cpu_count() or 1))
+        with cf.ThreadPoolExecutor(n) as ex:
+            list(ex.map(run, starts))
     return rq, rk
 
 

@@ -47,6 +47,18 @@ MUTATIONS = {
                                      "var = np.sum(c * c, axis=-1, keepdims=True) / (head_dim - 1)", True),
     "layer_norm_bias_dropped": ("        out = out + np.asarray(b, dtype=np.float64)", "        out = out", True),
     "layer_norm_not_centered": ("    c = x - mean\n", "    c = x - 0 * mean\n", True),
+    "layernorm_io_weights_swapped": ("dec(wq_bits), dec(wk_bits), dec(bq_bits), dec(bk_bits)",
+                                     "dec(wk_bits), dec(wq_bits), dec(bq_bits), dec(bk_bits)", True),
+    "layernorm_io_biases_swapped": ("dec(wq_bits), dec(wk_bits), dec(bq_bits), dec(bk_bits)",
+                                    "dec(wq_bits), dec(wk_bits), dec(bk_bits), dec(bq_bits)", True),
+    "layernorm_io_k_weight_on_q": ("dec(wq_bits), dec(wk_bits), dec(bq_bits), dec(bk_bits)",
+                                   "dec(wk_bits), dec(wk_bits), dec(bq_bits), dec(bk_bits)", True),
+    "layernorm_k_bias_from_q": ("nk = layer_norm(k, wk, bk, eps64)", "nk = layer_norm(k, wk, bq, eps64)", True),
+    "layernorm_q_weight_from_k": ("nq = layer_norm(q, wq, bq, eps64)", "nq = layer_norm(q, wk, bq, eps64)", True),
+    "layernorm_io_pairing_inverted": ("positions, is_neox=is_neox, eps=eps, rope_dim=rope_dim)\n    return round_to_io_bits(oq",
+                                      "positions, is_neox=not is_neox, eps=eps, rope_dim=rope_dim)\n    return round_to_io_bits(oq", True),
+    "layernorm_io_eps_dropped": ("positions, is_neox=is_neox, eps=eps, rope_dim=rope_dim)\n    return round_to_io_bits(oq",
+                                 "positions, is_neox=is_neox, eps=0.0, rope_dim=rope_dim)\n    return round_to_io_bits(oq", True),
     "equivalent_rewrite": ("np.sum(x * x, axis=-1", "np.sum(np.abs(x) * np.abs(x), axis=-1", False),
 }
 

@@ -670,3 +670,70 @@ def test_qk_layernorm_rope_composes_norm_and_rotation(neox):
     np.testing.assert_allclose(oq[..., ia], zc.real, atol=2e-6 * np.abs(nq).max())
     np.testing.assert_allclose(oq[..., ib], zc.imag, atol=2e-6 * np.abs(nq).max())
     np.testing.assert_array_equal(oq[..., R:], nq[..., R:])
+
+
+def _io_bits(vals, dtype):
+    """Exact values -> I/O bit patterns, encoded by torch (not by the oracle)."""
+    torch = pytest.importorskip("torch")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    t = torch.tensor(vals, dtype=torch.float64).to(tdt)
+    assert torch.equal(t.double(), torch.tensor(vals, dtype=torch.float64)), "value not exact"
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("neox", [False, True])
+@pytest.mark.parametrize("bias", [True, False])
+def test_golden_layernorm_io_entry(dtype, neox, bias):
+    """The LayerNorm sibling's I/O entry on the hand-derived example
+    (tests/golden/hand_examples.json, layernorm_examples): distinct q/k inputs,
+    weights and biases, a quarter turn picked by position 1, with and without
+    the bias rows. Outputs are decoded by torch and compared as values."""
+    torch = pytest.importorskip("torch")
+    ex = _golden()["layernorm_examples"]["cases"][0]
+    D = len(ex["q"])
+    bits = lambda v: _io_bits(v, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    dec = lambda b: torch.from_numpy(b.view(np.int16)).view(tdt).double().numpy()
+    q = bits(ex["q"]).reshape(1, 1, D)
+    k = bits(ex["k"]).reshape(1, 1, D)
+    cache = np.asarray(ex["cache"], dtype=np.float32)
+    pos = np.asarray(ex["positions"], dtype=np.int64)
+    rq, rk = O.qk_layernorm_rope_io(q, k, bits(ex["wq"]), bits(ex["wk"]),
+                                    bits(ex["bq"]) if bias else None,
+                                    bits(ex["bk"]) if bias else None, cache, pos,
+                                    is_neox=neox, eps=ex["eps"], dtype=dtype,
+                                    rope_dim=ex["rope_dim"])
+    key = ("neox" if neox else "interleaved") + ("" if bias else "_no_bias")
+    np.testing.assert_array_equal(dec(rq).reshape(D), ex[f"out_q_{key}"])
+    np.testing.assert_array_equal(dec(rk).reshape(D), ex[f"out_k_{key}"])
+
+
+def test_layernorm_io_entry_rounds_once_and_routes_rows():
+    """The I/O entry against the fp64 composition on random heads: Q rows get
+    wq and bq, K rows wk and bk, one correct rounding (bf16 by torch's
+    round-to-nearest-even from a float64 that is exact in float32)."""
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(31)
+    T, Hq, Hkv, D, R = 7, 3, 2, 32, 16
+    enc = lambda v: torch.from_numpy(np.asarray(v, np.float64)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+    dec = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).double().numpy()
+    q, k = enc(g.standard_normal((T, Hq, D))), enc(g.standard_normal((T, Hkv, D)))
+    wq, wk = enc(g.uniform(0.5, 1.5, D)), enc(g.uniform(-1.5, -0.5, D))
+    bq, bk = enc(g.standard_normal(D)), enc(g.standard_normal(D) + 4.0)
+    cache = _cache_formula(20, R)
+    pos = g.integers(0, 20, T)
+    for neox in (False, True):
+        rq, rk = O.qk_layernorm_rope_io(q, k, wq, wk, bq, bk, cache, pos, is_neox=neox,
+                                        eps=1e-5, dtype="bf16", rope_dim=R)
+        fq, fk = O.qk_layernorm_rope(dec(q), dec(k), dec(wq), dec(wk), dec(bq), dec(bk), cache,
+                                     pos, is_neox=neox, eps=1e-5, rope_dim=R)
+        for got, f in ((rq, fq), (rk, fk)):
+            # float64 -> float32 is exact for all but a few values; where it is not,
+            # allow the one-ulp difference of a double rounding
+            f32 = f.astype(np.float32)
+            want = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            exact = f32.astype(np.float64) == f
+            np.testing.assert_array_equal(got[exact], want[exact])
+            assert np.all(np.abs(dec(got) - f) <= np.abs(f) * 2.0 ** -8 + 1e-30)
