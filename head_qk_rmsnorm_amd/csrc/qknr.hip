@@ -98,7 +98,9 @@ const void* pick_seg_kernel(int dtype, bool full, int U, int mode, int shift) {
 }
 
 const void* pick_elem_kernel(int dtype, int mode, int slots, int pw) {
-  return dtype == QKNR_BF16 ? pick_elem<Bf16>(mode, slots, pw) : pick_elem<Fp16>(mode, slots, pw);
+  if (pw <= 2)
+    return dtype == QKNR_BF16 ? pick_elem<Bf16, 3>(mode, slots, pw) : pick_elem<Fp16, 3>(mode, slots, pw);
+  return dtype == QKNR_BF16 ? pick_elem<Bf16, 5>(mode, slots, pw) : pick_elem<Fp16, 5>(mode, slots, pw);
 }
 
 // NeoX pairs (d, d + R/2): with E elements per lane the partner sits a fixed
@@ -343,50 +345,93 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
 }
 
-// Plan of the element-granular kernel: one head per wave instruction, a work
-// item is a run of heads (Q, then K) of one token; S slots of pw elements per
-// lane (accesses of 2*pw bytes), S the smallest power of two with
-// 64*S*pw >= head_dim. The widest pw (4, 2 or 1) that divides head_dim and
-// whose access size divides every pointer and stride (align: their common
-// alignment, 8 at most) gives the fewest slots; the narrowest pw with that many
-// slots is taken, which keeps the most lanes busy and 16/(S*pw) heads in
-// flight (measured: head_dim 100 and 128 run fastest with 4-byte accesses, 200
-// and 256 with 8-byte ones).
-int elem_slots(int32_t D, int pw) {
-  int s = 1;
-  while (s * kWave * pw < D) s *= 2;
-  return s;
+// Plan of the element-granular kernel. Runs of pw elements (accesses of 2*pw
+// bytes): any pw in {8, 4, 2, 1} that divides head_dim and whose access size
+// divides every pointer and used stride (align: their common alignment, 16 at
+// most). A head takes L lanes of S runs each (L*S*pw >= head_dim, S*pw <= 8),
+// a wave instruction G = 64/L heads of Q or of K of one token. Among the
+// candidates (every allowed pw and S, with L rounded up to a power of two or
+// exact), the plan takes the fewest wave instructions per token,
+// S * (ceil(Hq/G) + ceil(Hkv/G)); ties go to a power-of-two L (DPP sums), then
+// to the wider access, then to fewer slots. A group of several heads needs its
+// lane offsets below 2^31; where they are not, one head per group is planned
+// (its base address is 64-bit). 16/(S*pw) groups are loaded before the first is
+// computed.
+struct ElemShape {
+  int pw = 1, S = 1, L = 64, G = 1;
+  bool seg = false;
+};
+
+int pow2_at_least(int n) {
+  int c = 1;
+  while (c < n) c *= 2;
+  return c;
+}
+
+ElemShape elem_shape(int32_t D, int align, int32_t Hq, int32_t Hkv, bool groups_fit) {
+  ElemShape best;
+  int64_t best_cost = INT64_MAX;
+  auto consider = [&](int pw, int S, int L, bool seg) {
+    const int G = groups_fit ? kWave / L : 1;
+    const int64_t cost = static_cast<int64_t>(S) * ((Hq + G - 1) / G + (Hkv + G - 1) / G);
+    // lexicographic: cost, then power-of-two lanes, then wider runs, then fewer slots
+    const bool better = cost < best_cost ||
+                        (cost == best_cost && (best.seg && !seg)) ||
+                        (cost == best_cost && best.seg == seg && pw > best.pw) ||
+                        (cost == best_cost && best.seg == seg && pw == best.pw && S < best.S);
+    if (better) {
+      best_cost = cost;
+      best.pw = pw;
+      best.S = S;
+      best.L = L;
+      best.G = G;
+      best.seg = seg;
+    }
+  };
+  for (int pw : {8, 4, 2, 1}) {
+    if (D % pw != 0 || align < 2 * pw) continue;
+    for (int S = 1; S * pw <= kElemPerLane; ++S) {
+      const int lx = (D + S * pw - 1) / (S * pw);  // lanes a head needs
+      if (lx > kWave) continue;
+      const int lp = pow2_at_least(lx);
+      consider(pw, S, lp, false);
+      if (lx != lp && groups_fit) consider(pw, S, lx, true);
+    }
+  }
+  return best;
 }
 
 int32_t make_elem_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t neox,
-                       int32_t dtype, int align, const qknr_launch_cfg& c, Plan* pl) {
-  const int H = Hq + Hkv;
+                       int32_t dtype, int align, int64_t q_head, int64_t k_head,
+                       const qknr_launch_cfg& c, Plan* pl) {
+  // several heads per group only where every group's lane offsets fit 32 bits
+  const bool groups_fit = lane_offsets_fit(kWave, Hq, q_head, D) && lane_offsets_fit(kWave, Hkv, k_head, D);
+  const ElemShape sh = elem_shape(D, align, Hq, Hkv, groups_fit);
   pl->elem = true;
   pl->shift = 0;
-  int pw = (align >= 8 && D % 4 == 0) ? 4 : (align >= 4 && D % 2 == 0) ? 2 : 1;
-  const int fewest = elem_slots(D, pw);
-  while (pw > 1 && elem_slots(D, pw / 2) <= fewest) pw /= 2;
-  pl->pw = pw;
-  const int slots = fewest;
-  const int U = 2 * kElemSlots / (slots * pl->pw);
-  pl->E = pl->pw * ((D + kWave * pl->pw - 1) / (kWave * pl->pw));
-  pl->L = kWave;
+  pl->pw = sh.pw;
+  pl->E = sh.S * sh.pw;
+  pl->L = sh.L;
+  pl->G = sh.G;
+  pl->seg = sh.seg;
   pl->dmax = D;
   pl->exact = false;
-  pl->G = 1;
-  pl->ngq = Hq;
-  pl->ng = H;
+  pl->ngq = (Hq + sh.G - 1) / sh.G;
+  pl->ng = pl->ngq + (Hkv + sh.G - 1) / sh.G;
+  const int U = 2 * kElemPerLane / pl->E;
   const int want = c.groups_per_item == 0 ? kDefaultElemRounds * U : c.groups_per_item;
-  pl->gpi = std::max(1, std::min(want, H));
-  pl->nc = (H + pl->gpi - 1) / pl->gpi;
+  pl->gpi = std::max(1, std::min(want, pl->ng));
+  pl->nc = (pl->ng + pl->gpi - 1) / pl->gpi;
   pl->items = T * pl->nc;
   if (pl->items > kMaxItems) return QKNR_E_SHAPE;
   pl->U = U;
   pl->wpb = c.block_waves == 0 ? kDefaultBlockWaves : c.block_waves;
   pl->max_blocks = c.max_blocks;
-  // NeoX rotation exchanges partners through one LDS row of head_dim floats per wave
-  pl->lds = (rotates(mode) && neox) ? static_cast<size_t>(pl->wpb) * D * sizeof(float) : 0;
-  pl->fn = pick_elem_kernel(dtype, mode, slots, pl->pw);
+  // partners through LDS (NeoX, or interleaved with single-element runs): a
+  // row of 64 lanes x E floats per wave
+  pl->lds = (rotates(mode) && (neox || sh.pw == 1))
+                ? static_cast<size_t>(pl->wpb) * kWave * pl->E * sizeof(float) : 0;
+  pl->fn = pick_elem_kernel(dtype, mode, sh.S, sh.pw);
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
 }
 
@@ -472,7 +517,7 @@ int32_t prepare(int mode, const Call& c, const qknr_launch_cfg* cfg, Plan* pl,
   const bool need_rot = rotates(mode);
   const bool bias = (mode == kLayerRope || mode == kLayerOnly) && (c.bq || c.bk);
   bool vec_aligned = true;
-  int elem_align = 8;  // common alignment of the views (2, 4 or 8 bytes) for the element-granular kernel
+  int elem_align = 16;  // common alignment of the views (2 to 16 bytes) for the element-granular kernel
   if (!empty) {
     if ((c.Hq > 0 && (!c.q || (need_w && !c.wq) || (bias && !c.bq))) ||
         (c.Hkv > 0 && (!c.k || (need_w && !c.wk) || (bias && !c.bk))) ||
@@ -505,7 +550,7 @@ int32_t prepare(int mode, const Call& c, const qknr_launch_cfg* cfg, Plan* pl,
     return QKNR_E_ARG;
   }
   if (rc != QKNR_OK) {
-    rc = make_elem_plan(mode, c.T, c.Hq, c.Hkv, c.D, c.neox, c.dtype, elem_align, lc, pl);
+    rc = make_elem_plan(mode, c.T, c.Hq, c.Hkv, c.D, c.neox, c.dtype, elem_align, c.qh, c.kh, lc, pl);
     if (rc != QKNR_OK) return rc;
   }
   if (info) {
@@ -553,10 +598,15 @@ int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
     ElemParams ep;
     ep.q_tok = c.qt;
     ep.k_tok = c.kt;
-    ep.q_head = qh;
-    ep.k_head = kh;
+    ep.q_grp = qh * pl.G;
+    ep.k_grp = kh * pl.G;
+    // with one head per group only the 64-bit group stride is used
+    ep.q_head = pl.G > 1 ? static_cast<uint32_t>(qh) : 0u;
+    ep.k_head = pl.G > 1 ? static_cast<uint32_t>(kh) : 0u;
     ep.Hq = c.Hq;
-    ep.H = c.Hq + c.Hkv;
+    ep.Hkv = c.Hkv;
+    ep.ngq = pl.ngq;
+    ep.ng = pl.ng;
     ep.D = c.D;
     ep.R = c.R;
     ep.inv_d = static_cast<float>(1.0 / c.D);
@@ -564,7 +614,10 @@ int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
     ep.neox = c.neox ? 1 : 0;
     ep.pos64 = c.pdt == QKNR_I64;
     ep.has_bias = (c.bq || c.bk) ? 1 : 0;
-    ep.hpi = pl.gpi;
+    ep.L = pl.L;
+    ep.G = pl.G;
+    ep.seg = pl.seg ? 1 : 0;
+    ep.gpi = pl.gpi;
     ep.nc = pl.nc;
     ep.n_items = static_cast<int32_t>(pl.items);
     void* args[] = {&qarg, &karg, &wqarg, &wkarg, &carg, &parg, &bqarg, &bkarg, &ep};
@@ -716,6 +769,22 @@ QKNR_API int32_t qknr_unfused_inplace(void* q, void* k, const void* wq, const vo
   return rc != QKNR_OK ? rc : launch(c, rot, nullptr);
 }
 
+QKNR_API int32_t qknr_layernorm_rope_inplace_ex(
+    void* q, void* k, const void* wq, const void* wk, const void* bq, const void* bk,
+    const float* cos_sin_cache, const void* positions, int64_t T, int32_t Hq, int32_t Hkv,
+    int32_t head_dim, int32_t rope_dim, int32_t is_neox, float eps, int64_t q_tok_stride_B,
+    int64_t q_head_stride_B, int64_t k_tok_stride_B, int64_t k_head_stride_B, int32_t dtype,
+    int32_t pos_dtype, hipStream_t stream, const qknr_launch_cfg* cfg, qknr_launch_info* info) {
+  const bool rotate = rope_dim != 0;
+  const Call c{q, k, wq, wk, rotate ? cos_sin_cache : nullptr, rotate ? positions : nullptr, bq, bk,
+               T, Hq, Hkv, head_dim, rotate ? rope_dim : head_dim, rotate ? is_neox : 0, eps,
+               q_tok_stride_B, q_head_stride_B, k_tok_stride_B, k_head_stride_B, dtype,
+               rotate ? pos_dtype : QKNR_I32, stream};
+  Plan pl;
+  const int32_t rc = prepare(rotate ? kLayerRope : kLayerOnly, c, cfg, &pl, info);
+  return rc != QKNR_OK ? rc : launch(c, pl, info);
+}
+
 QKNR_API int32_t qknr_layernorm_rope_inplace(void* q, void* k, const void* wq, const void* wk,
                                              const void* bq, const void* bk,
                                              const float* cos_sin_cache, const void* positions,
@@ -724,14 +793,10 @@ QKNR_API int32_t qknr_layernorm_rope_inplace(void* q, void* k, const void* wq, c
                                              int64_t q_tok_stride_B, int64_t q_head_stride_B,
                                              int64_t k_tok_stride_B, int64_t k_head_stride_B,
                                              int32_t dtype, int32_t pos_dtype, hipStream_t stream) {
-  const bool rotate = rope_dim != 0;
-  const Call c{q, k, wq, wk, rotate ? cos_sin_cache : nullptr, rotate ? positions : nullptr, bq, bk,
-               T, Hq, Hkv, head_dim, rotate ? rope_dim : head_dim, rotate ? is_neox : 0, eps,
-               q_tok_stride_B, q_head_stride_B, k_tok_stride_B, k_head_stride_B, dtype,
-               rotate ? pos_dtype : QKNR_I32, stream};
-  Plan pl;
-  const int32_t rc = prepare(rotate ? kLayerRope : kLayerOnly, c, nullptr, &pl, nullptr);
-  return rc != QKNR_OK ? rc : launch(c, pl, nullptr);
+  return qknr_layernorm_rope_inplace_ex(q, k, wq, wk, bq, bk, cos_sin_cache, positions, T, Hq, Hkv,
+                                        head_dim, rope_dim, is_neox, eps, q_tok_stride_B,
+                                        q_head_stride_B, k_tok_stride_B, k_head_stride_B, dtype,
+                                        pos_dtype, stream, nullptr, nullptr);
 }
 
 static int32_t stream_launch(const void* fn, void** args, int64_t n16, hipStream_t stream) {

@@ -629,36 +629,45 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 
 // ----------------------------------------------------------------------------
 // Element-granular kernel: the shapes and layouts the vectorised kernel above
-// cannot take (head_dims that are not multiples of 8, NeoX halves that are not
-// a multiple of any lane width, pointers or strides that are only 2- or
-// 4-byte aligned, head strides beyond 32-bit lane offsets). Same operation,
-// same fp32 formulas and FMA forms, same rounding; only the order of the sums
-// differs.
+// cannot take (head_dims that are not multiples of 8, odd NeoX halves,
+// pointers or strides aligned to less than 16 bytes, head strides beyond
+// 32-bit lane offsets). Same operation, same fp32 formulas and FMA forms,
+// same rounding; only the order of the sums differs.
 //
-// One head vector per wave instruction. A lane slot holds PW consecutive
-// elements (PW = 1, 2 or 4: 2-, 4- or 8-byte accesses); PW divides head_dim and
-// every pointer and used stride is 2*PW-byte aligned (the host picks PW).
-// Element e sits in lane (e / PW) % 64, slot e / (64 PW), S slots (a power of
-// two covering head_dim <= 512). Every access is a buffer access relative to the head's own
-// base address, which is wave-uniform (64-bit, no limit on strides); lane
-// offsets stay below 1 KiB and the descriptor covers exactly the head vector.
-// Interleaved partners (e, e ^ 1) lie in one slot (PW = 2, 4) or in
-// neighbouring lanes of one slot (PW = 1, DPP); NeoX partners (e, e +- R/2) can
-// sit in any lane and slot, so the normalised row goes through a per-wave row
-// of LDS. A work item is a run of heads (Q then K) of one token; 16/(S PW)
-// heads are loaded before the first is computed, so every instance keeps the
-// same number of bytes in flight per wave whatever its head_dim.
+// Lane mapping. A lane slot holds a run of PW consecutive elements (PW = 1, 2,
+// 4 or 8: 2-, 4-, 8- or 16-byte accesses); PW divides head_dim and every
+// pointer and used stride is 2*PW-byte aligned (the host picks PW). A head
+// takes L lanes and S slots per lane (L*S*PW >= head_dim): element e of a head
+// sits in lane-in-head (e / PW) % L, slot e / (L*PW). A wave instruction covers
+// a head group of G = 64 / L heads of Q, or of K, of one token (G = 1 and
+// L up to 64 for large heads), so a group's base address is wave-uniform and
+// each lane adds a 32-bit offset (the host checks that a group's offsets fit,
+// else it plans one head per group, whose 64-bit base has no stride limit).
+// L is a power of two (sum over the head's lanes by DPP steps) or, when that
+// fits more heads into a wave instruction, head_dim/(S*PW) rounded up (exact
+// fit: a ds_bpermute tree toward the head's first lane plus a broadcast); the
+// lanes past the last head of a group and the elements past head_dim are
+// masked. Interleaved partners (e, e ^ 1) lie in one run when PW >= 2; NeoX
+// partners (e, e +- R/2), and interleaved ones when PW = 1, can sit in any lane
+// and slot, so the normalised values of a group go through a per-wave LDS row
+// (G heads x L*S*PW floats, head-major) and each element reads its partner.
+// A work item is a run of head groups of one token; 16/(S*PW) groups are
+// loaded before the first is computed, so every instance keeps 16 elements per
+// lane in flight whatever its head_dim.
 // ----------------------------------------------------------------------------
-constexpr int kElemSlots = 8;
-constexpr int kElemMaxDim = kElemSlots * kWave;  // 512
+constexpr int kElemPerLane = 8;            // S * PW at most
+constexpr int kElemMaxDim = 512;
 
 struct ElemParams {
-  int64_t q_tok, k_tok, q_head, k_head;  // byte strides
-  int32_t Hq, H;                         // Q heads; Q + K heads (K heads follow Q heads)
+  int64_t q_tok, k_tok;          // token strides (bytes)
+  int64_t q_grp, k_grp;          // bytes between consecutive head groups (G head strides)
+  uint32_t q_head, k_head;       // head strides inside a group (0 with G = 1)
+  int32_t Hq, Hkv, ngq, ng;      // heads; Q head groups per token (K groups follow); groups per token
   int32_t D, R;
   float inv_d, eps;
   int32_t neox, pos64, has_bias;
-  int32_t hpi, nc, n_items;              // heads per item, items per token, items
+  int32_t L, G, seg;             // lanes per head, heads per wave instruction, L not a power of two
+  int32_t gpi, nc, n_items;      // groups per item, items per token, items
 };
 
 // one I/O element <-> fp32 (the low half of the packed conversions above)
@@ -670,23 +679,103 @@ __device__ __forceinline__ float widen1(uint32_t bits) {
 }
 
 template <class IO>
-__device__ __forceinline__ uint16_t narrow1(float v) {
-  return static_cast<uint16_t>(IO::pack(v, 0.0f) & 0xffffu);
+__device__ __forceinline__ uint32_t narrow1(float v) {
+  return IO::pack(v, 0.0f) & 0xffffu;
 }
 
-// PW elements of a row of I/O values starting at element e (e a multiple of
-// PW, the row 2*PW-byte aligned) -> fp32
+// A run of PW elements kept as NW packed dwords (PW = 1: the low half of one).
+template <int PW>
+struct Run {
+  static constexpr int NW = PW >= 2 ? PW / 2 : 1;
+  uint32_t w[NW];
+};
+
 template <class IO, int PW>
-__device__ __forceinline__ void load_row_elems(const uint16_t* r, int e, float* v) {
-  if constexpr (PW == 4) {
-    const u32x2_t w = *reinterpret_cast<const u32x2_t*>(r + e);
-    IO::unpack(w.x, v[0], v[1]);
-    IO::unpack(w.y, v[2], v[3]);
-  } else if constexpr (PW == 2) {
-    IO::unpack(*reinterpret_cast<const uint32_t*>(r + e), v[0], v[1]);
+__device__ __forceinline__ void unpack_run(const Run<PW>& r, float* v) {
+  if constexpr (PW == 1) {
+    v[0] = widen1<IO>(r.w[0]);
   } else {
-    v[0] = widen1<IO>(r[e]);
+#pragma unroll
+    for (int i = 0; i < PW / 2; ++i) IO::unpack(r.w[i], v[2 * i], v[2 * i + 1]);
   }
+}
+
+template <class IO, int PW>
+__device__ __forceinline__ Run<PW> pack_run(const float* v) {
+  Run<PW> r;
+  if constexpr (PW == 1) {
+    r.w[0] = narrow1<IO>(v[0]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < PW / 2; ++i) r.w[i] = IO::pack(v[2 * i], v[2 * i + 1]);
+  }
+  return r;
+}
+
+template <int PW>
+__device__ __forceinline__ Run<PW> load_run(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  Run<PW> r;
+  if constexpr (PW == 8) {
+    const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kLoadPolicy));
+    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  } else if constexpr (PW == 4) {
+    const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kLoadPolicy));
+    r.w[0] = v.x; r.w[1] = v.y;
+  } else if constexpr (PW == 2) {
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kLoadPolicy);
+  } else {
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, kLoadPolicy);
+  }
+  return r;
+}
+
+template <int PW>
+__device__ __forceinline__ void store_run(__amdgpu_buffer_rsrc_t rs, uint32_t off, const Run<PW>& r) {
+  if constexpr (PW == 8) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{r.w[0], r.w[1], r.w[2], r.w[3]}, rs, off, 0, kStorePolicy);
+  } else if constexpr (PW == 4) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{r.w[0], r.w[1]}, rs, off, 0, kStorePolicy);
+  } else if constexpr (PW == 2) {
+    __builtin_amdgcn_raw_buffer_store_b32(r.w[0], rs, off, 0, kStorePolicy);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(r.w[0]), rs, off, 0, kStorePolicy);
+  }
+}
+
+// PW elements of a weight or bias row starting at element e (e a multiple of
+// PW, the row 2*PW-byte aligned)
+template <int PW>
+__device__ __forceinline__ Run<PW> load_row_run(const void* row, int e) {
+  const char* const p = static_cast<const char*>(row) + 2 * e;
+  Run<PW> r;
+  if constexpr (PW == 8) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  } else if constexpr (PW == 4) {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+    r.w[0] = v.x; r.w[1] = v.y;
+  } else if constexpr (PW == 2) {
+    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else {
+    r.w[0] = *reinterpret_cast<const uint16_t*>(p);
+  }
+  return r;
+}
+
+// Sum over aligned groups of L lanes, L a power of two chosen at run time
+// (wave-uniform): the steps of group_sum<L> taken while they stay inside a
+// group. Every lane of a group gets the same bits.
+__device__ __forceinline__ float group_sum_rt(float v, int L) {
+  if (L >= 2) v += dpp_mov<kDppQuadXor1>(v);
+  if (L >= 4) v += dpp_mov<kDppQuadXor2>(v);
+  if (L >= 8) v += dpp_mov<kDppRowHalfMirror>(v);
+  if (L >= 16) v += dpp_mov<kDppRowMirror>(v);
+  if (L >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16));
+  if (L == 64) {
+    v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  }
+  return v;
 }
 
 template <class IO, int MODE, int S, int PW>
@@ -695,116 +784,129 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
                  const void* __restrict__ wkp, const float* __restrict__ cache,
                  const void* __restrict__ posp, const void* __restrict__ bqp,
                  const void* __restrict__ bkp, const ElemParams p) {
-  static_assert(S == 1 || S == 2 || S == 4 || S == 8, "slots per lane");
-  static_assert(PW == 1 || PW == 2 || PW == 4, "elements per lane slot");
-  static_assert(S * PW <= kElemSlots, "at most 512 elements");
+  static_assert(PW == 1 || PW == 2 || PW == 4 || PW == 8, "elements per lane slot");
+  static_assert(S >= 1 && S * PW <= kElemPerLane, "at most 8 elements per lane");
   constexpr int NE = S * PW;                  // elements per lane
-  constexpr int U = 2 * kElemSlots / NE;      // heads loaded before the first is computed
-  constexpr int SPAN = kWave * PW;            // elements per slot of the wave
+  constexpr int U = 2 * kElemPerLane / NE;    // groups loaded before the first is computed
   constexpr bool kRotate = MODE == kFused || MODE == kRopeOnly || MODE == kLayerRope;
   constexpr bool kRms = MODE == kFused || MODE == kNormOnly;
   constexpr bool kLayer = MODE == kLayerRope || MODE == kLayerOnly;
-  extern __shared__ float elem_rows[];  // NeoX rotation: head_dim floats per wave
+  extern __shared__ float elem_rows[];  // partner exchange: kWave * NE floats per wave
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
+  const int L = p.L, G = p.G;
+  const int sub = lane / L;       // head slot in the group
+  const int li = lane - sub * L;  // lane inside the head
+  const bool in_grp = sub < G;
   const int D = p.D, R = p.R, half = R / 2;
+  const int span = L * PW;        // elements of one head per slot
   const bool neox = p.neox != 0;  // wave-uniform
-  float* const row = elem_rows + wib * D;
-  // element of slot s, position i in the slot; head_dim is a multiple of PW,
-  // so the elements of a slot are all in the head or none is
-  auto elem = [&](int s, int i) { return (s * kWave + lane) * PW + i; };
+  // partners through LDS: NeoX pairing, or interleaved pairs split over lanes
+  const bool exch = kRotate && (neox || PW == 1);
+  float* const xrow = elem_rows + wib * (kWave * NE);
+  const int head0 = sub * (L * NE);  // this head's first element in the row
+  const uint32_t q_off = static_cast<uint32_t>(sub) * p.q_head + 2 * li * PW;
+  const uint32_t k_off = static_cast<uint32_t>(sub) * p.k_head + 2 * li * PW;
 
-  // weights, biases and rotation roles of this lane's elements (index s*PW + i)
-  const uint16_t* const wq16 = static_cast<const uint16_t*>(wqp);
-  const uint16_t* const wk16 = static_cast<const uint16_t*>(wkp);
-  const uint16_t* const bq16 = static_cast<const uint16_t*>(bqp);
-  const uint16_t* const bk16 = static_cast<const uint16_t*>(bkp);
-  float wq[NE], wk[NE], bq[NE], bk[NE];
-  int col[NE], partner[NE];  // cos/sin column, partner element
-  bool rot[NE], neg[NE];     // rotated element; partner term subtracted
-  bool have_w = false;       // weights are loaded after the first head loads
+  // run s of this lane: elements e0[s] .. e0[s] + PW - 1, all in the head or
+  // none (head_dim is a multiple of PW)
+  int e0[S];
+  bool run_ok[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    e0[s] = (s * L + li) * PW;
+    run_ok[s] = in_grp && e0[s] < D;
+  }
+
+  // rotation roles of this lane's elements (index s*PW + i): cos/sin column,
+  // partner element, partner term subtracted
+  int col[NE], partner[NE];
+  bool rot[NE], neg[NE];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int j = s * PW + i;
+      const int e = e0[s] + i;
+      rot[j] = kRotate && run_ok[s] && e < R;
+      if (neox) {
+        const bool lower = e < half;
+        col[j] = lower ? e : e - half;
+        partner[j] = lower ? e + half : e - half;
+        neg[j] = lower;
+      } else {
+        col[j] = e >> 1;
+        partner[j] = e ^ 1;
+        neg[j] = (e & 1) == 0;
+      }
+      if (!rot[j]) {
+        col[j] = 0;
+        partner[j] = e0[s] + i;
+      }
+    }
+  }
+
+  auto head_sum = [&](float v) { return p.seg ? seg_sum(v, lane, li, L) : group_sum_rt(v, L); };
+
+  // weights and biases of this lane's runs, kept packed; loaded once, after
+  // the first head loads are in flight
+  Run<PW> wq[S], wk[S], bq[S], bk[S];
+  bool have_w = false;
   auto load_weights = [&]() {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const int e = elem(s, 0);
-      const bool act = e < D;
 #pragma unroll
-      for (int i = 0; i < PW; ++i) wq[s * PW + i] = wk[s * PW + i] = bq[s * PW + i] = bk[s * PW + i] = 0.0f;
+      for (int w = 0; w < Run<PW>::NW; ++w) wq[s].w[w] = wk[s].w[w] = bq[s].w[w] = bk[s].w[w] = 0u;
       if constexpr (kRms || kLayer) {
-        if (act) {
-          load_row_elems<IO, PW>(wq16, e, &wq[s * PW]);
-          load_row_elems<IO, PW>(wk16, e, &wk[s * PW]);
+        if (run_ok[s]) {
+          wq[s] = load_row_run<PW>(wqp, e0[s]);
+          wk[s] = load_row_run<PW>(wkp, e0[s]);
         }
       }
       if constexpr (kLayer) {
-        if (act && p.has_bias) {
-          load_row_elems<IO, PW>(bq16, e, &bq[s * PW]);
-          load_row_elems<IO, PW>(bk16, e, &bk[s * PW]);
+        if (run_ok[s] && p.has_bias) {
+          bq[s] = load_row_run<PW>(bqp, e0[s]);
+          bk[s] = load_row_run<PW>(bkp, e0[s]);
         }
       }
     }
   };
-#pragma unroll
-  for (int j = 0; j < NE; ++j) {
-    const int e = elem(j / PW, j % PW);
-    rot[j] = kRotate && e < R;
-    if (neox) {
-      const bool lower = e < half;
-      col[j] = lower ? e : e - half;
-      partner[j] = lower ? e + half : e - half;
-      neg[j] = lower;
-    } else {
-      col[j] = e >> 1;
-      partner[j] = e ^ 1;
-      neg[j] = (e & 1) == 0;
-    }
-    if (!rot[j]) {
-      col[j] = 0;
-      partner[j] = 0;
-    }
-  }
 
   const int total_waves = gridDim.x * wpb;
   for (int item = blockIdx.x * wpb + wib; item < p.n_items; item += total_waves) {
     const int t = item / p.nc;
-    const int h_begin = (item - t * p.nc) * p.hpi;
-    const int h_end = min(h_begin + p.hpi, p.H);
+    const int g_begin = (item - t * p.nc) * p.gpi;
+    const int g_end = min(g_begin + p.gpi, p.ng);
+    char* const qrow = qb + t * p.q_tok;
+    char* const krow = kb + t * p.k_tok;
 
-    float x[U][NE];
+    Run<PW> raw[U][S];
     __amdgpu_buffer_rsrc_t rs[U];
+    uint32_t off[U];
     bool ok[U], isk[U];
-    auto issue = [&](int h) {
+    auto issue = [&](int g) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int hh = h + u;
-        ok[u] = hh < h_end;  // wave-uniform
-        isk[u] = hh >= p.Hq;
-        char* const base = isk[u] ? kb + t * p.k_tok + (hh - p.Hq) * p.k_head
-                                  : qb + t * p.q_tok + hh * p.q_head;
-        rs[u] = __builtin_amdgcn_make_buffer_rsrc(base, 0, 2 * D, kBufferFlags);
+        const int gu = g + u;
+        isk[u] = gu >= p.ngq;  // wave-uniform
+        const int gg = isk[u] ? gu - p.ngq : gu;
+        rs[u] = __builtin_amdgcn_make_buffer_rsrc(isk[u] ? krow + gg * p.k_grp : qrow + gg * p.q_grp,
+                                                  0, 0x7FFFFFFF, kBufferFlags);
+        off[u] = isk[u] ? k_off : q_off;
+        ok[u] = gu < g_end && gg * G + sub < (isk[u] ? p.Hkv : p.Hq);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          const int e = elem(s, 0);
+          if (ok[u] && run_ok[s]) {
+            raw[u][s] = load_run<PW>(rs[u], off[u] + 2 * s * span);
+          } else {
 #pragma unroll
-          for (int i = 0; i < PW; ++i) x[u][s * PW + i] = 0.0f;
-          if (ok[u] && s * SPAN < D && e < D) {
-            if constexpr (PW == 4) {
-              const u32x2_t w = __builtin_bit_cast(
-                  u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs[u], 2 * e, 0, kLoadPolicy));
-              IO::unpack(w.x, x[u][s * PW], x[u][s * PW + 1]);
-              IO::unpack(w.y, x[u][s * PW + 2], x[u][s * PW + 3]);
-            } else if constexpr (PW == 2) {
-              IO::unpack(__builtin_amdgcn_raw_buffer_load_b32(rs[u], 2 * e, 0, kLoadPolicy),
-                         x[u][s * PW], x[u][s * PW + 1]);
-            } else {
-              x[u][s] = widen1<IO>(__builtin_amdgcn_raw_buffer_load_b16(rs[u], 2 * e, 0, kLoadPolicy));
-            }
+            for (int w = 0; w < Run<PW>::NW; ++w) raw[u][s].w[w] = 0u;
           }
         }
       }
     };
-    issue(h_begin);
+    issue(g_begin);
     __builtin_amdgcn_sched_barrier(0);  // the head loads leave first
     if (!have_w) {
       load_weights();
@@ -823,7 +925,7 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
       const float* const crow = cache + token_position(posp, p.pos64, t) * R;
 #pragma unroll
       for (int j = 0; j < NE; ++j) {
-        if ((j / PW) * SPAN < R && rot[j]) {
+        if (rot[j]) {
           cs[j] = crow[col[j]];
           const float v = crow[half + col[j]];
           sn[j] = neg[j] ? -v : v;
@@ -831,39 +933,52 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
       }
     }
 
-    for (int h = h_begin; h < h_end; h += U) {
-      if (h != h_begin) issue(h);
+    for (int g = g_begin; g < g_end; g += U) {
+      if (g != g_begin) issue(g);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (!ok[u]) continue;
+        if (g + u >= g_end) continue;  // wave-uniform: every lane takes part below
+        float x[NE];
+#pragma unroll
+        for (int s = 0; s < S; ++s) unpack_run<IO, PW>(raw[u][s], &x[s * PW]);
         float n[NE];
         if constexpr (kLayer) {
           float sm = 0.0f;
 #pragma unroll
-          for (int j = 0; j < NE; ++j) sm += x[u][j];
-          const float mean = group_sum<kWave>(sm) * p.inv_d;
+          for (int j = 0; j < NE; ++j) sm += x[j];
+          const float mean = head_sum(sm) * p.inv_d;
           float c[NE], ss = 0.0f;
 #pragma unroll
           for (int j = 0; j < NE; ++j) {
-            c[j] = elem(j / PW, j % PW) < D ? x[u][j] - mean : 0.0f;
+            c[j] = run_ok[j / PW] ? x[j] - mean : 0.0f;
             ss = fmaf(c[j], c[j], ss);
           }
-          ss = group_sum<kWave>(ss);
+          ss = head_sum(ss);
           const float r = __builtin_amdgcn_rsqf(fmaf(ss, p.inv_d, p.eps));
 #pragma unroll
-          for (int j = 0; j < NE; ++j)
-            n[j] = fmaf(c[j] * r, isk[u] ? wk[j] : wq[j], isk[u] ? bk[j] : bq[j]);
+          for (int s = 0; s < S; ++s) {
+            float w[PW], b[PW];
+            unpack_run<IO, PW>(isk[u] ? wk[s] : wq[s], w);
+            unpack_run<IO, PW>(isk[u] ? bk[s] : bq[s], b);
+#pragma unroll
+            for (int i = 0; i < PW; ++i) n[s * PW + i] = fmaf(c[s * PW + i] * r, w[i], b[i]);
+          }
         } else if constexpr (kRms) {
           float ss = 0.0f;
 #pragma unroll
-          for (int j = 0; j < NE; ++j) ss = fmaf(x[u][j], x[u][j], ss);
-          ss = group_sum<kWave>(ss);
+          for (int j = 0; j < NE; ++j) ss = fmaf(x[j], x[j], ss);
+          ss = head_sum(ss);
           const float r = __builtin_amdgcn_rsqf(fmaf(ss, p.inv_d, p.eps));
 #pragma unroll
-          for (int j = 0; j < NE; ++j) n[j] = x[u][j] * r * (isk[u] ? wk[j] : wq[j]);
+          for (int s = 0; s < S; ++s) {
+            float w[PW];
+            unpack_run<IO, PW>(isk[u] ? wk[s] : wq[s], w);
+#pragma unroll
+            for (int i = 0; i < PW; ++i) n[s * PW + i] = x[s * PW + i] * r * w[i];
+          }
         } else {
 #pragma unroll
-          for (int j = 0; j < NE; ++j) n[j] = x[u][j];
+          for (int j = 0; j < NE; ++j) n[j] = x[j];
         }
 
         float o[NE];
@@ -871,41 +986,45 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
         for (int j = 0; j < NE; ++j) o[j] = n[j];
         if constexpr (kRotate) {
           float pn[NE];
-          if (neox) {
-            wave_lds_fence();  // the previous head's reads are done
+          if (exch) {
+            wave_lds_fence();  // the previous group's reads are done
 #pragma unroll
-            for (int j = 0; j < NE; ++j) {
-              const int e = elem(j / PW, j % PW);
-              if ((j / PW) * SPAN < R && e < R) row[e] = n[j];
+            for (int s = 0; s < S; ++s) {
+              if (run_ok[s]) {
+                float* const dst = xrow + head0 + e0[s];
+                if constexpr (PW == 8) {
+                  *reinterpret_cast<float4*>(dst) = make_float4(n[s * PW], n[s * PW + 1], n[s * PW + 2], n[s * PW + 3]);
+                  *reinterpret_cast<float4*>(dst + 4) =
+                      make_float4(n[s * PW + 4], n[s * PW + 5], n[s * PW + 6], n[s * PW + 7]);
+                } else if constexpr (PW == 4) {
+                  *reinterpret_cast<float4*>(dst) = make_float4(n[s * PW], n[s * PW + 1], n[s * PW + 2], n[s * PW + 3]);
+                } else if constexpr (PW == 2) {
+                  *reinterpret_cast<float2*>(dst) = make_float2(n[s * PW], n[s * PW + 1]);
+                } else {
+                  *dst = n[s];
+                }
+              }
             }
             wave_lds_fence();
 #pragma unroll
-            for (int j = 0; j < NE; ++j) pn[j] = ((j / PW) * SPAN < R && rot[j]) ? row[partner[j]] : 0.0f;
-          } else if constexpr (PW >= 2) {
-#pragma unroll
-            for (int j = 0; j < NE; ++j) pn[j] = n[j ^ 1];
+            for (int j = 0; j < NE; ++j) pn[j] = rot[j] ? xrow[head0 + partner[j]] : 0.0f;
           } else {
+            if constexpr (PW >= 2) {
 #pragma unroll
-            for (int j = 0; j < NE; ++j) pn[j] = dpp_mov<kDppQuadXor1>(n[j]);
+              for (int j = 0; j < NE; ++j) pn[j] = n[j ^ 1];
+            } else {
+#pragma unroll
+              for (int j = 0; j < NE; ++j) pn[j] = 0.0f;  // PW = 1 always exchanges
+            }
           }
 #pragma unroll
           for (int j = 0; j < NE; ++j)
             if (rot[j]) o[j] = fmaf(n[j], cs[j], pn[j] * sn[j]);
         }
+        if (ok[u]) {
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-          const int e = elem(s, 0);
-          if (s * SPAN < D && e < D) {
-            if constexpr (PW == 4) {
-              __builtin_amdgcn_raw_buffer_store_b64(
-                  u32x2_t{IO::pack(o[s * PW], o[s * PW + 1]), IO::pack(o[s * PW + 2], o[s * PW + 3])},
-                  rs[u], 2 * e, 0, kStorePolicy);
-            } else if constexpr (PW == 2) {
-              __builtin_amdgcn_raw_buffer_store_b32(IO::pack(o[s * PW], o[s * PW + 1]), rs[u], 2 * e, 0,
-                                                    kStorePolicy);
-            } else {
-              __builtin_amdgcn_raw_buffer_store_b16(narrow1<IO>(o[s]), rs[u], 2 * e, 0, kStorePolicy);
-            }
+          for (int s = 0; s < S; ++s) {
+            if (run_ok[s]) store_run<PW>(rs[u], off[u] + 2 * s * span, pack_run<IO, PW>(&o[s * PW]));
           }
         }
       }
@@ -913,6 +1032,7 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
   }
 }
 
+// ----------------------------------------------------------------------------
 // One instance group of the kernel table, defined in qknr_inst.hip and built
 // once per (I/O type, group): group 0 the fused op with compile-time head_dim,
 // group 1 the other modes with compile-time head_dim, groups 2 and 4 the fused
@@ -929,9 +1049,10 @@ const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int 
 template <class IO, int GROUP>
 const void* pick_seg(bool full, int U, int mode, int shift);
 
-// Group 3: the element-granular kernel of a mode (kFused ... kLayerOnly) with
-// S slots per lane (1, 2, 4 or 8) of pw elements each (1, 2 or 4; S * pw <= 8).
-template <class IO>
+// Groups 3 and 5: the element-granular kernel of a mode (kFused ... kLayerOnly)
+// with S slots per lane of pw elements each (pw 1, 2, 4 or 8; S * pw <= 8);
+// group 3 holds pw 1 and 2, group 5 pw 4 and 8.
+template <class IO, int GROUP>
 const void* pick_elem(int mode, int slots, int pw);
 
 }  // namespace qknr_impl

@@ -1,11 +1,11 @@
 // qknr_inst.hip -- one instance group of the fused QK RMSNorm + RoPE kernel
 // table (see qknr_device.h). Built once per (I/O type, group) with
-// -DQKNR_INST_IO=Bf16|Fp16 -DQKNR_INST_GROUP=0..4, so the groups compile in
+// -DQKNR_INST_IO=Bf16|Fp16 -DQKNR_INST_GROUP=0..5, so the groups compile in
 // parallel; the host library (qknr.hip) calls pick_group<IO, GROUP> (the
 // vectorised kernel: group 0 the fused op at head_dim 64/128/256, group 1 the
 // other modes there, groups 2 and 4 the run-time head_dims at unroll 2 and 4)
-// and pick_elem<IO> (group 3, the element-granular kernel with 2-, 4- or
-// 8-byte accesses).
+// and pick_elem<IO, GROUP> (groups 3 and 5, the element-granular kernel with
+// 2- and 4-byte, and 8- and 16-byte accesses).
 
 #include "qknr_device.h"
 
@@ -13,7 +13,7 @@
 #error "build with -DQKNR_INST_IO=Bf16 or Fp16"
 #endif
 #ifndef QKNR_INST_GROUP
-#error "build with -DQKNR_INST_GROUP=0, 1, 2, 3 or 4"
+#error "build with -DQKNR_INST_GROUP=0, 1, 2, 3, 4 or 5"
 #endif
 
 namespace qknr_impl {
@@ -227,14 +227,28 @@ const void* pick_seg(bool full, int U, int mode, int shift) {
   }
 }
 
-#if QKNR_INST_GROUP == 3
+#if QKNR_INST_GROUP == 3 || QKNR_INST_GROUP == 5
 template <class IO, int MODE, int PW>
 const void* pick_elem_slots(int slots) {
   switch (slots) {
     case 1: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 1, PW>);
-    case 2: return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 2, PW>);
+    case 2:
+      if constexpr (2 * PW <= kElemPerLane) return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 2, PW>);
+      return nullptr;
+    case 3:
+      if constexpr (3 * PW <= kElemPerLane) return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 3, PW>);
+      return nullptr;
     case 4:
-      if constexpr (PW <= 2) return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 4, PW>);
+      if constexpr (4 * PW <= kElemPerLane) return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 4, PW>);
+      return nullptr;
+    case 5:
+      if constexpr (PW == 1) return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 5, 1>);
+      return nullptr;
+    case 6:
+      if constexpr (PW == 1) return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 6, 1>);
+      return nullptr;
+    case 7:
+      if constexpr (PW == 1) return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 7, 1>);
       return nullptr;
     case 8:
       if constexpr (PW == 1) return reinterpret_cast<const void*>(&qknr_elem_kernel<IO, MODE, 8, 1>);
@@ -243,17 +257,25 @@ const void* pick_elem_slots(int slots) {
   }
 }
 
+// group 3: runs of 1 or 2 elements; group 5: runs of 4 or 8
 template <class IO, int MODE>
 const void* pick_elem_pw(int slots, int pw) {
-  switch (pw) {
-    case 1: return pick_elem_slots<IO, MODE, 1>(slots);
-    case 2: return pick_elem_slots<IO, MODE, 2>(slots);
-    case 4: return pick_elem_slots<IO, MODE, 4>(slots);
-    default: return nullptr;
+  if constexpr (QKNR_INST_GROUP == 3) {
+    switch (pw) {
+      case 1: return pick_elem_slots<IO, MODE, 1>(slots);
+      case 2: return pick_elem_slots<IO, MODE, 2>(slots);
+      default: return nullptr;
+    }
+  } else {
+    switch (pw) {
+      case 4: return pick_elem_slots<IO, MODE, 4>(slots);
+      case 8: return pick_elem_slots<IO, MODE, 8>(slots);
+      default: return nullptr;
+    }
   }
 }
 
-template <class IO>
+template <class IO, int GROUP>
 const void* pick_elem(int mode, int slots, int pw) {
   switch (mode) {
     case kFused: return pick_elem_pw<IO, kFused>(slots, pw);
@@ -265,7 +287,7 @@ const void* pick_elem(int mode, int slots, int pw) {
   }
 }
 
-template const void* pick_elem<QKNR_INST_IO>(int, int, int);
+template const void* pick_elem<QKNR_INST_IO, QKNR_INST_GROUP>(int, int, int);
 #else
 template const void* pick_group<QKNR_INST_IO, QKNR_INST_GROUP>(int, int, bool, bool, int, int, int);
 template const void* pick_seg<QKNR_INST_IO, QKNR_INST_GROUP>(bool, int, int, int);

@@ -39,13 +39,17 @@
  *     stride a multiple of 16 bytes; lane offsets inside a head group below
  *     2^31 bytes (a mapping with fewer heads per group is tried first); and,
  *     for the unfused steps, head_dim 64, 128 or 256;
- *   - the element-granular kernel (one head per wave instruction) for every
- *     other supported case, with 2-, 4- or 8-byte accesses: 8 (4) bytes need
- *     head_dim a multiple of 4 (2) and q, k, weights (and biases) and every
- *     used stride 8 (4)-byte aligned; of the allowed widths it takes the
- *     narrowest that still needs no more accesses per head than the widest.
- *     It needs only element alignment and has no stride limit; it computes
- *     the same formulas.
+ *   - the element-granular kernel for every other supported case, with
+ *     2-, 4-, 8- or 16-byte accesses: 2*r bytes need head_dim a multiple of r
+ *     and q, k, weights (and biases) and every used stride 2*r-byte aligned. A
+ *     head takes L lanes of S runs of r elements (L*S*r >= head_dim, S*r <= 8)
+ *     and a wave instruction 64/L heads; of the allowed (r, S, L) -- L a power
+ *     of two, or the exact lane count a head needs -- it takes the one with
+ *     the fewest wave instructions per token, then a power-of-two L, the
+ *     wider access, fewer slots. Several heads per instruction need their
+ *     lane offsets below 2^31 bytes; otherwise one head per instruction (no
+ *     stride limit). It needs only element alignment and computes the same
+ *     formulas.
  * qknr_inplace_ex reports which one a call takes (qknr_launch_info.generic).
  *
  * All entry points are thread-safe and keep no state besides small per-device
@@ -157,13 +161,14 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
  *   generic          1: take the element-granular kernel even where the
  *                    vectorised one applies (lanes_per_head must then be 0);
  *                    0: choose [0].
- * On the element-granular kernel a "group" is one head: groups_per_item is
- * the heads per work item [twice the heads loaded together], block_waves and
- * max_blocks apply as above, unroll is set by the kernel instance (16/(S*r)
- * heads loaded before the first is computed, with S slots of r elements per
- * lane; reported in qknr_launch_info.unroll; any valid value is accepted), and
- * lanes_per_head must be 0 (an explicit lane mapping that the case cannot use
- * is QKNR_E_ARG).
+ * On the element-granular kernel a group is the 64/L heads of one wave
+ * instruction (see "Supported shapes"): groups_per_item is the groups per work
+ * item [twice the groups loaded together], block_waves and max_blocks apply as
+ * above [4 waves], unroll is set by the kernel instance (16/(S*r) groups loaded
+ * before the first is computed, with S slots of r elements per lane; reported
+ * in qknr_launch_info.unroll; any valid value is accepted), and lanes_per_head
+ * must be 0 (an explicit lane mapping that the case cannot use is
+ * QKNR_E_ARG).
  */
 typedef struct qknr_launch_cfg {
   int32_t lanes_per_head;
@@ -176,10 +181,10 @@ typedef struct qknr_launch_cfg {
 
 /* What a call launches (filled by qknr_inplace_ex, also for empty work, where
  * grid_blocks stays 0). On the element-granular kernel (generic = 1) a lane
- * owns elems_per_lane elements in runs of access_bytes/2 (1, 2 or 4), runs 64
- * apart, one head per wave instruction. access_bytes was added in the struct's
- * former tail padding: the size (48 bytes) and the other offsets are
- * unchanged. */
+ * owns elems_per_lane elements in runs of access_bytes/2 (1, 2, 4 or 8),
+ * lanes_per_head lanes apart, and heads_per_wave heads share a wave
+ * instruction. access_bytes was added in the struct's former tail padding: the
+ * size (48 bytes) and the other offsets are unchanged. */
 typedef struct qknr_launch_info {
   int32_t lanes_per_head;
   int32_t elems_per_lane;
@@ -270,6 +275,24 @@ QKNR_API int32_t qknr_layernorm_rope_inplace(void* q, void* k, const void* wq, c
                                              int64_t k_tok_stride_B, int64_t k_head_stride_B,
                                              int32_t dtype, int32_t pos_dtype, hipStream_t stream);
 
+/* qknr_layernorm_rope_inplace with an explicit launch configuration (cfg may
+ * be NULL) and an optional report of what was launched (info may be NULL),
+ * as qknr_inplace_ex is to qknr_inplace. The LayerNorm instances at head_dim
+ * 64, 128 and 256 exist at unroll 2 only (another unroll value runs as 2);
+ * the fields mean what they mean for qknr_inplace_ex. Same contract and
+ * status codes as qknr_layernorm_rope_inplace. */
+QKNR_API int32_t qknr_layernorm_rope_inplace_ex(void* q, void* k, const void* wq, const void* wk,
+                                                const void* bq, const void* bk,
+                                                const float* cos_sin_cache, const void* positions,
+                                                int64_t T, int32_t Hq, int32_t Hkv,
+                                                int32_t head_dim, int32_t rope_dim,
+                                                int32_t is_neox, float eps,
+                                                int64_t q_tok_stride_B, int64_t q_head_stride_B,
+                                                int64_t k_tok_stride_B, int64_t k_head_stride_B,
+                                                int32_t dtype, int32_t pos_dtype,
+                                                hipStream_t stream, const qknr_launch_cfg* cfg,
+                                                qknr_launch_info* info);
+
 /*
  * qknr_can_use -- 1 if qknr_inplace supports this combination, else 0: the
  * "Supported shapes" set above (a superset of the page's capability predicate,
@@ -280,7 +303,12 @@ QKNR_API int32_t qknr_can_use(int32_t head_dim, int32_t rope_dim, int32_t is_neo
                               int32_t dtype, int32_t pos_dtype);
 
 /* Static, never-freed description of a status code ("unknown status" for
- * codes not listed above). Pure host function. */
+ * codes not listed above). Pure host function. The Python binding raises an
+ * exception carrying this text whenever a call returns a non-zero status: the
+ * SGLang Kernel Design Agent (KDA) kernel-directory page, in its maintenance
+ * rules ("directory maintenance conventions and extension guide", rule 3),
+ * asks that a public kernel come with a can_use predicate and fail by raising
+ * rather than by returning None, which callers forget to check. */
 QKNR_API const char* qknr_status_string(int32_t status);
 
 #ifdef __cplusplus

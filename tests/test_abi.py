@@ -191,11 +191,8 @@ def test_rejections(kw, code):
     assert _call(**kw) == code
 
 
-def _elem_width(kw):
-    """Elements per access of the element-granular kernel: 4 (8-byte accesses)
-    when head_dim is a multiple of 4 and q, k, the weights and the used strides
-    are 8-byte aligned, 2 when head_dim is even and they are 4-byte aligned,
-    else 1."""
+def _elem_align(kw):
+    """Common alignment (2 to 16 bytes) of q, k, the weights and the used strides."""
     a = dict(q=P(A), k=P(A + 0x100000), wq=P(A), wk=P(A), D=128, qt=4 * 256, qh=256, kt=4 * 256,
              kh=256)
     a.update({n: v for n, v in kw.items() if n in a})
@@ -204,30 +201,54 @@ def _elem_width(kw):
         return (all(a[n].value % b == 0 for n in ("q", "k", "wq", "wk"))
                 and all(a[n] % b == 0 for n in ("qt", "qh", "kt", "kh")))
 
-    return elem_width(a["D"], 8 if aligned(8) else 4 if aligned(4) else 2)
+    return next(b for b in (16, 8, 4, 2) if aligned(b))
 
 
-def elem_width(D, align):
-    """The widest run length the alignment allows gives the fewest slots per
-    lane; the narrowest run length with that many slots is taken."""
-    def slots(pw):
-        s = 1
-        while 64 * s * pw < D:
-            s *= 2
-        return s
+def elem_plan(D, align, Hq, Hkv, groups_fit=True):
+    """The element-granular kernel's lane mapping (include/qknr.h), restated:
+    runs of pw elements with pw in {8, 4, 2, 1} dividing head_dim and
+    2*pw <= align; S runs per lane with S*pw <= 8; L lanes per head, the lanes
+    a head needs (ceil(head_dim / (S*pw)) <= 64) either rounded up to a power
+    of two or exact; G = 64 // L heads per wave instruction (1 if a group's
+    lane offsets would not fit 32 bits). The plan with the fewest wave
+    instructions per token, S * (ceil(Hq/G) + ceil(Hkv/G)), wins; ties go to a
+    power-of-two L, then the wider run, then fewer slots.
+    Returns (pw, S, L, G, exact_fit)."""
+    cands = []
+    for pw in (8, 4, 2, 1):
+        if D % pw or align < 2 * pw:
+            continue
+        S = 1
+        while S * pw <= 8:
+            lx = -(-D // (S * pw))
+            if lx <= 64:
+                lp = 1
+                while lp < lx:
+                    lp *= 2
+                shapes = [(lp, False)] + ([(lx, True)] if lx != lp and groups_fit else [])
+                for L, exact in shapes:
+                    G = 64 // L if groups_fit else 1
+                    cost = S * (-(-Hq // G) + -(-Hkv // G))
+                    cands.append(((cost, exact, -pw, S), (pw, S, L, G, exact)))
+            S += 1
+    return min(cands)[1]
 
-    pw = 4 if D % 4 == 0 and align >= 8 else 2 if D % 2 == 0 and align >= 4 else 1
-    fewest = slots(pw)
-    while pw > 1 and slots(pw // 2) <= fewest:
-        pw //= 2
-    return pw
 
-
-def test_element_width_rule_covers_every_width():
-    assert {_elem_width(kw) for kw in GENERIC} == {1, 2, 4}
-    # head_dim 100 and 128 take pairs, 200 and 256 runs of 4, 64 and 40 single elements
-    assert [elem_width(D, 8) for D in (100, 128, 200, 256, 64, 40, 300, 512)] == [2, 2, 4, 4, 1, 1, 4, 4]
-    assert [elem_width(D, 4) for D in (100, 200, 130, 45)] == [2, 2, 2, 1]
+def test_element_plan_rule_examples():
+    # head_dim 100 (8-byte runs): 32 lanes, 2 heads per instruction (4 before);
+    # 40 with 16-byte runs: exact groups of 5 lanes, 12 heads; 130 (4-byte runs):
+    # 17 lanes x 4 slots, 3 heads; odd head_dims take single elements
+    assert elem_plan(100, 8, 24, 24)[:4] == (4, 1, 32, 2)
+    assert elem_plan(40, 16, 24, 24) == (8, 1, 5, 12, True)
+    assert elem_plan(40, 8, 24, 24) == (4, 1, 10, 6, True)
+    assert elem_plan(130, 16, 24, 24) == (2, 4, 17, 3, True)
+    assert elem_plan(255, 16, 24, 24)[0] == 1
+    assert elem_plan(128, 16, 24, 24)[:4] == (8, 1, 16, 4)
+    assert elem_plan(512, 16, 24, 24)[:4] == (8, 1, 64, 1)
+    # without room for 32-bit group offsets: one head per instruction
+    assert elem_plan(100, 8, 24, 24, groups_fit=False)[3] == 1
+    # few heads: fewer lanes per head are no use
+    assert elem_plan(40, 16, 1, 0)[3] >= 1
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: run on a host without a GPU")
@@ -236,22 +257,22 @@ def test_element_granular_cases_are_accepted(kw):
     rc, info = _call_info(**kw)
     assert rc == B.QKNR_E_DEVICE, B.qknr_status_string(rc)
     D = kw.get("D", 128)
-    pw = _elem_width(kw)
-    assert info["generic"] == 1 and info["lanes_per_head"] == 64 and info["heads_per_wave"] == 1
-    assert info["access_bytes"] == 2 * pw
-    assert info["elems_per_lane"] == pw * -(-D // (64 * pw))
-    assert info["groups_per_token"] == 8  # one group per head
-    # slots per lane: the smallest power of two covering head_dim / (64 pw);
-    # 16/(slots pw) heads are loaded before the first is computed, two such
-    # rounds per item
-    slots = 1
-    while 64 * slots * pw < D:
-        slots *= 2
-    U = 16 // (slots * pw)
+    pw, S, L, G, _ = elem_plan(D, _elem_align(kw), 4, 4)
+    assert info["generic"] == 1
+    assert (info["access_bytes"], info["elems_per_lane"], info["lanes_per_head"],
+            info["heads_per_wave"]) == (2 * pw, S * pw, L, G), info
+    ng = 2 * -(-4 // G)
+    assert info["groups_per_token"] == ng
+    # 16/(S pw) groups are loaded before the first is computed, two such rounds per item
+    U = 16 // (S * pw)
     cfg = kw.get("cfg")
-    want = min(cfg.groups_per_item if cfg is not None and cfg.groups_per_item else 2 * U, 8)
+    want = min(cfg.groups_per_item if cfg is not None and cfg.groups_per_item else 2 * U, ng)
     assert info["groups_per_item"] == want and info["unroll"] == U
-    assert info["items"] == 5 * -(-8 // want)
+    assert info["items"] == 5 * -(-ng // want)
+
+
+def test_element_plan_covers_every_width():
+    assert {elem_plan(kw.get("D", 128), _elem_align(kw), 4, 4)[0] for kw in GENERIC} == {1, 2, 4, 8}
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: run on a host without a GPU")
@@ -288,7 +309,9 @@ def test_plan_lane_mapping(D):
                 continue
             info = _plan(D, R, neox)
             if not _vectorised(D, R, neox):
-                assert info["generic"] == 1 and info["lanes_per_head"] == 64, (D, R, neox)
+                pw, S, L, G, _ = elem_plan(D, 16, 24, 24)
+                assert info["generic"] == 1 and (info["lanes_per_head"], info["heads_per_wave"],
+                                                 info["access_bytes"]) == (L, G, 2 * pw), (D, R, neox)
                 continue
             assert info["generic"] == 0
             fits = lambda e: (not neox) or ((R // 2) % e == 0 and R // 2 >= e)
@@ -466,31 +489,40 @@ def test_plan_explicit_cfg():
 
 
 def test_plan_element_granular():
-    """head_dims the vectorised kernel does not take, NeoX halves that are not
-    a multiple of a lane width, and an explicit request, plan one head per
-    wave instruction; a lane slot holds a run of 1, 2 or 4 elements (2-, 4- or
-    8-byte accesses; contiguous aligned views here), runs 64 apart."""
-    info = _plan(100, 100, 1, Hq=7, Hkv=3)   # 1 slot of pairs: 8 heads in flight
-    assert info == dict(lanes_per_head=64, elems_per_lane=2, heads_per_wave=1,
-                        groups_per_token=10, groups_per_item=10, unroll=8, block_threads=256,
-                        grid_blocks=0, items=0, generic=1, access_bytes=4)
-    big = _plan(300, 300, 1, Hq=30, Hkv=10)  # 2 slots of 4: 2 heads in flight, 4 per item
-    assert (big["elems_per_lane"], big["unroll"], big["groups_per_item"]) == (8, 2, 4)
-    wide = _plan(200, 98, 1, Hq=30, Hkv=10)  # 1 slot of 4: 4 heads in flight, 8 per item
-    assert (wide["elems_per_lane"], wide["unroll"], wide["access_bytes"]) == (4, 4, 8)
-    small = _plan(40, 6, 1, Hq=30, Hkv=10)   # 1 slot of 1: 16 heads in flight, 32 per item
-    assert (small["elems_per_lane"], small["unroll"], small["groups_per_item"]) == (1, 16, 32)
-    odd = _plan(45, 6, 1, Hq=30, Hkv=10)     # odd head_dim: 2-byte accesses, 1 slot, 16 heads
-    assert (odd["elems_per_lane"], odd["unroll"], odd["access_bytes"]) == (1, 16, 2)
+    """head_dims the vectorised kernel does not take, NeoX halves that are not a
+    multiple of a lane width, and an explicit request, plan the element-granular
+    kernel: runs of 1, 2, 4 or 8 elements, several heads per wave instruction
+    (expected values worked out by hand from the rule in elem_plan)."""
+    info = _plan(100, 100, 1, Hq=7, Hkv=3)   # runs of 4, 32 lanes (25 used): 2 heads per group
+    assert info == dict(lanes_per_head=32, elems_per_lane=4, heads_per_wave=2,
+                        groups_per_token=6, groups_per_item=6, unroll=4, block_threads=256,
+                        grid_blocks=0, items=0, generic=1, access_bytes=8)
+    big = _plan(300, 300, 1, Hq=30, Hkv=10)  # 2 slots of 4 on a full wave: 2 groups in flight, 4 per item
+    assert (big["elems_per_lane"], big["lanes_per_head"], big["unroll"], big["groups_per_item"]) == (8, 64, 2, 4)
+    wide = _plan(200, 98, 1, Hq=30, Hkv=10)  # 16-byte runs, 32 lanes (25 used), 2 heads per group
+    assert (wide["elems_per_lane"], wide["unroll"], wide["access_bytes"], wide["heads_per_wave"]) == (8, 2, 16, 2)
+    small = _plan(40, 6, 1, Hq=30, Hkv=10)   # 16-byte runs, exact groups of 5 lanes: 12 heads
+    assert (small["lanes_per_head"], small["heads_per_wave"], small["groups_per_token"],
+            small["groups_per_item"]) == (5, 12, 4, 4)
+    odd = _plan(45, 6, 1, Hq=30, Hkv=10)     # odd head_dim: 2-byte runs, 4 slots of 12 lanes, 5 heads
+    assert (odd["elems_per_lane"], odd["lanes_per_head"], odd["heads_per_wave"], odd["unroll"],
+            odd["access_bytes"]) == (4, 12, 5, 4, 2)
     assert _plan(72, 70, 1)["generic"] == 1          # NeoX half 35: no lane width divides it
     assert _plan(72, 72, 1)["elems_per_lane"] == 8   # NeoX half 36 = 8*4 + 4: 16-byte lanes
     assert _plan(72, 68, 1)["elems_per_lane"] == 8   # NeoX half 34 = 8*4 + 2: shifted partners
     assert _plan(72, 72, 0)["generic"] == 0          # interleaved: 16-byte lanes
-    assert _plan(130, 64, 0)["elems_per_lane"] == 4  # not a multiple of 8: pairs in 2 slots
+    odd130 = _plan(130, 64, 0)                       # pairs in 4 slots of 17 lanes, 3 heads
+    assert (odd130["elems_per_lane"], odd130["lanes_per_head"], odd130["heads_per_wave"]) == (8, 17, 3)
     assert _plan(132, 64, 0)["access_bytes"] == 8    # a multiple of 4: runs of 4
     forced = _plan(128, 128, 0, cfg=B.LaunchCfg(generic=1, groups_per_item=48, block_waves=2))
-    assert forced["generic"] == 1 and forced["groups_per_item"] == 48
-    assert forced["block_threads"] == 128
+    assert forced["generic"] == 1 and forced["heads_per_wave"] == 4
+    assert forced["groups_per_item"] == 12 and forced["block_threads"] == 128
+    for D, R, neox, Hq, Hkv in ((100, 100, 1, 7, 3), (300, 300, 1, 30, 10), (200, 98, 1, 30, 10),
+                                (40, 6, 1, 30, 10), (45, 6, 1, 30, 10), (130, 64, 0, 24, 24)):
+        pw, S, L, G, _ = elem_plan(D, 16, Hq, Hkv)
+        i = _plan(D, R, neox, Hq=Hq, Hkv=Hkv)
+        assert (i["access_bytes"], i["elems_per_lane"], i["lanes_per_head"], i["heads_per_wave"]) == \
+            (2 * pw, S * pw, L, G), (D, R, i)
 
 
 def test_binding_rejects_host_tensors():
@@ -539,8 +571,8 @@ def test_plan_falls_back_to_fewer_heads_per_group_for_huge_head_strides():
     assert rc == 0 and info["lanes_per_head"] == 32
     rc, info = plan(128, 3 << 30)
     assert rc == 0 and info["lanes_per_head"] == 64
-    rc, info = plan(64, 3 << 30)  # no vectorised mapping fits: element-granular
-    assert rc == 0 and info["generic"] == 1
+    rc, info = plan(64, 3 << 30)  # no vectorised mapping fits: element-granular, one head per group
+    assert rc == 0 and info["generic"] == 1 and info["heads_per_wave"] == 1
     rc, info = plan(64, 3 << 30, Hq=1)  # one head: its stride is never used
     assert rc == 0 and info["lanes_per_head"] == 8
 

@@ -9,7 +9,7 @@ import pytest
 
 from head_qk_rmsnorm_amd import workloads as W
 from tests import qknr_harness as Hn
-from tests.test_abi import elem_width
+from tests.test_abi import elem_plan
 
 pytestmark = pytest.mark.gpu
 
@@ -23,6 +23,29 @@ def _gpu():
 
     B.lib()
     yield
+
+
+def _view_align(dc):
+    """Common alignment (2 to 16 bytes) of q, k, the weights and the strides
+    that are used (token stride with T > 1, head stride with H > 1)."""
+    vals = []
+    for t in (dc.q, dc.k):
+        es = t.element_size()
+        vals.append(t.data_ptr())
+        if t.size(0) > 1:
+            vals.append(t.stride(0) * es)
+        if t.size(1) > 1:
+            vals.append(t.stride(1) * es)
+    vals += [dc.wq.data_ptr(), dc.wk.data_ptr()]
+    return next(b for b in (16, 8, 4, 2) if all(v % b == 0 for v in vals))
+
+
+def _check_plan(info, dc):
+    """The launch report of an element-granular call follows the lane-mapping rule."""
+    c = dc.cfg
+    pw, S, L, G, _ = elem_plan(c.head_dim, _view_align(dc), c.Hq, c.Hkv)
+    assert (info["access_bytes"], info["elems_per_lane"], info["lanes_per_head"],
+            info["heads_per_wave"]) == (2 * pw, S * pw, L, G), info
 
 
 def _check(wl, layout=None, launch=None, min_exact=0.99):
@@ -70,10 +93,10 @@ def test_shapes(D, R, neox):
     pdt = W.I64 if i % 3 == 0 else W.I32
     cfg = W.case(37, 5, 3, D, R, neox, dtype=dt, pos_dtype=pdt, seed=500 + i)
     print("case", cfg.name, flush=True)
-    info, _, _ = _check(W.make_workload(cfg))
+    info, _, dc = _check(W.make_workload(cfg))
     assert info["generic"] == (0 if _vectorised(D, R, neox) else 1), info
-    if info["generic"]:  # contiguous, aligned views: the access width follows head_dim
-        assert info["access_bytes"] == 2 * elem_width(D, 8), info
+    if info["generic"]:
+        _check_plan(info, dc)
 
 
 @pytest.mark.parametrize("layout", ["shifted", "shifted4", "odd_pad", "padded", "head_major", "qkv"])
@@ -82,13 +105,11 @@ def test_shapes(D, R, neox):
 def test_layouts(layout, D, R, neox):
     cfg = W.case(29, 6, 2, D, R, neox, dtype=W.BF16, pos_dtype=W.I64, seed=D + R + 7)
     print("case", cfg.name, layout, flush=True)
-    info, _, _ = _check(W.make_workload(cfg), layout=layout)
-    element_aligned_only = layout in ("shifted", "odd_pad")
+    info, _, dc = _check(W.make_workload(cfg), layout=layout)
     want = 0 if (_vectorised(D, R, neox) and layout not in ("shifted", "shifted4", "odd_pad")) else 1
     assert info["generic"] == want, (layout, info)
-    if want:  # 8-byte (4-byte) accesses need head_dim % 4 (% 2) == 0 and 8 (4)-byte aligned views
-        view_align = 2 if element_aligned_only else 4 if layout == "shifted4" else 8
-        assert info["access_bytes"] == 2 * elem_width(D, view_align), (layout, info)
+    if want:  # 2*pw-byte accesses need head_dim % pw == 0 and 2*pw-byte aligned views
+        _check_plan(info, dc)
 
 
 @pytest.mark.parametrize("D,R,neox", [(64, 64, True), (64, 32, False), (128, 128, False),
@@ -124,7 +145,7 @@ def test_launch_variants(launch, D, R, neox):
     info, _, _ = _check(W.make_workload(cfg), launch=launch)
     assert info["generic"] == 1
     if launch.get("groups_per_item"):
-        assert info["groups_per_item"] == min(launch["groups_per_item"], 12)
+        assert info["groups_per_item"] == min(launch["groups_per_item"], info["groups_per_token"])
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(0, 4), (4, 0), (1, 1), (1, 0), (31, 1), (3, 13)])

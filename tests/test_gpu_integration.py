@@ -60,7 +60,10 @@ def test_plain_c_caller(cfg):
         print(r.stdout, r.stderr, flush=True)
         assert r.returncode == 0, r.stderr
         got = np.fromfile(out, dtype=np.uint16)
-    assert "launch: generic=1 lanes_per_head=64" in r.stdout, r.stdout
+    from tests.test_abi import elem_plan
+
+    lanes = elem_plan(cfg.head_dim, 16, cfg.Hq, cfg.Hkv)[2]
+    assert f"launch: generic=1 lanes_per_head={lanes} " in r.stdout, r.stdout
     nq, nk = wl.q.size, wl.k.size
     assert got.size == 2 * (nq + nk)
     rq, rk = Hn.oracle_ref(wl)
