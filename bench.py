@@ -2,7 +2,11 @@
 """One-GPU benchmark of the fused in-place QK RMSNorm + RoPE (HIP, gfx950).
 
 A step is one launch of the op over one batch: every Q/K head vector of the
-workload normalised and rotated in place. Default workload: the DiT-shaped
+workload normalised and rotated in place. After a settle phase (untimed launches
+for --settle seconds, so the clocks settle) and --warmup untimed launches, 5
+batches of max(--steps, 50) launches are timed with HIP events on the launch
+stream; the line reports their median (and min/max). The other workloads are
+timed the same way in the same run (the line's "configs" object). Default workload: the DiT-shaped
 image+text sequence (T=4608 tokens, 24+24 heads, head_dim 128, interleaved
 pairing, bf16, int64 positions). The metric is achieved HBM bandwidth in
 algorithmic bytes (every Q/K element read and written once, one positions entry
@@ -32,25 +36,50 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 ROT_BYTES = 1 << 30    # rotate through >= 1 GiB of copies
 MAX_ROT = 64           # (tiny workloads: at most 64 copies; they are latency-bound anyway)
-KERNEL_SRC = os.path.join(ROOT, "head_qk_rmsnorm_amd", "csrc", "qknr_device.h")
+CSRC = os.path.join(ROOT, "head_qk_rmsnorm_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(CSRC, n) for n in ("qknr_device.h", "qknr_inst.hip", "qknr.hip")]
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+BATCHES = 5           # timed batches; the line reports their median
+MIN_BATCH = 50        # launches per batch at least
+SETTLE_S = 0.3        # seconds of launches before any timing, so the clocks settle
+LAUNCH_INFO_KEYS = ("lanes_per_head", "elems_per_lane", "heads_per_wave", "groups_per_token",
+                    "groups_per_item", "unroll", "block_threads", "grid_blocks", "items", "generic",
+                    "access_bytes")
 
 
-def kernel_sha() -> str:
-    """Hash of the fused kernel's device code (between its begin/end markers)."""
-    with open(KERNEL_SRC, "rb") as f:
-        src = f.read()
-    a = src.index(b"// ==== fused-kernel device code begin")
-    b = src.index(b"// ==== fused-kernel device code end")
-    return hashlib.sha256(src[a:b]).hexdigest()[:16]
+def source_sha() -> str:
+    """Hash of the library's kernel and planner sources (device code, instance
+    table, host planner): counters taken on other sources are not attached."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=1000,
-                    help="untimed launches before the timed ones (1000 lets the clocks settle)")
+    ap.add_argument("--steps", type=int, default=2000,
+                    help=f"launches per timed batch (at least {MIN_BATCH}); {BATCHES} batches are "
+                         "timed and their median reported")
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed launches right before the timed batches")
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed launches before anything is timed (clock settling)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other workloads for the line's 'configs' object")
     ap.add_argument("--config", default="dit",
                     help="tiny | dit | gqa | partial | large, or a one-GPU shard: gqa_tp8 | "
                          "dit_hp8 | dit_sp8")
@@ -167,46 +196,67 @@ class Rig:
             torch.cuda.synchronize(self.dev)
             self.graph = g
 
-    def time(self, steps, warmup):
+    def _launch_pass(self, n):
+        """n launches (eager) or n passes over the copies (graph replay)."""
+        if self.graph is not None:
+            for _ in range(n):
+                self.graph.replay()
+        else:
+            k = self.n_rot
+            for i in range(n):
+                self.calls[i % k]()
+
+    def settle(self, seconds):
+        """Untimed launches for about `seconds` of wall time, so the clocks have
+        settled before anything is timed. Returns (launches, seconds)."""
         import torch
 
-        n = self.n_rot
-        if self.graph is not None:
-            # whole passes over the copies: steps and warmup rounded up to multiples of n
-            reps, wreps = max(1, -(-steps // n)), max(1, -(-warmup // n))
-            for _ in range(wreps):
-                self.graph.replay()
+        per = 1 if self.graph is not None else 50
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            self._launch_pass(per)
+            n += per * (self.n_rot if self.graph is not None else 1)
             torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return n, time.perf_counter() - t0
+
+    def time(self, steps, warmup, batches=BATCHES):
+        """`warmup` untimed launches, then `batches` batches of max(steps,
+        MIN_BATCH) launches on the launch stream, each between two HIP events.
+        Graph replay times whole passes over the copies (rounded up). Returns
+        the per-launch ms of every batch, their median, the launches per batch
+        and the host's ms per launch."""
+        import statistics
+
+        import torch
+
+        n = max(steps, MIN_BATCH)
+        graph = self.graph is not None
+        reps = max(1, -(-n // self.n_rot)) if graph else n
+        per_batch = reps * self.n_rot if graph else n
+        self._launch_pass(max(1, -(-warmup // self.n_rot)) if graph else warmup)
+        torch.cuda.synchronize()
+        out, host = [], []
+        for _ in range(batches):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             h0 = time.perf_counter()
             e0.record()
-            for _ in range(reps):
-                self.graph.replay()
+            self._launch_pass(reps)
             e1.record()
-            host_s = time.perf_counter() - h0
+            host.append((time.perf_counter() - h0) / per_batch * 1e3)
             torch.cuda.synchronize()
-            wall_s = time.perf_counter() - h0
-            return e0.elapsed_time(e1) / (reps * n), host_s / (reps * n) * 1e3, wall_s
-        for i in range(warmup):
-            self.calls[i % n]()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        h0 = time.perf_counter()
-        e0.record()
-        for i in range(steps):
-            self.calls[i % n]()
-        e1.record()
-        host_s = time.perf_counter() - h0
-        torch.cuda.synchronize()
-        wall_s = time.perf_counter() - h0
-        ms = e0.elapsed_time(e1) / steps
-        return ms, host_s / steps * 1e3, wall_s
+            out.append(e0.elapsed_time(e1) / per_batch)
+        return {"batch_ms": out, "ms": statistics.median(out), "launches_per_batch": per_batch,
+                "host_ms": statistics.median(host)}
 
 
 def yardstick(nbytes, steps, warmup, dev):
-    """In-place read-xor(0)-write over the op's Q/K byte count, rotated copies."""
+    """In-place read-xor(0)-write over the op's Q/K byte count, rotated copies,
+    timed like the op (median of the batches)."""
+    import statistics
+
     import torch
 
     from head_qk_rmsnorm_amd import binding as B
@@ -214,18 +264,22 @@ def yardstick(nbytes, steps, warmup, dev):
     nbytes = (nbytes + 15) // 16 * 16
     n_rot = min(MAX_ROT, max(2, math.ceil(ROT_BYTES / nbytes)))
     bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(i) for i in range(n_rot)]
-    for i in range(warmup):
+    n = max(steps, MIN_BATCH)
+    for i in range(max(warmup, n)):
         B.qknr_rmw(bufs[i % n_rot], nbytes, 0)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        B.qknr_rmw(bufs[i % n_rot], nbytes, 0)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    out = []
+    for _ in range(BATCHES):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            B.qknr_rmw(bufs[i % n_rot], nbytes, 0)
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / n)
     del bufs
+    ms = statistics.median(out)
     return ms, 2 * nbytes / (ms * 1e-3) / 1e9
 
 
@@ -289,13 +343,16 @@ def cpu_baseline(cfg, seconds):
         "kind": "oracle",
         "sample": f"{done} tokens ({done * cfg.heads} head vectors) of the '{cfg.name}' workload "
                   f"in chunks of {chunk} tokens, {el:.1f} s, numpy fp64 on {workers} threads",
-        "host_cpu": platform.processor() or platform.machine(), "host_logical_cpus": os.cpu_count(),
+        "host_cpu": host_cpu_model(), "host_logical_cpus": os.cpu_count(),
         "gheads_per_s": round(done * cfg.heads / el / 1e9, 9),
     }
 
 
-def counters_for(cfg_name):
-    """Counter-based HBM traffic per launch, if it was measured on this kernel source."""
+def counters_for(cfg_name, launch_info, forced_launch):
+    """Counter-based HBM traffic per launch, if it was measured on these library
+    sources and in this launch shape (never for an explicit --launch)."""
+    if forced_launch:
+        return None, "explicit launch configuration: counters cover the automatic launch only"
     if not os.path.exists(COUNTERS):
         return None, "no counter file"
     with open(COUNTERS) as f:
@@ -303,8 +360,11 @@ def counters_for(cfg_name):
     ent = data.get(cfg_name)
     if not ent:
         return None, "workload not in counter file"
-    if ent.get("kernel_sha") != kernel_sha():
-        return None, "kernel changed since the counters were taken"
+    if ent.get("source_sha") != source_sha():
+        return None, "library sources changed since the counters were taken"
+    want = {k: launch_info.get(k) for k in LAUNCH_INFO_KEYS}
+    if {k: ent.get("launch", {}).get(k) for k in LAUNCH_INFO_KEYS} != want:
+        return None, "launch shape differs from the one the counters were taken in"
     return ent, None
 
 
@@ -317,7 +377,7 @@ def unfused_bytes(cfg):
 
 
 def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None, want_unfused=True,
-            op="fused", graph=False):
+            op="fused", graph=False, settle=0.0):
     own = rig is None
     layernorm = op == "layernorm"
     if own:
@@ -326,19 +386,23 @@ def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None, want_unfu
         rig.prepare(layernorm=True)
     elif not own:
         rig.prepare(launch)
-    ms, host_ms, wall = rig.time(steps, warmup)
+    settled = rig.settle(settle) if settle > 0 else (0, 0.0)
+    tm = rig.time(steps, warmup)
+    ms = tm["ms"]
     # the LayerNorm sibling also reads the two bias rows
     B = cfg.algorithmic_bytes() + (2 * cfg.head_dim * cfg.io_bytes if layernorm else 0)
     gbs = B / (ms * 1e-3) / 1e9
     out = {
         "workload": cfg.name, "ms_per_step": ms, "GB_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
-        "gheads_per_s": cfg.units / (ms * 1e-3) / 1e9, "host_ms_per_launch": host_ms,
+        "gheads_per_s": cfg.units / (ms * 1e-3) / 1e9, "host_ms_per_launch": tm["host_ms"],
+        "batch_ms": tm["batch_ms"], "launches_per_batch": tm["launches_per_batch"],
+        "settle": {"launches": settled[0], "seconds": round(settled[1], 3)},
         "algorithmic_bytes": B, "n_rot": rig.n_rot, "footprint_bytes": rig.footprint,
         "launch": rig.info, "op": op, "graph": rig.gstream is not None,
     }
     if want_unfused and not layernorm:
         rig.prepare(unfused=True)
-        ums, _, _ = rig.time(steps, warmup)
+        ums = rig.time(steps, warmup)["ms"]
         ub = unfused_bytes(cfg)
         out["unfused"] = {
             "ms_per_step": ums, "launches_per_step": 2, "bytes_per_step": ub,
@@ -349,10 +413,36 @@ def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None, want_unfu
     if own:
         del rig
     if want_yard:
-        ymsn, ygbs = yardstick(cfg.units * cfg.head_dim * 2, steps, warmup // 4 + 1, dev)
+        ymsn, ygbs = yardstick(cfg.units * cfg.head_dim * 2, steps, warmup, dev)
         out["yardstick_GB_s"] = ygbs
         out["frac_of_yardstick"] = gbs / ygbs
     return out
+
+
+def config_entry(r, forced_launch):
+    """One workload's figures for the line's 'configs' object."""
+    ms = r["ms_per_step"]
+    e = {
+        "ms_per_launch": round(ms, 6),
+        "ms_per_launch_min_max": [round(min(r["batch_ms"]), 6), round(max(r["batch_ms"]), 6)],
+        "GB_s": round(r["GB_s"], 3), "frac_of_hbm_peak": round(r["frac_of_peak"], 5),
+        "gheads_per_s": round(r["gheads_per_s"], 4),
+        "launch_mode": "hip graph replay" if r["graph"] else "eager launches from python",
+        "launches_per_batch": r["launches_per_batch"], "algorithmic_bytes": r["algorithmic_bytes"],
+        "launch": r["launch"],
+    }
+    if "yardstick_GB_s" in r:
+        e["yardstick_GB_s"] = round(r["yardstick_GB_s"], 3)
+        e["frac_of_yardstick"] = round(r["frac_of_yardstick"], 5)
+    ent, why = counters_for(r["workload"], r["launch"], forced_launch)
+    if ent:
+        traffic = ent["fetch_bytes_per_launch"] + ent["write_bytes_per_launch"]
+        e["traffic"] = traffic
+        e["traffic_over_algorithmic"] = round(traffic / r["algorithmic_bytes"], 4)
+    else:
+        e["traffic"] = None
+        e["traffic_note"] = why
+    return e
 
 
 # (head_dim, rope_dim, NeoX) shapes of the head_dim scan: the compile-time 128
@@ -461,10 +551,14 @@ def main():
                 extra.flush()
 
     r = measure(cfg, dev, args.steps, args.warmup, launch, want_yard=not args.no_yardstick,
-                want_unfused=not args.no_unfused, op=args.op, graph=args.graph)
-    print(f"[bench] {cfg.name}: {r['GB_s']:.1f} GB/s, {r['ms_per_step'] * 1e3:.2f} us/launch",
+                want_unfused=not args.no_unfused, op=args.op, graph=args.graph,
+                settle=args.settle)
+    print(f"[bench] {cfg.name}: {r['GB_s']:.1f} GB/s, {r['ms_per_step'] * 1e3:.2f} us/launch "
+          f"(median of {BATCHES} batches of {r['launches_per_batch']}; "
+          f"{min(r['batch_ms']) * 1e3:.2f}-{max(r['batch_ms']) * 1e3:.2f} us)",
           file=sys.stderr, flush=True)
-    ent, why = counters_for(cfg.name) if args.op == "fused" else (None, "counters cover the fused op")
+    ent, why = (counters_for(cfg.name, r["launch"], launch is not None) if args.op == "fused"
+                else (None, "counters cover the fused op"))
     traffic = None
     if ent:
         traffic = ent["fetch_bytes_per_launch"] + ent["write_bytes_per_launch"]
@@ -477,13 +571,21 @@ def main():
         "value": round(r["GB_s"], 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
+        "io_dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
                    "head_dim": cfg.head_dim, "rope_dim": cfg.rope_dim,
                    "pairing": "neox" if cfg.is_neox else "interleaved", "io_dtype": cfg.dtype,
                    "pos_dtype": cfg.pos_dtype, "layout": cfg.layout,
                    "algorithmic_bytes_per_step": r["algorithmic_bytes"], "launch": r["launch"],
                    "rotated_copies": r["n_rot"]},
+        "timing": {"batches": BATCHES, "launches_per_batch": r["launches_per_batch"],
+                   "statistic": "median of the batches' per-launch times",
+                   "ms_per_launch_min_median_max": [round(min(r["batch_ms"]), 6),
+                                                    round(r["ms_per_step"], 6),
+                                                    round(max(r["batch_ms"]), 6)],
+                   "settle": dict(r["settle"], what="untimed launches before any timing, so "
+                                                     "the clocks settle"),
+                   "events": "HIP events on the launch stream around each batch"},
         "gheads_per_s": round(r["gheads_per_s"], 4),
         "frac_of_hbm_peak": round(r["frac_of_peak"], 5),
         "launch_mode": "hip graph replay" if args.graph else "eager launches from python",
@@ -509,6 +611,23 @@ def main():
                           "fused: about half the memory traffic and close to 2x faster (no "
                           "hardware or measured figure given)",
         }
+    if not (args.no_configs or args.case or args.op != "fused" or launch is not None):
+        # the other workloads in the same run, timed the same way (the 16-token
+        # workload is shorter than a launch from Python: HIP graph replay)
+        line["configs"] = {}
+        for name in W.CONFIG_ORDER:
+            if name == cfg.name:
+                continue
+            c = W.CONFIGS[name]
+            # (no yardstick for the latency-bound 16-token workload: its eager
+            # launches would time the host, not the memory)
+            rc = measure(c, dev, args.steps, args.warmup, None,
+                         want_yard=not args.no_yardstick and name != "tiny",
+                         want_unfused=False, graph=name == "tiny", settle=0.05)
+            line["configs"][name] = config_entry(rc, False)
+            print(f"[bench] config {name}: {rc['GB_s']:.1f} GB/s ({rc['frac_of_peak'] * 100:.1f}% of "
+                  f"peak), {rc['ms_per_step'] * 1e3:.2f} us/launch", file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
     line["host_ms_per_launch"] = round(r["host_ms_per_launch"], 5)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)

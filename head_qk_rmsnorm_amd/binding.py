@@ -8,7 +8,8 @@ fallback: if the library is missing or rejects the call, an exception is raised.
 
 Names mirror the C entry points (``qknr_inplace``, ``qknr_inplace_ex``,
 ``qknr_can_use``, ``qknr_status_string``, the unfused baseline
-``qknr_rmsnorm_inplace`` / ``qknr_rope_inplace`` / ``qknr_unfused_inplace``,
+``qknr_rmsnorm_inplace`` / ``qknr_rope_inplace`` / ``qknr_unfused_inplace``, the
+LayerNorm sibling ``qknr_layernorm_rope_inplace`` / ``qknr_layernorm_rope_inplace_ex``,
 and the measurement aids ``qknr_copy`` / ``qknr_rmw``), plus ``fused_inplace_qknorm_rope``
 with the signature of the op on the page "SGLang Diffusion fused operator
 fused_inplace_qknorm_rope: in-depth technical analysis" (m.lsln.cn/news/241376),
@@ -98,6 +99,10 @@ def lib() -> ctypes.CDLL:
                                                       _I32, _I32, _I32, _I32, ctypes.c_float,
                                                       _I64, _I64, _I64, _I64, _I32, _I32, _P]
             L.qknr_layernorm_rope_inplace.restype = _I32
+            L.qknr_layernorm_rope_inplace_ex.argtypes = (
+                L.qknr_layernorm_rope_inplace.argtypes
+                + [ctypes.POINTER(LaunchCfg), ctypes.POINTER(LaunchInfo)])
+            L.qknr_layernorm_rope_inplace_ex.restype = _I32
             L.qknr_copy.argtypes = [_P, _P, _I64, _P]
             L.qknr_copy.restype = _I32
             L.qknr_rmw.argtypes = [_P, _I64, ctypes.c_uint32, _P]
@@ -315,6 +320,35 @@ def qknr_layernorm_rope_inplace(q, k, q_weight, k_weight, q_bias=None, k_bias=No
             _stream_of(q, stream)))
 
 
+def qknr_layernorm_rope_inplace_ex(q, k, q_weight, k_weight, q_bias=None, k_bias=None,
+                                   cos_sin_cache=None, positions=None, *, is_neox: bool = False,
+                                   eps: float = 1e-6, rope_dim: int = 0, stream=None,
+                                   launch: Optional[dict] = None) -> dict:
+    """qknr_layernorm_rope_inplace with an explicit launch configuration (keys of
+    LaunchCfg); returns what was launched (LaunchInfo as a dict)."""
+    import torch
+
+    v = _qk(q, k, 0)
+    wq, wk = _weights(q, q_weight, k_weight, v["D"])
+    bq = bk = ctypes.c_void_p(0)
+    if (q_bias is None) != (k_bias is None):
+        raise ValueError("give both biases or neither")
+    if q_bias is not None:
+        bq, bk = _weights(q, q_bias, k_bias, v["D"])
+    cache = pos = ctypes.c_void_p(0)
+    R, pcode = 0, QKNR_I32
+    if cos_sin_cache is not None:
+        cache, pos, R, pcode = _rotation(q, cos_sin_cache, positions, v["T"], rope_dim)
+    cfg = LaunchCfg(**(launch or {}))
+    info = LaunchInfo()
+    with torch.cuda.device(q.device):
+        _check(lib().qknr_layernorm_rope_inplace_ex(
+            v["q"], v["k"], wq, wk, bq, bk, cache, pos, v["T"], v["Hq"], v["Hkv"], v["D"], R,
+            int(bool(is_neox)), float(eps), v["qt"], v["qh"], v["kt"], v["kh"], v["dtype"], pcode,
+            _stream_of(q, stream), ctypes.byref(cfg), ctypes.byref(info)))
+    return info.as_dict()
+
+
 def fused_inplace_qknorm_rope(q, k, q_weight, k_weight, cos_sin_cache, positions, *,
                               is_neox: bool, eps: float = 1e-6, head_dim: int = 0,
                               rope_dim: int = 0) -> None:
@@ -361,15 +395,17 @@ class PreparedCall:
                         head_dim, rope_dim)
         self._cfg = LaunchCfg(**(launch or {}))
         self.info = LaunchInfo()
-        if (unfused or layernorm_bias is not None) and launch:
-            raise ValueError("only the fused op takes a launch configuration")
+        if unfused and launch:
+            raise ValueError("the unfused pair takes no launch configuration")
         if unfused:
             self._args = args + (_stream_of(q, stream),)
             self._fn = lib().qknr_unfused_inplace
         elif layernorm_bias is not None:
             bq, bk = _weights(q, layernorm_bias[0], layernorm_bias[1], int(args[9]))
-            self._args = args[:4] + (bq, bk) + args[4:] + (_stream_of(q, stream),)
-            self._fn = lib().qknr_layernorm_rope_inplace
+            self._args = args[:4] + (bq, bk) + args[4:] + (_stream_of(q, stream),
+                                                          ctypes.byref(self._cfg),
+                                                          ctypes.byref(self.info))
+            self._fn = lib().qknr_layernorm_rope_inplace_ex
         else:
             self._args = args + (_stream_of(q, stream), ctypes.byref(self._cfg),
                                  ctypes.byref(self.info))

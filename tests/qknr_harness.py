@@ -293,7 +293,11 @@ def unfused_check(wl, which, layout=None, tokens=None):
     return out
 
 
-def layernorm_check(wl, rope_dim, bias, layout=None, bias_seed=0):
+def layernorm_check(wl, rope_dim, bias, layout=None, bias_seed=0, launch=None):
+    """The LayerNorm sibling on fresh device copies against the oracle (every
+    Q/K element; bytes outside untouched). With ``launch`` (a dict, {} for the
+    automatic choice) the call goes through qknr_layernorm_rope_inplace_ex and
+    its launch report is returned."""
     from head_qk_rmsnorm_amd import binding as B
 
     c = wl.cfg
@@ -306,10 +310,18 @@ def layernorm_check(wl, rope_dim, bias, layout=None, bias_seed=0):
         bk_bits = W.to_io_bits(g.standard_normal(c.head_dim) * 0.5, c.dtype)
         bq = torch_from_bits(bq_bits, dc)
         bk = torch_from_bits(bk_bits, dc)
-    B.qknr_layernorm_rope_inplace(dc.q, dc.k, dc.wq, dc.wk, bq, bk,
-                                  dc.cache if rope_dim else None,
-                                  dc.positions if rope_dim else None,
-                                  is_neox=c.is_neox, eps=c.eps, rope_dim=rope_dim)
+    info = None
+    if launch is None:
+        B.qknr_layernorm_rope_inplace(dc.q, dc.k, dc.wq, dc.wk, bq, bk,
+                                      dc.cache if rope_dim else None,
+                                      dc.positions if rope_dim else None,
+                                      is_neox=c.is_neox, eps=c.eps, rope_dim=rope_dim)
+    else:
+        info = B.qknr_layernorm_rope_inplace_ex(dc.q, dc.k, dc.wq, dc.wk, bq, bk,
+                                                dc.cache if rope_dim else None,
+                                                dc.positions if rope_dim else None,
+                                                is_neox=c.is_neox, eps=c.eps, rope_dim=rope_dim,
+                                                launch=launch)
     rq, rk = O.qk_layernorm_rope_io(wl.q, wl.k, wl.wq, wl.wk, bq_bits, bk_bits,
                                     wl.cache[:, :rope_dim] if rope_dim else None, wl.positions,
                                     is_neox=c.is_neox, eps=c.eps, dtype=c.dtype,
@@ -322,6 +334,7 @@ def layernorm_check(wl, rope_dim, bias, layout=None, bias_seed=0):
         cmp = compare_bits(g, r, c.dtype)
         assert cmp.bad == 0, f"layernorm {c.name} {name}: {cmp}"
         assert cmp.exact_frac >= 0.99, f"layernorm {c.name} {name}: {cmp}"
+    return info
 
 
 def torch_from_bits(bits, dc):

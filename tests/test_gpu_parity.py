@@ -488,3 +488,22 @@ def test_layernorm_sibling_layouts(layout):
 def test_layernorm_sibling_on_dit_workload():
     """The DiT workload with LayerNorm instead of RMSNorm (all tokens)."""
     Hn.layernorm_check(W.make_workload(W.CONFIGS["dit"]), 128, True)
+
+
+@pytest.mark.parametrize("D,R,neox,launch,want", [
+    (128, 128, False, {}, dict(generic=0, lanes_per_head=16, elems_per_lane=8, heads_per_wave=4)),
+    (128, 64, True, {"block_waves": 2, "groups_per_item": 3},
+     dict(generic=0, block_threads=128, groups_per_item=3)),
+    (80, 20, True, {}, dict(generic=0, elems_per_lane=8)),
+    (100, 100, True, {}, dict(generic=1, access_bytes=8)),
+    (128, 0, False, {"generic": 1}, dict(generic=1, access_bytes=16)),
+])
+def test_layernorm_launch_report(D, R, neox, launch, want):
+    """qknr_layernorm_rope_inplace_ex reports what it launched (and honours a
+    launch configuration) while the result still matches the oracle."""
+    cfg = W.case(37, 6, 3, D, R or D, neox, pos_dtype=W.I64, seed=D + R + 3, x_std=2.0)
+    _say("case layernorm report", cfg.name, launch)
+    info = Hn.layernorm_check(W.make_workload(cfg), R, True, launch=launch)
+    for k, v in want.items():
+        assert info[k] == v, info
+    assert info["grid_blocks"] > 0 and info["items"] > 0, info
