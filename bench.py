@@ -383,7 +383,7 @@ def measure(cfg, dev, steps, warmup, launch, want_yard=True, rig=None, want_unfu
     if own:
         rig = Rig(cfg, dev, launch=launch, graph=graph)
     if layernorm:
-        rig.prepare(layernorm=True)
+        rig.prepare(launch, layernorm=True)
     elif not own:
         rig.prepare(launch)
     settled = rig.settle(settle) if settle > 0 else (0, 0.0)

@@ -185,12 +185,15 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // the benchmark workloads): one work item per wave with no persistent grid,
 // 2 head groups per item, both loaded before the first is computed, 3 waves
 // per workgroup when a head takes at most 16 lanes (head_dim <= 128 with
-// 16-byte lanes; repeated A/Bs: +1.3-2% DiT, +0.4-3% Partial, GQA unchanged)
-// and 4 otherwise (head_dim 256: 3 waves measured 1-1.5% slower there).
+// 16-byte lanes; repeated A/Bs: +1.3-2% DiT, +0.4-3% Partial, GQA unchanged),
+// 6 for the fused op at head_dim 256 with 16-byte lanes (32 lanes per head:
+// +3.0% and +3.1% over 4 waves on two machines, 8 waves +2.4%, 5 waves +1.1%;
+// the LayerNorm sibling there: 6 waves -0.5%, so it keeps 4) and 4 otherwise.
 constexpr int kDefaultGroupsPerItem = 2;
 constexpr int kDefaultUnroll = 2;
 constexpr int kDefaultBlockWaves = 4;
 constexpr int kDefaultBlockWavesNarrow = 3;  // lane groups of at most 16 lanes
+constexpr int kDefaultBlockWavesHalf = 6;    // head_dim 256 on 16-byte lanes
 // Run-time head_dim instances of the fused op and of the LayerNorm sibling take
 // longer work items with NeoX pairing, or when a head group holds at most 640
 // bytes (spare lanes in the padded lane group, or few heads per wave
@@ -330,10 +333,11 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   pl->items = T * pl->nc;
   if (pl->items > kMaxItems) return QKNR_E_SHAPE;
   pl->U = U;
-  pl->wpb = c.block_waves != 0 ? c.block_waves
-            : long_items       ? kLongItemBlockWaves
-            : pl->L <= 16      ? kDefaultBlockWavesNarrow
-                               : kDefaultBlockWaves;
+  pl->wpb = c.block_waves != 0        ? c.block_waves
+            : long_items              ? kLongItemBlockWaves
+            : pl->L <= 16             ? kDefaultBlockWavesNarrow
+            : mode == kFused && exact && pl->L == 32 && E == 8 ? kDefaultBlockWavesHalf
+                                      : kDefaultBlockWaves;
   pl->max_blocks = c.max_blocks;
   // partners 2 or 6 slots over are exchanged through a per-wave LDS row of
   // 64 lanes x E floats

@@ -152,8 +152,10 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
  *                    [2; 4 for long items] A head_dim other than 64/128/256
  *                    runs at 2 or 4 (1 runs as 2).
  *   block_waves      wavefronts per workgroup: 1..8. [3 when a head takes at
- *                    most 16 lanes, else 4; 2 for long items; 4 on the
- *                    element-granular kernel]
+ *                    most 16 lanes; 6 at head_dim 256 with 16-byte lanes
+ *                    (32 lanes per head; the LayerNorm sibling keeps 4); 2
+ *                    for long items; else 4, also on the element-granular
+ *                    kernel]
  *   max_blocks       0: one workgroup per block_waves work items, each wave
  *                    handles one item [default]; -1: a persistent grid of
  *                    (occupancy x CUs) workgroups striding over the items;

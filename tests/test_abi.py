@@ -425,11 +425,14 @@ def test_plan_head_dim_96_takes_12_byte_lanes():
 
 def test_plan_defaults():
     """Automatic launch: 2 head groups per work item, both loaded up front,
-    3 waves per workgroup when a head takes at most 16 lanes, else 4."""
+    3 waves per workgroup when a head takes at most 16 lanes, 6 at head_dim 256
+    on 16-byte lanes, else 4."""
     info = _plan(128, 128, 0)
     assert info["groups_per_item"] == 2 and info["unroll"] == 2
     assert info["block_threads"] == 192
-    assert _plan(256, 256, 0)["block_threads"] == 256          # 32 lanes per head
+    assert _plan(256, 256, 0)["block_threads"] == 384          # 32 lanes per head
+    assert _plan(256, 44, 1)["block_threads"] == 384           # shifted partners, 32 lanes
+    assert _plan(128, 128, 0, cfg=B.LaunchCfg(lanes_per_head=32))["block_threads"] == 256
     assert _plan(64, 64, 1)["block_threads"] == 192            # 8 lanes per head
     assert _plan(96, 96, 0)["block_threads"] == 192            # run-time head_dim, 16 lanes
     assert _plan(128, 12, 1)["lanes_per_head"] == 16            # NeoX 12: shifted partners
@@ -463,7 +466,8 @@ def test_plan_defaults_long_items(D, R, neox, long_items):
         assert (info["unroll"], info["groups_per_item"], info["block_threads"]) == (4, 4, 128), info
     else:
         assert (info["unroll"], info["groups_per_item"]) == (2, 2), info
-        assert info["block_threads"] == (192 if L <= 16 else 256), info
+        want = 192 if L <= 16 else 384 if (D == 256 and L == 32) else 256
+        assert info["block_threads"] == want, info
     explicit = _plan(D, R, neox, cfg=B.LaunchCfg(groups_per_item=3, block_waves=5, unroll=2))
     assert (explicit["unroll"], explicit["groups_per_item"], explicit["block_threads"]) == (2, 3, 320)
     four = _plan(D, R, neox, cfg=B.LaunchCfg(unroll=4))
@@ -684,7 +688,7 @@ def test_benchmark_workloads_plan_the_measured_launch(name):
     """Every benchmark and shard workload, with the strides the benchmark uses
     (contiguous or views into a fused qkv buffer), plans onto the vectorised
     kernel with 16-byte lanes, 2 head groups per item loaded together, and 3
-    waves per workgroup (4 for the half-wave heads of head_dim 256)."""
+    waves per workgroup (6 for the half-wave heads of head_dim 256)."""
     from head_qk_rmsnorm_amd import workloads as W
 
     c = W.CONFIGS[name]
@@ -703,7 +707,7 @@ def test_benchmark_workloads_plan_the_measured_launch(name):
     i = info.as_dict()
     assert i["generic"] == 0 and i["lanes_per_head"] == D // 8 and i["elems_per_lane"] == 8, i
     assert i["groups_per_item"] == min(2, i["groups_per_token"]) and i["unroll"] == 2, i
-    assert i["block_threads"] == (256 if D // 8 > 16 else 192), i
+    assert i["block_threads"] == (384 if D // 8 > 16 else 192), i
 
 
 def test_head_dim_scan_shapes_are_vectorised():
