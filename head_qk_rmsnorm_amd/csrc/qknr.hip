@@ -283,7 +283,13 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
     const int g_pad = kWave / (dmax / E), g_fit = kWave / lanes;
     const bool more = mode == kFused ? 4 * g_fit >= 5 * g_pad
                                      : mode == kLayerRope && 2 * g_fit >= 3 * g_pad;
-    seg = (sh == 2 || sh == 6) && lanes <= 32 && more;
+    // Partners 4 slots over (one ds_bpermute per element) gain from exact-fit
+    // groups only in groups of 5 to 8 lanes (head_dim 40: +7.3% at rope_dim 40,
+    // +8.8% at 24); head_dim 24 (3 lanes) lost 8.2% and groups of 9 or more
+    // lanes 5-9% (the tree reduction and its broadcast cost more than the
+    // busier lanes save)
+    seg = ((sh == 2 || sh == 6) || (sh == 4 && mode == kFused && lanes >= 5 && lanes <= 8)) &&
+          lanes <= 32 && more;
     const int G = kWave / (seg ? lanes : dmax / E);
     if (c.lanes_per_head != 0 && c.lanes_per_head != (seg ? lanes : dmax / E)) return QKNR_E_ARG;
     if (!lane_offsets_fit(G, Hq, q_head, D) || !lane_offsets_fit(G, Hkv, k_head, D))
@@ -431,10 +437,12 @@ int32_t make_elem_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, 
   pl->U = U;
   pl->wpb = c.block_waves == 0 ? kDefaultBlockWaves : c.block_waves;
   pl->max_blocks = c.max_blocks;
-  // partners through LDS (NeoX, or interleaved with single-element runs): a
-  // row of 64 lanes x E floats per wave
-  pl->lds = (rotates(mode) && (neox || sh.pw == 1))
-                ? static_cast<size_t>(pl->wpb) * kWave * pl->E * sizeof(float) : 0;
+  // per wave: a row of 64 lanes x E floats (partners through LDS: NeoX, or
+  // interleaved with single-element runs) and, with a rotation, room for one
+  // cos|sin row (the kernel's layout; the exchange row is reserved in every
+  // rotating instance)
+  pl->lds = static_cast<size_t>(pl->wpb) * (kWave * pl->E + (rotates(mode) ? kElemMaxDim : 0)) *
+            sizeof(float);
   pl->fn = pick_elem_kernel(dtype, mode, sh.S, sh.pw);
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
 }
@@ -618,6 +626,7 @@ int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
     ep.neox = c.neox ? 1 : 0;
     ep.pos64 = c.pdt == QKNR_I64;
     ep.has_bias = (c.bq || c.bk) ? 1 : 0;
+    ep.cs2 = (reinterpret_cast<uintptr_t>(c.cache) % 8) == 0 ? 1 : 0;
     ep.L = pl.L;
     ep.G = pl.G;
     ep.seg = pl.seg ? 1 : 0;

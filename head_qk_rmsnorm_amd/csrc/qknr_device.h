@@ -666,6 +666,7 @@ struct ElemParams {
   int32_t D, R;
   float inv_d, eps;
   int32_t neox, pos64, has_bias;
+  int32_t cs2;                   // cos|sin table 8-byte aligned (rows copied as float2)
   int32_t L, G, seg;             // lanes per head, heads per wave instruction, L not a power of two
   int32_t gpi, nc, n_items;      // groups per item, items per token, items
 };
@@ -712,19 +713,19 @@ __device__ __forceinline__ Run<PW> pack_run(const float* v) {
   return r;
 }
 
-template <int PW>
+template <int PW, int POLICY>
 __device__ __forceinline__ Run<PW> load_run(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   Run<PW> r;
   if constexpr (PW == 8) {
-    const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kLoadPolicy));
+    const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, POLICY));
     r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
   } else if constexpr (PW == 4) {
-    const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kLoadPolicy));
+    const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, POLICY));
     r.w[0] = v.x; r.w[1] = v.y;
   } else if constexpr (PW == 2) {
-    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kLoadPolicy);
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, POLICY);
   } else {
-    r.w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, kLoadPolicy);
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, POLICY);
   }
   return r;
 }
@@ -791,7 +792,14 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
   constexpr bool kRotate = MODE == kFused || MODE == kRopeOnly || MODE == kLayerRope;
   constexpr bool kRms = MODE == kFused || MODE == kNormOnly;
   constexpr bool kLayer = MODE == kLayerRope || MODE == kLayerOnly;
-  extern __shared__ float elem_rows[];  // partner exchange: kWave * NE floats per wave
+  // Runs narrower than 16 bytes leave several wave instructions (slots, or
+  // neighbouring head groups) touching one cache line; those loads keep the
+  // default policy so the line stays in the caches between them (nontemporal
+  // loads there measured 6-19% slower), 16-byte runs stream nontemporally
+  constexpr int kElemLoadPolicy = PW == 8 ? kLoadPolicy : 0;
+  // per wave: the partner-exchange row (kWave * NE floats) and, with a
+  // rotation, the token's cos|sin row (kElemMaxDim floats)
+  extern __shared__ float elem_rows[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
@@ -804,7 +812,9 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
   const bool neox = p.neox != 0;  // wave-uniform
   // partners through LDS: NeoX pairing, or interleaved pairs split over lanes
   const bool exch = kRotate && (neox || PW == 1);
-  float* const xrow = elem_rows + wib * (kWave * NE);
+  constexpr int kRowFloats = kWave * NE + (kRotate ? kElemMaxDim : 0);
+  float* const xrow = elem_rows + wib * kRowFloats;
+  float* const csrow = xrow + kWave * NE;
   const int head0 = sub * (L * NE);  // this head's first element in the row
   const uint32_t q_off = static_cast<uint32_t>(sub) * p.q_head + 2 * li * PW;
   const uint32_t k_off = static_cast<uint32_t>(sub) * p.k_head + 2 * li * PW;
@@ -898,7 +908,7 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
 #pragma unroll
         for (int s = 0; s < S; ++s) {
           if (ok[u] && run_ok[s]) {
-            raw[u][s] = load_run<PW>(rs[u], off[u] + 2 * s * span);
+            raw[u][s] = load_run<PW, kElemLoadPolicy>(rs[u], off[u] + 2 * s * span);
           } else {
 #pragma unroll
             for (int w = 0; w < Run<PW>::NW; ++w) raw[u][s].w[w] = 0u;
@@ -922,12 +932,23 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
       sn[j] = 0.0f;
     }
     if constexpr (kRotate) {
+      // the wave copies the token's row into LDS with coalesced 8-byte loads
+      // (4-byte ones when the table is only 4-byte aligned), then each lane
+      // reads the columns of its own elements from there
       const float* const crow = cache + token_position(posp, p.pos64, t) * R;
+      wave_lds_fence();  // the previous item's reads of the row are done
+      if (p.cs2) {
+        for (int c = 2 * lane; c < R; c += 2 * kWave)
+          *reinterpret_cast<float2*>(csrow + c) = *reinterpret_cast<const float2*>(crow + c);
+      } else {
+        for (int c = lane; c < R; c += kWave) csrow[c] = crow[c];
+      }
+      wave_lds_fence();
 #pragma unroll
       for (int j = 0; j < NE; ++j) {
         if (rot[j]) {
-          cs[j] = crow[col[j]];
-          const float v = crow[half + col[j]];
+          cs[j] = csrow[col[j]];
+          const float v = csrow[half + col[j]];
           sn[j] = neg[j] ? -v : v;
         }
       }

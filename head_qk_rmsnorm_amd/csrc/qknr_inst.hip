@@ -199,13 +199,17 @@ const void* pick_group(int D, int E, bool neox, bool full, int U, int mode, int 
 }
 
 // Exact-fit lane groups (SEG) for NeoX partners 2 or 6 slots over (the fused
-// op and the LayerNorm sibling): lanes per
+// op and the LayerNorm sibling) and 4 slots over (the fused op): lanes per
 // head and heads per wave instruction are run-time values, so DMAX plays no
 // part (fixed at 256).
 template <class IO, int UU, bool FULL, int MODE>
 const void* pick_seg_shift(int shift) {
   switch (shift) {
     case 2: return reinterpret_cast<const void*>(&qknr_kernel<IO, 256, 8, true, FULL, UU, MODE, false, 2, true>);
+    case 4:  // the fused op only: partners 4 slots over in groups of at most 8 lanes
+      if constexpr (MODE == kFused)
+        return reinterpret_cast<const void*>(&qknr_kernel<IO, 256, 8, true, FULL, UU, MODE, false, 4, true>);
+      return nullptr;
     case 6: return reinterpret_cast<const void*>(&qknr_kernel<IO, 256, 8, true, FULL, UU, MODE, false, 6, true>);
     default: return nullptr;
   }

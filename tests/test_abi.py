@@ -326,6 +326,24 @@ def test_plan_lane_mapping(D):
             assert gqa["groups_per_token"] == -(-7 // gqa["heads_per_wave"]) + -(-3 // gqa["heads_per_wave"])
 
 
+def test_plan_exact_fit_groups_for_small_heads_with_partners_4_slots_over():
+    """NeoX partners 4 slots over keep padded lane groups except in groups of 5
+    to 8 lanes that fit at least 25% more heads (fused op): head_dim 40 takes 5
+    lanes (12 heads per instruction, padded: 8); head_dim 24 (3 lanes), 56 (7
+    lanes, 9 heads against 8) and 72 (9 lanes) stay padded; the LayerNorm
+    sibling stays padded."""
+    for D, R, lanes, G in ((40, 40, 5, 12), (40, 24, 5, 12), (24, 24, 4, 16), (24, 8, 4, 16),
+                           (56, 56, 8, 8), (72, 72, 16, 4), (136, 136, 32, 2)):
+        i = _plan(D, R, 1)
+        assert (i["generic"], i["lanes_per_head"], i["heads_per_wave"], i["elems_per_lane"]) == \
+            (0, lanes, G, 8), (D, R, i)
+    info = B.LaunchInfo()
+    z = P(0)
+    rc = B.lib().qknr_layernorm_rope_inplace_ex(z, z, z, z, z, z, z, z, 0, 24, 24, 40, 40, 1, 1e-6,
+                                                 0, 0, 0, 0, 0, 0, z, None, ctypes.byref(info))
+    assert rc == 0 and info.lanes_per_head == 8, info.lanes_per_head
+
+
 @pytest.mark.parametrize("D,lanes", [(16, 2), (24, 4), (40, 8), (80, 16), (112, 16),
                                      (160, 32), (192, 32), (320, 64), (512, 64)])
 def test_plan_run_time_head_dims(D, lanes):

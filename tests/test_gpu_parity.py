@@ -159,7 +159,8 @@ SHIFTED = [(96, 24), (72, 72), (40, 40), (88, 88), (136, 136), (264, 264), (200,
            (16, 8), (64, 24), (128, 40), (128, 8), (256, 104), (256, 24),
            (80, 20), (96, 12), (40, 12), (56, 20), (104, 52), (120, 60), (200, 100), (504, 12),
            (16, 4), (24, 12), (128, 20), (64, 12), (256, 44), (128, 4), (64, 60),
-           (72, 20), (152, 44), (88, 28), (96, 20), (168, 44)]
+           (72, 20), (152, 44), (88, 28), (96, 20), (168, 44),
+           (24, 24), (40, 24), (24, 8), (56, 56)]
 SHIFTED_LAUNCHES = [None, dict(unroll=4, groups_per_item=3), dict(unroll=2, groups_per_item=1, block_waves=1)]
 
 
