@@ -345,10 +345,11 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
             : mode == kFused && exact && pl->L == 32 && E == 8 ? kDefaultBlockWavesHalf
                                       : kDefaultBlockWaves;
   pl->max_blocks = c.max_blocks;
-  // partners 2 or 6 slots over are exchanged through a per-wave LDS row of
-  // 64 lanes x E floats
-  if (pl->shift == 2 || pl->shift == 6)
-    pl->lds = static_cast<size_t>(pl->wpb) * kWave * E * sizeof(float);
+  // shifted partners: per wave, a row of 64 lanes x E floats (the exchange of
+  // partners 2 or 6 slots over) followed by room for the token's cos|sin row
+  // (up to 512 floats)
+  if (pl->shift != 0)
+    pl->lds = static_cast<size_t>(pl->wpb) * (kWave * E + 512) * sizeof(float);
   pl->seg = seg;
   pl->fn = seg ? pick_seg_kernel(dtype, R == D, U, mode, pl->shift)
                : pick_kernel(dtype, dmax, E, neox != 0, R == D, U, mode, exact, pl->shift);

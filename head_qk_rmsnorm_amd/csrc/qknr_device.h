@@ -282,7 +282,19 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   static_assert(SHIFT == 0 || ((SHIFT == 2 || SHIFT == 4 || SHIFT == 6) && NEOX && E == 8),
                 "partner slot shift");
   constexpr bool kShift26 = SHIFT == 2 || SHIFT == 6;
-  extern __shared__ float shift_rows[];  // SHIFT 2/6: kWave * E floats per wave
+  constexpr bool kLayerMode = MODE == kLayerRope || MODE == kLayerOnly;
+  // Shifted partners read the token's cos|sin row from a copy in LDS instead
+  // of per-lane global loads (A/B: partners 2 or 6 slots over +5 to +16%,
+  // 4 slots over +7 to +13%), except where the copy measured slower: the
+  // LayerNorm sibling's exact-fit groups with partners 2 or 6 slots over
+  // (head_dim 80 / rope_dim 20: -4.4%) and partners 4 slots over in lane
+  // groups padded to 32 or 64 lanes (head_dim 136: -3.5%, LayerNorm -5.8%)
+  constexpr bool kStageCs = (SHIFT == 4 && (EXACT || DMAX < 256)) || (kShift26 && !(kLayerMode && SEG));
+  // shifted partners, per wave: the exchange row (kWave * E floats; SHIFT 2/6),
+  // then room for the token's cos|sin row (kCsRow floats)
+  extern __shared__ float shift_rows[];
+  constexpr int kCsRow = 512;
+  constexpr int kShiftRow = kWave * E + kCsRow;
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
@@ -393,7 +405,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
     }
   }
   const bool ro_26[2] = {in_head && d0 < 2 * half, in_head && d0 + 4 < 2 * half};
-  const bool cs_pairs = kShift26 && (reinterpret_cast<uintptr_t>(cache) & 7) == 0;
+  const bool cs_pairs = (reinterpret_cast<uintptr_t>(cache) & 7) == 0;
 
   auto head_sum = [&](float v) {
     if constexpr (SEG) {
@@ -462,14 +474,35 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
     float cs[NCS], sn[NCS];
     if constexpr (kRotate) {
       const float* row = cache + pos * R;
+      // the wave copies the row into LDS with coalesced loads (8-byte ones when
+      // the table is 8-byte aligned; R is even), then each lane reads its own
+      // columns from there
+      // (an LDS pointer of its own: kept apart from the global row pointer so
+      // that reads through it stay LDS instructions)
+      float* const csr = shift_rows + wib * kShiftRow + kWave * E;
+      if constexpr (kStageCs) {
+        wave_lds_fence();  // the previous item's reads of the row are done
+        if (cs_pairs) {
+          for (int c = 2 * lane; c < R; c += 2 * kWave)
+            *reinterpret_cast<float2*>(csr + c) = *reinterpret_cast<const float2*>(row + c);
+        } else {
+          for (int c = lane; c < R; c += kWave) csr[c] = row[c];
+        }
+        wave_lds_fence();
+      }
       if constexpr (kShift26) {
+        // aligned pairs of this lane's columns (a pair never straddles a half)
 #pragma unroll
         for (int q2 = 0; q2 < E / 2; ++q2) {
           const int d = d0 + 2 * q2;
           const bool lo = d < half;
           const int j = (in_head && d < 2 * half) ? (lo ? d : d - half) : 0;
           float c0, c1, s0, s1;
-          if (cs_pairs) {
+          if constexpr (kStageCs) {
+            const float2 c2 = *reinterpret_cast<const float2*>(csr + j);
+            const float2 s2 = *reinterpret_cast<const float2*>(csr + half + j);
+            c0 = c2.x; c1 = c2.y; s0 = s2.x; s1 = s2.y;
+          } else if (cs_pairs) {
             const float2 c2 = *reinterpret_cast<const float2*>(row + j);
             const float2 s2 = *reinterpret_cast<const float2*>(row + half + j);
             c0 = c2.x; c1 = c2.y; s0 = s2.x; s1 = s2.y;
@@ -482,7 +515,13 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
       } else if constexpr (SHIFT == 4) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-          if (p.cs_vec) {
+          if constexpr (kStageCs) {
+            // columns jc and half + jc are multiples of 4: aligned 16-byte reads
+            const float4 c4 = *reinterpret_cast<const float4*>(csr + jc_s[k]);
+            const float4 s4 = *reinterpret_cast<const float4*>(csr + half + jc_s[k]);
+            cs[4 * k] = c4.x; cs[4 * k + 1] = c4.y; cs[4 * k + 2] = c4.z; cs[4 * k + 3] = c4.w;
+            sn[4 * k] = s4.x; sn[4 * k + 1] = s4.y; sn[4 * k + 2] = s4.z; sn[4 * k + 3] = s4.w;
+          } else if (p.cs_vec) {
             const float4 c4 = *reinterpret_cast<const float4*>(row + jc_s[k]);
             const float4 s4 = *reinterpret_cast<const float4*>(row + half + jc_s[k]);
             cs[4 * k] = c4.x; cs[4 * k + 1] = c4.y; cs[4 * k + 2] = c4.z; cs[4 * k + 3] = c4.w;
@@ -577,7 +616,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
         } else if constexpr (kShift26) {
           // R = 16m + 2*SHIFT ends on slot 4 of a lane: each run of 4 slots is
           // rotated as a whole or passed through
-          float* const xrow = shift_rows + wib * (kWave * E);
+          float* const xrow = shift_rows + wib * kShiftRow;
           wave_lds_fence();  // the previous group's reads are done
           *reinterpret_cast<float4*>(xrow + lane * E) = make_float4(n[0], n[1], n[2], n[3]);
           *reinterpret_cast<float4*>(xrow + lane * E + 4) = make_float4(n[4], n[5], n[6], n[7]);
