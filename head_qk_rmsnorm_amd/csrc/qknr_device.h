@@ -769,16 +769,16 @@ __device__ __forceinline__ Run<PW> load_run(__amdgpu_buffer_rsrc_t rs, uint32_t 
   return r;
 }
 
-template <int PW>
+template <int PW, int POLICY>
 __device__ __forceinline__ void store_run(__amdgpu_buffer_rsrc_t rs, uint32_t off, const Run<PW>& r) {
   if constexpr (PW == 8) {
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{r.w[0], r.w[1], r.w[2], r.w[3]}, rs, off, 0, kStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{r.w[0], r.w[1], r.w[2], r.w[3]}, rs, off, 0, POLICY);
   } else if constexpr (PW == 4) {
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{r.w[0], r.w[1]}, rs, off, 0, kStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{r.w[0], r.w[1]}, rs, off, 0, POLICY);
   } else if constexpr (PW == 2) {
-    __builtin_amdgcn_raw_buffer_store_b32(r.w[0], rs, off, 0, kStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b32(r.w[0], rs, off, 0, POLICY);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(r.w[0]), rs, off, 0, kStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(r.w[0]), rs, off, 0, POLICY);
   }
 }
 
@@ -836,6 +836,11 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
   // default policy so the line stays in the caches between them (nontemporal
   // loads there measured 6-19% slower), 16-byte runs stream nontemporally
   constexpr int kElemLoadPolicy = PW == 8 ? kLoadPolicy : 0;
+  // Likewise stores of 2 or 4 bytes are left to merge in the L2 (default
+  // policy) rather than written through one by one: written through, the
+  // 4-byte stores of head_dim 130 wrote 1.43x the stored bytes (default policy
+  // there: +29%); 8-byte stores keep the streaming policy (default: -5%)
+  constexpr int kElemStorePolicy = PW <= 2 ? 0 : kStorePolicy;
   // per wave: the partner-exchange row (kWave * NE floats) and, with a
   // rotation, the token's cos|sin row (kElemMaxDim floats)
   extern __shared__ float elem_rows[];
@@ -1084,7 +1089,7 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
         if (ok[u]) {
 #pragma unroll
           for (int s = 0; s < S; ++s) {
-            if (run_ok[s]) store_run<PW>(rs[u], off[u] + 2 * s * span, pack_run<IO, PW>(&o[s * PW]));
+            if (run_ok[s]) store_run<PW, kElemStorePolicy>(rs[u], off[u] + 2 * s * span, pack_run<IO, PW>(&o[s * PW]));
           }
         }
       }
