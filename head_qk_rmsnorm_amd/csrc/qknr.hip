@@ -320,6 +320,11 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   if (mode == kFused && exact) U = c.unroll == 0 ? kDefaultUnroll : c.unroll;
   if ((mode == kFused || layer) && !exact && (c.unroll == 4 || (c.unroll == 0 && long_items)))
     U = kLongItemUnroll;
+  // exact-fit groups of 5 lanes with NeoX partners 4 slots over (head_dim 40)
+  // keep unroll 2 within their long items: 12 heads per wave instruction, 4
+  // groups per item, +3.4 to +3.6% over unroll 4 at rope_dim 40, 24 and 8 (2
+  // groups per item instead: -5.4%; head_dim 48 in groups of 6 lanes: -1.5%)
+  if (seg && L == 5 && lane_shift(mode, R, neox, E) == 4 && c.unroll == 0) U = 2;
 
   pl->elem = false;
   pl->lds = 0;
@@ -350,6 +355,10 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   // (up to 512 floats)
   if (pl->shift != 0)
     pl->lds = static_cast<size_t>(pl->wpb) * (kWave * E + 512) * sizeof(float);
+  // the fused op's NeoX instances at head_dim 64/128 on 16-byte lanes: the
+  // token's cos|sin row per wave
+  if (pl->shift == 0 && mode == kFused && exact && E == 8 && neox && D <= 128)
+    pl->lds = static_cast<size_t>(pl->wpb) * D * sizeof(float);
   pl->seg = seg;
   pl->fn = seg ? pick_seg_kernel(dtype, R == D, U, mode, pl->shift)
                : pick_kernel(dtype, dmax, E, neox != 0, R == D, U, mode, exact, pl->shift);

@@ -289,12 +289,20 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   // LayerNorm sibling's exact-fit groups with partners 2 or 6 slots over
   // (head_dim 80 / rope_dim 20: -4.4%) and partners 4 slots over in lane
   // groups padded to 32 or 64 lanes (head_dim 136: -3.5%, LayerNorm -5.8%)
-  constexpr bool kStageCs = (SHIFT == 4 && (EXACT || DMAX < 256)) || (kShift26 && !(kLayerMode && SEG));
-  // shifted partners, per wave: the exchange row (kWave * E floats; SHIFT 2/6),
-  // then room for the token's cos|sin row (kCsRow floats)
+  // The fused op's NeoX instances at head_dim 64 and 128 (16-byte lanes) stage
+  // the row too (one coalesced copy per wave instead of 4 vector loads per
+  // lane; A/B: GQA +1.2%, Partial +0.7%, head_dim 64/128 NeoX +1.8/+1.9%);
+  // interleaved DiT was level and head_dim 256 lost (Large -9%, 256
+  // interleaved -7.6%), so they keep per-lane loads.
+  constexpr bool kStageCs0 = SHIFT == 0 && MODE == kFused && EXACT && E == 8 && NEOX && DMAX <= 128;
+  constexpr bool kStageCs = kStageCs0 || (SHIFT == 4 && (EXACT || DMAX < 256)) || (kShift26 && !(kLayerMode && SEG));
+  // per wave: with shifted partners the exchange row (kWave * E floats; SHIFT
+  // 2/6) and then room for the token's cos|sin row (kCsRow floats); without
+  // them (kStageCs0) the row alone (DMAX floats)
   extern __shared__ float shift_rows[];
-  constexpr int kCsRow = 512;
-  constexpr int kShiftRow = kWave * E + kCsRow;
+  constexpr int kCsRow = SHIFT != 0 ? 512 : DMAX;
+  constexpr int kXRow = SHIFT != 0 ? kWave * E : 0;
+  constexpr int kShiftRow = kXRow + kCsRow;
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
@@ -479,7 +487,7 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
       // columns from there
       // (an LDS pointer of its own: kept apart from the global row pointer so
       // that reads through it stay LDS instructions)
-      float* const csr = shift_rows + wib * kShiftRow + kWave * E;
+      float* const csr = shift_rows + wib * kShiftRow + kXRow;
       if constexpr (kStageCs) {
         wave_lds_fence();  // the previous item's reads of the row are done
         if (cs_pairs) {
@@ -535,6 +543,22 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) sn[4 * k + i] = lo_s[k] ? -sn[4 * k + i] : sn[4 * k + i];
+        }
+      } else if (kStageCs0 && NCS % 4 == 0 && p.cs_vec) {
+        const int jv = (FULL || NEOX || j0 < half) ? j0 : 0;
+#pragma unroll
+        for (int i = 0; i < NCS; i += 4) {
+          const float4 c4 = *reinterpret_cast<const float4*>(csr + jv + i);
+          const float4 s4 = *reinterpret_cast<const float4*>(csr + half + jv + i);
+          cs[i] = c4.x; cs[i + 1] = c4.y; cs[i + 2] = c4.z; cs[i + 3] = c4.w;
+          sn[i] = s4.x; sn[i + 1] = s4.y; sn[i + 2] = s4.z; sn[i + 3] = s4.w;
+        }
+      } else if (kStageCs0) {
+#pragma unroll
+        for (int i = 0; i < NCS; ++i) {
+          const int j = (FULL || NEOX) ? j0 + i : min(j0 + i, half - 1);
+          cs[i] = csr[j];
+          sn[i] = csr[half + j];
         }
       } else if (NCS % 4 == 0 && p.cs_vec) {
         // interleaved with a partial rotation: R/2 is a multiple of 4 here, so a

@@ -460,9 +460,16 @@ def test_plan_defaults():
     assert tiny["groups_per_token"] == 2 and tiny["groups_per_item"] == 2
 
 
+def _seg4_unroll2(D, R, neox):
+    """Exact-fit lane groups of 5 lanes with NeoX partners 4 slots over (head_dim
+    40 with rope_dim/2 = 8m + 4): the planner keeps them at unroll 2."""
+    return bool(neox) and D == 40 and (R // 2) % 8 == 4
+
+
 @pytest.mark.parametrize("D,R,neox,long_items", [
     (80, 80, 1, True), (96, 96, 1, True), (96, 24, 1, False), (80, 32, 1, True), (160, 160, 1, True),
     (192, 64, 1, True), (320, 320, 1, True), (48, 48, 1, True), (40, 40, 1, True),
+    (40, 24, 1, True), (48, 40, 1, True), (56, 56, 1, True),
     (24, 24, 1, True), (112, 112, 1, True), (224, 224, 1, True), (72, 72, 1, True),
     (136, 136, 1, True), (104, 52, 1, True),
     (40, 40, 0, True), (80, 80, 0, True), (144, 144, 0, True), (160, 160, 0, True),
@@ -472,16 +479,18 @@ def test_plan_defaults():
 def test_plan_defaults_long_items(D, R, neox, long_items):
     """Head_dims other than 64/128/256 default to long work items (unroll 4,
     4 groups per item, 2-wave workgroups) with NeoX pairing or when a head group
-    holds at most 640 bytes; every other shape keeps unroll 2, 2 groups per
-    item and 3 or 4 waves. Explicit settings are honoured; a run-time head_dim
-    runs unroll 1 as 2."""
+    holds at most 640 bytes, except that exact-fit groups of 5 lanes with
+    partners 4 slots over (head_dim 40) keep unroll 2 in them; every other shape keeps
+    unroll 2, 2 groups per item and 3 or 4 waves. Explicit settings are
+    honoured; a run-time head_dim runs unroll 1 as 2."""
     info = _plan(D, R, neox)
     assert info["generic"] == 0, info
     G, L = info["heads_per_wave"], info["lanes_per_head"]
     assert long_items == (D not in (64, 128, 256) and not _fit96(D, R, neox)
                           and (neox == 1 or G * 2 * D <= 640))
     if long_items:
-        assert (info["unroll"], info["groups_per_item"], info["block_threads"]) == (4, 4, 128), info
+        want_u = 2 if _seg4_unroll2(D, R, neox) else 4
+        assert (info["unroll"], info["groups_per_item"], info["block_threads"]) == (want_u, 4, 128), info
     else:
         assert (info["unroll"], info["groups_per_item"]) == (2, 2), info
         want = 192 if L <= 16 else 384 if (D == 256 and L == 32) else 256
