@@ -355,9 +355,9 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   // (up to 512 floats)
   if (pl->shift != 0)
     pl->lds = static_cast<size_t>(pl->wpb) * (kWave * E + 512) * sizeof(float);
-  // the fused op's NeoX instances at head_dim 64/128 on 16-byte lanes: the
-  // token's cos|sin row per wave
-  if (pl->shift == 0 && mode == kFused && exact && E == 8 && neox && D <= 128)
+  // NeoX instances at head_dim 64/128 on 16-byte lanes (the fused op and the
+  // LayerNorm sibling): the token's cos|sin row per wave
+  if (pl->shift == 0 && (mode == kFused || mode == kLayerRope) && exact && E == 8 && neox && D <= 128)
     pl->lds = static_cast<size_t>(pl->wpb) * D * sizeof(float);
   pl->seg = seg;
   pl->fn = seg ? pick_seg_kernel(dtype, R == D, U, mode, pl->shift)

@@ -289,12 +289,13 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   // LayerNorm sibling's exact-fit groups with partners 2 or 6 slots over
   // (head_dim 80 / rope_dim 20: -4.4%) and partners 4 slots over in lane
   // groups padded to 32 or 64 lanes (head_dim 136: -3.5%, LayerNorm -5.8%)
-  // The fused op's NeoX instances at head_dim 64 and 128 (16-byte lanes) stage
-  // the row too (one coalesced copy per wave instead of 4 vector loads per
-  // lane; A/B: GQA +1.2%, Partial +0.7%, head_dim 64/128 NeoX +1.8/+1.9%);
+  // NeoX instances at head_dim 64 and 128 (16-byte lanes) of the fused op and
+  // the LayerNorm sibling stage the row too (one coalesced copy per wave
+  // instead of 4 vector loads per lane; A/B: GQA +1.2%, Partial +0.7%,
+  // head_dim 64/128 NeoX +1.8/+1.9%; LayerNorm GQA +1.7%, Partial +3.2%);
   // interleaved DiT was level and head_dim 256 lost (Large -9%, 256
   // interleaved -7.6%), so they keep per-lane loads.
-  constexpr bool kStageCs0 = SHIFT == 0 && MODE == kFused && EXACT && E == 8 && NEOX && DMAX <= 128;
+  constexpr bool kStageCs0 = SHIFT == 0 && (MODE == kFused || MODE == kLayerRope) && EXACT && E == 8 && NEOX && DMAX <= 128;
   constexpr bool kStageCs = kStageCs0 || (SHIFT == 4 && (EXACT || DMAX < 256)) || (kShift26 && !(kLayerMode && SEG));
   // per wave: with shifted partners the exchange row (kWave * E floats; SHIFT
   // 2/6) and then room for the token's cos|sin row (kCsRow floats); without
