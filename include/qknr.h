@@ -149,8 +149,10 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
  *                    items": a head_dim other than 64/128/256 with NeoX
  *                    pairing, or whose head group holds at most 640 bytes]
  *   unroll           head groups loaded before the first is computed: 1, 2 or 4.
- *                    [2; 4 for long items] A head_dim other than 64/128/256
- *                    runs at 2 or 4 (1 runs as 2).
+ *                    [2; 4 for long items, except head_dim 40 in exact-fit
+ *                    groups of 5 lanes with NeoX partners 4 slots over, which
+ *                    keeps 2] A head_dim other than 64/128/256 runs at 2 or 4
+ *                    (1 runs as 2).
  *   block_waves      wavefronts per workgroup: 1..8. [3 when a head takes at
  *                    most 16 lanes; 6 at head_dim 256 with 16-byte lanes
  *                    (32 lanes per head; the LayerNorm sibling keeps 4); 2
