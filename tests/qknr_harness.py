@@ -68,7 +68,7 @@ class DeviceCase:
     """Inputs of one call placed on the device, with host copies of everything."""
 
     def __init__(self, wl: W.Workload, layout: Optional[str] = None, device: str = "cuda:0",
-                 fill_seed: int = 0):
+                 fill_seed: int = 0, cache_offset: int = 0):
         import torch
 
         self.wl = wl
@@ -114,6 +114,14 @@ class DeviceCase:
         self.wq = torch.from_numpy(wl.wq.view(np.int16)).to(self.device).view(tdt)
         self.wk = torch.from_numpy(wl.wk.view(np.int16)).to(self.device).view(tdt)
         self.cache = torch.from_numpy(wl.cache).to(self.device)
+        if cache_offset:
+            # the table as a view cache_offset floats into its allocation (so
+            # aligned to 4 or 8 bytes only), NaN in front of it
+            buf = torch.full((self.cache.numel() + cache_offset,), float("nan"),
+                             dtype=torch.float32, device=self.device)
+            view = buf[cache_offset:].view(self.cache.shape)
+            view.copy_(self.cache)
+            self.cache = view
         self.positions = torch.from_numpy(wl.positions).to(self.device)
 
     @staticmethod
@@ -235,12 +243,13 @@ def compare_bits(got: np.ndarray, ref: np.ndarray, dtype: str) -> Compare:
 
 def run_and_check(wl: W.Workload, layout: Optional[str] = None, launch: Optional[dict] = None,
                   tokens: Optional[np.ndarray] = None, min_exact: float = 0.99,
-                  stream=None) -> Tuple[Compare, Compare]:
+                  stream=None, cache_offset: int = 0) -> Tuple[Compare, Compare]:
     """One call on fresh device copies; asserts the oracle tolerance on every
     (sampled) Q/K element, untouched bytes everywhere else, unchanged read-only
     inputs, and that at least ``min_exact`` of the elements equal the oracle's
-    correctly rounded value bit for bit."""
-    dc = DeviceCase(wl, layout=layout)
+    correctly rounded value bit for bit. ``cache_offset`` places the cos|sin
+    table that many floats into its allocation (see DeviceCase)."""
+    dc = DeviceCase(wl, layout=layout, cache_offset=cache_offset)
     dc.run(launch=launch, stream=stream)
     after = dc.fetch()
     dc.check_untouched(after)
@@ -293,7 +302,7 @@ def unfused_check(wl, which, layout=None, tokens=None):
     return out
 
 
-def layernorm_check(wl, rope_dim, bias, layout=None, bias_seed=0, launch=None):
+def layernorm_check(wl, rope_dim, bias, layout=None, bias_seed=0, launch=None, cache_offset=0):
     """The LayerNorm sibling on fresh device copies against the oracle (every
     Q/K element; bytes outside untouched). With ``launch`` (a dict, {} for the
     automatic choice) the call goes through qknr_layernorm_rope_inplace_ex and
@@ -301,7 +310,7 @@ def layernorm_check(wl, rope_dim, bias, layout=None, bias_seed=0, launch=None):
     from head_qk_rmsnorm_amd import binding as B
 
     c = wl.cfg
-    dc = DeviceCase(wl, layout=layout)
+    dc = DeviceCase(wl, layout=layout, cache_offset=cache_offset)
     bq_bits = bk_bits = None
     bq = bk = None
     if bias:

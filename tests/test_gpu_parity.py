@@ -508,3 +508,29 @@ def test_layernorm_launch_report(D, R, neox, launch, want):
     for k, v in want.items():
         assert info[k] == v, info
     assert info["grid_blocks"] > 0 and info["items"] > 0, info
+
+
+@pytest.mark.parametrize("off", [1, 2], ids=["cache_4B", "cache_8B"])
+@pytest.mark.parametrize("D,R,neox", [(128, 128, True), (128, 64, True), (64, 64, True),
+                                      (128, 128, False), (128, 64, False), (256, 256, True),
+                                      (96, 24, True), (80, 20, True), (40, 40, True), (136, 136, True),
+                                      (72, 72, True), (128, 20, True), (100, 100, True),
+                                      (130, 130, False), (40, 38, True)])
+def test_cache_alignment(D, R, neox, off):
+    """A cos|sin table aligned to 4 or 8 bytes only (a view one or two floats
+    into its allocation, NaN in front of it) takes every cos/sin read path that
+    an aligned table skips: per-lane scalar loads, the LDS staging copy in
+    single floats or in pairs, the element kernel's scalar row copy."""
+    cfg = W.case(37, 5, 3, D, R, neox, dtype=W.BF16, pos_dtype=W.I64, seed=D + R + off)
+    _say("case cache offset", off, cfg.name)
+    Hn.run_and_check(W.make_workload(cfg), cache_offset=off)
+
+
+@pytest.mark.parametrize("off", [1, 2], ids=["cache_4B", "cache_8B"])
+@pytest.mark.parametrize("D,R", [(128, 128), (64, 32), (80, 20), (96, 24), (40, 40)])
+def test_cache_alignment_layernorm(D, R, off):
+    """The LayerNorm sibling (NeoX, weight and bias) on a cos|sin table aligned
+    to 4 or 8 bytes only."""
+    cfg = W.case(29, 4, 2, D, R, True, dtype=W.FP16, pos_dtype=W.I32, seed=3 * D + R + off)
+    _say("case layernorm cache offset", off, cfg.name)
+    Hn.layernorm_check(W.make_workload(cfg), R, True, cache_offset=off)
