@@ -68,7 +68,7 @@ class DeviceCase:
     """Inputs of one call placed on the device, with host copies of everything."""
 
     def __init__(self, wl: W.Workload, layout: Optional[str] = None, device: str = "cuda:0",
-                 fill_seed: int = 0, cache_offset: int = 0):
+                 fill_seed: int = 0, cache_offset: int = 0, w_offset: int = 0):
         import torch
 
         self.wl = wl
@@ -113,6 +113,15 @@ class DeviceCase:
         self.q, self.k = tensors
         self.wq = torch.from_numpy(wl.wq.view(np.int16)).to(self.device).view(tdt)
         self.wk = torch.from_numpy(wl.wk.view(np.int16)).to(self.device).view(tdt)
+        if w_offset:
+            # each weight row as a view w_offset elements into its allocation
+            # (aligned to 2 * w_offset bytes at most)
+            def shifted(w):
+                buf = torch.zeros(w.numel() + w_offset, dtype=tdt, device=self.device)
+                view = buf[w_offset:]
+                view.copy_(w)
+                return view
+            self.wq, self.wk = shifted(self.wq), shifted(self.wk)
         self.cache = torch.from_numpy(wl.cache).to(self.device)
         if cache_offset:
             # the table as a view cache_offset floats into its allocation (so
@@ -243,13 +252,14 @@ def compare_bits(got: np.ndarray, ref: np.ndarray, dtype: str) -> Compare:
 
 def run_and_check(wl: W.Workload, layout: Optional[str] = None, launch: Optional[dict] = None,
                   tokens: Optional[np.ndarray] = None, min_exact: float = 0.99,
-                  stream=None, cache_offset: int = 0) -> Tuple[Compare, Compare]:
+                  stream=None, cache_offset: int = 0, w_offset: int = 0) -> Tuple[Compare, Compare]:
     """One call on fresh device copies; asserts the oracle tolerance on every
     (sampled) Q/K element, untouched bytes everywhere else, unchanged read-only
     inputs, and that at least ``min_exact`` of the elements equal the oracle's
     correctly rounded value bit for bit. ``cache_offset`` places the cos|sin
-    table that many floats into its allocation (see DeviceCase)."""
-    dc = DeviceCase(wl, layout=layout, cache_offset=cache_offset)
+    table that many floats into its allocation, ``w_offset`` the weight rows
+    that many elements into theirs (see DeviceCase)."""
+    dc = DeviceCase(wl, layout=layout, cache_offset=cache_offset, w_offset=w_offset)
     dc.run(launch=launch, stream=stream)
     after = dc.fetch()
     dc.check_untouched(after)

@@ -534,3 +534,19 @@ def test_cache_alignment_layernorm(D, R, off):
     cfg = W.case(29, 4, 2, D, R, True, dtype=W.FP16, pos_dtype=W.I32, seed=3 * D + R + off)
     _say("case layernorm cache offset", off, cfg.name)
     Hn.layernorm_check(W.make_workload(cfg), R, True, cache_offset=off)
+
+
+@pytest.mark.parametrize("w_off", [1, 2, 4], ids=["w_2B", "w_4B", "w_8B"])
+@pytest.mark.parametrize("D,R,neox", [(128, 128, True), (128, 64, False), (64, 64, True),
+                                      (96, 24, True), (80, 20, True), (256, 256, False)])
+def test_weight_alignment(D, R, neox, w_off):
+    """Weight rows aligned to 2, 4 or 8 bytes only: the vectorised kernel needs
+    16, so every such call runs element-granular with accesses as wide as the
+    weights allow, and matches the oracle."""
+    cfg = W.case(33, 6, 2, D, R, neox, dtype=W.FP16, pos_dtype=W.I64, seed=7 * D + R + w_off)
+    wl = W.make_workload(cfg)
+    _say("case weight offset", w_off, cfg.name)
+    dc = Hn.DeviceCase(wl, w_offset=w_off)
+    info = dc.run(launch={})
+    assert info["generic"] == 1 and info["access_bytes"] <= 2 * w_off, info
+    Hn.run_and_check(wl, w_offset=w_off)
