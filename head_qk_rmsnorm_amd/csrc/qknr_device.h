@@ -249,6 +249,8 @@ struct Params {
   float eps;
   int32_t ng, gpi, nc, n_items;  // groups per token, groups per item, items per token, items
   int32_t seg_l, seg_g;          // exact-fit lane groups: lanes per head, heads per wave instruction
+  int32_t tail_item0, tail_t0;   // fused op: items from tail_item0 on hold one head group each, for
+                                 // tokens tail_t0.. (tail_item0 = n_items: no such items)
 };
 
 // What a launch computes: the fused op, one of the two steps of the unfused
@@ -431,9 +433,19 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   if constexpr (kLayer && kRotate) pos_next = token_position(posp, p.pos64, item / p.nc);
 
   for (; item < p.n_items; item += total_waves) {
-    const int t = item / p.nc;
-    const int g_begin = (item - t * p.nc) * p.gpi;
-    const int g_end = min(g_begin + p.gpi, p.ng);
+    int t, g_begin, g_end;
+    if (MODE == kFused && item >= p.tail_item0) {
+      // the last items: one head group each, so the final waves are short
+      const int it = item - p.tail_item0;
+      const int tt = it / p.ng;
+      t = p.tail_t0 + tt;
+      g_begin = it - tt * p.ng;
+      g_end = g_begin + 1;
+    } else {
+      t = item / p.nc;
+      g_begin = (item - t * p.nc) * p.gpi;
+      g_end = min(g_begin + p.gpi, p.ng);
+    }
     int64_t pos = 0;
     if constexpr (kLayer && kRotate) {
       pos = pos_next;

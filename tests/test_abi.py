@@ -788,3 +788,36 @@ def test_launch_info_layout():
     assert ctypes.sizeof(B.LaunchInfo) == 48
     assert B.LaunchInfo.items.offset == 32 and B.LaunchInfo.generic.offset == 40
     assert B.LaunchInfo.access_bytes.offset == 44
+
+
+def _tail_items(T, Hq, Hkv, D, R, neox, cfg=None):
+    rc, info = _call_info(T=T, Hq=Hq, Hkv=Hkv, D=D, R=R, neox=neox, qt=Hq * D * 2, qh=D * 2,
+                          kt=Hkv * D * 2, kh=D * 2, cfg=cfg)
+    assert rc == B.QKNR_E_DEVICE, B.qknr_status_string(rc)
+    return info
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: run on a host without a GPU")
+@pytest.mark.parametrize("T,Hq,Hkv,D,R,neox,tail", [
+    (4608, 24, 24, 128, 128, 0, 171),    # DiT: 12 groups per token, 6 items of 2
+    (8192, 32, 8, 128, 128, 1, 205),     # GQA: 10 groups, 5 items
+    (16384, 16, 16, 128, 64, 1, 256),    # partial rotation: 8 groups, 4 items
+    (8192, 24, 24, 256, 256, 0, 86),     # head_dim 256: 24 groups, 12 items
+    (1368, 24, 24, 128, 128, 1, 171),    # just long enough: T = 8 x the tail
+    (1367, 24, 24, 128, 128, 1, 0),      # one token short: no tail
+    (8192, 4, 1, 128, 128, 1, 0),        # a token is one item: no tail
+    (4608, 24, 24, 96, 96, 1, 0),        # run-time head_dim (long items): no tail
+])
+def test_plan_tail_items(T, Hq, Hkv, D, R, neox, tail):
+    """The fused op at head_dim 64/128/256 ends on ceil(2048 / groups per
+    token) tokens whose items hold one head group each, when a token has at
+    least 3 items and the launch is at least 8 times that long; an explicit
+    groups_per_item turns it off."""
+    info = _tail_items(T, Hq, Hkv, D, R, neox)
+    ng, gpi = info["groups_per_token"], info["groups_per_item"]
+    nc = -(-ng // gpi)
+    if tail:
+        assert tail == -(-2048 // ng) and nc >= 3 and T >= 8 * tail
+    assert info["items"] == (T - tail) * nc + tail * ng, info
+    plain = _tail_items(T, Hq, Hkv, D, R, neox, cfg=B.LaunchCfg(groups_per_item=gpi))
+    assert plain["items"] == T * nc, plain
