@@ -345,14 +345,16 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   pl->gpi = std::max(1, std::min(want_gpi, pl->ng));
   pl->nc = (pl->ng + pl->gpi - 1) / pl->gpi;
   pl->items = T * pl->nc;
-  // The fused op at head_dim 64/128/256 with its default items (several per
-  // token) ends on about kTailItems items of one head group each: the last
-  // waves of the launch are half as long, so the machine drains sooner
-  // (DiT +0.8%, GQA +0.4%, Partial and Large level; not where a token is one
-  // item: the 4+1-head GQA shard lost 5%)
+  // The fused op at head_dim 64/128/256 on 16-byte lanes with its default
+  // items (several per token) ends on about kTailItems items of one head group
+  // each: the last waves of the launch are half as long, so the machine drains
+  // sooner (DiT +0.6%, GQA +0.6%, Partial +0.3%, Large level; not where a
+  // token is one item: the 4+1-head GQA shard lost 5%; not on the 12-byte
+  // lanes of head_dim 96: -2.3% at rope_dim 24)
   pl->tail_item0 = -1;
   pl->tail_t0 = 0;
-  if (mode == kFused && exact && !seg && c.groups_per_item == 0 && pl->gpi > 1 && pl->nc >= 3) {
+  if (mode == kFused && fast_head_dim(D) && E == 8 && !seg && c.groups_per_item == 0 &&
+      pl->gpi > 1 && pl->nc >= 3) {
     const int64_t tail = (kTailItems + pl->ng - 1) / pl->ng;  // tokens
     if (T >= 8 * tail) {
       pl->tail_t0 = T - tail;

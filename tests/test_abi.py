@@ -807,10 +807,11 @@ def _tail_items(T, Hq, Hkv, D, R, neox, cfg=None):
     (1367, 24, 24, 128, 128, 1, 0),      # one token short: no tail
     (8192, 4, 1, 128, 128, 1, 0),        # a token is one item: no tail
     (4608, 24, 24, 96, 96, 1, 0),        # run-time head_dim (long items): no tail
+    (6144, 24, 24, 96, 24, 1, 0),        # head_dim 96 on 12-byte lanes: no tail
 ])
 def test_plan_tail_items(T, Hq, Hkv, D, R, neox, tail):
-    """The fused op at head_dim 64/128/256 ends on ceil(2048 / groups per
-    token) tokens whose items hold one head group each, when a token has at
+    """The fused op at head_dim 64/128/256 on 16-byte lanes ends on ceil(2048 /
+    groups per token) tokens whose items hold one head group each, when a token has at
     least 3 items and the launch is at least 8 times that long; an explicit
     groups_per_item turns it off."""
     info = _tail_items(T, Hq, Hkv, D, R, neox)
