@@ -205,7 +205,7 @@ constexpr int kDefaultBlockWavesHalf = 6;    // head_dim 256 on 16-byte lanes
 // same shapes. Interleaved groups of 768-896 bytes lose 1.4-3.4% with it, and
 // the compile-time head_dims 3.5-7.4% (4 groups per item at unroll 2), so they
 // keep the usual defaults.
-constexpr int kTailItems = 2048;  // one-group items at the end of a fused-op launch
+constexpr int kTailItems = 2048;  // shorter items at the end of a fused-op launch
 constexpr int kLongItemGroupBytes = 640;
 constexpr int kLongItemUnroll = 4;
 constexpr int kLongItemGroups = 4;
@@ -229,8 +229,9 @@ struct Plan {
   int pw = 1;          // element-granular kernel: elements per lane slot (2-byte accesses x pw)
   bool seg = false;    // exact-fit lane groups of a run-time head_dim (L lanes, G heads)
   int shift = 0;       // NeoX partner slot shift (0, 2, 4 or 6)
-  int64_t tail_item0 = -1;  // vectorised fused op: first item of one head group (-1: none)
+  int64_t tail_item0 = -1;  // vectorised fused op: first item of the shorter last ones (-1: none)
   int64_t tail_t0 = 0;      // ... and its token
+  int tail_nc = 1;          // such items per token (each holds gpi/2 groups)
   size_t lds = 0;      // dynamic LDS bytes per workgroup
 };
 
@@ -345,21 +346,26 @@ int32_t make_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, int32
   pl->gpi = std::max(1, std::min(want_gpi, pl->ng));
   pl->nc = (pl->ng + pl->gpi - 1) / pl->gpi;
   pl->items = T * pl->nc;
-  // The fused op at head_dim 64/128/256 on 16-byte lanes with its default
-  // items (several per token) ends on about kTailItems items of one head group
-  // each: the last waves of the launch are half as long, so the machine drains
-  // sooner (DiT +0.6%, GQA +0.6%, Partial +0.3%, Large level; not where a
-  // token is one item: the 4+1-head GQA shard lost 5%; not on the 12-byte
-  // lanes of head_dim 96: -2.3% at rope_dim 24)
+  // The fused op on 16-byte lanes with its default items (several per token)
+  // ends on about kTailItems items of half as many head groups: the last
+  // waves of the launch are half as long, so the machine drains sooner
+  // (one-group items after two-group ones: DiT +0.6%, GQA +0.6%, Partial
+  // +0.3%, Large level; two-group items after the run-time head_dims' four:
+  // +0.6 to +1.9% at head_dim 80 to 192). Not where a token is one or two
+  // items (the 4+1-head GQA shard lost 5%), not with shifted NeoX partners
+  // (head_dim 72: -1.2%), not in exact-fit groups and not on the 12-byte lanes
+  // of head_dim 96.
   pl->tail_item0 = -1;
   pl->tail_t0 = 0;
-  if (mode == kFused && fast_head_dim(D) && E == 8 && !seg && c.groups_per_item == 0 &&
-      pl->gpi > 1 && pl->nc >= 3) {
-    const int64_t tail = (kTailItems + pl->ng - 1) / pl->ng;  // tokens
+  if (mode == kFused && E == 8 && !seg && pl->shift == 0 && c.groups_per_item == 0 &&
+      (pl->gpi == 2 || pl->gpi == 4) && pl->nc >= 3) {
+    const int tail_gpi = pl->gpi / 2;
+    pl->tail_nc = (pl->ng + tail_gpi - 1) / tail_gpi;
+    const int64_t tail = (kTailItems + pl->tail_nc - 1) / pl->tail_nc;  // tokens
     if (T >= 8 * tail) {
       pl->tail_t0 = T - tail;
       pl->tail_item0 = pl->tail_t0 * pl->nc;
-      pl->items = pl->tail_item0 + tail * pl->ng;
+      pl->items = pl->tail_item0 + tail * pl->tail_nc;
     }
   }
   if (pl->items > kMaxItems) return QKNR_E_SHAPE;
@@ -690,10 +696,13 @@ int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
   prm.gpi = pl.gpi;
   prm.nc = pl.nc;
   prm.n_items = static_cast<int32_t>(pl.items);
-  prm.seg_l = pl.L;
-  prm.seg_g = pl.G;
-  prm.tail_item0 = static_cast<int32_t>(pl.tail_item0 < 0 ? pl.items : pl.tail_item0);
-  prm.tail_t0 = static_cast<int32_t>(pl.tail_t0);
+  if (pl.seg) {
+    prm.aux0 = pl.L;
+    prm.aux1 = pl.G;
+  } else {
+    prm.aux0 = static_cast<int32_t>(pl.tail_item0 < 0 ? pl.items : pl.tail_item0);
+    prm.aux1 = static_cast<int32_t>(pl.tail_t0);
+  }
   void* args[] = {&qarg, &karg, &wqarg, &wkarg, &carg, &parg, &bqarg, &bkarg, &prm};
   if (hipLaunchKernel(pl.fn, dim3(grid), dim3(threads), args, pl.lds, c.stream) != hipSuccess)
     return QKNR_E_LAUNCH;

@@ -248,9 +248,13 @@ struct Params {
   int32_t has_bias;              // LayerNorm sibling: bias rows given
   float eps;
   int32_t ng, gpi, nc, n_items;  // groups per token, groups per item, items per token, items
-  int32_t seg_l, seg_g;          // exact-fit lane groups: lanes per head, heads per wave instruction
-  int32_t tail_item0, tail_t0;   // fused op: items from tail_item0 on hold one head group each, for
-                                 // tokens tail_t0.. (tail_item0 = n_items: no such items)
+  // Exact-fit lane groups (SEG instances): lanes per head, heads per wave
+  // instruction. Instances that can end on shorter items (kTail): the first
+  // such item (n_items: none) and its token; those items hold half the groups
+  // of the others. (One pair of fields for both keeps the argument block at
+  // its size: 16 more bytes cost the exact-fit instances 1-1.4%, though their
+  // code was unchanged.)
+  int32_t aux0, aux1;
 };
 
 // What a launch computes: the fused op, one of the two steps of the unfused
@@ -309,10 +313,10 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
-  // SEG: exact-fit lane groups of head_dim/E lanes (p.seg_l, any count up to
-  // 32), p.seg_g heads per wave instruction, the lanes past them idle
-  const int L = SEG ? p.seg_l : LC;
-  const int G = SEG ? p.seg_g : GC;
+  // SEG: exact-fit lane groups of head_dim/E lanes (p.aux0, any count up to
+  // 32), p.aux1 heads per wave instruction, the lanes past them idle
+  const int L = SEG ? p.aux0 : LC;
+  const int G = SEG ? p.aux1 : GC;
   const int sub = SEG ? lane / L : lane / LC;  // head slot in the group
   const int li = lane - sub * L;               // lane inside the head
   const int d0 = li * E;     // first dim owned by this lane
@@ -325,6 +329,10 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 
   constexpr bool kRotate = MODE == kFused || MODE == kRopeOnly || MODE == kLayerRope;
   constexpr bool kRms = MODE == kFused || MODE == kNormOnly;
+  // launches of the fused op on 16-byte lanes with aligned partners may end
+  // on items of half as many groups, from item p.aux0 (token p.aux1) on; the
+  // other instances have none
+  constexpr bool kTail = MODE == kFused && E == 8 && !SEG && SHIFT == 0;
   constexpr bool kLayer = MODE == kLayerRope || MODE == kLayerOnly;
 
   // Weights (and LayerNorm biases) of this lane's dims, kept packed; loaded
@@ -434,13 +442,16 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 
   for (; item < p.n_items; item += total_waves) {
     int t, g_begin, g_end;
-    if (MODE == kFused && item >= p.tail_item0) {
-      // the last items: one head group each, so the final waves are short
-      const int it = item - p.tail_item0;
-      const int tt = it / p.ng;
-      t = p.tail_t0 + tt;
-      g_begin = it - tt * p.ng;
-      g_end = g_begin + 1;
+    if (kTail && item >= p.aux0) {
+      // the last items: half the groups each (the host ends launches on them
+      // only with 2 or 4 groups per item), so the final waves are short
+      const int half_gpi = p.gpi == 4 ? 2 : 1;
+      const int tail_nc = p.gpi == 4 ? (p.ng + 1) >> 1 : p.ng;
+      const int it = item - p.aux0;
+      const int tt = it / tail_nc;
+      t = p.aux1 + tt;
+      g_begin = (it - tt * tail_nc) * half_gpi;
+      g_end = min(g_begin + half_gpi, p.ng);
     } else {
       t = item / p.nc;
       g_begin = (item - t * p.nc) * p.gpi;

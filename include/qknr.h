@@ -148,12 +148,12 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
  *                    a work item never spans two tokens. [2; 4 for "long
  *                    items": a head_dim other than 64/128/256 with NeoX
  *                    pairing, or whose head group holds at most 640 bytes.
- *                    Left automatic, the fused op at head_dim 64/128/256 on
- *                    16-byte lanes with at least 3 items per token ends on
- *                    ceil(2048 / groups
- *                    per token) tokens whose items hold one group each, if
- *                    the launch has at least 8 times that many tokens;
- *                    qknr_launch_info.items counts them]
+ *                    Left automatic, the fused op on 16-byte lanes (not in
+ *                    exact-fit groups) with at least 3 items per token ends
+ *                    on ceil(2048 / n) tokens whose items hold half as many
+ *                    groups (n such items per token), if the launch has at
+ *                    least 8 times that many tokens; qknr_launch_info.items
+ *                    counts them]
  *   unroll           head groups loaded before the first is computed: 1, 2 or 4.
  *                    [2; 4 for long items, except head_dim 40 in exact-fit
  *                    groups of 5 lanes with NeoX partners 4 slots over, which

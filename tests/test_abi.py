@@ -798,27 +798,38 @@ def _tail_items(T, Hq, Hkv, D, R, neox, cfg=None):
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="fake device pointers: run on a host without a GPU")
-@pytest.mark.parametrize("T,Hq,Hkv,D,R,neox,tail", [
-    (4608, 24, 24, 128, 128, 0, 171),    # DiT: 12 groups per token, 6 items of 2
-    (8192, 32, 8, 128, 128, 1, 205),     # GQA: 10 groups, 5 items
-    (16384, 16, 16, 128, 64, 1, 256),    # partial rotation: 8 groups, 4 items
-    (8192, 24, 24, 256, 256, 0, 86),     # head_dim 256: 24 groups, 12 items
-    (1368, 24, 24, 128, 128, 1, 171),    # just long enough: T = 8 x the tail
-    (1367, 24, 24, 128, 128, 1, 0),      # one token short: no tail
-    (8192, 4, 1, 128, 128, 1, 0),        # a token is one item: no tail
-    (4608, 24, 24, 96, 96, 1, 0),        # run-time head_dim (long items): no tail
-    (6144, 24, 24, 96, 24, 1, 0),        # head_dim 96 on 12-byte lanes: no tail
+@pytest.mark.parametrize("T,Hq,Hkv,D,R,neox,on", [
+    (4608, 24, 24, 128, 128, 0, True),    # DiT: 12 groups per token, 6 items of 2
+    (8192, 32, 8, 128, 128, 1, True),     # GQA: 10 groups, 5 items
+    (16384, 16, 16, 128, 64, 1, True),    # partial rotation: 8 groups, 4 items
+    (8192, 24, 24, 256, 256, 0, True),    # head_dim 256: 24 groups, 12 items
+    (1368, 24, 24, 128, 128, 1, True),    # just long enough: T = 8 x the 171 tail tokens
+    (1367, 24, 24, 128, 128, 1, False),   # one token short: no tail
+    (8192, 4, 1, 128, 128, 1, False),     # a token is one item: no tail
+    (4608, 24, 24, 96, 96, 1, True),      # run-time head_dim: 3 items of 4, tail items of 2
+    (4608, 24, 24, 80, 80, 0, True),      # run-time head_dim, interleaved long items
+    (6144, 24, 24, 96, 24, 1, False),     # head_dim 96 on 12-byte lanes
+    (14745, 24, 24, 40, 40, 1, False),    # exact-fit lane groups
+    (7372, 24, 24, 80, 20, 1, False),     # exact-fit lane groups
+    (4608, 24, 24, 128, 20, 1, False),    # NeoX partners 2 slots over
+    (6144, 24, 24, 72, 72, 1, False),     # NeoX partners 4 slots over
 ])
-def test_plan_tail_items(T, Hq, Hkv, D, R, neox, tail):
-    """The fused op at head_dim 64/128/256 on 16-byte lanes ends on ceil(2048 /
-    groups per token) tokens whose items hold one head group each, when a token has at
-    least 3 items and the launch is at least 8 times that long; an explicit
-    groups_per_item turns it off."""
+def test_plan_tail_items(T, Hq, Hkv, D, R, neox, on):
+    """The fused op on 16-byte lanes, with aligned partners outside exact-fit
+    groups, with at least 3 items per token ends on ceil(2048 / tail items per token) tokens whose
+    items hold half the groups of the others, when the launch is at least 8
+    times that long; an explicit groups_per_item turns it off."""
     info = _tail_items(T, Hq, Hkv, D, R, neox)
     ng, gpi = info["groups_per_token"], info["groups_per_item"]
     nc = -(-ng // gpi)
-    if tail:
-        assert tail == -(-2048 // ng) and nc >= 3 and T >= 8 * tail
-    assert info["items"] == (T - tail) * nc + tail * ng, info
+    tail = 0
+    if on:
+        tgpi = gpi // 2
+        tnc = -(-ng // tgpi)
+        tail = -(-2048 // tnc)
+        assert nc >= 3 and T >= 8 * tail and info["elems_per_lane"] == 8
+        assert info["items"] == (T - tail) * nc + tail * tnc, info
+    else:
+        assert info["items"] == T * nc, info
     plain = _tail_items(T, Hq, Hkv, D, R, neox, cfg=B.LaunchCfg(groups_per_item=gpi))
     assert plain["items"] == T * nc, plain

@@ -559,16 +559,20 @@ def test_weight_alignment(D, R, neox, w_off):
                                                (2100, 16, 16, 128, 64, True),
                                                (700, 24, 24, 256, 256, False),
                                                (2800, 24, 24, 64, 64, True),
-                                               (1400, 24, 24, 128, 20, True)])
+                                               (2800, 24, 24, 96, 96, True),
+                                               (2800, 24, 24, 80, 80, False),
+                                               (1400, 24, 24, 160, 160, True),
+                                               (2800, 24, 24, 112, 32, True)])
 def test_tail_items(T, Hq, Hkv, D, R, neox, dt):
-    """Launches long enough to end on one-group items (the last ceil(2048 /
-    groups per token) tokens): the launch report counts them, and every Q/K
-    element matches the oracle."""
+    """Launches long enough to end on items of half as many head groups (the
+    last ceil(2048 / such items per token) tokens): the launch report counts
+    them, and every Q/K element matches the oracle."""
     cfg = W.case(T, Hq, Hkv, D, R, neox, dtype=dt, pos_dtype=W.I64, seed=T + D + R)
     wl = W.make_workload(cfg)
     _say("case tail items", cfg.name)
     info = Hn.DeviceCase(wl).run(launch={})
     ng, gpi = info["groups_per_token"], info["groups_per_item"]
-    tail = -(-2048 // ng)
-    assert T >= 8 * tail and info["items"] == (T - tail) * -(-ng // gpi) + tail * ng, info
+    tnc = -(-ng // (gpi // 2))
+    tail = -(-2048 // tnc)
+    assert T >= 8 * tail and info["items"] == (T - tail) * -(-ng // gpi) + tail * tnc, info
     Hn.run_and_check(wl)
