@@ -213,6 +213,17 @@ constexpr int kLongItemBlockWaves = 2;
 // element-granular kernel: heads per work item, in units of the heads it loads
 // before computing the first (16 / slots)
 constexpr int kDefaultElemRounds = 2;
+// Element-granular instances that keep at most this many waves resident per
+// SIMD (their register count decides it) are launched as a persistent grid
+// (every wave loops over items) unless max_blocks is given: at the same bytes
+// per launch that measured +4 to +20% on head_dim 40/38, 128/26, 72/70,
+// 200/98, 66 NeoX and 130 interleaved (5 or 4 waves per SIMD; the LayerNorm
+// sibling +10 to +12%), where a wave that ends leaves its slot idle while the
+// next is launched and fetches its first loads. Instances holding 6 or 7 waves
+// (head_dim 100, 50) lost 1-16% with it: their last round of items runs with
+// part of the grid idle, which costs more than relaunches they already hide.
+constexpr int kElemPersistentWaves = 5;
+constexpr int kSimdsPerCu = 4;
 // Work items per launch stay below 2^30 so a wave's item index plus the grid's
 // wave count never overflows 32 bits.
 constexpr int64_t kMaxItems = int64_t{1} << 30;
@@ -627,7 +638,9 @@ int32_t launch(const Call& c, const Plan& pl, qknr_launch_info* info) {
   const int64_t needed = (pl.items + pl.wpb - 1) / pl.wpb;
   int64_t cap = needed;
   if (pl.max_blocks > 0) cap = pl.max_blocks;
-  if (pl.max_blocks == -1) cap = static_cast<int64_t>(cus) * per_cu;
+  if (pl.max_blocks == -1 ||
+      (pl.elem && pl.max_blocks == 0 && per_cu * pl.wpb <= kElemPersistentWaves * kSimdsPerCu))
+    cap = static_cast<int64_t>(cus) * per_cu;
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min(needed, cap)));
   if (info) info->grid_blocks = grid;
 

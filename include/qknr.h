@@ -165,8 +165,10 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
  *                    for long items; else 4, also on the element-granular
  *                    kernel]
  *   max_blocks       0: one workgroup per block_waves work items, each wave
- *                    handles one item [default]; -1: a persistent grid of
- *                    (occupancy x CUs) workgroups striding over the items;
+ *                    handles one item [default; on the element-granular
+ *                    kernel, instances that keep at most 5 waves per SIMD
+ *                    resident take the persistent grid]; -1: a persistent grid
+ *                    of (occupancy x CUs) workgroups striding over the items;
  *                    > 0: at most that many workgroups, striding.
  *   generic          1: take the element-granular kernel even where the
  *                    vectorised one applies (lanes_per_head must then be 0);
