@@ -217,12 +217,14 @@ constexpr int kDefaultElemRounds = 2;
 // SIMD (their register count decides it) are launched as a persistent grid
 // (every wave loops over items) unless max_blocks is given: at the same bytes
 // per launch that measured +4 to +20% on head_dim 40/38, 128/26, 72/70,
-// 200/98, 66 NeoX and 130 interleaved (5 or 4 waves per SIMD; the LayerNorm
-// sibling +10 to +12%), where a wave that ends leaves its slot idle while the
-// next is launched and fetches its first loads. Instances holding 6 or 7 waves
+// 200/98, 66 NeoX and 130 interleaved (4 to 6 waves per SIMD; the LayerNorm
+// sibling +10 to +26%), where a wave that ends leaves its slot idle while the
+// next is launched and fetches its first loads. Instances holding 7 waves
 // (head_dim 100, 50) lost 1-16% with it: their last round of items runs with
 // part of the grid idle, which costs more than relaunches they already hide.
-constexpr int kElemPersistentWaves = 5;
+// One exception measured: interleaved 16-byte runs of head_dim 128 (the
+// vectorised kernel's shape, taken here only when forced) lose 13%.
+constexpr int kElemPersistentWaves = 6;
 constexpr int kSimdsPerCu = 4;
 // Work items per launch stay below 2^30 so a wave's item index plus the grid's
 // wave count never overflows 32 bits.
@@ -486,9 +488,9 @@ int32_t make_elem_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, 
   pl->max_blocks = c.max_blocks;
   // per wave: a row of 64 lanes x E floats (partners through LDS: NeoX, or
   // interleaved with single-element runs) and, with a rotation, room for one
-  // cos|sin row (the kernel's layout; the exchange row is reserved in every
-  // rotating instance)
-  pl->lds = static_cast<size_t>(pl->wpb) * (kWave * pl->E + (rotates(mode) ? kElemMaxDim : 0)) *
+  // cos|sin row plus a pad holding -0.0f and a discard area (the kernel's
+  // layout; the exchange row is reserved in every instance)
+  pl->lds = static_cast<size_t>(pl->wpb) * (kWave * pl->E + (rotates(mode) ? kElemMaxDim + kElemRowPad : 0)) *
             sizeof(float);
   pl->fn = pick_elem_kernel(dtype, mode, sh.S, sh.pw);
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;

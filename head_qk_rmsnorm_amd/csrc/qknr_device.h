@@ -733,17 +733,24 @@ qknr_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __restrict
 // L is a power of two (sum over the head's lanes by DPP steps) or, when that
 // fits more heads into a wave instruction, head_dim/(S*PW) rounded up (exact
 // fit: a ds_bpermute tree toward the head's first lane plus a broadcast); the
-// lanes past the last head of a group and the elements past head_dim are
-// masked. Interleaved partners (e, e ^ 1) lie in one run when PW >= 2; NeoX
-// partners (e, e +- R/2), and interleaved ones when PW = 1, can sit in any lane
-// and slot, so the normalised values of a group go through a per-wave LDS row
-// (G heads x L*S*PW floats, head-major) and each element reads its partner.
+// lanes past the last head of a group and the elements past head_dim take lane
+// offsets outside their descriptor's range (loads read zeros, stores are
+// dropped), so no access is guarded by a branch. Interleaved partners
+// (e, e ^ 1) lie in one run when PW >= 2; NeoX partners (e, e +- R/2), and
+// interleaved ones when PW = 1, can sit in any lane and slot, so the
+// normalised values of a group go through a per-wave LDS row (G heads x
+// L*S*PW floats, head-major) and each element reads its partner.
 // A work item is a run of head groups of one token; 16/(S*PW) groups are
 // loaded before the first is computed, so every instance keeps 16 elements per
 // lane in flight whatever its head_dim.
 // ----------------------------------------------------------------------------
 constexpr int kElemPerLane = 8;            // S * PW at most
 constexpr int kElemMaxDim = 512;
+constexpr int kElemRowPad = 12;            // LDS floats per wave after the cos|sin row
+// Lane offsets at or past this value lie outside every descriptor's range (the
+// host keeps real offsets below 2^31): such loads return zeros without touching
+// memory and such stores are dropped.
+constexpr uint32_t kElemOob = 0x80000000u;
 
 struct ElemParams {
   int64_t q_tok, k_tok;          // token strides (bytes)
@@ -830,26 +837,6 @@ __device__ __forceinline__ void store_run(__amdgpu_buffer_rsrc_t rs, uint32_t of
   }
 }
 
-// PW elements of a weight or bias row starting at element e (e a multiple of
-// PW, the row 2*PW-byte aligned)
-template <int PW>
-__device__ __forceinline__ Run<PW> load_row_run(const void* row, int e) {
-  const char* const p = static_cast<const char*>(row) + 2 * e;
-  Run<PW> r;
-  if constexpr (PW == 8) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
-    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
-  } else if constexpr (PW == 4) {
-    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
-    r.w[0] = v.x; r.w[1] = v.y;
-  } else if constexpr (PW == 2) {
-    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else {
-    r.w[0] = *reinterpret_cast<const uint16_t*>(p);
-  }
-  return r;
-}
-
 // Sum over aligned groups of L lanes, L a power of two chosen at run time
 // (wave-uniform): the steps of group_sum<L> taken while they stay inside a
 // group. Every lane of a group gets the same bits.
@@ -890,8 +877,12 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
   // there: +29%); 8-byte stores keep the streaming policy (default: -5%)
   constexpr int kElemStorePolicy = PW <= 2 ? 0 : kStorePolicy;
   // per wave: the partner-exchange row (kWave * NE floats) and, with a
-  // rotation, the token's cos|sin row (kElemMaxDim floats)
+  // rotation, the token's cos|sin row (kElemMaxDim floats) and kElemRowPad
+  // floats: -0.0f, then a discard area for the runs that hold no element
   extern __shared__ float elem_rows[];
+  constexpr int kRowFloats = kWave * NE + (kRotate ? kElemMaxDim + kElemRowPad : 0);
+  constexpr int kNegZero = kWave * NE + kElemMaxDim;  // indices into the wave's row
+  constexpr int kDiscard = kNegZero + 4;
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
@@ -900,77 +891,73 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
   const int li = lane - sub * L;  // lane inside the head
   const bool in_grp = sub < G;
   const int D = p.D, R = p.R, half = R / 2;
-  const int span = L * PW;        // elements of one head per slot
   const bool neox = p.neox != 0;  // wave-uniform
   // partners through LDS: NeoX pairing, or interleaved pairs split over lanes
   const bool exch = kRotate && (neox || PW == 1);
-  constexpr int kRowFloats = kWave * NE + (kRotate ? kElemMaxDim : 0);
   float* const xrow = elem_rows + wib * kRowFloats;
   float* const csrow = xrow + kWave * NE;
   const int head0 = sub * (L * NE);  // this head's first element in the row
-  const uint32_t q_off = static_cast<uint32_t>(sub) * p.q_head + 2 * li * PW;
-  const uint32_t k_off = static_cast<uint32_t>(sub) * p.k_head + 2 * li * PW;
 
-  // run s of this lane: elements e0[s] .. e0[s] + PW - 1, all in the head or
-  // none (head_dim is a multiple of PW)
+  // Run s of this lane: elements e0[s] .. e0[s] + PW - 1, all in the head or
+  // none (head_dim is a multiple of PW). A run outside the head, or in a lane
+  // past the group's last head slot, takes a lane offset outside every
+  // descriptor's range: its loads return zeros and its stores are dropped, so
+  // no access needs a branch. Its normalised values go to the discard area of
+  // the row.
   int e0[S];
-  bool run_ok[S];
+  uint32_t qo[S], ko[S];
+  int widx[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     e0[s] = (s * L + li) * PW;
-    run_ok[s] = in_grp && e0[s] < D;
+    const bool ok = in_grp && e0[s] < D;
+    qo[s] = ok ? static_cast<uint32_t>(sub) * p.q_head + 2u * static_cast<uint32_t>(e0[s]) : kElemOob;
+    ko[s] = ok ? static_cast<uint32_t>(sub) * p.k_head + 2u * static_cast<uint32_t>(e0[s]) : kElemOob;
+    widx[s] = ok ? head0 + e0[s] : kDiscard;
   }
-
-  // rotation roles of this lane's elements (index s*PW + i): cos/sin column,
-  // partner element, partner term subtracted
-  int col[NE], partner[NE];
-  bool rot[NE], neg[NE];
+  // where each element reads its partner in the row: the partner's slot for a
+  // rotated element, else the -0.0f slot (with cos 1 and sin +0 the rotation
+  // then returns the normalised value itself, signed zeros and non-finite
+  // values included)
+  int pidx[NE];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-      const int j = s * PW + i;
       const int e = e0[s] + i;
-      rot[j] = kRotate && run_ok[s] && e < R;
-      if (neox) {
-        const bool lower = e < half;
-        col[j] = lower ? e : e - half;
-        partner[j] = lower ? e + half : e - half;
-        neg[j] = lower;
-      } else {
-        col[j] = e >> 1;
-        partner[j] = e ^ 1;
-        neg[j] = (e & 1) == 0;
-      }
-      if (!rot[j]) {
-        col[j] = 0;
-        partner[j] = e0[s] + i;
-      }
+      const bool rot = kRotate && in_grp && e < R;
+      const int pe = neox ? (e < half ? e + half : e - half) : (e ^ 1);
+      pidx[s * PW + i] = rot ? head0 + pe : kNegZero;
     }
+  }
+  if constexpr (kRotate) {
+    if (lane == 0) xrow[kNegZero] = -0.0f;  // ordered before its reads by the fences below
   }
 
   auto head_sum = [&](float v) { return p.seg ? seg_sum(v, lane, li, L) : group_sum_rt(v, L); };
 
   // weights and biases of this lane's runs, kept packed; loaded once, after
-  // the first head loads are in flight
+  // the first head loads are in flight, through descriptors whose range is
+  // the row (no bias: an empty range), so runs past head_dim read zeros
   Run<PW> wq[S], wk[S], bq[S], bk[S];
   bool have_w = false;
   auto load_weights = [&]() {
+    const uint32_t wrec = static_cast<uint32_t>(2 * D);
+    const uint32_t brec = p.has_bias ? wrec : 0u;
+    const __amdgpu_buffer_rsrc_t rwq = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(wqp), 0, wrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rwk = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(wkp), 0, wrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rbq = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(bqp), 0, brec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rbk = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(bkp), 0, brec, kBufferFlags);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-#pragma unroll
-      for (int w = 0; w < Run<PW>::NW; ++w) wq[s].w[w] = wk[s].w[w] = bq[s].w[w] = bk[s].w[w] = 0u;
+      const uint32_t wo = 2u * static_cast<uint32_t>(e0[s]);
       if constexpr (kRms || kLayer) {
-        if (run_ok[s]) {
-          wq[s] = load_row_run<PW>(wqp, e0[s]);
-          wk[s] = load_row_run<PW>(wkp, e0[s]);
-        }
+        wq[s] = load_run<PW, 0>(rwq, wo);
+        wk[s] = load_run<PW, 0>(rwk, wo);
       }
       if constexpr (kLayer) {
-        if (run_ok[s] && p.has_bias) {
-          bq[s] = load_row_run<PW>(bqp, e0[s]);
-          bk[s] = load_row_run<PW>(bkp, e0[s]);
-        }
+        bq[s] = load_run<PW, 0>(rbq, wo);
+        bk[s] = load_run<PW, 0>(rbk, wo);
       }
     }
   };
@@ -985,27 +972,24 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
 
     Run<PW> raw[U][S];
     __amdgpu_buffer_rsrc_t rs[U];
-    uint32_t off[U];
-    bool ok[U], isk[U];
+    bool isk[U];
+    // a group's descriptor spans its heads that exist (the last group of Q or
+    // K may hold fewer than G): lanes of the missing heads fall outside it
     auto issue = [&](int g) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int gu = g + u;
         isk[u] = gu >= p.ngq;  // wave-uniform
+        if (gu >= g_end) continue;
         const int gg = isk[u] ? gu - p.ngq : gu;
+        const int nvalid = min(G, (isk[u] ? p.Hkv : p.Hq) - gg * G);
+        const uint32_t rec = static_cast<uint32_t>(nvalid - 1) * (isk[u] ? p.k_head : p.q_head) +
+                             static_cast<uint32_t>(2 * D);
         rs[u] = __builtin_amdgcn_make_buffer_rsrc(isk[u] ? krow + gg * p.k_grp : qrow + gg * p.q_grp,
-                                                  0, 0x7FFFFFFF, kBufferFlags);
-        off[u] = isk[u] ? k_off : q_off;
-        ok[u] = gu < g_end && gg * G + sub < (isk[u] ? p.Hkv : p.Hq);
+                                                  0, rec, kBufferFlags);
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-          if (ok[u] && run_ok[s]) {
-            raw[u][s] = load_run<PW, kElemLoadPolicy>(rs[u], off[u] + 2 * s * span);
-          } else {
-#pragma unroll
-            for (int w = 0; w < Run<PW>::NW; ++w) raw[u][s].w[w] = 0u;
-          }
-        }
+        for (int s = 0; s < S; ++s)
+          raw[u][s] = load_run<PW, kElemLoadPolicy>(rs[u], isk[u] ? ko[s] : qo[s]);
       }
     };
     issue(g_begin);
@@ -1015,8 +999,8 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
       have_w = true;
     }
 
-    // cos / sin of this lane's elements at this token; the sign of the
-    // partner term folded into sin
+    // cos / sin of this lane's elements at this token, the sign of the
+    // partner term folded into sin; cos 1 and sin +0 where nothing rotates
     float cs[NE], sn[NE];
 #pragma unroll
     for (int j = 0; j < NE; ++j) {
@@ -1026,7 +1010,8 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
     if constexpr (kRotate) {
       // the wave copies the token's row into LDS with coalesced 8-byte loads
       // (4-byte ones when the table is only 4-byte aligned), then each lane
-      // reads the columns of its own elements from there
+      // reads the columns of its own elements from there (column 0 where
+      // nothing rotates, so every read is in the row)
       const float* const crow = cache + token_position(posp, p.pos64, t) * R;
       wave_lds_fence();  // the previous item's reads of the row are done
       if (p.cs2) {
@@ -1037,11 +1022,18 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
       }
       wave_lds_fence();
 #pragma unroll
-      for (int j = 0; j < NE; ++j) {
-        if (rot[j]) {
-          cs[j] = csrow[col[j]];
-          const float v = csrow[half + col[j]];
-          sn[j] = neg[j] ? -v : v;
+      for (int s = 0; s < S; ++s) {
+#pragma unroll
+        for (int i = 0; i < PW; ++i) {
+          const int j = s * PW + i;
+          const int e = e0[s] + i;
+          const bool rot = in_grp && e < R;
+          const int col = rot ? (neox ? (e < half ? e : e - half) : e >> 1) : 0;
+          const bool neg = neox ? e < half : (e & 1) == 0;
+          const float c = csrow[col];
+          const float v = csrow[half + col];
+          cs[j] = rot ? c : 1.0f;
+          sn[j] = rot ? (neg ? -v : v) : 0.0f;
         }
       }
     }
@@ -1063,7 +1055,7 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
           float c[NE], ss = 0.0f;
 #pragma unroll
           for (int j = 0; j < NE; ++j) {
-            c[j] = run_ok[j / PW] ? x[j] - mean : 0.0f;
+            c[j] = e0[j / PW] < D ? x[j] - mean : 0.0f;  // runs past head_dim add nothing
             ss = fmaf(c[j], c[j], ss);
           }
           ss = head_sum(ss);
@@ -1103,43 +1095,45 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
             wave_lds_fence();  // the previous group's reads are done
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-              if (run_ok[s]) {
-                float* const dst = xrow + head0 + e0[s];
-                if constexpr (PW == 8) {
-                  *reinterpret_cast<float4*>(dst) = make_float4(n[s * PW], n[s * PW + 1], n[s * PW + 2], n[s * PW + 3]);
-                  *reinterpret_cast<float4*>(dst + 4) =
-                      make_float4(n[s * PW + 4], n[s * PW + 5], n[s * PW + 6], n[s * PW + 7]);
-                } else if constexpr (PW == 4) {
-                  *reinterpret_cast<float4*>(dst) = make_float4(n[s * PW], n[s * PW + 1], n[s * PW + 2], n[s * PW + 3]);
-                } else if constexpr (PW == 2) {
-                  *reinterpret_cast<float2*>(dst) = make_float2(n[s * PW], n[s * PW + 1]);
-                } else {
-                  *dst = n[s];
-                }
+              float* const dst = xrow + widx[s];
+              if constexpr (PW == 8) {
+                *reinterpret_cast<float4*>(dst) = make_float4(n[s * PW], n[s * PW + 1], n[s * PW + 2], n[s * PW + 3]);
+                *reinterpret_cast<float4*>(dst + 4) =
+                    make_float4(n[s * PW + 4], n[s * PW + 5], n[s * PW + 6], n[s * PW + 7]);
+              } else if constexpr (PW == 4) {
+                *reinterpret_cast<float4*>(dst) = make_float4(n[s * PW], n[s * PW + 1], n[s * PW + 2], n[s * PW + 3]);
+              } else if constexpr (PW == 2) {
+                *reinterpret_cast<float2*>(dst) = make_float2(n[s * PW], n[s * PW + 1]);
+              } else {
+                *dst = n[s];
               }
             }
             wave_lds_fence();
 #pragma unroll
-            for (int j = 0; j < NE; ++j) pn[j] = rot[j] ? xrow[head0 + partner[j]] : 0.0f;
+            for (int j = 0; j < NE; ++j) pn[j] = xrow[pidx[j]];
           } else {
             if constexpr (PW >= 2) {
+              // interleaved pairs inside a run (R even, runs start at even
+              // elements): element e rotates iff e < R
 #pragma unroll
-              for (int j = 0; j < NE; ++j) pn[j] = n[j ^ 1];
+              for (int s = 0; s < S; ++s) {
+#pragma unroll
+                for (int i = 0; i < PW; ++i) {
+                  const int j = s * PW + i;
+                  pn[j] = e0[s] < R - i ? n[j ^ 1] : -0.0f;
+                }
+              }
             } else {
 #pragma unroll
-              for (int j = 0; j < NE; ++j) pn[j] = 0.0f;  // PW = 1 always exchanges
+              for (int j = 0; j < NE; ++j) pn[j] = -0.0f;  // PW = 1 always exchanges
             }
           }
 #pragma unroll
-          for (int j = 0; j < NE; ++j)
-            if (rot[j]) o[j] = fmaf(n[j], cs[j], pn[j] * sn[j]);
+          for (int j = 0; j < NE; ++j) o[j] = fmaf(n[j], cs[j], pn[j] * sn[j]);
         }
-        if (ok[u]) {
 #pragma unroll
-          for (int s = 0; s < S; ++s) {
-            if (run_ok[s]) store_run<PW, kElemStorePolicy>(rs[u], off[u] + 2 * s * span, pack_run<IO, PW>(&o[s * PW]));
-          }
-        }
+        for (int s = 0; s < S; ++s)
+          store_run<PW, kElemStorePolicy>(rs[u], isk[u] ? ko[s] : qo[s], pack_run<IO, PW>(&o[s * PW]));
       }
     }
   }

@@ -166,7 +166,7 @@ QKNR_API int32_t qknr_inplace(void* q, void* k, const void* wq, const void* wk,
  *                    kernel]
  *   max_blocks       0: one workgroup per block_waves work items, each wave
  *                    handles one item [default; on the element-granular
- *                    kernel, instances that keep at most 5 waves per SIMD
+ *                    kernel, instances that keep at most 6 waves per SIMD
  *                    resident take the persistent grid]; -1: a persistent grid
  *                    of (occupancy x CUs) workgroups striding over the items;
  *                    > 0: at most that many workgroups, striding.
