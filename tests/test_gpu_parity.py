@@ -294,6 +294,59 @@ def test_special_values():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("generic", [0, 1])
+@pytest.mark.parametrize("neox", [True, False])
+def test_pass_through_signed_zeros_and_non_finite(neox, generic):
+    """Dims past rope_dim keep the normalised value bit for bit on both kernels:
+    signed zeros (an all-zero head with negative weights there, negative-zero
+    inputs) match the oracle exactly, and an infinite input there turns only
+    its own element into NaN (the sum of squares is infinite, so the scale is
+    0: every other element of that head is a signed zero) without reaching
+    its rotation partner slot or its neighbours."""
+    import torch
+
+    from oracle import qknr_oracle as O
+
+    D, R = 128, 64
+    T, Hq, Hkv = 3, 3, 2
+    cfg = W.case(T, Hq, Hkv, D, R, neox, seed=11)
+    wl = W.make_workload(cfg)
+    wl.q[0, 0] = 0                                   # all-zero head
+    wl.wq[R:] |= np.uint16(0x8000)                   # negative weights past rope_dim
+    wl.q[2, 2, R::3] = np.uint16(0x8000)             # negative zeros past rope_dim
+    launch = {"generic": 1} if generic else None
+    _say("case pass-through zeros", neox, generic)
+    Hn.run_and_check(wl, launch=launch)
+    dc = Hn.DeviceCase(wl)
+    dc.run(launch=launch)
+    gq, gk = dc.outputs(dc.fetch())
+    refq, refk = Hn.oracle_ref(wl)
+    assert np.array_equal(gq[0, 0], refq[0, 0])      # signed zeros bit for bit
+    assert np.all(gq[0, 0, R:] == 0x8000)            # +0 times a negative weight
+    assert np.array_equal(gq[2, 2, R::3], refq[2, 2, R::3])
+
+    # an infinite input past rope_dim (K head 1 of token 1)
+    inf_dim = R + 5
+    ref_q, ref_k = Hn.oracle_ref(wl)                 # every other head is independent of it
+    wl.k[1, 1, inf_dim] = np.uint16(0x7F80)
+    _say("case pass-through inf", neox, generic)
+    dc = Hn.DeviceCase(wl)
+    dc.run(launch=launch)
+    after = dc.fetch()
+    dc.check_untouched(after)
+    gq, gk = dc.outputs(after)
+    torch.cuda.synchronize()
+    head = O.decode_io(gk[1, 1], cfg.dtype)
+    assert np.isnan(head[inf_dim])
+    rest = np.delete(head, inf_dim)
+    assert np.all(rest == 0.0), rest[rest != 0.0]
+    mask = np.ones(gk.shape, dtype=bool)
+    mask[1, 1] = False
+    for name, g, r in (("q", gq, ref_q), ("k", gk[mask], ref_k[mask])):
+        cmp = Hn.compare_bits(g, r, cfg.dtype)
+        assert cmp.bad == 0 and cmp.exact_frac >= 0.99, f"{name}: {cmp}"
+
+
 def test_outlier_magnitudes_fp16():
     cfg = W.case(64, 4, 4, 256, 256, False, dtype=W.FP16, outlier_frac=0.05,
                  outlier_scale=50.0, seed=8)
