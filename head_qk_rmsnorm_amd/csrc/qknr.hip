@@ -222,8 +222,8 @@ constexpr int kDefaultElemRounds = 2;
 // next is launched and fetches its first loads. Instances holding 7 waves
 // (head_dim 100, 50) lost 1-16% with it: their last round of items runs with
 // part of the grid idle, which costs more than relaunches they already hide.
-// One exception measured: interleaved 16-byte runs of head_dim 128 (the
-// vectorised kernel's shape, taken here only when forced) lose 13%.
+// Forced onto this kernel, head_dim 64-256 with either pairing (5 waves) gain
+// 5-15% from it as well.
 constexpr int kElemPersistentWaves = 6;
 constexpr int kSimdsPerCu = 4;
 // Work items per launch stay below 2^30 so a wave's item index plus the grid's
