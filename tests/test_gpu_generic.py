@@ -148,6 +148,31 @@ def test_launch_variants(launch, D, R, neox):
         assert info["groups_per_item"] == min(launch["groups_per_item"], info["groups_per_token"])
 
 
+@pytest.mark.parametrize("D,R,neox,persistent", [(40, 38, True, True), (100, 100, True, None),
+                                                  (130, 130, False, None)])
+def test_grid_rule(D, R, neox, persistent):
+    """The automatic grid of the element-granular kernel: one work item per wave,
+    or (instances that keep few waves resident) a persistent grid of whole
+    rounds of workgroups over the CUs; an explicit max_blocks overrides it.
+    Every launch shape computes the same result."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    cfg = W.case(6000, 24, 24, D, R, neox, dtype=W.BF16, pos_dtype=W.I64, seed=D + R + 5)
+    wl = W.make_workload(cfg)
+    info, _, _ = _check(wl)
+    assert info["generic"] == 1
+    needed = -(-info["items"] // (info["block_threads"] // 64))
+    grid = info["grid_blocks"]
+    assert grid == needed or (grid < needed and grid % cus == 0), (info, cus)
+    if persistent is not None:
+        assert (grid < needed) == persistent, (info, cus)
+    one, _, _ = _check(wl, launch={"max_blocks": 1 << 30})
+    assert one["grid_blocks"] == needed, one
+    full, _, _ = _check(wl, launch={"max_blocks": -1})
+    assert full["grid_blocks"] % cus == 0 and full["grid_blocks"] <= needed, full
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(0, 4), (4, 0), (1, 1), (1, 0), (31, 1), (3, 13)])
 def test_head_counts(Hq, Hkv):
     cfg = W.case(23, Hq, Hkv, 100, 98, True, dtype=W.FP16, pos_dtype=W.I32, seed=Hq * 17 + Hkv)
