@@ -490,8 +490,11 @@ int32_t make_elem_plan(int mode, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, 
   // interleaved with single-element runs) and, with a rotation, room for one
   // cos|sin row plus a pad holding -0.0f and a discard area (the kernel's
   // layout; the exchange row is reserved in every instance)
-  pl->lds = static_cast<size_t>(pl->wpb) * (kWave * pl->E + (rotates(mode) ? kElemMaxDim + kElemRowPad : 0)) *
-            sizeof(float);
+  // (the LayerNorm sibling's 16-byte instances add a cos / sin pair per element
+  // of a head: 2 * head_dim floats rounded up to 4)
+  const int pairs = mode == kLayerRope && sh.pw == 8 ? (2 * D + 3) & ~3 : 0;
+  pl->lds = static_cast<size_t>(pl->wpb) *
+            (kWave * pl->E + (rotates(mode) ? kElemMaxDim + kElemRowPad : 0) + pairs) * sizeof(float);
   pl->fn = pick_elem_kernel(dtype, mode, sh.S, sh.pw);
   return pl->fn ? QKNR_OK : QKNR_E_UNSUPPORTED;
 }

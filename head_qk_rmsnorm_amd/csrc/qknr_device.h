@@ -876,13 +876,23 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
   // 4-byte stores of head_dim 130 wrote 1.43x the stored bytes (default policy
   // there: +29%); 8-byte stores keep the streaming policy (default: -5%)
   constexpr int kElemStorePolicy = PW <= 2 ? 0 : kStorePolicy;
+  // The LayerNorm sibling's 16-byte instances lay the token's cos and signed
+  // sin out once per item as a pair per element of a head, read back as
+  // vectors: no per-element column, sign or rotation flag is kept across the
+  // item loop, where that instance is short of scalar registers (+7 to +9% at
+  // head_dim 40/38, 128/26, 72/70 and 200/98; the fused op's instances and the
+  // narrower ones lost 1-9% with it).
+  constexpr bool kPairs = MODE == kLayerRope && PW == 8;
   // per wave: the partner-exchange row (kWave * NE floats) and, with a
   // rotation, the token's cos|sin row (kElemMaxDim floats) and kElemRowPad
-  // floats: -0.0f, then a discard area for the runs that hold no element
+  // floats: -0.0f, then a discard area for the runs that hold no element;
+  // with kPairs then the pairs (2 * head_dim floats, rounded up to 4)
   extern __shared__ float elem_rows[];
-  constexpr int kRowFloats = kWave * NE + (kRotate ? kElemMaxDim + kElemRowPad : 0);
   constexpr int kNegZero = kWave * NE + kElemMaxDim;  // indices into the wave's row
   constexpr int kDiscard = kNegZero + 4;
+  constexpr int kPairRow = kNegZero + kElemRowPad;
+  const int row_floats = kWave * NE + (kRotate ? kElemMaxDim + kElemRowPad : 0) +
+                         (kPairs ? (2 * p.D + 3) & ~3 : 0);
   const int lane = threadIdx.x & (kWave - 1);
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
@@ -894,7 +904,7 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
   const bool neox = p.neox != 0;  // wave-uniform
   // partners through LDS: NeoX pairing, or interleaved pairs split over lanes
   const bool exch = kRotate && (neox || PW == 1);
-  float* const xrow = elem_rows + wib * kRowFloats;
+  float* const xrow = elem_rows + wib * row_floats;
   float* const csrow = xrow + kWave * NE;
   const int head0 = sub * (L * NE);  // this head's first element in the row
 
@@ -1021,19 +1031,46 @@ qknr_elem_kernel(char* __restrict__ qb, char* __restrict__ kb, const void* __res
         for (int c = lane; c < R; c += kWave) csrow[c] = crow[c];
       }
       wave_lds_fence();
+      if constexpr (kPairs) {
+        // pair e: (cos, -sin) for the first element of a rotation pair,
+        // (cos, +sin) for the second, (1, +0) past rope_dim
+        float* const prow = xrow + kPairRow;
+        for (int e = lane; e < D; e += kWave) {
+          float c = 1.0f, v = 0.0f;
+          if (e < R) {
+            const int col = neox ? (e < half ? e : e - half) : e >> 1;
+            c = csrow[col];
+            v = csrow[half + col];
+            if (neox ? e < half : (e & 1) == 0) v = -v;
+          }
+          *reinterpret_cast<float2*>(prow + 2 * e) = make_float2(c, v);
+        }
+        wave_lds_fence();
+        // runs past head_dim (and lanes past the last head) read pair 0
+        const float* const src = prow + (in_grp && e0[0] < D ? 2 * e0[0] : 0);
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
+        for (int i = 0; i < PW; i += 2) {
+          const float4 v = *reinterpret_cast<const float4*>(src + 2 * i);
+          cs[i] = v.x;
+          sn[i] = v.y;
+          cs[i + 1] = v.z;
+          sn[i + 1] = v.w;
+        }
+      } else {
 #pragma unroll
-        for (int i = 0; i < PW; ++i) {
-          const int j = s * PW + i;
-          const int e = e0[s] + i;
-          const bool rot = in_grp && e < R;
-          const int col = rot ? (neox ? (e < half ? e : e - half) : e >> 1) : 0;
-          const bool neg = neox ? e < half : (e & 1) == 0;
-          const float c = csrow[col];
-          const float v = csrow[half + col];
-          cs[j] = rot ? c : 1.0f;
-          sn[j] = rot ? (neg ? -v : v) : 0.0f;
+        for (int s = 0; s < S; ++s) {
+#pragma unroll
+          for (int i = 0; i < PW; ++i) {
+            const int j = s * PW + i;
+            const int e = e0[s] + i;
+            const bool rot = in_grp && e < R;
+            const int col = rot ? (neox ? (e < half ? e : e - half) : e >> 1) : 0;
+            const bool neg = neox ? e < half : (e & 1) == 0;
+            const float c = csrow[col];
+            const float v = csrow[half + col];
+            cs[j] = rot ? c : 1.0f;
+            sn[j] = rot ? (neg ? -v : v) : 0.0f;
+          }
         }
       }
     }
