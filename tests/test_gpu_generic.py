@@ -242,6 +242,27 @@ def test_layernorm_sibling(D, R, neox, bias, layout):
     Hn.layernorm_check(wl, R, bias, layout=layout)
 
 
+@pytest.mark.parametrize("D,R,neox,bias", [
+    (40, 38, True, True), (128, 26, True, False), (72, 70, True, True), (200, 98, True, False),
+    (128, 64, False, True), (256, 256, True, True), (64, 8, True, False)])
+def test_layernorm_sixteen_byte_runs(D, R, neox, bias):
+    """The LayerNorm sibling on the element-granular kernel's 16-byte instance,
+    which lays the token's cos and signed sin out per element in LDS: odd NeoX
+    halves, partial rotations, shapes forced off the vectorised kernel, with
+    and without bias; once with the automatic grid and once with 8 workgroups,
+    so that every wave rebuilds the pairs for many tokens in turn."""
+    cfg = W.case(300, 7, 3, D, R, neox, dtype=W.BF16, pos_dtype=W.I64, seed=D + R + 23,
+                 x_std=2.0)
+    wl = W.make_workload(cfg)
+    from oracle import qknr_oracle as O
+
+    wl.q[...] = O.round_to_io_bits(O.decode_io(wl.q, W.BF16) + 0.75, W.BF16)
+    print("case layernorm 16-byte", cfg.name, bias, flush=True)
+    for launch in ({"generic": 1}, {"generic": 1, "max_blocks": 8}):
+        info = Hn.layernorm_check(wl, R, bias, launch=launch)
+        assert info["generic"] == 1 and info["access_bytes"] == 16, info
+
+
 @pytest.mark.parametrize("D,R,neox,launch,want", [
     (128, 128, True, None, dict(lanes_per_head=64, generic=0)),   # one head per group
     (128, 64, False, None, dict(lanes_per_head=64, generic=0)),
