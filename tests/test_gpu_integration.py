@@ -75,14 +75,18 @@ def test_plain_c_caller(cfg):
             assert cmp.bad == 0 and cmp.exact_frac >= 0.99, (base, cmp)
 
 
-def test_hip_graph_capture_and_replay():
+@pytest.mark.parametrize("T,Hq,Hkv,D,R,neox", [
+    (129, 8, 4, 128, 64, True),      # vectorised kernel
+    (200, 8, 4, 80, 20, True),       # shifted partners through LDS
+    (3000, 24, 24, 40, 38, True)])   # element-granular kernel, persistent grid
+def test_hip_graph_capture_and_replay(T, Hq, Hkv, D, R, neox):
     """The op allocates nothing and never synchronises, so it can be captured
     in a HIP graph. Each replay applies it again in place: after n replays
     the tensors equal n eager applications, bit for bit, on every replay."""
     import torch
     from head_qk_rmsnorm_amd import binding as B
 
-    cfg = W.case(129, 8, 4, 128, 64, True, seed=12)
+    cfg = W.case(T, Hq, Hkv, D, R, neox, seed=12 + D)
     wl = W.make_workload(cfg)
     g_case = Hn.DeviceCase(wl)
     e_case = Hn.DeviceCase(wl)
